@@ -1,0 +1,185 @@
+"""Benchmark of the speculative-decoding verification step on one MI355X.
+
+One step = the whole hot path over one batch: the scoring GEMM over the
+gamma+1 positions of every sequence (one pass over the LM-head weights) and
+the rejection-sampling kernels.  Inputs are synthetic, seeded, and resident in
+HBM before timing starts.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published peak
+METRIC = "verified positions/sec and achieved HBM GB/s (% of peak) per verify step"
+
+
+def algorithmic_bytes(w):
+    """Bytes the step must move at minimum: W and X read once, fp32 logits written once and read once by the
+    statistics pass, draft logits read once, and the one (target, draft) row pair where each sequence ends
+    read again by the draw."""
+    N = w.B * (w.gamma + 1)
+    gemm = w.V * w.d * 2 + N * w.d * 2 + N * w.V * 4
+    if w.temperature == 0.0:
+        reject = N * w.V * 4
+    else:
+        reject = N * w.V * 4 + w.B * w.gamma * w.V * 4 + w.B * w.V * 8
+    return gemm, gemm + reject
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="lmhead_b1_g4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-steps", type=int, default=3, help="oracle steps timed for the CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import speculative_decoding_verification_09_amd as sd
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    w = synth.WORKLOADS[args.workload]
+    if w.d == 0:
+        print(f"workload {w.name} has no scoring GEMM; pick an LM-head workload", file=sys.stderr)
+        sys.exit(2)
+    B, g, V, d, T = w.B, w.gamma, w.V, w.d, w.temperature
+    N = B * (g + 1)
+    dev = torch.device("cuda")
+
+    # ---- inputs (untimed): hidden states and weights from the seeded generator
+    Xb, Wb = synth.lm_head_inputs(w)
+    X = torch.from_numpy(Xb.view(np.int16)).to(dev).view(torch.bfloat16)
+    W = torch.from_numpy(Wb.view(np.int16)).to(dev).view(torch.bfloat16)
+    del Xb, Wb
+    logits = torch.empty((N, V), dtype=torch.float32, device=dev)
+    out_tok = torch.empty((B, g + 1), dtype=torch.int32, device=dev)
+    out_num = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws = sd.new_workspace(B, g, V)
+    uni = torch.from_numpy(synth.step_uniforms(w)).to(dev)
+    # Draft logits = target logits + N(0, noise) and drafted tokens ~ q: built with the library itself
+    # (one scoring pass, then one draw per drafted row as gamma = 0 steps), outside the timed region.
+    sd.specdec_verify_logits(X, W, logits)
+    if T > 0:
+        tl = logits.view(B, g + 1, V)[:, :g]
+        noise = torch.from_numpy(synth.normal_f32((B, g, V), w.noise_std, w.seed, synth.STREAM_DRAFT_NOISE)).to(dev)
+        draft = (tl + noise).contiguous()
+        du = torch.zeros((B * g, 1, 2), dtype=torch.float32, device=dev)
+        du[:, 0, 1] = torch.from_numpy(synth.draft_sample_uniforms(w).reshape(-1)).to(dev)
+        dt = torch.empty((B * g, 1), dtype=torch.int32, device=dev)
+        dn = torch.empty((B * g,), dtype=torch.int32, device=dev)
+        dws = sd.new_workspace(B * g, 0, V)
+        sd.specdec_reject_sample(draft.view(B * g, 1, V), None, torch.empty((B * g, 0), dtype=torch.int32, device=dev),
+                                 T, du, dt, dn, dws)
+        tokens = dt.view(B, g).contiguous()
+        del noise, dws
+    else:
+        draft = None
+        am = logits.view(B, g + 1, V)[:, :g].argmax(dim=2).to(torch.int32)
+        rep = torch.from_numpy(synth.bernoulli((B, g), w.replace_prob, w.seed, synth.STREAM_REPLACE)).to(dev)
+        rnd = torch.from_numpy(synth.integers((B, g), 0, V, w.seed, synth.STREAM_REPLACE + 10)).to(dev)
+        tokens = torch.where(rep, rnd, am).contiguous()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(mid_event=None):
+        sd.specdec_verify_logits(X, W, logits, stream=stream)
+        if mid_event is not None:
+            mid_event.record(stream)
+        sd.specdec_reject_sample(logits.view(B, g + 1, V), draft, tokens, T, uni if T > 0 else None, out_tok,
+                                 out_num, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps; events before each step and after its GEMM, on the launch stream
+    K = args.steps
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    evm = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    evs = torch.cuda.Event(enable_timing=True)
+    eve = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    evs.record(stream)
+    for i in range(K):
+        ev0[i].record(stream)
+        step(evm[i])
+    eve.record(stream)
+    torch.cuda.synchronize()
+    total_ms = evs.elapsed_time(eve)
+    ms_step = total_ms / K
+    gemm_ms = float(np.mean([ev0[i].elapsed_time(evm[i]) for i in range(K)]))
+    emitted = int(out_num.sum().item())
+
+    gemm_bytes, step_bytes = algorithmic_bytes(w)
+    gemm_gbps = gemm_bytes / (gemm_ms * 1e-3) / 1e9
+    step_gbps = step_bytes / (ms_step * 1e-3) / 1e9
+    positions_per_s = N / (ms_step * 1e-3)
+
+    # ---- CPU baseline: the oracle as it stands, single-threaded, on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        orc = oracle.load()
+        Xh, Wh = synth.lm_head_inputs(w)
+        rows_per_seq = g + 1
+        seqs = min(B, max(1, args.cpu_steps))
+        uh = synth.step_uniforms(w)
+        toks = tokens.cpu().numpy()
+        dr = draft.cpu().numpy() if draft is not None else None
+        t0 = time.perf_counter()
+        for b in range(seqs):
+            zb = orc.linear(Xh[b * rows_per_seq:(b + 1) * rows_per_seq], Wh).astype(np.float32)
+            orc.verify(zb[None], dr[b:b + 1] if dr is not None else None, toks[b:b + 1], uh[b:b + 1], T)
+        cpu_s = time.perf_counter() - t0
+        # B == 1: each sample is one full step; otherwise one sequence (gamma+1 positions) of a step.
+        cpu = {"value": seqs * rows_per_seq / cpu_s, "unit": "positions/s", "cores": 1, "kind": "oracle",
+               "sample": f"{seqs} sequence(s) of {rows_per_seq} positions: fp64 scoring over the full "
+                         f"{V}x{d} weights plus the rule, single-threaded C ({cpu_s:.1f} s)"}
+
+    out = {
+        "metric": METRIC,
+        "value": positions_per_s,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "gamma": g, "d": d, "V": V, "N": N, "temperature": T,
+                   "draft_noise_std": w.noise_std},
+        "step_hbm_gbps": step_gbps,
+        "step_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
+        "step_bytes": step_bytes,
+        "emitted_tokens_per_s": emitted / (ms_step * 1e-3),
+        "roofline": {"kernel": "skinny_gemm_kernel", "bound": "hbm", "achieved": gemm_gbps, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": gemm_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "bytes_per_launch": gemm_bytes, "avg_launch_ms": gemm_ms},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

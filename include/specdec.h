@@ -1,0 +1,148 @@
+/*
+ * specdec.h -- C ABI of the speculative-decoding verification step on MI355X (gfx950).
+ *
+ * The verification step scores the gamma+1 positions of every sequence in one
+ * pass over the LM-head weights, then runs the modified rejection sampling
+ * rule on the target and draft distributions.  Sources, cited by title and
+ * section (four web articles):
+ *   [LLMI] "LLM Inference & Speculative Decoding: From Roofline Physics to
+ *          Lossless Acceleration" (arman1o1.github.io)
+ *   [MATH] "Speculative Decoding: Mathematical Foundations, Distribution
+ *          Preservation Proofs, Tree-Structured Verification, and
+ *          Memory-Bandwidth Amortization" (llms.blog)
+ *   [LESS] "Speculative decoding." lesson (gtadkapally.com, learn-cs)
+ *   [PREP] "Speculative Decoding: Draft, Verify, Accept" (vanos001.github.io)
+ *
+ * Conventions for every entry point
+ *   - Pointers named as device buffers are device memory owned by the caller;
+ *     the library never allocates, frees, or synchronises.  Work is enqueued
+ *     on `stream` (a hipStream_t; NULL is the null stream) and the call
+ *     returns at once.  Kernel faults surface at the caller's next stream
+ *     synchronisation.
+ *   - Sizes are element counts.  Arrays are dense and row-major.
+ *   - Invalid arguments are reported by the return value (a specdec_status)
+ *     before anything is launched: null required pointer, bad size, pointer
+ *     not 16-byte aligned where 128-bit accesses need it, temperature < 0 or
+ *     NaN, workspace too small.  Token ids in device buffers cannot be
+ *     checked from the host: ids outside [0, V) are clamped into range by the
+ *     kernels, never used to index out of bounds.
+ *   - The library keeps no state between calls and may be called from several
+ *     host threads; calls on different streams must use different outputs and
+ *     workspaces.
+ *   - Numeric degenerate cases are defined behaviour, not errors: q(x) is
+ *     floored at 1e-12 before dividing ([LLMI] section 2 listing); a residual
+ *     with no mass falls back to p ([PREP] demo); T == 0 selects the greedy
+ *     rule ([LLMI] section 4, failure mode 1).
+ */
+#ifndef SPECDEC_H
+#define SPECDEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPECDEC_OK = 0,
+  SPECDEC_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  SPECDEC_ERR_SHAPE = 2,       /* a size is out of range                            */
+  SPECDEC_ERR_ALIGN = 3,       /* a pointer or row pitch is not 16-byte aligned     */
+  SPECDEC_ERR_TEMPERATURE = 4, /* temperature < 0 or NaN                            */
+  SPECDEC_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required           */
+  SPECDEC_ERR_LAUNCH = 6,      /* the HIP runtime refused a launch                  */
+  SPECDEC_ERR_ARG = 7          /* an enumerated argument has an unknown value       */
+} specdec_status;
+
+/* How the draft distribution is given. */
+#define SPECDEC_DRAFT_LOGITS 0 /* q = softmax(draft / T), formed on the device      */
+#define SPECDEC_DRAFT_PROBS 1  /* q used as given (one-hot, lookup or any vector)   */
+
+/* Element type of the scores written by specdec_verify_logits. */
+#define SPECDEC_OUT_F32 0
+#define SPECDEC_OUT_BF16 1
+
+/* Largest number of drafted tokens per sequence. */
+#define SPECDEC_MAX_GAMMA 63
+
+/* Human-readable name of a status code; never NULL. */
+const char* specdec_status_string(int status);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int specdec_version(void);
+
+/* Bytes of device workspace that specdec_reject_sample and specdec_verify_step
+ * need for B sequences of gamma drafts over a vocabulary of V entries.  The
+ * workspace holds per-chunk softmax partials, per-sequence decisions and
+ * completion counters; its contents need no initialisation and are
+ * meaningless after the call.  Returns 0 for invalid sizes. */
+size_t specdec_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
+
+/* Scores: Y = X W^T, the one pass of the target's output layer over all
+ * N = B*(gamma+1) positions ([LLMI] section 0, the linear layer Y = XW over N
+ * tokens; [MATH] "Prefill vs. Verification Arithmetic Intensity").
+ *   X  device, bf16 [N, d]: hidden states, row n = b*(gamma+1) + i
+ *   W  device, bf16 [V, d]: weights, one row per output entry (so Y = X W^T;
+ *      the pages write the same map as X times a d x V matrix)
+ *   Y  device, [N, V]: fp32 (out_dtype SPECDEC_OUT_F32) or bf16 rounded to
+ *      nearest even (SPECDEC_OUT_BF16)
+ * Products are exact and accumulate in fp32.  Requires N >= 1, d >= 8 with
+ * d % 8 == 0, V >= 1; X and W 16-byte aligned.  Y needs 16-byte alignment
+ * and V % 4 == 0 for the fast store path; other V use element stores. */
+int specdec_verify_logits(const void* X, const void* W, void* Y, int64_t N, int64_t d, int64_t V, int out_dtype,
+                          void* stream);
+
+/* The rejection-sampling rule on given target logits ([LLMI] section 2,
+ * acceptance rule, residual distribution and bonus token; [MATH] "The
+ * Modified Rejection Sampling Algorithm" and "Greedy Decoding Equivalence";
+ * [LESS] "Draft, then verify" and "The acceptance rule").
+ *   target_logits device fp32 [B, gamma+1, V]: row i scores the position after
+ *                 the i-th drafted token; row gamma is the bonus row
+ *   draft         device fp32 [B, gamma, V]: draft logits (draft_kind
+ *                 SPECDEC_DRAFT_LOGITS) or probabilities (SPECDEC_DRAFT_PROBS);
+ *                 unused (may be NULL) when temperature == 0 or gamma == 0
+ *   draft_tokens  device int32 [B, gamma]: the drafted ids x_i
+ *   temperature   T >= 0.  T > 0: p = softmax(target / T) and, for logits,
+ *                 q = softmax(draft / T) ([LESS] "First: what an output
+ *                 distribution is"; temperature is applied to both, per
+ *                 [LESS] "Why the output is exactly p").  T == 0: greedy rule.
+ *   uniforms      device fp32 [B, gamma+1, 2], each in [0, 1): [b, i, 0]
+ *                 decides the accept test at row i, [b, i, 1] drives the draw
+ *                 if the step ends at row i.  Unused (may be NULL) at T == 0.
+ *   out_tokens    device int32 [B, gamma+1]: emitted tokens, -1 after the last
+ *   out_num_emitted device int32 [B]: 1 .. gamma+1
+ *   out_probs     optional device fp32 [B, gamma, 2]: p_i(x_i), q_i(x_i) for
+ *                 every drafted row (NULL to skip; unused at T == 0)
+ *   workspace     device, at least specdec_workspace_bytes(B, gamma, V) bytes,
+ *                 16-byte aligned
+ * Row i keeps x_i iff u[b,i,0] < min(1, p_i(x_i) / max(q_i(x_i), 1e-12)); the
+ * step emits x_0 .. x_{k-1} for the first rejected row k, then one token drawn
+ * by inverse CDF (smallest v with u[b,k,1] * S < C_v, C the running sum in
+ * vocabulary order) from (p_k - q_k)+, or from p_gamma when all gamma are
+ * kept.  p, q, (p - q)+ and p/q are fp32 values; normalisers and running sums
+ * are accumulated in fp64.  At T == 0 row i keeps x_i iff x_i is the row's
+ * argmax (lowest index on ties); the first mismatch, or the bonus row, emits
+ * the argmax.  Requires B >= 1, 0 <= gamma <= SPECDEC_MAX_GAMMA, V >= 1. */
+int specdec_reject_sample(const float* target_logits, const float* draft, int draft_kind,
+                          const int32_t* draft_tokens, float temperature, const float* uniforms, int64_t B,
+                          int64_t gamma, int64_t V, int32_t* out_tokens, int32_t* out_num_emitted,
+                          float* out_probs, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The whole step: specdec_verify_logits (fp32 scores into `logits`) followed by
+ * specdec_reject_sample, enqueued on one stream.
+ *   X [B*(gamma+1), d] and W [V, d] bf16 as in specdec_verify_logits
+ *   logits   device fp32 [B*(gamma+1), V]: caller scratch that receives the
+ *            target logits
+ * Other arguments as in specdec_reject_sample. */
+int specdec_verify_step(const void* X, const void* W, const float* draft, int draft_kind,
+                        const int32_t* draft_tokens, float temperature, const float* uniforms, int64_t B,
+                        int64_t gamma, int64_t d, int64_t V, float* logits, int32_t* out_tokens,
+                        int32_t* out_num_emitted, float* out_probs, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECDEC_H */

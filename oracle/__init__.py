@@ -78,11 +78,11 @@ class Oracle:
         lib.oracle_accept.restype = ctypes.c_int
         lib.oracle_residual.argtypes = [P, P, _i64, P]
         lib.oracle_residual.restype = _f64
-        lib.oracle_draw.argtypes = [P, _i64, ctypes.c_float, P]
+        lib.oracle_draw.argtypes = [P, _i64, ctypes.c_float, P, P]
         lib.oracle_draw.restype = _i64
-        lib.oracle_verify_probs.argtypes = [P, P, P, P, _i64, _i64, _i64, P, P, P, P, P]
+        lib.oracle_verify_probs.argtypes = [P, P, P, P, _i64, _i64, _i64, P, P, P, P, P, P]
         lib.oracle_verify_probs.restype = ctypes.c_int
-        lib.oracle_verify.argtypes = [P, P, ctypes.c_int, P, _f64, P, _i64, _i64, _i64, P, P, P, P, P]
+        lib.oracle_verify.argtypes = [P, P, ctypes.c_int, P, _f64, P, _i64, _i64, _i64, P, P, P, P, P, P]
         lib.oracle_verify.restype = ctypes.c_int
         lib.oracle_sample_rows.argtypes = [P, _i64, _i64, _f64, P, P, P]
         lib.oracle_acceptance_rate.argtypes = [P, P, _i64]
@@ -157,7 +157,7 @@ class Oracle:
         """Inverse-CDF draw from unnormalised weights; returns (token or -1, margin)."""
         w = np.ascontiguousarray(w, dtype=np.float32)
         m = np.zeros(1)
-        t = self.lib.oracle_draw(w.ctypes.data, w.size, float(u), m.ctypes.data)
+        t = self.lib.oracle_draw(w.ctypes.data, w.size, float(u), m.ctypes.data, None)
         return int(t), float(m[0])
 
     def acceptance_rate(self, p, q) -> float:
@@ -177,7 +177,7 @@ class Oracle:
         """Step on probability rows.  p [B, g+1, V], q [B, g, V] fp32, tokens [B, g], uniforms [B, g+1, 2].
 
         Returns dict(tokens [B, g+1] int32 (-1 padded), num_emitted [B], accept_margin [B, g],
-        draw_margin [B])."""
+        draw_margin [B], draw_mass [B])."""
         p = np.ascontiguousarray(p, dtype=np.float32)
         B, g1, V = p.shape
         g = g1 - 1
@@ -189,7 +189,7 @@ class Oracle:
         rc = self.lib.oracle_verify_probs(p.ctypes.data, q.ctypes.data, x.ctypes.data, u.ctypes.data, B, g, V,
                                           scratch.ctypes.data, out["tokens"].ctypes.data,
                                           out["num_emitted"].ctypes.data, out["accept_margin"].ctypes.data,
-                                          out["draw_margin"].ctypes.data)
+                                          out["draw_margin"].ctypes.data, out["draw_mass"].ctypes.data)
         if rc != 0:
             raise ValueError(f"oracle_verify_probs rejected its inputs (code {rc})")
         return out
@@ -212,7 +212,7 @@ class Oracle:
         rc = self.lib.oracle_verify(z.ctypes.data, d.ctypes.data, int(draft_kind), x.ctypes.data, float(temperature),
                                     u.ctypes.data, B, g, V, scratch.ctypes.data, out["tokens"].ctypes.data,
                                     out["num_emitted"].ctypes.data, out["accept_margin"].ctypes.data,
-                                    out["draw_margin"].ctypes.data)
+                                    out["draw_margin"].ctypes.data, out["draw_mass"].ctypes.data)
         if rc != 0:
             raise ValueError(f"oracle_verify rejected its inputs (code {rc})")
         return out
@@ -234,6 +234,7 @@ class Oracle:
             "num_emitted": np.empty(B, dtype=np.int32),
             "accept_margin": np.empty((B, g), dtype=np.float64),
             "draw_margin": np.empty(B, dtype=np.float64),
+            "draw_mass": np.empty(B, dtype=np.float64),
         }
 
 

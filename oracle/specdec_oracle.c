@@ -219,10 +219,11 @@ double oracle_residual(const float* p, const float* q, int64_t V, float* r) {
  * never chosen.  If rounding leaves no such v, the largest v with w[v] > 0 is
  * taken.  Returns -1 when S == 0.  *margin receives min(t - C_{v-1}, C_v - t)/S
  * with t = u*S: the normalised distance of the draw from the nearest slice
- * edge. */
-int64_t oracle_draw(const float* w, int64_t V, float u, double* margin) {
+ * edge; *mass receives S. */
+int64_t oracle_draw(const float* w, int64_t V, float u, double* margin, double* mass) {
   double S = 0.0;
   for (int64_t v = 0; v < V; ++v) S += (double)w[v];
+  if (mass) *mass = S;
   if (!(S > 0.0)) {
     if (margin) *margin = INFINITY;
     return -1;
@@ -270,7 +271,7 @@ int64_t oracle_draw(const float* w, int64_t V, float u, double* margin) {
  * record how close each decision was. */
 static int verify_one_probs(const float* p, const float* q, const int32_t* x, const float* u, int64_t gamma,
                             int64_t V, float* scratch, int32_t* tokens, double* accept_margin,
-                            double* draw_margin) {
+                            double* draw_margin, double* draw_mass) {
   int64_t slot_acc = 0, slot_smp = 1;
 #if ORACLE_PLANT == PLANT_UNIFORM_SLOTS
   slot_acc = 1;
@@ -301,29 +302,34 @@ static int verify_one_probs(const float* p, const float* q, const int32_t* x, co
 #endif
     const float* w = (S > 0.0) ? scratch : pi;
     double dm = 0.0;
-    tokens[i] = (int32_t)oracle_draw(w, V, u[i * 2 + slot_smp], &dm);
+    double dS = 0.0;
+    tokens[i] = (int32_t)oracle_draw(w, V, u[i * 2 + slot_smp], &dm, &dS);
     if (draw_margin) *draw_margin = dm;
+    if (draw_mass) *draw_mass = dS;
     return (int)(i + 1);
   }
 #if ORACLE_PLANT == PLANT_NO_BONUS
   if (draw_margin) *draw_margin = INFINITY;
+  if (draw_mass) *draw_mass = 0.0;
   return (int)gamma;
 #else
-  double dm = 0.0;
-  tokens[gamma] = (int32_t)oracle_draw(p + gamma * V, V, u[gamma * 2 + slot_smp], &dm);
+  double dm = 0.0, dS = 0.0;
+  tokens[gamma] = (int32_t)oracle_draw(p + gamma * V, V, u[gamma * 2 + slot_smp], &dm, &dS);
   if (draw_margin) *draw_margin = dm;
+  if (draw_mass) *draw_mass = dS;
   return (int)(gamma + 1);
 #endif
 }
 
 /* Batched step on probability rows: p [B, gamma+1, V], q [B, gamma, V],
  * x [B, gamma], u [B, gamma+1, 2]; outputs tokens [B, gamma+1] (-1 padded),
- * num_emitted [B], optional accept_margin [B, gamma] (NaN where untested) and
- * draw_margin [B].  scratch must hold V floats.  Returns 0, or -1 on a draft
- * token outside [0, V). */
+ * num_emitted [B], optional accept_margin [B, gamma] (NaN where untested),
+ * draw_margin [B] and draw_mass [B] (total weight S of the distribution the
+ * last token was drawn from).  scratch must hold V floats.  Returns 0, or -1
+ * on a draft token outside [0, V). */
 int oracle_verify_probs(const float* p, const float* q, const int32_t* x, const float* u, int64_t B, int64_t gamma,
                         int64_t V, float* scratch, int32_t* tokens, int32_t* num_emitted, double* accept_margin,
-                        double* draw_margin) {
+                        double* draw_margin, double* draw_mass) {
   for (int64_t b = 0; b < B; ++b)
     for (int64_t i = 0; i < gamma; ++i)
       if (x[b * gamma + i] < 0 || x[b * gamma + i] >= V) return -1;
@@ -333,7 +339,7 @@ int oracle_verify_probs(const float* p, const float* q, const int32_t* x, const 
     num_emitted[b] = verify_one_probs(p + b * (gamma + 1) * V, q + b * gamma * V, x + b * gamma,
                                       u + b * (gamma + 1) * 2, gamma, V, scratch, tokens + b * (gamma + 1),
                                       accept_margin ? accept_margin + b * gamma : 0,
-                                      draw_margin ? draw_margin + b : 0);
+                                      draw_margin ? draw_margin + b : 0, draw_mass ? draw_mass + b : 0);
   }
   return 0;
 }
@@ -382,7 +388,7 @@ static int verify_one_greedy(const float* z, const int32_t* x, int64_t gamma, in
  * Returns 0, -1 on a token outside [0, V), -2 on T < 0 or NaN. */
 int oracle_verify(const float* target, const float* draft, int draft_kind, const int32_t* x, double T, const float* u,
                   int64_t B, int64_t gamma, int64_t V, float* scratch, int32_t* tokens, int32_t* num_emitted,
-                  double* accept_margin, double* draw_margin) {
+                  double* accept_margin, double* draw_margin, double* draw_mass) {
   if (!(T >= 0.0)) return -2;
   for (int64_t b = 0; b < B; ++b)
     for (int64_t i = 0; i < gamma; ++i)
@@ -396,6 +402,8 @@ int oracle_verify(const float* target, const float* draft, int draft_kind, const
     int32_t* tb = tokens + b * (gamma + 1);
     double* amb = accept_margin ? accept_margin + b * gamma : 0;
     double* dmb = draw_margin ? draw_margin + b : 0;
+    double* dsb = draw_mass ? draw_mass + b : 0;
+    if (dsb) *dsb = 0.0;
     if (amb)
       for (int64_t i = 0; i < gamma; ++i) amb[i] = NAN;
     if (T == 0.0) {
@@ -410,7 +418,7 @@ int oracle_verify(const float* target, const float* draft, int draft_kind, const
       else
         oracle_softmax(dq, V, T, qrow + i * V, 0, 0);
     }
-    num_emitted[b] = verify_one_probs(prow, qrow, xb, u + b * (gamma + 1) * 2, gamma, V, work, tb, amb, dmb);
+    num_emitted[b] = verify_one_probs(prow, qrow, xb, u + b * (gamma + 1) * 2, gamma, V, work, tb, amb, dmb, dsb);
   }
   return 0;
 }
@@ -423,7 +431,7 @@ void oracle_sample_rows(const float* z, int64_t rows, int64_t V, double T, const
                         int32_t* out) {
   for (int64_t r = 0; r < rows; ++r) {
     oracle_softmax(z + r * V, V, T, scratch, 0, 0);
-    out[r] = (int32_t)oracle_draw(scratch, V, u[r], 0);
+    out[r] = (int32_t)oracle_draw(scratch, V, u[r], 0, 0);
   }
 }
 

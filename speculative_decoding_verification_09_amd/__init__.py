@@ -1,0 +1,177 @@
+"""Speculative-decoding verification step on MI355X (gfx950).
+
+Thin ctypes binding over the C ABI in ``include/specdec.h`` (library
+``libspecdec.so`` next to this file).  The functions carry the C names and do
+argument marshalling only: they take torch tensors for device memory and the
+current torch stream, check dtypes and shapes, and call the library.  Every
+step of the computation runs in the HIP kernels.  There is no fallback: if the
+library is missing, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libspecdec.so")
+
+SPECDEC_OK = 0
+SPECDEC_DRAFT_LOGITS = 0
+SPECDEC_DRAFT_PROBS = 1
+SPECDEC_OUT_F32 = 0
+SPECDEC_OUT_BF16 = 1
+SPECDEC_MAX_GAMMA = 63
+
+EXPORTED = [
+    "specdec_status_string",
+    "specdec_version",
+    "specdec_workspace_bytes",
+    "specdec_verify_logits",
+    "specdec_reject_sample",
+    "specdec_verify_step",
+]
+
+
+class SpecdecError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIBRARY):
+        raise ImportError(f"{LIBRARY} is not built; run `python speculative_decoding_verification_09_amd/build.py`")
+    lib = ctypes.CDLL(LIBRARY)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.specdec_status_string.argtypes = [I]
+    lib.specdec_status_string.restype = ctypes.c_char_p
+    lib.specdec_version.restype = I
+    lib.specdec_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.specdec_workspace_bytes.restype = ctypes.c_size_t
+    lib.specdec_verify_logits.argtypes = [P, P, P, I64, I64, I64, I, P]
+    lib.specdec_verify_logits.restype = I
+    lib.specdec_reject_sample.argtypes = [P, P, I, P, ctypes.c_float, P, I64, I64, I64, P, P, P, P, ctypes.c_size_t, P]
+    lib.specdec_reject_sample.restype = I
+    lib.specdec_verify_step.argtypes = [P, P, P, I, P, ctypes.c_float, P, I64, I64, I64, I64, P, P, P, P, P,
+                                        ctypes.c_size_t, P]
+    lib.specdec_verify_step.restype = I
+    return lib
+
+
+_lib = _load()
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.specdec_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(_lib.specdec_version())
+
+
+def workspace_bytes(B: int, gamma: int, V: int) -> int:
+    return int(_lib.specdec_workspace_bytes(int(B), int(gamma), int(V)))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != SPECDEC_OK:
+        raise SpecdecError(status, where)
+
+
+def _expect(t, dtype, shape, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def specdec_verify_logits(X: torch.Tensor, W: torch.Tensor, Y: torch.Tensor, out_dtype: int = SPECDEC_OUT_F32,
+                          stream=None) -> torch.Tensor:
+    """Y = X W^T.  X bf16 [N, d], W bf16 [V, d], Y fp32 or bf16 [N, V] (written)."""
+    N, d = X.shape
+    V = W.shape[0]
+    _expect(X, torch.bfloat16, (N, d), "X")
+    _expect(W, torch.bfloat16, (V, d), "W")
+    _expect(Y, torch.float32 if out_dtype == SPECDEC_OUT_F32 else torch.bfloat16, (N, V), "Y")
+    _check(_lib.specdec_verify_logits(_ptr(X), _ptr(W), _ptr(Y), N, d, V, int(out_dtype), _stream(stream)),
+           "specdec_verify_logits")
+    return Y
+
+
+def specdec_reject_sample(target_logits, draft, draft_tokens, temperature: float, uniforms, out_tokens,
+                          out_num_emitted, workspace, out_probs=None, draft_kind: int = SPECDEC_DRAFT_LOGITS,
+                          stream=None):
+    """The rejection-sampling rule; see include/specdec.h.  Shapes: target [B, g+1, V] fp32, draft [B, g, V]
+    fp32 (or None at T == 0), draft_tokens [B, g] int32, uniforms [B, g+1, 2] fp32 (or None at T == 0),
+    out_tokens [B, g+1] int32, out_num_emitted [B] int32, workspace uint8 >= workspace_bytes(B, g, V)."""
+    B, g1, V = target_logits.shape
+    g = g1 - 1
+    _expect(target_logits, torch.float32, (B, g1, V), "target_logits")
+    if draft is not None:
+        _expect(draft, torch.float32, (B, g, V), "draft")
+    _expect(draft_tokens, torch.int32, (B, g), "draft_tokens")
+    if uniforms is not None:
+        _expect(uniforms, torch.float32, (B, g1, 2), "uniforms")
+    _expect(out_tokens, torch.int32, (B, g1), "out_tokens")
+    _expect(out_num_emitted, torch.int32, (B,), "out_num_emitted")
+    if out_probs is not None:
+        _expect(out_probs, torch.float32, (B, g, 2), "out_probs")
+    _check(_lib.specdec_reject_sample(_ptr(target_logits), _ptr(draft), int(draft_kind), _ptr(draft_tokens),
+                                      float(temperature), _ptr(uniforms), B, g, V, _ptr(out_tokens),
+                                      _ptr(out_num_emitted), _ptr(out_probs), _ptr(workspace), workspace.numel(),
+                                      _stream(stream)), "specdec_reject_sample")
+    return out_tokens, out_num_emitted
+
+
+def specdec_verify_step(X, W, draft, draft_tokens, temperature: float, uniforms, logits, out_tokens,
+                        out_num_emitted, workspace, out_probs=None, draft_kind: int = SPECDEC_DRAFT_LOGITS,
+                        stream=None):
+    """specdec_verify_logits into `logits` [B*(g+1), V] fp32, then specdec_reject_sample on it."""
+    B, g = draft_tokens.shape
+    N, d = X.shape
+    V = W.shape[0]
+    if N != B * (g + 1):
+        raise ValueError(f"X has {N} rows, expected B*(gamma+1) = {B * (g + 1)}")
+    _expect(X, torch.bfloat16, (N, d), "X")
+    _expect(W, torch.bfloat16, (V, d), "W")
+    _expect(logits, torch.float32, (N, V), "logits")
+    if draft is not None:
+        _expect(draft, torch.float32, (B, g, V), "draft")
+    _expect(draft_tokens, torch.int32, (B, g), "draft_tokens")
+    if uniforms is not None:
+        _expect(uniforms, torch.float32, (B, g + 1, 2), "uniforms")
+    _expect(out_tokens, torch.int32, (B, g + 1), "out_tokens")
+    _expect(out_num_emitted, torch.int32, (B,), "out_num_emitted")
+    if out_probs is not None:
+        _expect(out_probs, torch.float32, (B, g, 2), "out_probs")
+    _check(_lib.specdec_verify_step(_ptr(X), _ptr(W), _ptr(draft), int(draft_kind), _ptr(draft_tokens),
+                                    float(temperature), _ptr(uniforms), B, g, d, V, _ptr(logits), _ptr(out_tokens),
+                                    _ptr(out_num_emitted), _ptr(out_probs), _ptr(workspace), workspace.numel(),
+                                    _stream(stream)), "specdec_verify_step")
+    return out_tokens, out_num_emitted
+
+
+def new_workspace(B: int, gamma: int, V: int, device="cuda") -> torch.Tensor:
+    """A device byte buffer of the size specdec_reject_sample needs."""
+    return torch.empty(workspace_bytes(B, gamma, V), dtype=torch.uint8, device=device)

@@ -1,0 +1,136 @@
+// C ABI of the verification step: argument checks, then launches on the
+// caller's stream.  Every check runs before any HIP call, so invalid
+// arguments never reach the device.  The declarations, with the meaning and
+// layout of every argument, are in include/specdec.h.
+#include <math.h>
+
+#include "../../include/specdec.h"
+#include "internal.h"
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Largest sizes the kernels index with 32-bit arithmetic in places.
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+constexpr int64_t kMaxRows = (int64_t)1 << 26;
+
+int check_logits_args(const void* X, const void* W, const void* Y, int64_t N, int64_t d, int64_t V, int out_dtype) {
+  if (!X || !W || !Y) return SPECDEC_ERR_NULL;
+  if (N < 1 || N > kMaxRows || d < 8 || d % 8 != 0 || d > kMaxDim || V < 1 || V > kMaxDim) return SPECDEC_ERR_SHAPE;
+  if ((size_t)N * (size_t)V > ((size_t)1 << 40) || (size_t)V * (size_t)d > ((size_t)1 << 40)) return SPECDEC_ERR_SHAPE;
+  if (out_dtype != SPECDEC_OUT_F32 && out_dtype != SPECDEC_OUT_BF16) return SPECDEC_ERR_ARG;
+  if (!aligned16(X) || !aligned16(W)) return SPECDEC_ERR_ALIGN;
+  if (V % 4 == 0) {
+    const size_t es = out_dtype == SPECDEC_OUT_F32 ? 16 : 8;
+    if (((uintptr_t)Y % es) != 0) return SPECDEC_ERR_ALIGN;
+  } else if (((uintptr_t)Y % (out_dtype == SPECDEC_OUT_F32 ? 4 : 2)) != 0) {
+    return SPECDEC_ERR_ALIGN;
+  }
+  return SPECDEC_OK;
+}
+
+int check_reject_args(const float* target, const float* draft, int draft_kind, const int32_t* tokens, float T,
+                      const float* uniforms, int64_t B, int64_t gamma, int64_t V, const int32_t* out_tokens,
+                      const int32_t* out_num, const float* out_probs, const void* ws, size_t ws_bytes) {
+  if (B < 1 || B > kMaxRows || gamma < 0 || gamma > SPECDEC_MAX_GAMMA || V < 1 || V > kMaxDim)
+    return SPECDEC_ERR_SHAPE;
+  if ((size_t)B * (size_t)(gamma + 1) * (size_t)V > ((size_t)1 << 40)) return SPECDEC_ERR_SHAPE;
+  if (draft_kind != SPECDEC_DRAFT_LOGITS && draft_kind != SPECDEC_DRAFT_PROBS) return SPECDEC_ERR_ARG;
+  if (isnan(T) || T < 0.0f || isinf(T)) return SPECDEC_ERR_TEMPERATURE;
+  const bool greedy = T == 0.0f;
+  if (!target || !out_tokens || !out_num) return SPECDEC_ERR_NULL;
+  if (gamma > 0 && !tokens) return SPECDEC_ERR_NULL;
+  if (!greedy && !uniforms) return SPECDEC_ERR_NULL;
+  if (!greedy && gamma > 0 && !draft) return SPECDEC_ERR_NULL;
+  if (!aligned16(target) || (draft && !aligned16(draft))) return SPECDEC_ERR_ALIGN;
+  if (((uintptr_t)out_tokens & 3) || ((uintptr_t)out_num & 3) || (tokens && ((uintptr_t)tokens & 3)) ||
+      (uniforms && ((uintptr_t)uniforms & 3)) || (out_probs && ((uintptr_t)out_probs & 3)))
+    return SPECDEC_ERR_ALIGN;
+  const size_t need = specdec::reject_workspace_bytes(B, gamma, V);
+  if (!ws || ws_bytes < need) return SPECDEC_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SPECDEC_ERR_ALIGN;
+  return SPECDEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* specdec_status_string(int status) {
+  switch (status) {
+    case SPECDEC_OK: return "ok";
+    case SPECDEC_ERR_NULL: return "a required pointer is NULL";
+    case SPECDEC_ERR_SHAPE: return "a size is out of range";
+    case SPECDEC_ERR_ALIGN: return "a pointer is not aligned as required";
+    case SPECDEC_ERR_TEMPERATURE: return "temperature must be finite and >= 0";
+    case SPECDEC_ERR_WORKSPACE: return "workspace is NULL or too small";
+    case SPECDEC_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
+    case SPECDEC_ERR_ARG: return "an enumerated argument has an unknown value";
+    default: return "unknown status";
+  }
+}
+
+int specdec_version(void) { return kVersion; }
+
+size_t specdec_workspace_bytes(int64_t B, int64_t gamma, int64_t V) {
+  if (B < 1 || B > kMaxRows || gamma < 0 || gamma > SPECDEC_MAX_GAMMA || V < 1 || V > kMaxDim) return 0;
+  return specdec::reject_workspace_bytes(B, gamma, V);
+}
+
+int specdec_verify_logits(const void* X, const void* W, void* Y, int64_t N, int64_t d, int64_t V, int out_dtype,
+                          void* stream) {
+  const int st = check_logits_args(X, W, Y, N, d, V, out_dtype);
+  if (st != SPECDEC_OK) return st;
+  const hipError_t e = specdec::launch_skinny_gemm((const uint16_t*)X, (const uint16_t*)W, Y, N, d, V,
+                                                   out_dtype == SPECDEC_OUT_BF16, (hipStream_t)stream);
+  return e == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
+}
+
+int specdec_reject_sample(const float* target_logits, const float* draft, int draft_kind,
+                          const int32_t* draft_tokens, float temperature, const float* uniforms, int64_t B,
+                          int64_t gamma, int64_t V, int32_t* out_tokens, int32_t* out_num_emitted,
+                          float* out_probs, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_reject_args(target_logits, draft, draft_kind, draft_tokens, temperature, uniforms, B, gamma, V,
+                                   out_tokens, out_num_emitted, out_probs, workspace, workspace_bytes);
+  if (st != SPECDEC_OK) return st;
+  specdec::RejectArgs a;
+  a.target = target_logits;
+  a.draft = draft;
+  a.draft_kind = draft_kind;
+  a.tokens = draft_tokens;
+  a.temperature = temperature;
+  a.uniforms = uniforms;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.out_tokens = out_tokens;
+  a.out_num = out_num_emitted;
+  a.out_probs = temperature == 0.0f ? nullptr : out_probs;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  const hipError_t e = specdec::launch_reject_sample(a, (hipStream_t)stream);
+  return e == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
+}
+
+int specdec_verify_step(const void* X, const void* W, const float* draft, int draft_kind,
+                        const int32_t* draft_tokens, float temperature, const float* uniforms, int64_t B,
+                        int64_t gamma, int64_t d, int64_t V, float* logits, int32_t* out_tokens,
+                        int32_t* out_num_emitted, float* out_probs, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (B < 1 || B > kMaxRows || gamma < 0 || gamma > SPECDEC_MAX_GAMMA) return SPECDEC_ERR_SHAPE;
+  const int64_t N = B * (gamma + 1);
+  int st = check_logits_args(X, W, logits, N, d, V, SPECDEC_OUT_F32);
+  if (st != SPECDEC_OK) return st;
+  st = check_reject_args(logits, draft, draft_kind, draft_tokens, temperature, uniforms, B, gamma, V, out_tokens,
+                         out_num_emitted, out_probs, workspace, workspace_bytes);
+  if (st != SPECDEC_OK) return st;
+  return specdec_verify_logits(X, W, logits, N, d, V, SPECDEC_OUT_F32, stream) == SPECDEC_OK
+             ? specdec_reject_sample(logits, draft, draft_kind, draft_tokens, temperature, uniforms, B, gamma, V,
+                                     out_tokens, out_num_emitted, out_probs, workspace, workspace_bytes, stream)
+             : SPECDEC_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,32 @@
+// Internal interface between the C-ABI layer and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace specdec {
+
+// Y[n, v] = sum_k X[n, k] W[v, k]; X [N, d], W [V, d] bf16; Y fp32 or bf16.
+hipError_t launch_skinny_gemm(const uint16_t* X, const uint16_t* W, void* Y, int64_t N, int64_t d, int64_t V,
+                              bool out_bf16, hipStream_t stream);
+
+struct RejectArgs {
+  const float* target;     // [B, gamma+1, V]
+  const float* draft;      // [B, gamma, V] logits or probabilities
+  int draft_kind;          // 0 logits, 1 probabilities
+  const int32_t* tokens;   // [B, gamma]
+  float temperature;       // 0: greedy
+  const float* uniforms;   // [B, gamma+1, 2]
+  int64_t B, gamma, V;
+  int32_t* out_tokens;     // [B, gamma+1]
+  int32_t* out_num;        // [B]
+  float* out_probs;        // [B, gamma, 2] or null
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+size_t reject_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
+hipError_t launch_reject_sample(const RejectArgs& a, hipStream_t stream);
+
+}  // namespace specdec

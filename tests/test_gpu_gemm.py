@@ -1,0 +1,129 @@
+"""Parity of the scoring GEMM (specdec_verify_logits) with the oracle's fp64 linear layer.
+
+Tolerances come from the arithmetic: products of two bf16 values are exact in
+fp32 and the kernel accumulates in fp32, so |y_gpu - y| <= g_d * sum_k |x_k w_k|
+with g_d = d*u / (1 - d*u), u = 2**-24 (the standard bound for any order of
+fp32 summation).  Integer-valued inputs whose partial sums stay below 2**24
+are summed exactly in any order, so those results must be bit-identical.
+The stated criterion for bf16 outputs (relative error 2e-2, with a floor of
+1e-3 of the output RMS for entries near zero) is checked as well.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import announce, gemm, host
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0**-24
+# (N, d, V): every tile shape of the dispatcher, k tails (d % chunk != 0),
+# vocabulary tails (V % 128 != 0, V % 4 != 0), several token-column tiles.
+SHAPES = [
+    (1, 8, 1), (5, 64, 37), (16, 256, 128), (17, 264, 1000), (33, 512, 777), (64, 520, 1030),
+    (100, 1024, 2053), (200, 320, 515), (320, 136, 300), (513, 96, 129), (1, 4104, 4099),
+]
+
+
+def _bound(Xf, Wf, d):
+    g = d * U / (1 - d * U)
+    return g * (np.abs(Xf.astype(np.float64)) @ np.abs(Wf.astype(np.float64)).T)
+
+
+@pytest.mark.parametrize("N,d,V", SHAPES)
+def test_integer_inputs_bit_exact(orc, N, d, V):
+    X = synth.integer_bf16((N, d), 8, 17, N)
+    W = synth.integer_bf16((V, d), 8, 18, V)
+    announce(f"gemm integer N={N} d={d} V={V}")
+    Y = host(gemm(X, W))
+    ref = orc.linear(X, W)
+    assert np.array_equal(Y.astype(np.float64), ref), np.abs(Y - ref).max()
+
+
+@pytest.mark.parametrize("N,d,V", SHAPES)
+def test_normal_inputs_within_fp32_bound(orc, N, d, V):
+    X = synth.normal_bf16((N, d), 1.0, 27, N)
+    W = synth.normal_bf16((V, d), 0.02, 28, V)
+    announce(f"gemm normal N={N} d={d} V={V}")
+    Y = host(gemm(X, W)).astype(np.float64)
+    ref = orc.linear(X, W)
+    bound = _bound(synth.bf16_to_f32(X), synth.bf16_to_f32(W), d)
+    err = np.abs(Y - ref)
+    assert np.all(err <= bound + 1e-30), float((err - bound).max())
+    rms = float(np.sqrt(np.mean(ref**2)))
+    assert np.all(err <= 2e-2 * np.maximum(np.abs(ref), 1e-3 * rms))
+
+
+@pytest.mark.parametrize("N,d,V", [(5, 64, 37), (64, 520, 1030), (320, 136, 300), (513, 96, 129)])
+def test_bf16_output(orc, N, d, V):
+    X = synth.normal_bf16((N, d), 1.0, 37, N)
+    W = synth.normal_bf16((V, d), 0.02, 38, V)
+    announce(f"gemm bf16-out N={N} d={d} V={V}")
+    Y = gemm(X, W, out_bf16=True)
+    Yf = host(Y.float()).astype(np.float64)
+    ref = orc.linear(X, W)
+    bound = _bound(synth.bf16_to_f32(X), synth.bf16_to_f32(W), d)
+    # one rounding to bf16 (8 significant bits, nearest even) on top of the fp32 result
+    assert np.all(np.abs(Yf - ref) <= 2.0**-8 * (np.abs(ref) + bound) + bound + 1e-30)
+    rms = float(np.sqrt(np.mean(ref**2)))
+    assert np.all(np.abs(Yf - ref) <= 2e-2 * np.maximum(np.abs(ref), 1e-3 * rms))
+
+
+def test_nan_poisoned_output_fully_written(orc):
+    """Every output entry is written (the buffer starts as NaN)."""
+    X = synth.normal_bf16((37, 72), 1.0, 47, 0)
+    W = synth.normal_bf16((997, 72), 0.02, 48, 0)
+    announce("gemm coverage N=37 d=72 V=997")
+    Y = host(gemm(X, W))
+    assert np.all(np.isfinite(Y))
+
+
+def test_deterministic():
+    X = synth.normal_bf16((64, 1024), 1.0, 57, 0)
+    W = synth.normal_bf16((5000, 1024), 0.02, 58, 0)
+    announce("gemm determinism N=64 d=1024 V=5000")
+    a = host(gemm(X, W))
+    b = host(gemm(X, W))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# Full configuration sizes, in the launch configuration the benchmark times,
+# checked on sampled entries that the oracle computes one by one.
+
+FULL = [
+    ("lmhead_b1_g4", 5, 4096, 128256, 0.02, False),
+    ("lmhead_b8_g7", 64, 8192, 128256, 0.015, False),
+    ("greedy_b64_g4", 320, 5120, 152064, 0.02, False),
+    ("proj_up_n1", 1, 8192, 28672, 0.02, True),
+    ("proj_up_n64", 64, 8192, 28672, 0.02, True),
+    ("proj_up_n512", 512, 8192, 28672, 0.02, True),
+    ("proj_down_n5", 5, 28672, 8192, 0.02, True),
+    ("proj_down_n256", 256, 28672, 8192, 0.02, True),
+]
+
+
+@pytest.mark.parametrize("name,N,d,V,wstd,bf16", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled(orc, name, N, d, V, wstd, bf16):
+    seed = 9000 + N
+    X = synth.normal_bf16((N, d), 1.0, seed, synth.STREAM_X)
+    W = synth.normal_bf16((V, d), wstd, seed, synth.STREAM_W)
+    announce(f"gemm full-size {name} N={N} d={d} V={V} bf16_out={bf16}")
+    Y = gemm(X, W, out_bf16=bf16)
+    rng = np.random.default_rng(seed)
+    n_idx = np.concatenate([rng.integers(0, N, 3000), np.full(64, N - 1)])
+    v_idx = np.concatenate([rng.integers(0, V, 3000), np.arange(V - 64, V)])
+    got = Y[torch.from_numpy(n_idx).cuda(), torch.from_numpy(v_idx).cuda()].float().cpu().numpy().astype(np.float64)
+    ref = orc.linear_entries(X, W, n_idx, v_idx)
+    Xs = np.abs(synth.bf16_to_f32(X[n_idx]))
+    Ws = np.abs(synth.bf16_to_f32(W[v_idx]))
+    absdot = np.einsum("ij,ij->i", Xs, Ws, dtype=np.float64)
+    g = d * U / (1 - d * U)
+    bound = g * absdot
+    if bf16:
+        bound = bound + 2.0**-8 * (np.abs(ref) + bound)
+    assert np.all(np.abs(got - ref) <= bound + 1e-30)
+    rms = float(np.sqrt(np.mean(ref**2)))
+    assert np.all(np.abs(got - ref) <= 2e-2 * np.maximum(np.abs(ref), 1e-3 * rms))
+    assert bool(torch.isfinite(Y).all())
