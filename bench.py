@@ -40,6 +40,9 @@ def main():
     ap.add_argument("--workload", default="lmhead_b1_g4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=3, help="oracle steps timed for the CPU baseline")
+    ap.add_argument("--layout", choices=["packed", "rowmajor"], default="packed", help="weight layout")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 256 MiB device copy (a known byte count for hardware counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -65,8 +68,13 @@ def main():
     # ---- inputs (untimed): hidden states and weights from the seeded generator
     Xb, Wb = synth.lm_head_inputs(w)
     X = torch.from_numpy(Xb.view(np.int16)).to(dev).view(torch.bfloat16)
-    W = torch.from_numpy(Wb.view(np.int16)).to(dev).view(torch.bfloat16)
+    W_rows = torch.from_numpy(Wb.view(np.int16)).to(dev).view(torch.bfloat16)
     del Xb, Wb
+    # One-time weight preparation, as at model load: the packed tile layout.  Every step still reads all of it.
+    W = sd.specdec_pack_weights(W_rows) if args.layout == "packed" else W_rows
+    torch.cuda.synchronize()
+    if args.layout == "packed":
+        del W_rows
     logits = torch.empty((N, V), dtype=torch.float32, device=dev)
     out_tok = torch.empty((B, g + 1), dtype=torch.int32, device=dev)
     out_num = torch.empty((B,), dtype=torch.int32, device=dev)
@@ -97,35 +105,44 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
+    probs = None
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
-    def step(mid_event=None):
-        sd.specdec_verify_logits(X, W, logits, stream=stream)
-        if mid_event is not None:
-            mid_event.record(stream)
-        sd.specdec_reject_sample(logits.view(B, g + 1, V), draft, tokens, T, uni if T > 0 else None, out_tok,
-                                 out_num, ws, stream=stream)
+    def step():
+        sd.specdec_verify_step(X, W, draft, tokens, T, uni if T > 0 else None, logits, out_tok, out_num, ws,
+                               out_probs=probs, stream=stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps; events before each step and after its GEMM, on the launch stream
+    # ---- timed region 1 (the headline): K whole steps back to back, events on the launch stream
     K = args.steps
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    evm = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     evs = torch.cuda.Event(enable_timing=True)
     eve = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     evs.record(stream)
-    for i in range(K):
-        ev0[i].record(stream)
-        step(evm[i])
+    for _ in range(K):
+        step()
     eve.record(stream)
     torch.cuda.synchronize()
-    total_ms = evs.elapsed_time(eve)
-    ms_step = total_ms / K
-    gemm_ms = float(np.mean([ev0[i].elapsed_time(evm[i]) for i in range(K)]))
+    ms_step = evs.elapsed_time(eve) / K
     emitted = int(out_num.sum().item())
+
+    # ---- timed region 2 (the roofline of the dominant kernel): K scoring launches, each between two events
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        ev0[i].record(stream)
+        sd.specdec_verify_logits(X, W, logits, stream=stream)
+    ev0[K].record(stream)
+    torch.cuda.synchronize()
+    gemm_ms = float(np.mean([ev0[i].elapsed_time(ev0[i + 1]) for i in range(K)]))
 
     gemm_bytes, step_bytes = algorithmic_bytes(w)
     gemm_gbps = gemm_bytes / (gemm_ms * 1e-3) / 1e9
@@ -140,19 +157,20 @@ def main():
         orc = oracle.load()
         Xh, Wh = synth.lm_head_inputs(w)
         rows_per_seq = g + 1
-        seqs = min(B, max(1, args.cpu_steps))
+        reps = max(1, args.cpu_steps)
         uh = synth.step_uniforms(w)
         toks = tokens.cpu().numpy()
         dr = draft.cpu().numpy() if draft is not None else None
         t0 = time.perf_counter()
-        for b in range(seqs):
+        for r in range(reps):
+            b = r % B
             zb = orc.linear(Xh[b * rows_per_seq:(b + 1) * rows_per_seq], Wh).astype(np.float32)
             orc.verify(zb[None], dr[b:b + 1] if dr is not None else None, toks[b:b + 1], uh[b:b + 1], T)
         cpu_s = time.perf_counter() - t0
-        # B == 1: each sample is one full step; otherwise one sequence (gamma+1 positions) of a step.
-        cpu = {"value": seqs * rows_per_seq / cpu_s, "unit": "positions/s", "cores": 1, "kind": "oracle",
-               "sample": f"{seqs} sequence(s) of {rows_per_seq} positions: fp64 scoring over the full "
-                         f"{V}x{d} weights plus the rule, single-threaded C ({cpu_s:.1f} s)"}
+        cpu = {"value": reps * rows_per_seq / cpu_s, "unit": "positions/s", "cores": 1, "kind": "oracle",
+               "sample": f"{reps} sequence(s) of {rows_per_seq} positions (B={B}: "
+                         f"{'whole steps' if B == 1 else 'sequences of one step'}): fp64 scoring over the full "
+                         f"{V}x{d} weights plus the rule, single-threaded C, {cpu_s:.1f} s"}
 
     out = {
         "metric": METRIC,
@@ -168,12 +186,12 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "gamma": g, "d": d, "V": V, "N": N, "temperature": T,
-                   "draft_noise_std": w.noise_std},
+                   "draft_noise_std": w.noise_std, "weight_layout": args.layout},
         "step_hbm_gbps": step_gbps,
         "step_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
         "step_bytes": step_bytes,
         "emitted_tokens_per_s": emitted / (ms_step * 1e-3),
-        "roofline": {"kernel": "skinny_gemm_kernel", "bound": "hbm", "achieved": gemm_gbps, "peak": HBM_PEAK_GBPS,
+        "roofline": {"kernel": "scoring GEMM (sweep_kernel packed / tiled_kernel)", "bound": "hbm", "achieved": gemm_gbps, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": gemm_gbps / HBM_PEAK_GBPS, "traffic": None,
                      "bytes_per_launch": gemm_bytes, "avg_launch_ms": gemm_ms},
         "cpu_baseline": cpu,

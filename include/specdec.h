@@ -63,6 +63,10 @@ typedef enum {
 #define SPECDEC_OUT_F32 0
 #define SPECDEC_OUT_BF16 1
 
+/* Memory layout of the weights W. */
+#define SPECDEC_WEIGHTS_ROW_MAJOR 0 /* W [V, d] row-major, as a model stores it      */
+#define SPECDEC_WEIGHTS_PACKED 1    /* the tile layout written by specdec_pack_weights */
+
 /* Largest number of drafted tokens per sequence. */
 #define SPECDEC_MAX_GAMMA 63
 
@@ -74,24 +78,41 @@ int specdec_version(void);
 
 /* Bytes of device workspace that specdec_reject_sample and specdec_verify_step
  * need for B sequences of gamma drafts over a vocabulary of V entries.  The
- * workspace holds per-chunk softmax partials, per-sequence decisions and
- * completion counters; its contents need no initialisation and are
+ * workspace holds per-chunk softmax partials, per-row normalisers and
+ * per-sequence decisions; its contents need no initialisation and are
  * meaningless after the call.  Returns 0 for invalid sizes. */
 size_t specdec_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
+
+/* Bytes of the packed weight layout of a [V, d] bf16 matrix (d % 32 == 0):
+ * ceil(V/16)*16*d*2.  Returns 0 for invalid sizes. */
+size_t specdec_packed_weight_bytes(int64_t V, int64_t d);
+
+/* Rewrites W [V, d] (device, bf16, row-major) into the packed tile layout in
+ * W_packed (device, specdec_packed_weight_bytes(V, d) bytes, caller-owned,
+ * must not overlap W).  Inside 16-row tile t, the 32 k values of k-step s
+ * form one contiguous 1 KB block holding, for lane l = 16g + m of a wave,
+ * W[16t + m][32s + 8g .. 32s + 8g + 7]; rows past V are zero.  This is the
+ * operand order of the gfx950 bf16 matrix instruction, so the scoring kernels
+ * read each W byte once in fully contiguous 1 KB pieces.  A one-time
+ * preparation of the weights (as at model load); the scores it produces are
+ * identical to the row-major ones.  Requires d % 32 == 0. */
+int specdec_pack_weights(const void* W, void* W_packed, int64_t V, int64_t d, void* stream);
 
 /* Scores: Y = X W^T, the one pass of the target's output layer over all
  * N = B*(gamma+1) positions ([LLMI] section 0, the linear layer Y = XW over N
  * tokens; [MATH] "Prefill vs. Verification Arithmetic Intensity").
  *   X  device, bf16 [N, d]: hidden states, row n = b*(gamma+1) + i
  *   W  device, bf16 [V, d]: weights, one row per output entry (so Y = X W^T;
- *      the pages write the same map as X times a d x V matrix)
+ *      the pages write the same map as X times a d x V matrix), in
+ *      weight_layout SPECDEC_WEIGHTS_ROW_MAJOR, or the same matrix after
+ *      specdec_pack_weights (SPECDEC_WEIGHTS_PACKED, needs d % 32 == 0)
  *   Y  device, [N, V]: fp32 (out_dtype SPECDEC_OUT_F32) or bf16 rounded to
  *      nearest even (SPECDEC_OUT_BF16)
  * Products are exact and accumulate in fp32.  Requires N >= 1, d >= 8 with
  * d % 8 == 0, V >= 1; X and W 16-byte aligned.  Y needs 16-byte alignment
  * and V % 4 == 0 for the fast store path; other V use element stores. */
 int specdec_verify_logits(const void* X, const void* W, void* Y, int64_t N, int64_t d, int64_t V, int out_dtype,
-                          void* stream);
+                          int weight_layout, void* stream);
 
 /* The rejection-sampling rule on given target logits ([LLMI] section 2,
  * acceptance rule, residual distribution and bonus token; [MATH] "The
@@ -131,11 +152,12 @@ int specdec_reject_sample(const float* target_logits, const float* draft, int dr
 
 /* The whole step: specdec_verify_logits (fp32 scores into `logits`) followed by
  * specdec_reject_sample, enqueued on one stream.
- *   X [B*(gamma+1), d] and W [V, d] bf16 as in specdec_verify_logits
+ *   X [B*(gamma+1), d] and W [V, d] bf16 in weight_layout, as in
+ *            specdec_verify_logits
  *   logits   device fp32 [B*(gamma+1), V]: caller scratch that receives the
  *            target logits
  * Other arguments as in specdec_reject_sample. */
-int specdec_verify_step(const void* X, const void* W, const float* draft, int draft_kind,
+int specdec_verify_step(const void* X, const void* W, int weight_layout, const float* draft, int draft_kind,
                         const int32_t* draft_tokens, float temperature, const float* uniforms, int64_t B,
                         int64_t gamma, int64_t d, int64_t V, float* logits, int32_t* out_tokens,
                         int32_t* out_num_emitted, float* out_probs, void* workspace, size_t workspace_bytes,

@@ -22,12 +22,16 @@ SPECDEC_DRAFT_LOGITS = 0
 SPECDEC_DRAFT_PROBS = 1
 SPECDEC_OUT_F32 = 0
 SPECDEC_OUT_BF16 = 1
+SPECDEC_WEIGHTS_ROW_MAJOR = 0
+SPECDEC_WEIGHTS_PACKED = 1
 SPECDEC_MAX_GAMMA = 63
 
 EXPORTED = [
     "specdec_status_string",
     "specdec_version",
     "specdec_workspace_bytes",
+    "specdec_packed_weight_bytes",
+    "specdec_pack_weights",
     "specdec_verify_logits",
     "specdec_reject_sample",
     "specdec_verify_step",
@@ -50,11 +54,15 @@ def _load() -> ctypes.CDLL:
     lib.specdec_version.restype = I
     lib.specdec_workspace_bytes.argtypes = [I64, I64, I64]
     lib.specdec_workspace_bytes.restype = ctypes.c_size_t
-    lib.specdec_verify_logits.argtypes = [P, P, P, I64, I64, I64, I, P]
+    lib.specdec_packed_weight_bytes.argtypes = [I64, I64]
+    lib.specdec_packed_weight_bytes.restype = ctypes.c_size_t
+    lib.specdec_pack_weights.argtypes = [P, P, I64, I64, P]
+    lib.specdec_pack_weights.restype = I
+    lib.specdec_verify_logits.argtypes = [P, P, P, I64, I64, I64, I, I, P]
     lib.specdec_verify_logits.restype = I
     lib.specdec_reject_sample.argtypes = [P, P, I, P, ctypes.c_float, P, I64, I64, I64, P, P, P, P, ctypes.c_size_t, P]
     lib.specdec_reject_sample.restype = I
-    lib.specdec_verify_step.argtypes = [P, P, P, I, P, ctypes.c_float, P, I64, I64, I64, I64, P, P, P, P, P,
+    lib.specdec_verify_step.argtypes = [P, P, I, P, I, P, ctypes.c_float, P, I64, I64, I64, I64, P, P, P, P, P,
                                         ctypes.c_size_t, P]
     lib.specdec_verify_step.restype = I
     return lib
@@ -106,15 +114,51 @@ def _expect(t, dtype, shape, name):
         raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
-def specdec_verify_logits(X: torch.Tensor, W: torch.Tensor, Y: torch.Tensor, out_dtype: int = SPECDEC_OUT_F32,
-                          stream=None) -> torch.Tensor:
-    """Y = X W^T.  X bf16 [N, d], W bf16 [V, d], Y fp32 or bf16 [N, V] (written)."""
-    N, d = X.shape
-    V = W.shape[0]
-    _expect(X, torch.bfloat16, (N, d), "X")
+class PackedWeights:
+    """W [V, d] in the packed tile layout (specdec_pack_weights); `data` is the device byte buffer."""
+
+    def __init__(self, data: torch.Tensor, V: int, d: int):
+        self.data, self.V, self.d = data, int(V), int(d)
+
+
+def packed_weight_bytes(V: int, d: int) -> int:
+    return int(_lib.specdec_packed_weight_bytes(int(V), int(d)))
+
+
+def specdec_pack_weights(W: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> PackedWeights:
+    """Packs W bf16 [V, d] (d % 32 == 0) into the tile layout; returns a PackedWeights handle."""
+    V, d = W.shape
     _expect(W, torch.bfloat16, (V, d), "W")
+    nbytes = packed_weight_bytes(V, d)
+    if nbytes == 0:
+        raise ValueError(f"cannot pack a [{V}, {d}] matrix (d must be a multiple of 32)")
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+    if out.numel() * out.element_size() < nbytes:
+        raise ValueError("output buffer too small")
+    _check(_lib.specdec_pack_weights(_ptr(W), _ptr(out), V, d, _stream(stream)), "specdec_pack_weights")
+    return PackedWeights(out, V, d)
+
+
+def _weights(W):
+    """(pointer, V, d, layout) of a row-major bf16 tensor or a PackedWeights handle."""
+    if isinstance(W, PackedWeights):
+        return _ptr(W.data), W.V, W.d, SPECDEC_WEIGHTS_PACKED
+    V, d = W.shape
+    _expect(W, torch.bfloat16, (V, d), "W")
+    return _ptr(W), V, d, SPECDEC_WEIGHTS_ROW_MAJOR
+
+
+def specdec_verify_logits(X: torch.Tensor, W, Y: torch.Tensor, out_dtype: int = SPECDEC_OUT_F32,
+                          stream=None) -> torch.Tensor:
+    """Y = X W^T.  X bf16 [N, d], W bf16 [V, d] or PackedWeights, Y fp32 or bf16 [N, V] (written)."""
+    N, d = X.shape
+    wp, V, dw, layout = _weights(W)
+    if dw != d:
+        raise ValueError(f"X has d={d}, W has d={dw}")
+    _expect(X, torch.bfloat16, (N, d), "X")
     _expect(Y, torch.float32 if out_dtype == SPECDEC_OUT_F32 else torch.bfloat16, (N, V), "Y")
-    _check(_lib.specdec_verify_logits(_ptr(X), _ptr(W), _ptr(Y), N, d, V, int(out_dtype), _stream(stream)),
+    _check(_lib.specdec_verify_logits(_ptr(X), wp, _ptr(Y), N, d, V, int(out_dtype), layout, _stream(stream)),
            "specdec_verify_logits")
     return Y
 
@@ -147,14 +191,16 @@ def specdec_reject_sample(target_logits, draft, draft_tokens, temperature: float
 def specdec_verify_step(X, W, draft, draft_tokens, temperature: float, uniforms, logits, out_tokens,
                         out_num_emitted, workspace, out_probs=None, draft_kind: int = SPECDEC_DRAFT_LOGITS,
                         stream=None):
-    """specdec_verify_logits into `logits` [B*(g+1), V] fp32, then specdec_reject_sample on it."""
+    """specdec_verify_logits into `logits` [B*(g+1), V] fp32, then specdec_reject_sample on it.
+    W is a bf16 [V, d] tensor or a PackedWeights handle."""
     B, g = draft_tokens.shape
     N, d = X.shape
-    V = W.shape[0]
+    wp, V, dw, layout = _weights(W)
+    if dw != d:
+        raise ValueError(f"X has d={d}, W has d={dw}")
     if N != B * (g + 1):
         raise ValueError(f"X has {N} rows, expected B*(gamma+1) = {B * (g + 1)}")
     _expect(X, torch.bfloat16, (N, d), "X")
-    _expect(W, torch.bfloat16, (V, d), "W")
     _expect(logits, torch.float32, (N, V), "logits")
     if draft is not None:
         _expect(draft, torch.float32, (B, g, V), "draft")
@@ -165,7 +211,7 @@ def specdec_verify_step(X, W, draft, draft_tokens, temperature: float, uniforms,
     _expect(out_num_emitted, torch.int32, (B,), "out_num_emitted")
     if out_probs is not None:
         _expect(out_probs, torch.float32, (B, g, 2), "out_probs")
-    _check(_lib.specdec_verify_step(_ptr(X), _ptr(W), _ptr(draft), int(draft_kind), _ptr(draft_tokens),
+    _check(_lib.specdec_verify_step(_ptr(X), wp, layout, _ptr(draft), int(draft_kind), _ptr(draft_tokens),
                                     float(temperature), _ptr(uniforms), B, g, d, V, _ptr(logits), _ptr(out_tokens),
                                     _ptr(out_num_emitted), _ptr(out_probs), _ptr(workspace), workspace.numel(),
                                     _stream(stream)), "specdec_verify_step")

@@ -17,9 +17,12 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 constexpr int64_t kMaxRows = (int64_t)1 << 26;
 
-int check_logits_args(const void* X, const void* W, const void* Y, int64_t N, int64_t d, int64_t V, int out_dtype) {
+int check_logits_args(const void* X, const void* W, const void* Y, int64_t N, int64_t d, int64_t V, int out_dtype,
+                      int weight_layout) {
   if (!X || !W || !Y) return SPECDEC_ERR_NULL;
+  if (weight_layout != SPECDEC_WEIGHTS_ROW_MAJOR && weight_layout != SPECDEC_WEIGHTS_PACKED) return SPECDEC_ERR_ARG;
   if (N < 1 || N > kMaxRows || d < 8 || d % 8 != 0 || d > kMaxDim || V < 1 || V > kMaxDim) return SPECDEC_ERR_SHAPE;
+  if (weight_layout == SPECDEC_WEIGHTS_PACKED && d % 32 != 0) return SPECDEC_ERR_SHAPE;
   if ((size_t)N * (size_t)V > ((size_t)1 << 40) || (size_t)V * (size_t)d > ((size_t)1 << 40)) return SPECDEC_ERR_SHAPE;
   if (out_dtype != SPECDEC_OUT_F32 && out_dtype != SPECDEC_OUT_BF16) return SPECDEC_ERR_ARG;
   if (!aligned16(X) || !aligned16(W)) return SPECDEC_ERR_ALIGN;
@@ -80,12 +83,28 @@ size_t specdec_workspace_bytes(int64_t B, int64_t gamma, int64_t V) {
   return specdec::reject_workspace_bytes(B, gamma, V);
 }
 
+size_t specdec_packed_weight_bytes(int64_t V, int64_t d) {
+  if (V < 1 || V > kMaxDim || d < 32 || d % 32 != 0 || d > kMaxDim) return 0;
+  if ((size_t)V * (size_t)d > ((size_t)1 << 40)) return 0;
+  return (size_t)specdec::packed_weight_elems(V, d) * sizeof(uint16_t);
+}
+
+int specdec_pack_weights(const void* W, void* W_packed, int64_t V, int64_t d, void* stream) {
+  if (!W || !W_packed) return SPECDEC_ERR_NULL;
+  if (specdec_packed_weight_bytes(V, d) == 0) return SPECDEC_ERR_SHAPE;
+  if (!aligned16(W) || !aligned16(W_packed)) return SPECDEC_ERR_ALIGN;
+  const hipError_t e =
+      specdec::launch_pack_weights((const uint16_t*)W, (uint16_t*)W_packed, V, d, (hipStream_t)stream);
+  return e == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
+}
+
 int specdec_verify_logits(const void* X, const void* W, void* Y, int64_t N, int64_t d, int64_t V, int out_dtype,
-                          void* stream) {
-  const int st = check_logits_args(X, W, Y, N, d, V, out_dtype);
+                          int weight_layout, void* stream) {
+  const int st = check_logits_args(X, W, Y, N, d, V, out_dtype, weight_layout);
   if (st != SPECDEC_OK) return st;
-  const hipError_t e = specdec::launch_skinny_gemm((const uint16_t*)X, (const uint16_t*)W, Y, N, d, V,
-                                                   out_dtype == SPECDEC_OUT_BF16, (hipStream_t)stream);
+  const hipError_t e =
+      specdec::launch_skinny_gemm((const uint16_t*)X, (const uint16_t*)W, Y, N, d, V, out_dtype == SPECDEC_OUT_BF16,
+                                  weight_layout == SPECDEC_WEIGHTS_PACKED, (hipStream_t)stream);
   return e == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
 }
 
@@ -115,19 +134,19 @@ int specdec_reject_sample(const float* target_logits, const float* draft, int dr
   return e == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
 }
 
-int specdec_verify_step(const void* X, const void* W, const float* draft, int draft_kind,
+int specdec_verify_step(const void* X, const void* W, int weight_layout, const float* draft, int draft_kind,
                         const int32_t* draft_tokens, float temperature, const float* uniforms, int64_t B,
                         int64_t gamma, int64_t d, int64_t V, float* logits, int32_t* out_tokens,
                         int32_t* out_num_emitted, float* out_probs, void* workspace, size_t workspace_bytes,
                         void* stream) {
   if (B < 1 || B > kMaxRows || gamma < 0 || gamma > SPECDEC_MAX_GAMMA) return SPECDEC_ERR_SHAPE;
   const int64_t N = B * (gamma + 1);
-  int st = check_logits_args(X, W, logits, N, d, V, SPECDEC_OUT_F32);
+  int st = check_logits_args(X, W, logits, N, d, V, SPECDEC_OUT_F32, weight_layout);
   if (st != SPECDEC_OK) return st;
   st = check_reject_args(logits, draft, draft_kind, draft_tokens, temperature, uniforms, B, gamma, V, out_tokens,
                          out_num_emitted, out_probs, workspace, workspace_bytes);
   if (st != SPECDEC_OK) return st;
-  return specdec_verify_logits(X, W, logits, N, d, V, SPECDEC_OUT_F32, stream) == SPECDEC_OK
+  return specdec_verify_logits(X, W, logits, N, d, V, SPECDEC_OUT_F32, weight_layout, stream) == SPECDEC_OK
              ? specdec_reject_sample(logits, draft, draft_kind, draft_tokens, temperature, uniforms, B, gamma, V,
                                      out_tokens, out_num_emitted, out_probs, workspace, workspace_bytes, stream)
              : SPECDEC_ERR_LAUNCH;

@@ -7,9 +7,14 @@
 
 namespace specdec {
 
-// Y[n, v] = sum_k X[n, k] W[v, k]; X [N, d], W [V, d] bf16; Y fp32 or bf16.
+// Y[n, v] = sum_k X[n, k] W[v, k]; X [N, d] bf16; W [V, d] bf16 row-major or
+// in the packed tile layout; Y fp32 or bf16.
 hipError_t launch_skinny_gemm(const uint16_t* X, const uint16_t* W, void* Y, int64_t N, int64_t d, int64_t V,
-                              bool out_bf16, hipStream_t stream);
+                              bool out_bf16, bool packed, hipStream_t stream);
+
+// Packed tile layout of W [V, d] (d % 32 == 0): ceil(V/16)*16*d elements.
+int64_t packed_weight_elems(int64_t V, int64_t d);
+hipError_t launch_pack_weights(const uint16_t* W, uint16_t* Wp, int64_t V, int64_t d, hipStream_t stream);
 
 struct RejectArgs {
   const float* target;     // [B, gamma+1, V]

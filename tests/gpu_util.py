@@ -30,10 +30,21 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
-def gemm(X_bits, W_bits, out_bf16=False):
-    X = dev_bf16(X_bits)
+def weights(W_bits, packed: bool):
+    """Device weights in the requested layout (row-major tensor or packed handle)."""
     W = dev_bf16(W_bits)
-    N, V = X.shape[0], W.shape[0]
+    if not packed:
+        return W
+    Wp = sd.specdec_pack_weights(W)
+    torch.cuda.synchronize()
+    del W
+    return Wp
+
+
+def gemm(X_bits, W_bits, out_bf16=False, packed=False):
+    X = dev_bf16(X_bits)
+    W = weights(W_bits, packed)
+    N, V = X.shape[0], W_bits.shape[0]
     Y = torch.full((N, V), float("nan"), device="cuda", dtype=torch.bfloat16 if out_bf16 else torch.float32)
     sd.specdec_verify_logits(X, W, Y, sd.SPECDEC_OUT_BF16 if out_bf16 else sd.SPECDEC_OUT_F32)
     torch.cuda.synchronize()

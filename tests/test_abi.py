@@ -59,8 +59,8 @@ A = 0x100000  # 16-byte aligned fake address
 P = ctypes.c_void_p
 
 
-def _logits(X=A, W=A, Y=A, N=5, d=64, V=128, dt=0):
-    return sd.library().specdec_verify_logits(P(X), P(W), P(Y), N, d, V, dt, None)
+def _logits(X=A, W=A, Y=A, N=5, d=64, V=128, dt=0, layout=0):
+    return sd.library().specdec_verify_logits(P(X), P(W), P(Y), N, d, V, dt, layout, None)
 
 
 def _reject(target=A, draft=A, kind=0, tokens=A, T=1.0, u=A, B=2, g=3, V=128, ot=A, on=A, op=None, ws=A,
@@ -83,6 +83,25 @@ def test_logits_argument_checks():
     assert _logits(W=A + 4) == 3
     assert _logits(Y=A + 4) == 3
     assert _logits(Y=A + 8, dt=0) == 3
+    assert _logits(layout=2) == 7
+    assert _logits(d=72, layout=1) == 2
+
+
+@needs_no_gpu
+def test_pack_argument_checks():
+    lib = sd.library()
+    assert lib.specdec_pack_weights(P(0), P(A), 100, 64, None) == 1
+    assert lib.specdec_pack_weights(P(A), P(0), 100, 64, None) == 1
+    assert lib.specdec_pack_weights(P(A), P(A), 100, 72, None) == 2
+    assert lib.specdec_pack_weights(P(A), P(A), 0, 64, None) == 2
+    assert lib.specdec_pack_weights(P(A + 8), P(A), 100, 64, None) == 3
+
+
+def test_packed_weight_bytes():
+    assert sd.packed_weight_bytes(128256, 4096) == 128256 * 4096 * 2
+    assert sd.packed_weight_bytes(17, 64) == 32 * 64 * 2
+    assert sd.packed_weight_bytes(16, 72) == 0
+    assert sd.packed_weight_bytes(0, 64) == 0
 
 
 @needs_no_gpu
@@ -112,9 +131,9 @@ def test_reject_argument_checks():
 def test_step_argument_checks():
     lib = sd.library()
 
-    def step(X=A, W=A, draft=A, tokens=A, T=1.0, u=A, B=1, g=4, d=64, V=128, logits=A, ws=A, wsb=1 << 30):
-        return lib.specdec_verify_step(P(X), P(W), P(draft), 0, P(tokens), T, P(u), B, g, d, V, P(logits), P(A), P(A),
-                                       None, P(ws), wsb, None)
+    def step(X=A, W=A, draft=A, tokens=A, T=1.0, u=A, B=1, g=4, d=64, V=128, logits=A, ws=A, wsb=1 << 30, lay=0):
+        return lib.specdec_verify_step(P(X), P(W), lay, P(draft), 0, P(tokens), T, P(u), B, g, d, V, P(logits), P(A),
+                                       P(A), None, P(ws), wsb, None)
 
     assert step(X=0) == 1
     assert step(logits=0) == 1
@@ -123,6 +142,7 @@ def test_step_argument_checks():
     assert step(d=7) == 2
     assert step(T=-1.0) == 4
     assert step(wsb=16) == 5
+    assert step(lay=3) == 7
 
 
 def test_python_binding_rejects_host_tensors():

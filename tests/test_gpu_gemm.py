@@ -13,16 +13,24 @@ import pytest
 import torch
 
 import synth
-from gpu_util import announce, gemm, host
+from gpu_util import announce, gemm, host, weights
 
 pytestmark = pytest.mark.gpu
 
 U = 2.0**-24
-# (N, d, V): every tile shape of the dispatcher, k tails (d % chunk != 0),
+# (N, d, V): every kernel shape of the dispatcher, k tails (d % chunk != 0),
 # vocabulary tails (V % 128 != 0, V % 4 != 0), several token-column tiles.
 SHAPES = [
     (1, 8, 1), (5, 64, 37), (16, 256, 128), (17, 264, 1000), (33, 512, 777), (64, 520, 1030),
     (100, 1024, 2053), (200, 320, 515), (320, 136, 300), (513, 96, 129), (1, 4104, 4099),
+]
+# Packed weights (d % 32 == 0).  Covers the sweep kernel (N <= 16 with X in
+# LDS): one and several k-groups per wave, k-step counts that leave waves idle
+# or partly filled (d = 96, 5120), vocabulary tails; and the tiled kernels.
+PACKED_SHAPES = [
+    (1, 64, 17), (5, 4096, 1000), (5, 8192, 515), (3, 5120, 513), (7, 96, 50), (16, 4096, 300),
+    (16, 32, 16), (8, 28672, 40), (17, 256, 1000), (33, 512, 777), (64, 1024, 1030), (100, 512, 2053),
+    (200, 320, 515), (513, 96, 129),
 ]
 
 
@@ -70,6 +78,51 @@ def test_bf16_output(orc, N, d, V):
     assert np.all(np.abs(Yf - ref) <= 2e-2 * np.maximum(np.abs(ref), 1e-3 * rms))
 
 
+@pytest.mark.parametrize("N,d,V", PACKED_SHAPES)
+def test_packed_integer_bit_exact(orc, N, d, V):
+    X = synth.integer_bf16((N, d), 8, 71, N)
+    W = synth.integer_bf16((V, d), 8, 72, V)
+    announce(f"gemm packed integer N={N} d={d} V={V}")
+    Y = host(gemm(X, W, packed=True))
+    assert np.array_equal(Y.astype(np.float64), orc.linear(X, W))
+
+
+@pytest.mark.parametrize("N,d,V", PACKED_SHAPES)
+def test_packed_normal_within_fp32_bound(orc, N, d, V):
+    X = synth.normal_bf16((N, d), 1.0, 81, N)
+    W = synth.normal_bf16((V, d), 0.02, 82, V)
+    announce(f"gemm packed normal N={N} d={d} V={V}")
+    Y = host(gemm(X, W, packed=True)).astype(np.float64)
+    ref = orc.linear(X, W)
+    bound = _bound(synth.bf16_to_f32(X), synth.bf16_to_f32(W), d)
+    assert np.all(np.abs(Y - ref) <= bound + 1e-30)
+
+
+@pytest.mark.parametrize("N,d,V", [(5, 4096, 1000), (64, 1024, 1030)])
+def test_packed_bf16_output(orc, N, d, V):
+    X = synth.normal_bf16((N, d), 1.0, 91, N)
+    W = synth.normal_bf16((V, d), 0.02, 92, V)
+    announce(f"gemm packed bf16-out N={N} d={d} V={V}")
+    Yf = host(gemm(X, W, out_bf16=True, packed=True).float()).astype(np.float64)
+    ref = orc.linear(X, W)
+    bound = _bound(synth.bf16_to_f32(X), synth.bf16_to_f32(W), d)
+    assert np.all(np.abs(Yf - ref) <= 2.0**-8 * (np.abs(ref) + bound) + bound + 1e-30)
+
+
+@pytest.mark.parametrize("V,d", [(16, 32), (37, 64), (1000, 96)])
+def test_pack_layout(V, d):
+    """The packed buffer holds W[16t + m][32s + 8g + e] at ((t*nsteps + s)*64 + 16g + m)*8 + e; padded rows are 0."""
+    W = synth.integer_bf16((V, d), 100, 5, V)
+    announce(f"pack layout V={V} d={d}")
+    Wp = weights(W, packed=True)
+    got = host(Wp.data).view(np.uint16)
+    tiles, nsteps = (V + 15) // 16, d // 32
+    Wpad = np.zeros((tiles * 16, d), np.uint16)
+    Wpad[:V] = W
+    expect = Wpad.reshape(tiles, 16, nsteps, 4, 8).transpose(0, 2, 3, 1, 4).reshape(-1)
+    assert np.array_equal(got, expect)
+
+
 def test_nan_poisoned_output_fully_written(orc):
     """Every output entry is written (the buffer starts as NaN)."""
     X = synth.normal_bf16((37, 72), 1.0, 47, 0)
@@ -104,13 +157,14 @@ FULL = [
 ]
 
 
+@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
 @pytest.mark.parametrize("name,N,d,V,wstd,bf16", FULL, ids=[f[0] for f in FULL])
-def test_full_size_sampled(orc, name, N, d, V, wstd, bf16):
+def test_full_size_sampled(orc, name, N, d, V, wstd, bf16, packed):
     seed = 9000 + N
     X = synth.normal_bf16((N, d), 1.0, seed, synth.STREAM_X)
     W = synth.normal_bf16((V, d), wstd, seed, synth.STREAM_W)
-    announce(f"gemm full-size {name} N={N} d={d} V={V} bf16_out={bf16}")
-    Y = gemm(X, W, out_bf16=bf16)
+    announce(f"gemm full-size {name} N={N} d={d} V={V} bf16_out={bf16} packed={packed}")
+    Y = gemm(X, W, out_bf16=bf16, packed=packed)
     rng = np.random.default_rng(seed)
     n_idx = np.concatenate([rng.integers(0, N, 3000), np.full(64, N - 1)])
     v_idx = np.concatenate([rng.integers(0, V, 3000), np.arange(V - 64, V)])

@@ -19,13 +19,13 @@ import torch
 
 import speculative_decoding_verification_09_amd as sd
 import synth
-from gpu_util import abs_dot_bound, announce, compare_steps, dev, dev_bf16, host
+from gpu_util import abs_dot_bound, announce, compare_steps, dev, dev_bf16, host, weights
 
 pytestmark = pytest.mark.gpu
 
 
-def run_step(X, W, draft, tokens, u, T, B, g, V):
-    Xd, Wd = dev_bf16(X), dev_bf16(W)
+def run_step(X, W, draft, tokens, u, T, B, g, V, packed=True):
+    Xd, Wd = dev_bf16(X), weights(W, packed)
     logits = torch.full((B * (g + 1), V), float("nan"), device="cuda")
     ot = torch.full((B, g + 1), -7, dtype=torch.int32, device="cuda")
     on = torch.full((B,), -7, dtype=torch.int32, device="cuda")
@@ -76,19 +76,21 @@ def test_small_full_oracle(orc):
     target32 = orc.linear(X, W).astype(np.float32).reshape(B, g + 1, V)
     draft, tokens = _draft_and_tokens(orc, target32, g, 1.0, T, 401)
     u = synth.uniforms((B, g + 1, 2), 401, synth.STREAM_STEP_UNIFORMS)
-    announce(f"step small B={B} gamma={g} d={d} V={V}")
-    logits, tok, num = run_step(X, W, draft, tokens, u, T, B, g, V)
-    check_sequences(orc, X, W, logits, tok, num, draft, tokens, u, T, g, V, list(range(B)))
+    for packed in (False, True):
+        announce(f"step small B={B} gamma={g} d={d} V={V} packed={packed}")
+        logits, tok, num = run_step(X, W, draft, tokens, u, T, B, g, V, packed=packed)
+        check_sequences(orc, X, W, logits, tok, num, draft, tokens, u, T, g, V, list(range(B)))
 
 
-def test_lmhead_b1_g4_full_size(orc):
+@pytest.mark.parametrize("packed", [True, False], ids=["packed", "rowmajor"])
+def test_lmhead_b1_g4_full_size(orc, packed):
     w = synth.WORKLOADS["lmhead_b1_g4"]
     X, W = synth.lm_head_inputs(w)
     target32 = orc.linear(X, W).astype(np.float32).reshape(w.B, w.gamma + 1, w.V)
     draft, tokens = _draft_and_tokens(orc, target32, w.gamma, w.noise_std, w.temperature, w.seed)
     u = synth.step_uniforms(w)
-    announce(f"step {w.name} full size")
-    logits, tok, num = run_step(X, W, draft, tokens, u, w.temperature, w.B, w.gamma, w.V)
+    announce(f"step {w.name} full size packed={packed}")
+    logits, tok, num = run_step(X, W, draft, tokens, u, w.temperature, w.B, w.gamma, w.V, packed=packed)
     check_sequences(orc, X, W, logits, tok, num, draft, tokens, u, w.temperature, w.gamma, w.V, [0])
 
 
