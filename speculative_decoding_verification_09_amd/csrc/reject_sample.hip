@@ -14,23 +14,27 @@
 //   At T == 0 the rule is greedy: keep x_i iff it is the row's argmax (lowest
 //   index on ties); emit the argmax at the first mismatch or as the bonus.
 //
-// Launches on the caller's stream (no host synchronisation, no inter-wave
-// signalling inside a launch: kernel boundaries order every step):
+// Launches on the caller's stream; kernel boundaries order every step (no
+// inter-wave signalling inside a launch, no host synchronisation):
 //   1. stats: one wave per (row, 2048-entry vocabulary chunk) of every target
 //      row and, for draft logits at T > 0, every draft row.  T > 0: chunk max
 //      m_c of a = z * (1/T) and s_c = sum exp(a - m_c) (fp32 terms summed in
-//      fp64).  T == 0: chunk max value and its lowest index.
-//   2. merge: one wave per row: m = max m_c, Z = sum s_c exp(m_c - m) (fp64),
-//      and p_i(x_i) or q_i(x_i) of the drafted token (fp64, rounded once to fp32).
-//   3. draw sums: one wave per (sequence, 1024-entry chunk).  Each wave takes
-//      every accept test of its sequence at once (lane i <-> row i) and finds
-//      the first rejection k with a ballot, then sums its chunk of the draw
-//      weights of row k: r_v = max(0, p_v - q_v) and p_v (fp32 values, fp64 sums).
-//   4. select: one wave per sequence finds the chunk holding u*S with an fp64
-//      prefix sum over the chunk totals, rescans that chunk with an fp64
-//      running sum in vocabulary order and writes the token.
-//   Greedy steps run 1 and then one wave per sequence that merges the argmax
-//   partials and applies the greedy rule.
+//      fp64); the wave whose chunk holds the row's drafted token also records
+//      that logit.  T == 0: chunk max value and its lowest index.
+//   2. draw sums (T > 0): workgroups of 16 waves over consecutive 1024-entry
+//      chunks of one sequence.  The waves first merge the sequence's rows in
+//      parallel into LDS (M = max m_c, Z = sum s_c exp(m_c - M) in fp64, and
+//      p_i(x_i) or q_i(x_i) of the drafted token, fp64 rounded once to fp32);
+//      then lane i takes row i, every accept test is taken at once and the
+//      first rejection k found with a ballot, and each wave sums its chunk of
+//      the weights of row k: r_v = max(0, p_v - q_v) and p_v (fp32 values,
+//      fp64 sums).  The chunk-0 wave writes the kept prefix, the count, the
+//      probabilities and a per-sequence draw descriptor.
+//   3. select (T > 0): one wave per sequence finds the chunk holding u * S with
+//      an fp64 prefix sum over the chunk totals, rescans that chunk with an
+//      fp64 running sum in vocabulary order and writes the token.
+//   2'. greedy decide (T == 0): one wave per sequence merges the argmax
+//      partials of its rows (lane i <-> row i) and applies the greedy rule.
 // p, q, (p - q)+ and p/q are fp32 values, as the first source asks for T > 0
 // (section 4, failure mode 1); normalisers and running sums are fp64.
 #include "internal.h"
@@ -38,10 +42,10 @@
 namespace specdec {
 namespace {
 
-constexpr int kStatChunk = 2048;        // vocabulary entries per statistics work item (one wave)
-constexpr int kDrawChunk = 1024;        // vocabulary entries per draw work item (one wave)
+constexpr int kStatChunk = 2048;   // vocabulary entries per statistics work item (one wave)
+constexpr int kDrawChunk = 1024;   // vocabulary entries per draw work item (one wave)
+constexpr int kMergeBatch = 16;    // rows whose argmax partials one wave loads together
 constexpr int kWavesPerBlock = 4;
-constexpr int kRowBatch = 8;            // rows whose partials are loaded together
 constexpr float kQFloor = 1e-12f;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -50,51 +54,55 @@ __host__ __device__ inline int64_t stat_chunks(int64_t V) { return (V + kStatChu
 __host__ __device__ inline int64_t draw_chunks(int64_t V) { return (V + kDrawChunk - 1) / kDrawChunk; }
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
+// Where the step of one sequence ends and how to weigh that row.
+struct DrawDesc {
+  int32_t k;       // row index (gamma for the bonus row)
+  float mp, ip;    // target row: max of a and 1/Z
+  float mq, iq;    // draft row (draft logits only)
+  float u;         // the uniform that drives the draw
+  float pad[2];
+};
+
 // Workspace layout, every array 16-byte aligned.
 struct Layout {
-  size_t off_cmax, off_csum, off_cidx;  // per (row, chunk)
-  size_t off_rm, off_rz, off_px;        // per row
-  size_t off_kb;                        // per sequence
-  size_t off_sres, off_sp;              // per (sequence, draw chunk)
+  size_t off_cmax, off_csum, off_cidx;      // per (row, statistics chunk)
+  size_t off_zx;                            // per row
+  size_t off_desc;                          // per sequence
+  size_t off_sres, off_sp;                  // per (sequence, draw chunk)
   size_t total;
 };
 
 __host__ __device__ inline Layout make_layout(int64_t B, int64_t gamma, int64_t V) {
   Layout L;
-  const int64_t nch = stat_chunks(V), ndc = draw_chunks(V);
-  const size_t rc = (size_t)(B * (2 * gamma + 1)) * nch;
+  const size_t rows = (size_t)(B * (2 * gamma + 1));
+  const size_t rc = rows * (size_t)stat_chunks(V);
+  const size_t ndc = (size_t)(B * draw_chunks(V));
   size_t o = 0;
   L.off_cmax = o; o = align16(o + rc * sizeof(float));
   L.off_csum = o; o = align16(o + rc * sizeof(double));
   L.off_cidx = o; o = align16(o + rc * sizeof(int32_t));
-  const size_t rows = (size_t)(B * (2 * gamma + 1));
-  L.off_rm = o;   o = align16(o + rows * sizeof(double));
-  L.off_rz = o;   o = align16(o + rows * sizeof(double));
-  L.off_px = o;   o = align16(o + rows * sizeof(float));
-  L.off_kb = o;   o = align16(o + (size_t)B * sizeof(int32_t));
-  L.off_sres = o; o = align16(o + (size_t)B * ndc * sizeof(double));
-  L.off_sp = o;   o = align16(o + (size_t)B * ndc * sizeof(double));
+  L.off_zx = o;   o = align16(o + rows * sizeof(float));
+  L.off_desc = o; o = align16(o + (size_t)B * sizeof(DrawDesc));
+  L.off_sres = o; o = align16(o + ndc * sizeof(double));
+  L.off_sp = o;   o = align16(o + ndc * sizeof(double));
   L.total = o;
   return L;
 }
 
 struct Ws {
-  float* cmax;
-  double* csum;
-  int32_t* cidx;
-  double* rm;   // per row: max of a = z / T
-  double* rz;   // per row: sum exp(a - m)
-  float* px;    // per drafted row: p_i(x_i) (target rows) or q_i(x_i) (draft rows)
-  int32_t* kb;  // per sequence: row where the step ends
-  double* sres;
-  double* sp;
+  float* cmax;     // per (row, chunk): max of a = z / T (greedy: max of z)
+  double* csum;    // per (row, chunk): sum exp(a - chunk max)
+  int32_t* cidx;   // per (row, chunk): lowest index of the max (greedy)
+  float* zx;       // per drafted row: logit of the drafted token
+  DrawDesc* desc;  // per sequence
+  double* sres;    // per (sequence, draw chunk): sum of the residual weights
+  double* sp;      // per (sequence, draw chunk): sum of p
 };
 
 inline Ws bind(void* base, const Layout& L) {
   char* b = (char*)base;
-  return Ws{(float*)(b + L.off_cmax), (double*)(b + L.off_csum), (int32_t*)(b + L.off_cidx),
-            (double*)(b + L.off_rm),  (double*)(b + L.off_rz),   (float*)(b + L.off_px),
-            (int32_t*)(b + L.off_kb), (double*)(b + L.off_sres), (double*)(b + L.off_sp)};
+  return Ws{(float*)(b + L.off_cmax), (double*)(b + L.off_csum), (int32_t*)(b + L.off_cidx), (float*)(b + L.off_zx),
+            (DrawDesc*)(b + L.off_desc), (double*)(b + L.off_sres), (double*)(b + L.off_sp)};
 }
 
 // ---------------------------------------------------------------------------
@@ -134,39 +142,17 @@ __device__ __forceinline__ double wave_inclusive_scan(double x, int lane) {
   return x;
 }
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
-
-// Loads lane's PL entries of a (64*PL)-entry chunk, coalesced: entry 4*j + e
-// of the lane is chunk offset 256*j + 4*lane + e.  Entries past V read as fill.
-template <bool VEC, int PL>
-__device__ __forceinline__ void load_chunk(const float* __restrict__ row, int64_t V, int64_t c0, int lane, float fill,
-                                           float (&x)[PL]) {
-#pragma unroll
-  for (int j = 0; j < PL / 4; ++j) {
-    const int64_t v = c0 + 256 * j + 4 * lane;
-    if (VEC && v + 3 < V) {
-      const f32x4 t = *(const f32x4*)(row + v);
-      x[4 * j + 0] = t[0];
-      x[4 * j + 1] = t[1];
-      x[4 * j + 2] = t[2];
-      x[4 * j + 3] = t[3];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[4 * j + e] = (v + e < V) ? row[v + e] : fill;
-    }
-  }
-}
-__device__ __forceinline__ int64_t entry_index(int64_t c0, int lane, int e) {
-  return c0 + 256 * (e >> 2) + 4 * lane + (e & 3);
-}
-
 __device__ __forceinline__ int clamp_token(int32_t t, int64_t V) { return t < 0 ? 0 : (t >= V ? (int)(V - 1) : t); }
 
 // ---------------------------------------------------------------------------
-// 1. Chunk partials.  Target rows are [0, B*(gamma+1)) (row b*(gamma+1) + i),
+// 1. Chunk statistics.  Target rows are [0, B*(gamma+1)) (row b*(gamma+1) + i),
 //    draft rows [B*(gamma+1), B*(2*gamma+1)) (row B*(gamma+1) + b*gamma + i).
+//    Lane l of a wave takes the 32 entries 256*j + 4*l + e (j < 8, e < 4) of
+//    its 2048-entry chunk (1 KB per load instruction).
 template <bool VEC, bool GREEDY>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void stats_kernel(const float* __restrict__ target,
                                                                      const float* __restrict__ draft,
+                                                                     const int32_t* __restrict__ tokens,
                                                                      int64_t n_target_rows, int64_t n_rows,
                                                                      int64_t gamma, int64_t V, float inv_t, Ws ws) {
   constexpr int PL = kStatChunk / 64;
@@ -175,19 +161,33 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void stats_kernel(const float*
   const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (item >= n_rows * nch) return;
   const int64_t r = item / nch, c = item - r * nch;
-  const float* row = r < n_target_rows ? target + (size_t)r * V : draft + (size_t)(r - n_target_rows) * V;
+  const bool is_target = r < n_target_rows;
+  const float* row = is_target ? target + (size_t)r * V : draft + (size_t)(r - n_target_rows) * V;
   const int64_t c0 = c * kStatChunk;
   float x[PL];
-  load_chunk<VEC, PL>(row, V, c0, lane, -INFINITY, x);
+#pragma unroll
+  for (int j = 0; j < PL / 4; ++j) {
+    const int64_t v = c0 + 256 * j + 4 * lane;
+    if (VEC && v + 3 < V) {
+      const f32x4 t = __builtin_nontemporal_load((const f32x4*)(row + v));
+      x[4 * j + 0] = t[0];
+      x[4 * j + 1] = t[1];
+      x[4 * j + 2] = t[2];
+      x[4 * j + 3] = t[3];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * j + e] = (v + e < V) ? row[v + e] : -INFINITY;
+    }
+  }
   if (GREEDY) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
     for (int e = 0; e < PL; ++e) {
-      const int idx = (int)entry_index(c0, lane, e);
-      if (idx < V && (x[e] > bv || (x[e] == bv && idx < bi))) {
+      const int64_t idx = c0 + 256 * (e >> 2) + 4 * lane + (e & 3);
+      if (idx < V && (x[e] > bv || (x[e] == bv && (int)idx < bi))) {
         bv = x[e];
-        bi = idx;
+        bi = (int)idx;
       }
     }
     wave_argmax(bv, bi);
@@ -195,63 +195,53 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void stats_kernel(const float*
       ws.cmax[item] = bv;
       ws.cidx[item] = bi;
     }
-  } else {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < PL; ++e) {
-      x[e] = x[e] * inv_t;
-      mx = fmaxf(mx, x[e]);
-    }
-    mx = wave_max(mx);
-    double s = 0.0;
-#pragma unroll
-    for (int e = 0; e < PL; ++e) s += (double)expf(x[e] - mx);
-    s = wave_sum(s);
-    if (lane == 0) {
-      ws.cmax[item] = mx;
-      ws.csum[item] = s;
-    }
+    return;
   }
-}
-
-// 2. Row merge (T > 0): one wave per row.  m = max m_c, Z = sum s_c exp(m_c - m)
-//    (fp64), and for drafted rows the probability of the drafted token,
-//    p_i(x_i) or q_i(x_i) = exp(a_x - m) / Z (fp64, rounded once to fp32).
-__global__ __launch_bounds__(kWavesPerBlock * 64) void merge_kernel(const float* __restrict__ target,
-                                                                     const float* __restrict__ draft,
-                                                                     const int32_t* __restrict__ tokens,
-                                                                     int64_t n_target_rows, int64_t n_rows,
-                                                                     int64_t gamma, int64_t V, float inv_t, Ws ws) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (r >= n_rows) return;
-  const int64_t nch = stat_chunks(V);
-  // The drafted token of this row, gathered while the partials load.
-  const bool is_target = r < n_target_rows;
+  // The drafted token of this row, if it falls in this chunk.
   const int64_t g1 = gamma + 1;
   const int64_t b = is_target ? r / g1 : (r - n_target_rows) / gamma;
   const int64_t i = is_target ? r - b * g1 : (r - n_target_rows) - b * gamma;
-  const bool drafted = i < gamma;
-  float zx = 0.0f;
-  if (drafted) {
-    const int x = clamp_token(tokens[b * gamma + i], V);
-    zx = is_target ? target[(size_t)r * V + x] : draft[(size_t)(r - n_target_rows) * V + x];
+  if (i < gamma && lane == 0) {
+    const int xt = clamp_token(tokens[b * gamma + i], V);
+    if (xt >= c0 && xt < c0 + kStatChunk) ws.zx[r] = row[xt];
   }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < PL; ++e) {
+    x[e] = x[e] * inv_t;
+    mx = fmaxf(mx, x[e]);
+  }
+  mx = wave_max(mx);
+  double sum = 0.0;
+#pragma unroll
+  for (int e = 0; e < PL; ++e) sum += (double)expf(x[e] - mx);
+  sum = wave_sum(sum);
+  if (lane == 0) {
+    ws.cmax[item] = mx;
+    ws.csum[item] = sum;
+  }
+}
+
+// Merges the chunk partials of row r with one wave: M = max m_c, Z = sum s_c
+// exp(m_c - M) (fp64), and the probability of the drafted token exp(a_x - M)/Z
+// (fp64, rounded once to fp32; 0 for rows without a drafted token).
+__device__ __forceinline__ void merge_row(const Ws& ws, int64_t r, bool drafted, int64_t nch, float inv_t, int lane,
+                                          double& M_out, double& Z_out, float& px_out) {
   const size_t base = (size_t)r * nch;
-  float m = -INFINITY;
-  for (int64_t c = lane; c < nch; c += 64) m = fmaxf(m, ws.cmax[base + c]);
-  m = wave_max(m);
-  double z = 0.0;
-  for (int64_t c = lane; c < nch; c += 64) {
+  const float zx = drafted ? ws.zx[r] : 0.0f;  // loaded with the partials
+  const float cm = lane < nch ? ws.cmax[base + lane] : -INFINITY;
+  const double cs = lane < nch ? ws.csum[base + lane] : 0.0;
+  float M = wave_max(cm);
+  for (int64_t c = lane + 64; c < nch; c += 64) M = fmaxf(M, wave_max(ws.cmax[base + c]));
+  double z = cs > 0.0 ? cs * exp((double)cm - (double)M) : 0.0;
+  for (int64_t c = lane + 64; c < nch; c += 64) {
     const double sc = ws.csum[base + c];
-    if (sc > 0.0) z += sc * exp((double)ws.cmax[base + c] - (double)m);
+    if (sc > 0.0) z += sc * exp((double)ws.cmax[base + c] - (double)M);
   }
   z = wave_sum(z);
-  if (lane == 0) {
-    ws.rm[r] = (double)m;
-    ws.rz[r] = z;
-    ws.px[r] = drafted ? (float)(exp((double)(zx * inv_t) - (double)m) / z) : 0.0f;
-  }
+  M_out = (double)M;
+  Z_out = z;
+  px_out = drafted ? (float)(exp((double)(zx * inv_t) - (double)M) / z) : 0.0f;
 }
 
 // Weights of the draw at one entry: p_v and r_v = max(0, p_v - q_v), fp32.
@@ -273,89 +263,129 @@ __device__ __forceinline__ void weights(const DrawRow& R, float zp, float zq, fl
   }
 }
 
-// The accept tests of sequence b, lane i <-> drafted row i: every test at
-// once, first rejection by ballot.  Returns k (gamma if all are kept).
-__device__ __forceinline__ int first_rejection(const float* __restrict__ draft, int draft_kind,
-                                               const int32_t* __restrict__ tokens,
-                                               const float* __restrict__ uniforms, int64_t b, int64_t B,
-                                               int64_t gamma, int64_t V, int lane, const Ws& ws, float& p_x,
-                                               float& q_x) {
-  const int64_t g1 = gamma + 1;
-  const bool drafted = lane < gamma;
-  p_x = 0.0f;
-  q_x = 0.0f;
-  bool reject = false;
-  if (drafted) {
-    p_x = ws.px[b * g1 + lane];
-    if (draft_kind == 1) {
-      const int x = clamp_token(tokens[b * gamma + lane], V);
-      q_x = draft[(size_t)(b * gamma + lane) * V + x];
-    } else {
-      q_x = ws.px[B * g1 + b * gamma + lane];
-    }
-    const float ratio = p_x / (q_x > kQFloor ? q_x : kQFloor);
-    const float thr = ratio < 1.0f ? ratio : 1.0f;
-    reject = !(uniforms[(b * g1 + lane) * 2 + 0] < thr);
-  }
-  const uint64_t rej = ballot(reject);
-  return rej ? (int)__builtin_ctzll(rej) : (int)gamma;
-}
-
-__device__ __forceinline__ DrawRow draw_row(const float* __restrict__ target, const float* __restrict__ draft,
-                                            int draft_kind, int64_t b, int64_t B, int64_t gamma, int64_t V, int k,
-                                            float inv_t, const Ws& ws) {
-  const int64_t g1 = gamma + 1;
+__device__ __forceinline__ DrawRow make_row(const float* __restrict__ target, const float* __restrict__ draft,
+                                            int draft_kind, int64_t b, int64_t gamma, int64_t V, const DrawDesc& D,
+                                            float inv_t) {
   DrawRow R;
-  R.zp = target + (size_t)(b * g1 + k) * V;
-  R.zq = k < gamma ? draft + (size_t)(b * gamma + k) * V : nullptr;
-  R.mp = (float)ws.rm[b * g1 + k];
-  R.ip = (float)(1.0 / ws.rz[b * g1 + k]);
-  const bool ql = draft_kind == 0 && k < gamma;
-  R.mq = ql ? (float)ws.rm[B * g1 + b * gamma + k] : 0.0f;
-  R.iq = ql ? (float)(1.0 / ws.rz[B * g1 + b * gamma + k]) : 1.0f;
+  R.zp = target + (size_t)(b * (gamma + 1) + D.k) * V;
+  R.zq = D.k < gamma ? draft + (size_t)(b * gamma + D.k) * V : nullptr;
+  R.mp = D.mp;
+  R.ip = D.ip;
+  R.mq = D.mq;
+  R.iq = D.iq;
   R.inv_t = inv_t;
   R.q_probs = draft_kind == 1;
   return R;
 }
 
-// 3. Draw sums (T > 0): one wave per (sequence, chunk).  Every wave takes
-//    the accept tests of its sequence (cheap: one value per drafted row) and
-//    sums its chunk of the weights of the row where the step ends.  The
-//    chunk-0 wave writes the kept prefix, the count and the probabilities.
+// Loads lane's 16 entries of a 1024-entry chunk, coalesced (entry 4j + e at
+// chunk offset 256j + 4*lane + e).  Entries past V read as fill.
 template <bool VEC>
-__global__ __launch_bounds__(kWavesPerBlock * 64) void draw_sum_kernel(
+__device__ __forceinline__ void load_chunk16(const float* __restrict__ row, int64_t V, int64_t c0, int lane, float fill,
+                                             float (&x)[16]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t v = c0 + 256 * j + 4 * lane;
+    if (VEC && v + 3 < V) {
+      const f32x4 t = *(const f32x4*)(row + v);
+      x[4 * j + 0] = t[0];
+      x[4 * j + 1] = t[1];
+      x[4 * j + 2] = t[2];
+      x[4 * j + 3] = t[3];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * j + e] = (v + e < V) ? row[v + e] : fill;
+    }
+  }
+}
+
+// 2. Draw sums (T > 0).  A workgroup of WB waves takes WB consecutive chunks of
+//    one sequence.  Its waves first merge the sequence's rows in parallel (one
+//    row per wave at a time) into LDS; after one barrier every wave reads the
+//    statistics of all rows from LDS, lane i <-> row i.
+constexpr int kMaxRows = 2 * 63 + 1;
+template <int WB, bool VEC>
+__global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
     const float* __restrict__ target, const float* __restrict__ draft, int draft_kind,
     const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, int64_t B, int64_t gamma, int64_t V,
     float inv_t, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_num, float* __restrict__ out_probs,
     Ws ws) {
-  constexpr int PL = kDrawChunk / 64;
-  const int lane = threadIdx.x & 63;
+  __shared__ double sh_m[kMaxRows], sh_z[kMaxRows];
+  __shared__ float sh_px[kMaxRows];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t ndc = draw_chunks(V);
-  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (item >= B * ndc) return;
-  const int64_t b = item / ndc, c = item - b * ndc;
+  const int64_t gps = (ndc + WB - 1) / WB;  // workgroups per sequence
+  const int64_t b = blockIdx.x / gps;
+  const int64_t c = (blockIdx.x - b * gps) * WB + wv;
   const int64_t g1 = gamma + 1;
-  float p_x, q_x;
-  const int k = first_rejection(draft, draft_kind, tokens, uniforms, b, B, gamma, V, lane, ws, p_x, q_x);
-  if (c == 0) {
-    if (lane < g1 && lane != k) out_tokens[b * g1 + lane] = lane < k ? clamp_token(tokens[b * gamma + lane], V) : -1;
+  const bool q_probs = draft_kind == 1;
+  const int64_t nch = stat_chunks(V);
+  // Rows of the sequence: j < g1 target row j, then draft row j - g1 (draft logits).
+  const int nrows = (int)(q_probs ? g1 : g1 + gamma);
+  for (int j = wv; j < nrows; j += WB) {
+    const int64_t r = j < g1 ? b * g1 + j : B * g1 + b * gamma + (j - g1);
+    const bool drafted = j < g1 ? j < gamma : true;
+    double M, Z;
+    float px;
+    merge_row(ws, r, drafted, nch, inv_t, lane, M, Z, px);
     if (lane == 0) {
-      out_num[b] = k + 1;
-      ws.kb[b] = k;
+      sh_m[j] = M;
+      sh_z[j] = Z;
+      sh_px[j] = px;
     }
-    if (lane < gamma && out_probs) {
+  }
+  __syncthreads();
+  if (c >= ndc) return;  // no barrier below
+  const int64_t item = b * ndc + c;
+  const bool has_row = lane < g1;
+  const bool drafted = lane < gamma;
+  const double rmt = has_row ? sh_m[lane] : 0.0, rzt = has_row ? sh_z[lane] : 1.0;
+  const float p_x = drafted ? sh_px[lane] : 0.0f;
+  const bool ql = drafted && !q_probs;
+  const double rmq = ql ? sh_m[g1 + lane] : 0.0, rzq = ql ? sh_z[g1 + lane] : 1.0;
+  float q_x = ql ? sh_px[g1 + lane] : 0.0f;
+  const float u_acc = drafted ? uniforms[(b * g1 + lane) * 2 + 0] : 0.0f;
+  const float u_smp = has_row ? uniforms[(b * g1 + lane) * 2 + 1] : 0.0f;
+  const int xi = drafted ? clamp_token(tokens[b * gamma + lane], V) : 0;
+  if (drafted && q_probs) q_x = draft[(size_t)(b * gamma + lane) * V + xi];
+
+  bool reject = false;
+  if (drafted) {
+    const float ratio = p_x / (q_x > kQFloor ? q_x : kQFloor);
+    const float thr = ratio < 1.0f ? ratio : 1.0f;
+    reject = !(u_acc < thr);
+  }
+  const uint64_t rej = ballot(reject);
+  const int k = rej ? (int)__builtin_ctzll(rej) : (int)gamma;
+  DrawDesc D;
+  D.k = k;
+  D.mp = (float)__shfl(rmt, k);
+  D.ip = (float)(1.0 / __shfl(rzt, k));
+  const int kq = k < gamma ? k : 0;
+  D.mq = (float)__shfl(rmq, kq);
+  D.iq = (float)(1.0 / __shfl(rzq, kq));
+  D.u = __shfl(u_smp, k);
+  D.pad[0] = D.pad[1] = 0.0f;
+
+  if (c == 0) {
+    if (has_row && lane != k) out_tokens[b * g1 + lane] = lane < k ? xi : -1;
+    if (drafted && out_probs) {
       out_probs[(b * gamma + lane) * 2 + 0] = p_x;
       out_probs[(b * gamma + lane) * 2 + 1] = q_x;
     }
+    if (lane == 0) {
+      out_num[b] = k + 1;
+      ws.desc[b] = D;
+    }
   }
-  const DrawRow R = draw_row(target, draft, draft_kind, b, B, gamma, V, k, inv_t, ws);
+  const DrawRow R = make_row(target, draft, draft_kind, b, gamma, V, D, inv_t);
   const int64_t c0 = c * kDrawChunk;
-  float zp[PL], zq[PL];
-  load_chunk<VEC, PL>(R.zp, V, c0, lane, -INFINITY, zp);
-  if (R.zq) load_chunk<VEC, PL>(R.zq, V, c0, lane, R.q_probs ? 0.0f : -INFINITY, zq);
+  float zp[16], zq[16];
+  load_chunk16<VEC>(R.zp, V, c0, lane, -INFINITY, zp);
+  if (R.zq) load_chunk16<VEC>(R.zq, V, c0, lane, q_probs ? 0.0f : -INFINITY, zq);
   double sr = 0.0, sp = 0.0;
 #pragma unroll
-  for (int e = 0; e < PL; ++e) {
+  for (int e = 0; e < 16; ++e) {
     float p, r;
     weights(R, zp[e], R.zq ? zq[e] : 0.0f, p, r);
     sr += (double)r;
@@ -369,42 +399,43 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void draw_sum_kernel(
   }
 }
 
-// 4. Select (T > 0): one wave per sequence.  Chooses the residual, or p when
-//    the residual has no mass or the step ends on the bonus row; finds the
-//    chunk holding u*S with an fp64 prefix sum over the chunk totals, rescans
-//    that chunk with an fp64 running sum in vocabulary order and writes the token.
+// 3. Select (T > 0): one wave per sequence.  The residual's weights, or p
+//    when the residual has no mass or the step ends on the bonus row.
 template <bool VEC>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void select_kernel(
-    const float* __restrict__ target, const float* __restrict__ draft, int draft_kind,
-    const float* __restrict__ uniforms, int64_t B, int64_t gamma, int64_t V, float inv_t,
-    int32_t* __restrict__ out_tokens, Ws ws) {
-  constexpr int PL = kDrawChunk / 64;
+    const float* __restrict__ target, const float* __restrict__ draft, int draft_kind, int64_t B, int64_t gamma,
+    int64_t V, float inv_t, int32_t* __restrict__ out_tokens, Ws ws) {
   const int lane = threadIdx.x & 63;
   const int64_t b = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (b >= B) return;
   const int64_t ndc = draw_chunks(V);
   const int64_t g1 = gamma + 1;
-  const int k = ws.kb[b];
-  const DrawRow R = draw_row(target, draft, draft_kind, b, B, gamma, V, k, inv_t, ws);
-  const double* part = ws.sres + b * ndc;
+  // Descriptor and the first 64 chunk totals in one round of loads.
+  const DrawDesc D = ws.desc[b];
+  const double* pr = ws.sres + b * ndc;
+  const double* pp = ws.sp + b * ndc;
+  const double pj_r = lane < ndc ? pr[lane] : 0.0;
+  const double pj_p = lane < ndc ? pp[lane] : 0.0;
+  const DrawRow R = make_row(target, draft, draft_kind, b, gamma, V, D, inv_t);
   double tot = 0.0;
   if (R.zq) {
-    for (int64_t j0 = 0; j0 < ndc; j0 += 64) tot += wave_sum(j0 + lane < ndc ? part[j0 + lane] : 0.0);
+    tot = wave_sum(pj_r);
+    for (int64_t j0 = 64; j0 < ndc; j0 += 64) tot += wave_sum(j0 + lane < ndc ? pr[j0 + lane] : 0.0);
   }
   const bool use_p = !(tot > 0.0);
+  const double* part = use_p ? pp : pr;
+  double pj = use_p ? pj_p : pj_r;
   if (use_p) {
-    part = ws.sp + b * ndc;
-    tot = 0.0;
-    for (int64_t j0 = 0; j0 < ndc; j0 += 64) tot += wave_sum(j0 + lane < ndc ? part[j0 + lane] : 0.0);
+    tot = wave_sum(pj_p);
+    for (int64_t j0 = 64; j0 < ndc; j0 += 64) tot += wave_sum(j0 + lane < ndc ? pp[j0 + lane] : 0.0);
   }
-  const float u = uniforms[(b * g1 + k) * 2 + 1];
-  const double t = (double)u * tot;
+  const double t = (double)D.u * tot;
   // First chunk whose running total passes t (or, if rounding leaves none,
   // the last chunk with mass).
   int64_t cs = -1, clast = 0;
   double before = 0.0, run = 0.0;
   for (int64_t j0 = 0; j0 < ndc && cs < 0; j0 += 64) {
-    const double pj = j0 + lane < ndc ? part[j0 + lane] : 0.0;
+    if (j0 > 0) pj = j0 + lane < ndc ? part[j0 + lane] : 0.0;
     const double incl = run + wave_inclusive_scan(pj, lane);
     const uint64_t hit = ballot(j0 + lane < ndc && t < incl);
     const uint64_t pos = ballot(j0 + lane < ndc && pj > 0.0);
@@ -420,12 +451,12 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void select_kernel(
     cs = clast;
     before = run - part[clast];
   }
-  // Rescan: lane l takes the PL consecutive entries starting at cs*kDrawChunk + PL*l.
-  const int64_t s0 = cs * kDrawChunk + (int64_t)PL * lane;
-  float w[PL];
+  // Rescan: lane l takes the 16 consecutive entries starting at cs*1024 + 16*l.
+  const int64_t s0 = cs * kDrawChunk + 16 * (int64_t)lane;
+  float w[16];
   double lsum = 0.0;
 #pragma unroll
-  for (int j = 0; j < PL / 4; ++j) {
+  for (int j = 0; j < 4; ++j) {
     const int64_t v = s0 + 4 * j;
     float ap[4], aq[4];
     if (VEC && v + 3 < V) {
@@ -454,7 +485,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void select_kernel(
   double C = before + (incl - lsum);
   int hit = -1, lastpos = -1;
 #pragma unroll
-  for (int e = 0; e < PL; ++e) {
+  for (int e = 0; e < 16; ++e) {
     C += (double)w[e];
     if (w[e] > 0.0f) {
       lastpos = (int)(s0 + e);
@@ -465,10 +496,12 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void select_kernel(
   lastpos = wave_max_i(lastpos);
   int tok = hits ? __shfl(hit, __builtin_ctzll(hits)) : lastpos;
   if (tok < 0 || tok >= V) tok = 0;  // no positive weight anywhere (non-finite inputs)
-  if (lane == 0) out_tokens[b * g1 + k] = tok;
+  if (lane == 0) out_tokens[b * g1 + D.k] = tok;
 }
 
-// 2'. Greedy (T == 0): one wave per sequence; lane i holds row i's argmax.
+// 2'. Greedy decide (T == 0): one wave per sequence; lanes run over the chunk
+//     partials of each row in turn (all loads of a batch issued first), then
+//     lane i holds row i's argmax.
 __global__ __launch_bounds__(kWavesPerBlock * 64) void greedy_kernel(const int32_t* __restrict__ tokens, int64_t B,
                                                                       int64_t gamma, int64_t V,
                                                                       int32_t* __restrict__ out_tokens,
@@ -476,37 +509,37 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void greedy_kernel(const int32
   const int lane = threadIdx.x & 63;
   const int64_t b = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (b >= B) return;
-  const int64_t nch = stat_chunks(V);
   const int64_t g1 = gamma + 1;
+  const int64_t nch = stat_chunks(V);
+  const bool drafted = lane < gamma;
+  const int xi = drafted ? clamp_token(tokens[b * gamma + lane], V) : 0;
   int mine = 0;
-  for (int r0 = 0; r0 < g1; r0 += kRowBatch) {
-    float cv[kRowBatch];
-    int ci[kRowBatch];
+  for (int r0 = 0; r0 < g1; r0 += kMergeBatch) {
+    float cv[kMergeBatch];
+    int ci[kMergeBatch];
 #pragma unroll
-    for (int j = 0; j < kRowBatch; ++j) {
+    for (int j = 0; j < kMergeBatch; ++j) {
       cv[j] = -INFINITY;
       ci[j] = 0x7fffffff;
       if (r0 + j < g1) {
         const size_t base = (size_t)(b * g1 + r0 + j) * nch;
         for (int64_t c = lane; c < nch; c += 64) {
           const float v = ws.cmax[base + c];
-          const int i = ws.cidx[base + c];
-          if (v > cv[j] || (v == cv[j] && i < ci[j])) {
+          const int ix = ws.cidx[base + c];
+          if (v > cv[j] || (v == cv[j] && ix < ci[j])) {
             cv[j] = v;
-            ci[j] = i;
+            ci[j] = ix;
           }
         }
       }
     }
 #pragma unroll
-    for (int j = 0; j < kRowBatch; ++j) {
+    for (int j = 0; j < kMergeBatch; ++j) {
       if (r0 + j >= g1) break;
       wave_argmax(cv[j], ci[j]);
       if (lane == r0 + j) mine = (ci[j] >= 0 && ci[j] < V) ? ci[j] : 0;  // all-NaN row: any in-range id
     }
   }
-  const bool drafted = lane < gamma;
-  const int xi = drafted ? clamp_token(tokens[b * gamma + lane], V) : 0;
   const uint64_t miss = ballot(drafted && xi != mine);
   const int k = miss ? (int)__builtin_ctzll(miss) : (int)gamma;
   const int gk = __shfl(mine, k);
@@ -514,7 +547,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void greedy_kernel(const int32
   if (lane == 0) out_num[b] = k + 1;
 }
 
-inline unsigned blocks_for(int64_t items) { return (unsigned)((items + kWavesPerBlock - 1) / kWavesPerBlock); }
+inline unsigned blocks_for(int64_t items, int per) { return (unsigned)((items + per - 1) / per); }
 
 }  // namespace
 
@@ -528,12 +561,11 @@ hipError_t launch_reject_sample(const RejectArgs& a, hipStream_t stream) {
   const float inv_t = greedy ? 1.0f : (float)(1.0 / (double)a.temperature);
   const int64_t n_target = a.B * (a.gamma + 1);
   const int64_t n_rows = n_target + ((!greedy && a.draft_kind == 0) ? a.B * a.gamma : 0);
-  const int64_t nch = stat_chunks(a.V);
   const dim3 blk(kWavesPerBlock * 64);
-  const dim3 g1(blocks_for(n_rows * nch));
-#define SPECDEC_STATS(V4, GR)                                                                                      \
-  hipLaunchKernelGGL((stats_kernel<V4, GR>), g1, blk, 0, stream, a.target, a.draft, n_target, n_rows, a.gamma, a.V, \
-                     inv_t, ws)
+  const dim3 g1(blocks_for(n_rows * stat_chunks(a.V), kWavesPerBlock));
+#define SPECDEC_STATS(V4, GR)                                                                                        \
+  hipLaunchKernelGGL((stats_kernel<V4, GR>), g1, blk, 0, stream, a.target, a.draft, a.tokens, n_target, n_rows, \
+                     a.gamma, a.V, inv_t, ws)
   if (greedy) {
     if (vec) SPECDEC_STATS(true, true); else SPECDEC_STATS(false, true);
   } else {
@@ -543,30 +575,30 @@ hipError_t launch_reject_sample(const RejectArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (greedy) {
-    hipLaunchKernelGGL(greedy_kernel, dim3(blocks_for(a.B)), blk, 0, stream, a.tokens, a.B, a.gamma, a.V,
-                       a.out_tokens, a.out_num, ws);
+    hipLaunchKernelGGL(greedy_kernel, dim3(blocks_for(a.B, kWavesPerBlock)), blk, 0, stream, a.tokens, a.B, a.gamma,
+                       a.V, a.out_tokens, a.out_num, ws);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(merge_kernel, dim3(blocks_for(n_rows)), blk, 0, stream, a.target, a.draft, a.tokens, n_target,
-                     n_rows, a.gamma, a.V, inv_t, ws);
+  const int64_t ndc = draw_chunks(a.V);
+#define SPECDEC_DRAW(WB, V4)                                                                                    \
+  hipLaunchKernelGGL((draw_sum_kernel<WB, V4>), dim3((unsigned)(a.B * ((ndc + WB - 1) / WB))), dim3(WB * 64), 0, \
+                     stream, a.target, a.draft, a.draft_kind, a.tokens, a.uniforms, a.B, a.gamma, a.V, inv_t,      \
+                     a.out_tokens, a.out_num, a.out_probs, ws)
+  if (ndc >= 16) {
+    if (vec) SPECDEC_DRAW(16, true); else SPECDEC_DRAW(16, false);
+  } else {
+    if (vec) SPECDEC_DRAW(4, true); else SPECDEC_DRAW(4, false);
+  }
+#undef SPECDEC_DRAW
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 g3(blocks_for(a.B * draw_chunks(a.V)));
+  const dim3 g3(blocks_for(a.B, kWavesPerBlock));
   if (vec)
-    hipLaunchKernelGGL((draw_sum_kernel<true>), g3, blk, 0, stream, a.target, a.draft, a.draft_kind, a.tokens,
-                       a.uniforms, a.B, a.gamma, a.V, inv_t, a.out_tokens, a.out_num, a.out_probs, ws);
+    hipLaunchKernelGGL((select_kernel<true>), g3, blk, 0, stream, a.target, a.draft, a.draft_kind, a.B, a.gamma, a.V,
+                       inv_t, a.out_tokens, ws);
   else
-    hipLaunchKernelGGL((draw_sum_kernel<false>), g3, blk, 0, stream, a.target, a.draft, a.draft_kind, a.tokens,
-                       a.uniforms, a.B, a.gamma, a.V, inv_t, a.out_tokens, a.out_num, a.out_probs, ws);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 g4(blocks_for(a.B));
-  if (vec)
-    hipLaunchKernelGGL((select_kernel<true>), g4, blk, 0, stream, a.target, a.draft, a.draft_kind, a.uniforms, a.B,
-                       a.gamma, a.V, inv_t, a.out_tokens, ws);
-  else
-    hipLaunchKernelGGL((select_kernel<false>), g4, blk, 0, stream, a.target, a.draft, a.draft_kind, a.uniforms, a.B,
-                       a.gamma, a.V, inv_t, a.out_tokens, ws);
+    hipLaunchKernelGGL((select_kernel<false>), g3, blk, 0, stream, a.target, a.draft, a.draft_kind, a.B, a.gamma,
+                       a.V, inv_t, a.out_tokens, ws);
   return hipGetLastError();
 }
 
