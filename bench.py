@@ -10,6 +10,7 @@ HBM before timing starts.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -17,6 +18,32 @@ import time
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published peak
 METRIC = "verified positions/sec and achieved HBM GB/s (% of peak) per verify step"
+HERE = os.path.dirname(os.path.abspath(__file__))
+# The sources of the dominant kernel (the sweep scoring GEMM) that the traffic record below was measured on.
+GEMM_SOURCES = [os.path.join(HERE, "speculative_decoding_verification_09_amd", "csrc", f)
+                for f in ("gemm_common.h", "gemm_sweep.hip")]
+
+# HBM bytes per scoring launch, from hardware counters (FETCH_SIZE and WRITE_SIZE, each in its own rocprofv3
+# --pmc run of this script, scaled by what the same counter reads for a plain device copy of known size: 2.0 for
+# FETCH_SIZE, 1.0 for WRITE_SIZE).  Keyed by workload, weight layout and the SHA-256 of the GEMM source the
+# counters were taken on: once that source changes, the record no longer describes the kernel and traffic is null.
+MEASURED_TRAFFIC = {
+    ("lmhead_b1_g4", "packed"): {"fetch_bytes": 1051057782, "write_bytes": 2565120,
+                                 "source_sha256": "d11f64a8c3b89ea70066b2d171c3e2c90915c796e01ee3717845f98a8d135401"},
+}
+
+
+def measured_traffic(workload: str, layout: str):
+    rec = MEASURED_TRAFFIC.get((workload, layout))
+    if rec is None:
+        return None
+    h = hashlib.sha256()
+    for path in GEMM_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
 
 
 def algorithmic_bytes(w):
@@ -39,7 +66,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="lmhead_b1_g4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-steps", type=int, default=3, help="oracle steps timed for the CPU baseline")
+    ap.add_argument("--cpu-steps", type=int, default=8, help="oracle sequences timed for the CPU baseline")
     ap.add_argument("--layout", choices=["packed", "rowmajor"], default="packed", help="weight layout")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (a known byte count for hardware counters)")
@@ -134,15 +161,17 @@ def main():
     ms_step = evs.elapsed_time(eve) / K
     emitted = int(out_num.sum().item())
 
-    # ---- timed region 2 (the roofline of the dominant kernel): K scoring launches, each between two events
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    # ---- timed region 2 (the roofline of the dominant kernel): K scoring launches back to back on the same
+    # stream between two events.  (An event between every launch would add its own release to each interval.)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    for i in range(K):
-        ev0[i].record(stream)
+    ev0.record(stream)
+    for _ in range(K):
         sd.specdec_verify_logits(X, W, logits, stream=stream)
-    ev0[K].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
-    gemm_ms = float(np.mean([ev0[i].elapsed_time(ev0[i + 1]) for i in range(K)]))
+    gemm_ms = ev0.elapsed_time(ev1) / K
 
     gemm_bytes, step_bytes = algorithmic_bytes(w)
     gemm_gbps = gemm_bytes / (gemm_ms * 1e-3) / 1e9
@@ -191,9 +220,10 @@ def main():
         "step_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
         "step_bytes": step_bytes,
         "emitted_tokens_per_s": emitted / (ms_step * 1e-3),
-        "roofline": {"kernel": "scoring GEMM (sweep_kernel packed / tiled_kernel)", "bound": "hbm", "achieved": gemm_gbps, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": gemm_gbps / HBM_PEAK_GBPS, "traffic": None,
-                     "bytes_per_launch": gemm_bytes, "avg_launch_ms": gemm_ms},
+        "roofline": {"kernel": "scoring GEMM (specdec_verify_logits)", "bound": "hbm", "achieved": gemm_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gemm_gbps / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(w.name, args.layout), "bytes_per_launch": gemm_bytes,
+                     "avg_launch_ms": gemm_ms},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -12,6 +12,13 @@ namespace specdec {
 hipError_t launch_skinny_gemm(const uint16_t* X, const uint16_t* W, void* Y, int64_t N, int64_t d, int64_t V,
                               bool out_bf16, bool packed, hipStream_t stream);
 
+namespace gemm {
+// The sweep kernel (packed W, at most 8 positions, X held in LDS whole).
+bool sweep_applies(int64_t N, int64_t d);
+hipError_t launch_sweep(const uint16_t* X, const uint16_t* Wp, void* Y, int64_t N, int64_t d, int64_t V, bool out_bf16,
+                        hipStream_t stream);
+}  // namespace gemm
+
 // Packed tile layout of W [V, d] (d % 32 == 0): ceil(V/16)*16*d elements.
 int64_t packed_weight_elems(int64_t V, int64_t d);
 hipError_t launch_pack_weights(const uint16_t* W, uint16_t* Wp, int64_t V, int64_t d, hipStream_t stream);
