@@ -28,8 +28,8 @@ GEMM_SOURCES = [os.path.join(HERE, "speculative_decoding_verification_09_amd", "
 # FETCH_SIZE, 1.0 for WRITE_SIZE).  Keyed by workload, weight layout and the SHA-256 of the GEMM source the
 # counters were taken on: once that source changes, the record no longer describes the kernel and traffic is null.
 MEASURED_TRAFFIC = {
-    ("lmhead_b1_g4", "packed"): {"fetch_bytes": 1051057782, "write_bytes": 2565120,
-                                 "source_sha256": "d11f64a8c3b89ea70066b2d171c3e2c90915c796e01ee3717845f98a8d135401"},
+    ("lmhead_b1_g4", "packed"): {"fetch_bytes": 1081605294, "write_bytes": 2565120,
+                                 "source_sha256": "a4b5529c0f358de8da1c4a8bcecfe32f71ac33e0dcc8cd1ee171be161823297f"},
 }
 
 
@@ -105,11 +105,13 @@ def main():
     logits = torch.empty((N, V), dtype=torch.float32, device=dev)
     out_tok = torch.empty((B, g + 1), dtype=torch.int32, device=dev)
     out_num = torch.empty((B,), dtype=torch.int32, device=dev)
-    ws = sd.new_workspace(B, g, V)
+    layout = sd.SPECDEC_WEIGHTS_PACKED if args.layout == "packed" else sd.SPECDEC_WEIGHTS_ROW_MAJOR
+    ws = sd.new_step_workspace(B, g, d, V, layout)
+    gemm_ws = torch.empty(max(1, sd.logits_workspace_bytes(N, d, V, layout)), dtype=torch.uint8, device=dev)
     uni = torch.from_numpy(synth.step_uniforms(w)).to(dev)
     # Draft logits = target logits + N(0, noise) and drafted tokens ~ q: built with the library itself
     # (one scoring pass, then one draw per drafted row as gamma = 0 steps), outside the timed region.
-    sd.specdec_verify_logits(X, W, logits)
+    sd.specdec_verify_logits(X, W, logits, workspace=gemm_ws)
     if T > 0:
         tl = logits.view(B, g + 1, V)[:, :g]
         noise = torch.from_numpy(synth.normal_f32((B, g, V), w.noise_std, w.seed, synth.STREAM_DRAFT_NOISE)).to(dev)
@@ -168,7 +170,7 @@ def main():
     torch.cuda.synchronize()
     ev0.record(stream)
     for _ in range(K):
-        sd.specdec_verify_logits(X, W, logits, stream=stream)
+        sd.specdec_verify_logits(X, W, logits, workspace=gemm_ws, stream=stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     gemm_ms = ev0.elapsed_time(ev1) / K

@@ -83,6 +83,20 @@ int specdec_version(void);
  * meaningless after the call.  Returns 0 for invalid sizes. */
 size_t specdec_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
 
+/* Bytes of device workspace that specdec_verify_logits needs for N positions,
+ * hidden size d, V outputs and the given weight layout, on the current
+ * device.  0 means none (the workspace argument may then be NULL).  When the
+ * output rows are too few to occupy every compute unit, or X is too large to
+ * stage whole, the k range is split into groups whose fp32 partial sums are
+ * kept here and then added in group order.  Returns 0 for invalid sizes. */
+size_t specdec_logits_workspace_bytes(int64_t N, int64_t d, int64_t V, int weight_layout);
+
+/* Bytes of device workspace that specdec_verify_step needs: the larger of
+ * specdec_workspace_bytes(B, gamma, V) and
+ * specdec_logits_workspace_bytes(B*(gamma+1), d, V, weight_layout), since the
+ * two stages use it one after the other.  Returns 0 for invalid sizes. */
+size_t specdec_step_workspace_bytes(int64_t B, int64_t gamma, int64_t d, int64_t V, int weight_layout);
+
 /* Bytes of the packed weight layout of a [V, d] bf16 matrix (d % 32 == 0):
  * ceil(V/16)*16*d*2.  Returns 0 for invalid sizes. */
 size_t specdec_packed_weight_bytes(int64_t V, int64_t d);
@@ -108,11 +122,15 @@ int specdec_pack_weights(const void* W, void* W_packed, int64_t V, int64_t d, vo
  *      specdec_pack_weights (SPECDEC_WEIGHTS_PACKED, needs d % 32 == 0)
  *   Y  device, [N, V]: fp32 (out_dtype SPECDEC_OUT_F32) or bf16 rounded to
  *      nearest even (SPECDEC_OUT_BF16)
- * Products are exact and accumulate in fp32.  Requires N >= 1, d >= 8 with
- * d % 8 == 0, V >= 1; X and W 16-byte aligned.  Y needs 16-byte alignment
- * and V % 4 == 0 for the fast store path; other V use element stores. */
+ *   workspace  device, at least specdec_logits_workspace_bytes(N, d, V,
+ *      weight_layout) bytes, 16-byte aligned (may be NULL when that is 0);
+ *      needs no initialisation, meaningless after the call
+ * Products are exact and accumulate in fp32 (in k order within a k-group;
+ * k-groups, when the shape uses them, are added in order).  Requires N >= 1,
+ * d >= 8 with d % 8 == 0, V >= 1; X and W 16-byte aligned.  Y needs 16-byte
+ * alignment (8 for bf16) when V % 4 == 0; other V use element stores. */
 int specdec_verify_logits(const void* X, const void* W, void* Y, int64_t N, int64_t d, int64_t V, int out_dtype,
-                          int weight_layout, void* stream);
+                          int weight_layout, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The rejection-sampling rule on given target logits ([LLMI] section 2,
  * acceptance rule, residual distribution and bonus token; [MATH] "The
@@ -156,6 +174,8 @@ int specdec_reject_sample(const float* target_logits, const float* draft, int dr
  *            specdec_verify_logits
  *   logits   device fp32 [B*(gamma+1), V]: caller scratch that receives the
  *            target logits
+ *   workspace at least specdec_step_workspace_bytes(B, gamma, d, V,
+ *            weight_layout) bytes, shared by the two stages
  * Other arguments as in specdec_reject_sample. */
 int specdec_verify_step(const void* X, const void* W, int weight_layout, const float* draft, int draft_kind,
                         const int32_t* draft_tokens, float temperature, const float* uniforms, int64_t B,

@@ -30,6 +30,8 @@ EXPORTED = [
     "specdec_status_string",
     "specdec_version",
     "specdec_workspace_bytes",
+    "specdec_logits_workspace_bytes",
+    "specdec_step_workspace_bytes",
     "specdec_packed_weight_bytes",
     "specdec_pack_weights",
     "specdec_verify_logits",
@@ -54,11 +56,15 @@ def _load() -> ctypes.CDLL:
     lib.specdec_version.restype = I
     lib.specdec_workspace_bytes.argtypes = [I64, I64, I64]
     lib.specdec_workspace_bytes.restype = ctypes.c_size_t
+    lib.specdec_logits_workspace_bytes.argtypes = [I64, I64, I64, I]
+    lib.specdec_logits_workspace_bytes.restype = ctypes.c_size_t
+    lib.specdec_step_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
+    lib.specdec_step_workspace_bytes.restype = ctypes.c_size_t
     lib.specdec_packed_weight_bytes.argtypes = [I64, I64]
     lib.specdec_packed_weight_bytes.restype = ctypes.c_size_t
     lib.specdec_pack_weights.argtypes = [P, P, I64, I64, P]
     lib.specdec_pack_weights.restype = I
-    lib.specdec_verify_logits.argtypes = [P, P, P, I64, I64, I64, I, I, P]
+    lib.specdec_verify_logits.argtypes = [P, P, P, I64, I64, I64, I, I, P, ctypes.c_size_t, P]
     lib.specdec_verify_logits.restype = I
     lib.specdec_reject_sample.argtypes = [P, P, I, P, ctypes.c_float, P, I64, I64, I64, P, P, P, P, ctypes.c_size_t, P]
     lib.specdec_reject_sample.restype = I
@@ -84,7 +90,18 @@ def version() -> int:
 
 
 def workspace_bytes(B: int, gamma: int, V: int) -> int:
+    """Workspace of specdec_reject_sample."""
     return int(_lib.specdec_workspace_bytes(int(B), int(gamma), int(V)))
+
+
+def logits_workspace_bytes(N: int, d: int, V: int, weight_layout: int) -> int:
+    """Workspace of specdec_verify_logits (0: none needed)."""
+    return int(_lib.specdec_logits_workspace_bytes(int(N), int(d), int(V), int(weight_layout)))
+
+
+def step_workspace_bytes(B: int, gamma: int, d: int, V: int, weight_layout: int) -> int:
+    """Workspace of specdec_verify_step."""
+    return int(_lib.specdec_step_workspace_bytes(int(B), int(gamma), int(d), int(V), int(weight_layout)))
 
 
 def _ptr(t):
@@ -150,16 +167,23 @@ def _weights(W):
 
 
 def specdec_verify_logits(X: torch.Tensor, W, Y: torch.Tensor, out_dtype: int = SPECDEC_OUT_F32,
-                          stream=None) -> torch.Tensor:
-    """Y = X W^T.  X bf16 [N, d], W bf16 [V, d] or PackedWeights, Y fp32 or bf16 [N, V] (written)."""
+                          workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y = X W^T.  X bf16 [N, d], W bf16 [V, d] or PackedWeights, Y fp32 or bf16 [N, V] (written).
+    workspace: device bytes >= logits_workspace_bytes(N, d, V, layout); when None and the shape needs one,
+    a buffer is taken from torch's allocator for this call."""
     N, d = X.shape
     wp, V, dw, layout = _weights(W)
     if dw != d:
         raise ValueError(f"X has d={d}, W has d={dw}")
     _expect(X, torch.bfloat16, (N, d), "X")
     _expect(Y, torch.float32 if out_dtype == SPECDEC_OUT_F32 else torch.bfloat16, (N, V), "Y")
-    _check(_lib.specdec_verify_logits(_ptr(X), wp, _ptr(Y), N, d, V, int(out_dtype), layout, _stream(stream)),
-           "specdec_verify_logits")
+    if workspace is None:
+        need = logits_workspace_bytes(N, d, V, layout)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.specdec_verify_logits(_ptr(X), wp, _ptr(Y), N, d, V, int(out_dtype), layout, _ptr(workspace),
+                                      nbytes, _stream(stream)), "specdec_verify_logits")
     return Y
 
 
@@ -221,3 +245,8 @@ def specdec_verify_step(X, W, draft, draft_tokens, temperature: float, uniforms,
 def new_workspace(B: int, gamma: int, V: int, device="cuda") -> torch.Tensor:
     """A device byte buffer of the size specdec_reject_sample needs."""
     return torch.empty(workspace_bytes(B, gamma, V), dtype=torch.uint8, device=device)
+
+
+def new_step_workspace(B: int, gamma: int, d: int, V: int, weight_layout: int, device="cuda") -> torch.Tensor:
+    """A device byte buffer of the size specdec_verify_step needs."""
+    return torch.empty(step_workspace_bytes(B, gamma, d, V, weight_layout), dtype=torch.uint8, device=device)

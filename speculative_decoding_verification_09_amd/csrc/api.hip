@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kVersion = 10000;  // 1.0.0
+constexpr int kVersion = 10100;  // 1.1.0
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -17,13 +17,19 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 constexpr int64_t kMaxRows = (int64_t)1 << 26;
 
-int check_logits_args(const void* X, const void* W, const void* Y, int64_t N, int64_t d, int64_t V, int out_dtype,
-                      int weight_layout) {
-  if (!X || !W || !Y) return SPECDEC_ERR_NULL;
+int check_logits_shape(int64_t N, int64_t d, int64_t V, int weight_layout) {
   if (weight_layout != SPECDEC_WEIGHTS_ROW_MAJOR && weight_layout != SPECDEC_WEIGHTS_PACKED) return SPECDEC_ERR_ARG;
   if (N < 1 || N > kMaxRows || d < 8 || d % 8 != 0 || d > kMaxDim || V < 1 || V > kMaxDim) return SPECDEC_ERR_SHAPE;
   if (weight_layout == SPECDEC_WEIGHTS_PACKED && d % 32 != 0) return SPECDEC_ERR_SHAPE;
   if ((size_t)N * (size_t)V > ((size_t)1 << 40) || (size_t)V * (size_t)d > ((size_t)1 << 40)) return SPECDEC_ERR_SHAPE;
+  return SPECDEC_OK;
+}
+
+int check_logits_args(const void* X, const void* W, const void* Y, int64_t N, int64_t d, int64_t V, int out_dtype,
+                      int weight_layout) {
+  if (!X || !W || !Y) return SPECDEC_ERR_NULL;
+  const int st = check_logits_shape(N, d, V, weight_layout);
+  if (st != SPECDEC_OK) return st;
   if (out_dtype != SPECDEC_OUT_F32 && out_dtype != SPECDEC_OUT_BF16) return SPECDEC_ERR_ARG;
   if (!aligned16(X) || !aligned16(W)) return SPECDEC_ERR_ALIGN;
   if (V % 4 == 0) {
@@ -56,6 +62,27 @@ int check_reject_args(const float* target, const float* draft, int draft_kind, c
   if (!ws || ws_bytes < need) return SPECDEC_ERR_WORKSPACE;
   if (!aligned16(ws)) return SPECDEC_ERR_ALIGN;
   return SPECDEC_OK;
+}
+
+specdec::RejectArgs reject_args(const float* target, const float* draft, int draft_kind, const int32_t* tokens,
+                                float T, const float* uniforms, int64_t B, int64_t gamma, int64_t V,
+                                int32_t* out_tokens, int32_t* out_num, float* out_probs, void* ws, size_t ws_bytes) {
+  specdec::RejectArgs a;
+  a.target = target;
+  a.draft = draft;
+  a.draft_kind = draft_kind;
+  a.tokens = tokens;
+  a.temperature = T;
+  a.uniforms = uniforms;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.out_tokens = out_tokens;
+  a.out_num = out_num;
+  a.out_probs = T == 0.0f ? nullptr : out_probs;
+  a.workspace = ws;
+  a.workspace_bytes = ws_bytes;
+  return a;
 }
 
 }  // namespace
@@ -98,13 +125,31 @@ int specdec_pack_weights(const void* W, void* W_packed, int64_t V, int64_t d, vo
   return e == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
 }
 
+size_t specdec_logits_workspace_bytes(int64_t N, int64_t d, int64_t V, int weight_layout) {
+  if (check_logits_shape(N, d, V, weight_layout) != SPECDEC_OK) return 0;
+  return specdec::gemm_workspace_bytes(N, d, V, weight_layout == SPECDEC_WEIGHTS_PACKED);
+}
+
+size_t specdec_step_workspace_bytes(int64_t B, int64_t gamma, int64_t d, int64_t V, int weight_layout) {
+  if (B < 1 || B > kMaxRows || gamma < 0 || gamma > SPECDEC_MAX_GAMMA || V < 1 || V > kMaxDim) return 0;
+  const int64_t N = B * (gamma + 1);
+  if (check_logits_shape(N, d, V, weight_layout) != SPECDEC_OK) return 0;
+  const size_t r = specdec::reject_workspace_bytes(B, gamma, V);
+  const size_t g = specdec::gemm_workspace_bytes(N, d, V, weight_layout == SPECDEC_WEIGHTS_PACKED);
+  return r > g ? r : g;
+}
+
 int specdec_verify_logits(const void* X, const void* W, void* Y, int64_t N, int64_t d, int64_t V, int out_dtype,
-                          int weight_layout, void* stream) {
+                          int weight_layout, void* workspace, size_t workspace_bytes, void* stream) {
   const int st = check_logits_args(X, W, Y, N, d, V, out_dtype, weight_layout);
   if (st != SPECDEC_OK) return st;
-  const hipError_t e =
-      specdec::launch_skinny_gemm((const uint16_t*)X, (const uint16_t*)W, Y, N, d, V, out_dtype == SPECDEC_OUT_BF16,
-                                  weight_layout == SPECDEC_WEIGHTS_PACKED, (hipStream_t)stream);
+  const bool packed = weight_layout == SPECDEC_WEIGHTS_PACKED;
+  const size_t need = specdec::gemm_workspace_bytes(N, d, V, packed);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SPECDEC_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return SPECDEC_ERR_ALIGN;
+  const hipError_t e = specdec::launch_skinny_gemm((const uint16_t*)X, (const uint16_t*)W, Y, N, d, V,
+                                                   out_dtype == SPECDEC_OUT_BF16, packed, workspace,
+                                                   (hipStream_t)stream);
   return e == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
 }
 
@@ -115,21 +160,9 @@ int specdec_reject_sample(const float* target_logits, const float* draft, int dr
   const int st = check_reject_args(target_logits, draft, draft_kind, draft_tokens, temperature, uniforms, B, gamma, V,
                                    out_tokens, out_num_emitted, out_probs, workspace, workspace_bytes);
   if (st != SPECDEC_OK) return st;
-  specdec::RejectArgs a;
-  a.target = target_logits;
-  a.draft = draft;
-  a.draft_kind = draft_kind;
-  a.tokens = draft_tokens;
-  a.temperature = temperature;
-  a.uniforms = uniforms;
-  a.B = B;
-  a.gamma = gamma;
-  a.V = V;
-  a.out_tokens = out_tokens;
-  a.out_num = out_num_emitted;
-  a.out_probs = temperature == 0.0f ? nullptr : out_probs;
-  a.workspace = workspace;
-  a.workspace_bytes = workspace_bytes;
+  const specdec::RejectArgs a = reject_args(target_logits, draft, draft_kind, draft_tokens, temperature, uniforms, B,
+                                            gamma, V, out_tokens, out_num_emitted, out_probs, workspace,
+                                            workspace_bytes);
   const hipError_t e = specdec::launch_reject_sample(a, (hipStream_t)stream);
   return e == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
 }
@@ -146,10 +179,27 @@ int specdec_verify_step(const void* X, const void* W, int weight_layout, const f
   st = check_reject_args(logits, draft, draft_kind, draft_tokens, temperature, uniforms, B, gamma, V, out_tokens,
                          out_num_emitted, out_probs, workspace, workspace_bytes);
   if (st != SPECDEC_OK) return st;
-  return specdec_verify_logits(X, W, logits, N, d, V, SPECDEC_OUT_F32, weight_layout, stream) == SPECDEC_OK
-             ? specdec_reject_sample(logits, draft, draft_kind, draft_tokens, temperature, uniforms, B, gamma, V,
-                                     out_tokens, out_num_emitted, out_probs, workspace, workspace_bytes, stream)
-             : SPECDEC_ERR_LAUNCH;
+  if (workspace_bytes < specdec_step_workspace_bytes(B, gamma, d, V, weight_layout)) return SPECDEC_ERR_WORKSPACE;
+  const specdec::RejectArgs a = reject_args(logits, draft, draft_kind, draft_tokens, temperature, uniforms, B, gamma,
+                                            V, out_tokens, out_num_emitted, out_probs, workspace, workspace_bytes);
+  const hipStream_t s = (hipStream_t)stream;
+  // Packed weights and few positions: the scoring kernel also forms the
+  // softmax (or argmax) partials of every row, so the sampling stages start
+  // from them and no separate statistics pass reads the logits again.
+  specdec::FusedStats fs;
+  if (weight_layout == SPECDEC_WEIGHTS_PACKED && specdec::reject_fused_stats(a, &fs)) {
+    int64_t nparts = 0;
+    const hipError_t e =
+        specdec::launch_gemm_with_stats((const uint16_t*)X, (const uint16_t*)W, logits, N, d, V, fs, &nparts, s);
+    if (e == hipSuccess)
+      return specdec::launch_reject_after_fused(a, nparts, s) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
+    if (e != hipErrorNotSupported) return SPECDEC_ERR_LAUNCH;
+  }
+  // The scoring pass finishes (stream order) before the sampling kernels reuse the workspace.
+  if (specdec_verify_logits(X, W, logits, N, d, V, SPECDEC_OUT_F32, weight_layout, workspace, workspace_bytes,
+                            stream) != SPECDEC_OK)
+    return SPECDEC_ERR_LAUNCH;
+  return specdec::launch_reject_sample(a, s) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
 }
 
 }  // extern "C"

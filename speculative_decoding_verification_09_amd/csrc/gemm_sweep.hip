@@ -47,37 +47,82 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Sweep kernel (packed W, small N).  Work unit u = (tile, k-group): tile
-// t = blockIdx.x + (u / ngroups) * gridDim.x, group u % ngroups.  Wave w owns
-// k-steps [w*spw, (w+1)*spw) of every tile, taken SPW at a time.
-template <int NW, int SPW, bool NTL, bool OUT_BF16>
+// Sweep kernel (packed W, small N).  The k range may be split into groups of
+// spk k-steps (KG = ceil(nsteps / spk) groups): block b takes group b % KG of
+// the tiles t = b / KG + j * (gridDim.x / KG), holds only that slice of X in
+// LDS, and writes its partial sums to slice b % KG of Y (fp32 [KG][N][V]),
+// which the caller then sums in group order.  With one group Y is the output.
+// Inside a block, wave w owns k-steps [w*spw, (w+1)*spw) of the group, taken
+// SPW at a time; a work unit u is (tile u / ngroups, register group
+// u % ngroups).
+//
+// Inside the main loop every global load is issued unconditionally, with its
+// address clamped into the wave's k range where a register group runs past it
+// (those values are never used): the compiler can then count outstanding loads
+// exactly and keeps the next unit's loads in flight while the current unit
+// computes, instead of draining all of them at each branch join.
+//
+// Statistics epilogue (EPI 1: softmax at temperature T, EPI 2: argmax), used
+// by the whole verification step with one k-group: wave 0 folds every tile's
+// finished logits into a running per-lane state (max of a = z * fl32(1/T) and
+// an fp64 sum of fp32 exp(a - max), rescaled when the max grows; or the
+// largest z with its lowest index), records the logit of each row's drafted
+// token from the tile that holds it, and at the end leaves one partial per
+// (row, workgroup).  With draft logits, the workgroups that have one tile
+// fewer (they finish first) also summarise a slice of every draft row.
+template <int NW, int SPW, bool NTL, bool OUT_BF16, int EPI>
 __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp,
-                                                        void* __restrict__ Y, int N, int d, int V) {
+                                                        void* __restrict__ Y, int N, int d, int V, int spk,
+                                                        FusedStats fs) {
   extern __shared__ __align__(16) uint16_t lds[];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, m = lane & 15, g = lane >> 4;
-  const int pitch = d + kPad;
+  const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, g = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int nsteps = d >> 5;
   const int ntiles = (V + 15) >> 4;
-  const int spw = (nsteps + NW - 1) / NW;        // k-steps per wave and tile
-  const int ngroups = (spw + SPW - 1) / SPW;     // register groups per wave and tile
+  const int kgs = (nsteps + spk - 1) / spk;
+  const int kg = (int)blockIdx.x % kgs;
+  const int stream = (int)blockIdx.x / kgs, nstream = (int)gridDim.x / kgs;
+  const int ks0 = kg * spk;                       // first k-step of the group
+  const int kw = min(spk, nsteps - ks0);          // k-steps in the group (>= 1)
+  const int pitch = spk * 32 + kPad;
+  const int spw = (kw + NW - 1) / NW;             // k-steps per wave and tile
+  const int ngroups = (spw + SPW - 1) / SPW;      // register groups per wave and tile
   uint16_t* xs = lds;
   f32x4* red = (f32x4*)(lds + (((size_t)N * pitch + 7) & ~(size_t)7));
-  for (int i = tid; i < N * (d >> 3); i += NW * 64) {
-    const int n = i / (d >> 3), u = i - n * (d >> 3);
-    *(u32x4*)(xs + n * pitch + u * 8) = *(const u32x4*)(X + (size_t)n * d + u * 8);
+  const int units_per_row = kw * 4;               // 16-byte units of one X row slice
+  for (int i = tid; i < N * units_per_row; i += NW * 64) {
+    const int n = i / units_per_row, u = i - n * units_per_row;
+    *(u32x4*)(xs + n * pitch + u * 8) = *(const u32x4*)(X + (size_t)n * d + (size_t)ks0 * 32 + u * 8);
   }
   __syncthreads();
   const bool live = m < N;
-  const int my0 = wv * spw;                       // first k-step of this wave
-  const int my1 = min(my0 + spw, nsteps);         // one past the last
-  const int64_t units = (int64_t)((ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x) * ngroups;
+  const int mx = live ? m : N - 1;                // lanes past N read a valid row; their column is not stored
+  const int my0 = wv * spw;                       // first k-step of this wave, relative to ks0
+  const int my1 = min(my0 + spw, kw);             // one past the last
+  const int last = max(0, min(my1, kw) - 1);      // a k-step of the group this wave may address
+  const int64_t units = stream < ntiles ? (int64_t)((ntiles - stream + nstream - 1) / nstream) * ngroups : 0;
+  float* part = (float*)Y + (size_t)kg * N * V;   // this group's slice when the k range is split
+
+  // Statistics state of lane (token m, rows 4g .. 4g+3 of each tile).
+  float st_m = -INFINITY;
+  double st_s = 0.0;
+  int st_i = 0x7fffffff;
+  int st_x = -1;  // drafted token of this lane's row, if any
+  if (EPI != 0 && live) {
+    const int g1 = (int)fs.gamma + 1;
+    const int bq = m / g1, iq = m - bq * g1;
+    if (iq < fs.gamma) {
+      const int32_t x = fs.tokens[bq * fs.gamma + iq];
+      st_x = x < 0 ? 0 : (x >= V ? V - 1 : x);
+    }
+  }
 
   auto load = [&](u32x4(&dst)[SPW], int64_t u) {
-    const int t = (int)blockIdx.x + (int)(u / ngroups) * (int)gridDim.x;
+    const int t = stream + (int)(u / ngroups) * nstream;
     const int s0 = my0 + (int)(u % ngroups) * SPW;
-    const uint16_t* p = Wp + ((size_t)t * nsteps + s0) * 512 + lane * 8;
+    const uint16_t* p = Wp + ((size_t)t * nsteps + ks0) * 512 + lane * 8;
 #pragma unroll
-    for (int s = 0; s < SPW; ++s) dst[s] = (s0 + s < my1) ? load_w16<NTL>(p + (size_t)s * 512) : u32x4{0u, 0u, 0u, 0u};
+    for (int s = 0; s < SPW; ++s) dst[s] = load_w16<NTL>(p + (size_t)min(s0 + s, last) * 512);
   };
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   auto consume = [&](const u32x4(&a)[SPW], int64_t u) {
@@ -86,7 +131,7 @@ __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restri
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
       if (s0 + s < my1) {
-        const u32x4 bf = live ? *(const u32x4*)(xs + m * pitch + (s0 + s) * 32 + 8 * g) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 bf = *(const u32x4*)(xs + mx * pitch + (s0 + s) * 32 + 8 * g);
         acc = mfma(a[s], bf, acc);
       }
     }
@@ -105,48 +150,187 @@ __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restri
         sum[2] += o[2];
         sum[3] += o[3];
       }
-      const int t = (int)blockIdx.x + (int)(u / ngroups) * (int)gridDim.x;
+      const int t = stream + (int)(u / ngroups) * nstream;
       const int64_t v0 = (int64_t)t * 16 + 4 * g;
-      if (live && v0 < V) store4<OUT_BF16>(Y, (size_t)m * V + v0, v0, V, sum);
+      if (live && v0 < V) {
+        if (kgs == 1)
+          store4<OUT_BF16>(Y, (size_t)m * V + v0, v0, V, sum);
+        else
+          store4<false>(part, (size_t)m * V + v0, v0, V, sum);
+        if (EPI == 1) {
+          float a[4], mt = -INFINITY;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            a[j] = sum[j] * fs.inv_t;
+            if (v0 + j < V) mt = fmaxf(mt, a[j]);
+          }
+          if (mt > st_m) {
+            if (st_s > 0.0) st_s *= exp((double)st_m - (double)mt);
+            st_m = mt;
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (v0 + j < V) st_s += (double)expf(a[j] - st_m);
+        } else if (EPI == 2) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (v0 + j < V && (sum[j] > st_m || (sum[j] == st_m && (int)v0 + j < st_i))) {
+              st_m = sum[j];
+              st_i = (int)v0 + j;
+            }
+        }
+        if (EPI == 1 && st_x >= v0 && st_x < v0 + 4) fs.zx[m] = sum[st_x - (int)v0];
+      }
     }
     __syncthreads();
   };
+  if (units <= 0) return;
+  // Two units per trip so the prefetch registers swap roles without copies;
+  // the loop body loads only units that exist, and the last one or two units
+  // are peeled off so that no load is issued past the end.
   u32x4 a0[SPW], a1[SPW];
-  if (units > 0) load(a0, 0);
-  for (int64_t u = 0; u < units; u += 2) {
-    if (u + 1 < units) load(a1, u + 1);
+  load(a0, 0);
+  int64_t u = 0;
+  for (; u + 2 < units; u += 2) {
+    load(a1, u + 1);
     consume(a0, u);
-    if (u + 1 >= units) break;
-    if (u + 2 < units) load(a0, u + 2);
+    load(a0, u + 2);
     consume(a1, u + 1);
+  }
+  if (u + 1 < units) {
+    load(a1, u + 1);
+    consume(a0, u);
+    consume(a1, u + 1);
+  } else {
+    consume(a0, u);
+  }
+  if (EPI == 0) return;
+
+  // Partials of the target rows: combine the four lanes of each token.
+  if (wv == 0) {
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const float om = __shfl_xor(st_m, o);
+      if (EPI == 1) {
+        const double os = __shfl_xor(st_s, o);
+        const float M = fmaxf(st_m, om);
+        st_s = (st_s > 0.0 ? st_s * exp((double)st_m - (double)M) : 0.0) +
+               (os > 0.0 ? os * exp((double)om - (double)M) : 0.0);
+        st_m = M;
+      } else {
+        const int oi = __shfl_xor(st_i, o);
+        if (om > st_m || (om == st_m && oi < st_i)) {
+          st_m = om;
+          st_i = oi;
+        }
+      }
+    }
+    if (g == 0 && live) {
+      const size_t slot = (size_t)m * fs.pstride + blockIdx.x;
+      fs.cmax[slot] = st_m;
+      if (EPI == 1)
+        fs.csum[slot] = st_s;
+      else
+        fs.cidx[slot] = st_i;
+    }
+  }
+  if (EPI != 1 || fs.draft == nullptr) return;
+
+  // Draft rows: workgroups with the smaller tile count take consecutive
+  // vocabulary slices (a multiple of 4 entries each); the others leave empty
+  // partials.  Wave w takes draft rows w, w + NW, ...
+  const int G = (int)gridDim.x;
+  const int rem = ntiles % G;
+  const int ndraft = rem == 0 ? G : G - rem;
+  const int rank = rem == 0 ? (int)blockIdx.x : (int)blockIdx.x - rem;
+  const int L = (((V + ndraft - 1) / ndraft) + 3) & ~3;
+  const int s0 = rank >= 0 ? min(rank * L, V) : V, s1 = rank >= 0 ? min(s0 + L, V) : V;
+  const int nd = (int)(fs.B * fs.gamma);
+  for (int j = wv; j < nd; j += NW) {
+    const float* row = fs.draft + (size_t)j * V;
+    float mx = -INFINITY;
+    for (int v = s0 + lane; v < s1; v += 64) mx = fmaxf(mx, row[v] * fs.inv_t);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    double sm = 0.0;
+    if (mx > -INFINITY)
+      for (int v = s0 + lane; v < s1; v += 64) sm += (double)expf(row[v] * fs.inv_t - mx);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sm += __shfl_xor(sm, o);
+    if (lane == 0) {
+      const size_t slot = (size_t)(N + j) * fs.pstride + blockIdx.x;
+      fs.cmax[slot] = mx;
+      fs.csum[slot] = sm;
+      const int32_t x = fs.tokens[j];
+      const int xc = x < 0 ? 0 : (x >= V ? V - 1 : x);
+      if (xc >= s0 && xc < s1) fs.zx[N + j] = row[xc];
+    }
   }
 }
 
 constexpr int kSweepWaves = 8;
 constexpr int kSweepGroup = 16;
+constexpr size_t kSweepLdsLimit = 150 * 1024;
 
-size_t sweep_lds_bytes(int64_t N, int64_t d) {
-  return (((size_t)N * (size_t)(d + kPad) + 7) & ~(size_t)7) * sizeof(uint16_t) + (size_t)kSweepWaves * 64 * 16;
+size_t sweep_lds_bytes(int64_t N, int64_t spk) {
+  return (((size_t)N * (size_t)(spk * 32 + kPad) + 7) & ~(size_t)7) * sizeof(uint16_t) +
+         (size_t)kSweepWaves * 64 * 16;
 }
 
 }  // namespace
 
-bool sweep_applies(int64_t N, int64_t d) { return N <= 8 && sweep_lds_bytes(N, d) <= 150 * 1024; }
+SweepPlan plan_sweep(int64_t N, int64_t d, int64_t V, int cus) {
+  SweepPlan p{};
+  const int64_t nsteps = d / 32, ntiles = (V + 15) / 16;
+  if (N > 8 || nsteps < 1) return p;
+  // Fewest k-groups whose X slice fits in LDS and that give every CU a tile.
+  for (int64_t kgs = 1; kgs <= nsteps; ++kgs) {
+    const int64_t spk = (nsteps + kgs - 1) / kgs;
+    const int64_t groups = (nsteps + spk - 1) / spk;
+    if (sweep_lds_bytes(N, spk) > kSweepLdsLimit) continue;
+    if (ntiles * groups < cus && spk > 16) continue;
+    p.ok = true;
+    p.spk = spk;
+    p.kgroups = groups;
+    const int64_t streams = ntiles * groups < cus ? ntiles : (cus / groups > 0 ? cus / groups : 1);
+    p.grid = (streams < ntiles ? streams : ntiles) * groups;
+    return p;
+  }
+  return p;
+}
 
-hipError_t launch_sweep(const uint16_t* X, const uint16_t* Wp, void* Y, int64_t N, int64_t d, int64_t V, bool out_bf16,
-                        hipStream_t stream) {
-  const size_t lds = sweep_lds_bytes(N, d);
-  auto k = out_bf16 ? sweep_kernel<kSweepWaves, kSweepGroup, true, true>
-                    : sweep_kernel<kSweepWaves, kSweepGroup, true, false>;
+hipError_t launch_sweep(const SweepPlan& p, const uint16_t* X, const uint16_t* Wp, void* Y, int64_t N, int64_t d,
+                        int64_t V, bool out_bf16, hipStream_t stream) {
+  const size_t lds = sweep_lds_bytes(N, p.spk);
+  auto k = out_bf16 ? sweep_kernel<kSweepWaves, kSweepGroup, true, true, 0>
+                    : sweep_kernel<kSweepWaves, kSweepGroup, true, false, 0>;
   hipError_t e = allow_lds(k, lds);
   if (e != hipSuccess) return e;
-  const int64_t ntiles = (V + 15) / 16;
-  const int64_t grid = ntiles < device_cus() ? ntiles : device_cus();
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kSweepWaves * 64), lds, stream, X, Wp, Y, (int)N, (int)d, (int)V);
+  const FusedStats none{};
+  hipLaunchKernelGGL(k, dim3((unsigned)p.grid), dim3(kSweepWaves * 64), lds, stream, X, Wp, Y, (int)N, (int)d, (int)V,
+                     (int)p.spk, none);
   return hipGetLastError();
 }
 
 }  // namespace gemm
+
+hipError_t launch_gemm_with_stats(const uint16_t* X, const uint16_t* Wp, float* Y, int64_t N, int64_t d, int64_t V,
+                                  const FusedStats& fs, int64_t* nparts, hipStream_t stream) {
+  using namespace gemm;
+  const SweepPlan p = plan_sweep(N, d, V, device_cus());
+  if (!p.ok || p.kgroups != 1 || p.grid > kFusedStatsMaxParts || p.grid > fs.pstride || N > kFusedStatsMaxRows)
+    return hipErrorNotSupported;
+  const size_t lds = sweep_lds_bytes(N, p.spk);
+  auto k = fs.greedy ? sweep_kernel<kSweepWaves, kSweepGroup, true, false, 2>
+                     : sweep_kernel<kSweepWaves, kSweepGroup, true, false, 1>;
+  hipError_t e = allow_lds(k, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k, dim3((unsigned)p.grid), dim3(kSweepWaves * 64), lds, stream, X, Wp, (void*)Y, (int)N, (int)d,
+                     (int)V, (int)p.spk, fs);
+  e = hipGetLastError();
+  if (e == hipSuccess) *nparts = p.grid;
+  return e;
+}
 
 int64_t packed_weight_elems(int64_t V, int64_t d) { return ((V + 15) / 16) * 16 * d; }
 

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(const uint16_t* __restri
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int m = lane & 15;
   const int g = lane >> 4;
   const int ncols = min(N - n_base, NT * 16);
@@ -59,15 +59,18 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(const uint16_t* __restri
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (PACKED) {
-      wp[r] = W + ((size_t)((vwave >> 4) + r) * nsteps) * 512 + lane * 8;
+      wp[r] = W;
     } else {
       int64_t v = vwave + 16 * r + m;
       v = v < V ? v : (int64_t)V - 1;
-      wp[r] = W + (size_t)v * d + 8 * g;
+      wp[r] = W + (size_t)v * d;
     }
   }
   const int64_t ntiles = ((int64_t)V + 15) >> 4;
 
+  // Global loads are issued unconditionally from clamped addresses and the
+  // values past the edges replaced by zeros with a select, so the compiler
+  // can count outstanding loads and keep the prefetch in flight.
   u32x4 xr[kXPT];
   auto load_x = [&](int c) {
 #pragma unroll
@@ -75,7 +78,8 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(const uint16_t* __restri
       const int i = tid + j * kThreads;
       const int n = i / kUnits, u = i - n * kUnits;
       const int k = c * KC + u * 8;
-      xr[j] = (n < ncols && k < d) ? *(const u32x4*)(Xb + (size_t)n * d + k) : zero;
+      const u32x4 v = *(const u32x4*)(Xb + (size_t)min(n, ncols - 1) * d + min(k, d - 8));
+      xr[j] = (n < ncols && k < d) ? v : zero;
     }
   };
   auto store_x = [&](int buf) {
@@ -94,9 +98,13 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(const uint16_t* __restri
       for (int r = 0; r < R; ++r) {
         if (PACKED) {
           const bool ok = (c * KC + 32 * s) < d && (vwave >> 4) + r < ntiles;
-          dst[s][r] = ok ? load_w16<NTL>(wp[r] + (size_t)(c * kSteps + s) * 512) : zero;
+          const int64_t tile = min((vwave >> 4) + r, ntiles - 1);
+          const int step = min(c * kSteps + s, nsteps - 1);
+          const u32x4 v = load_w16<NTL>(W + ((size_t)tile * nsteps + step) * 512 + lane * 8);
+          dst[s][r] = ok ? v : zero;
         } else {
-          dst[s][r] = k < d ? load_w16<NTL>(wp[r] + c * KC + 32 * s) : zero;
+          const u32x4 v = load_w16<NTL>(wp[r] + min(k, d - 8));
+          dst[s][r] = k < d ? v : zero;
         }
       }
     }
@@ -130,22 +138,30 @@ __global__ __launch_bounds__(NW * 64) void tiled_kernel(const uint16_t* __restri
   // Two chunks per trip so the prefetch registers swap roles without copies.
   // X for the next chunk is loaded before W so that waiting for it does not
   // also wait for the W prefetch (loads complete in issue order).
-  for (int c = 0; c < nch; c += 2) {
-    if (c + 1 < nch) {
-      load_x(c + 1);
-      load_w(wb, c + 1);
-    }
+  // The last one or two chunks are peeled off so that the loop body loads
+  // without conditions and no load is issued past the end.
+  int c = 0;
+  for (; c + 2 < nch; c += 2) {
+    load_x(c + 1);
+    load_w(wb, c + 1);
     compute(wa, 0);
-    if (c + 1 < nch) store_x(1);
+    store_x(1);
     __syncthreads();
-    if (c + 1 >= nch) break;
-    if (c + 2 < nch) {
-      load_x(c + 2);
-      load_w(wa, c + 2);
-    }
+    load_x(c + 2);
+    load_w(wa, c + 2);
     compute(wb, 1);
-    if (c + 2 < nch) store_x(0);
+    store_x(0);
     __syncthreads();
+  }
+  if (c + 1 < nch) {
+    load_x(c + 1);
+    load_w(wb, c + 1);
+    compute(wa, 0);
+    store_x(1);
+    __syncthreads();
+    compute(wb, 1);
+  } else {
+    compute(wa, 0);
   }
 
   // Epilogue: lane holds tokens n = 16t + m, vocabulary rows v0 .. v0+3.
@@ -179,13 +195,16 @@ hipError_t launch_tiled(const uint16_t* X, const uint16_t* W, void* Y, int64_t N
   return hipSuccess;
 }
 // ---------------------------------------------------------------------------
-// Panel kernel.  Grid: vocabulary blocks of NW*R 16-row tiles x token passes
-// of NT*16 tokens, launched in an order where block id i runs on XCD i % 8 and
-// the passes of one vocabulary block take consecutive slots of one XCD.
-// KS: MFMA k-steps (32 k each) per LDS chunk.
+// Panel kernel.  Work items are (vocabulary block, k-group, token pass): a
+// vocabulary block is NW*R 16-row tiles, a token pass NT*16 tokens, and a
+// k-group cpk chunks of KS MFMA k-steps (32 k each).  Block id i runs on XCD
+// i % 8; the token passes of one (vocabulary block, k-group) take consecutive
+// slots of one XCD, so the W rows they share are read from HBM once.  With one
+// k-group the block writes Y; otherwise it writes fp32 partials to slice
+// `group` of Y ([groups][N][V]), which are then summed in group order.
 template <int NT, int R, int NW, int KS, bool OUT_BF16>
 __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp,
-                                                        void* __restrict__ Y, int N, int d, int V, int npass) {
+                                                        void* __restrict__ Y, int N, int d, int V, int npass, int cpk) {
   constexpr int kThreads = NW * 64;
   constexpr int kBlocks = NT * KS;                   // 1 KB X blocks per chunk
   constexpr int kXPT = (kBlocks * 64 + kThreads - 1) / kThreads;
@@ -195,18 +214,26 @@ __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restri
   const int nsteps = d >> 5;
   const int ntiles = (V + 15) >> 4;
   const int nvb = (ntiles + NW * R - 1) / (NW * R);
+  const int nch_all = (nsteps + KS - 1) / KS;
+  const int ngroups = (nch_all + cpk - 1) / cpk;
   const int id = (int)blockIdx.x;
   const int slot = id >> 3;
-  const int vb = (id & 7) + 8 * (slot / npass);
-  if (vb >= nvb) return;
+  const int gi = (id & 7) + 8 * (slot / npass);
+  if (gi >= nvb * ngroups) return;
+  const int vb = gi % nvb, group = gi / nvb;
+  const int c0 = group * cpk, c1 = min(c0 + cpk, nch_all);
   const int n0 = (slot % npass) * NT * 16;
   const int ncols = min(N - n0, NT * 16);
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, m = lane & 15, g = lane >> 4;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, g = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int vt0 = vb * NW * R + wv * R;              // this wave's first 16-row tile
-  const uint16_t* wbase = Wp + (size_t)vt0 * nsteps * 512 + lane * 8;
 
+  // Global loads are issued without conditions, their addresses clamped into
+  // the buffer where a row, tile or k-step lies past the end (such values are
+  // never used), so that the compiler counts outstanding loads exactly and
+  // keeps the prefetch in flight across the computation.
+  //
   // X staging: unit u (16 bytes) = block b = u / 64 (token tile b / KS, k-step
   // b % KS of the chunk), lane position l = u % 64.  Rows past N read row N-1:
   // they only feed output columns that are never stored.
@@ -214,13 +241,11 @@ __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restri
   auto load_x = [&](int c) {
 #pragma unroll
     for (int j = 0; j < kXPT; ++j) {
-      const int u = tid + j * kThreads;
-      if (kXPT * kThreads == kBlocks * 64 || u < kBlocks * 64) {
-        const int b = u >> 6, l = u & 63;
-        const int t = b / KS, s = c * KS + b % KS;
-        const int n = min(n0 + t * 16 + (l & 15), N - 1);
-        xr[j] = s < nsteps ? *(const u32x4*)(X + (size_t)n * d + s * 32 + 8 * (l >> 4)) : zero;
-      }
+      const int u = (tid + j * kThreads) % (kBlocks * 64);
+      const int b = u >> 6, l = u & 63;
+      const int t = b / KS, s = min(c * KS + b % KS, nsteps - 1);
+      const int n = min(n0 + t * 16 + (l & 15), N - 1);
+      xr[j] = *(const u32x4*)(X + (size_t)n * d + s * 32 + 8 * (l >> 4));
     }
   };
   auto store_x = [&](int buf) {
@@ -233,10 +258,12 @@ __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restri
   auto load_w = [&](u32x4(&dst)[KS][R], int c) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const int ks = c * KS + s;
+      const int ks = min(c * KS + s, nsteps - 1);
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-        dst[s][r] = (ks < nsteps && vt0 + r < ntiles) ? load_w16<true>(wbase + ((size_t)r * nsteps + ks) * 512) : zero;
+      for (int r = 0; r < R; ++r) {
+        const int vt = min(vt0 + r, ntiles - 1);
+        dst[s][r] = load_w16<true>(Wp + ((size_t)vt * nsteps + ks) * 512 + lane * 8);
+      }
     }
   };
 
@@ -260,31 +287,41 @@ __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restri
     }
   };
 
-  const int nch = (nsteps + KS - 1) / KS;
+  // Chunk c + 1 is fetched while chunk c computes.  The loop body only loads
+  // chunks that exist; the last one or two chunks are peeled off so that no
+  // load is issued past the end.
   u32x4 wa[KS][R], wb[KS][R];
-  load_x(0);
-  load_w(wa, 0);
+  load_x(c0);
+  load_w(wa, c0);
   store_x(0);
   __syncthreads();
-  for (int c = 0; c < nch; c += 2) {
-    if (c + 1 < nch) {
-      load_x(c + 1);
-      load_w(wb, c + 1);
-    }
+  int c = c0;
+  for (; c + 2 < c1; c += 2) {
+    load_x(c + 1);
+    load_w(wb, c + 1);
     compute(wa, 0, c);
-    if (c + 1 < nch) store_x(1);
+    store_x(1);
     __syncthreads();
-    if (c + 1 >= nch) break;
-    if (c + 2 < nch) {
-      load_x(c + 2);
-      load_w(wa, c + 2);
-    }
+    load_x(c + 2);
+    load_w(wa, c + 2);
     compute(wb, 1, c + 1);
-    if (c + 2 < nch) store_x(0);
+    store_x(0);
     __syncthreads();
+  }
+  if (c + 1 < c1) {
+    load_x(c + 1);
+    load_w(wb, c + 1);
+    compute(wa, 0, c);
+    store_x(1);
+    __syncthreads();
+    compute(wb, 1, c + 1);
+  } else {
+    compute(wa, 0, c);
   }
 
   // Lane holds tokens n0 + 16t + m, vocabulary rows 16*(vt0 + r) + 4g .. +3.
+  const bool split = ngroups > 1;
+  float* part = (float*)Y + (size_t)group * N * V;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t v0 = (int64_t)(vt0 + r) * 16 + 4 * g;
@@ -293,9 +330,87 @@ __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restri
     for (int t = 0; t < NT; ++t) {
       const int n = t * 16 + m;
       if (n >= ncols) continue;
-      store4<OUT_BF16>(Y, (size_t)(n0 + n) * V + v0, v0, V, acc[r][t]);
+      if (split)
+        store4<false>(part, (size_t)(n0 + n) * V + v0, v0, V, acc[r][t]);
+      else
+        store4<OUT_BF16>(Y, (size_t)(n0 + n) * V + v0, v0, V, acc[r][t]);
     }
   }
+}
+
+// Sums the k-group partials P [groups][N][V] in group order into Y.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, void* __restrict__ Y,
+                                                            int64_t N, int64_t V, int groups) {
+  const int64_t NV = N * V;
+  if ((V & 3) == 0) {
+    for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < NV; i += (int64_t)gridDim.x * 1024) {
+      f32x4 s = *(const f32x4*)(P + i);
+      for (int gq = 1; gq < groups; ++gq) {
+        const f32x4 o = *(const f32x4*)(P + (size_t)gq * NV + i);
+        s[0] += o[0];
+        s[1] += o[1];
+        s[2] += o[2];
+        s[3] += o[3];
+      }
+      const int64_t v0 = i % V;
+      store4<OUT_BF16>(Y, (size_t)i, v0, V, s);
+    }
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < NV; i += (int64_t)gridDim.x * 256) {
+      float s = P[i];
+      for (int gq = 1; gq < groups; ++gq) s += P[(size_t)gq * NV + i];
+      if (OUT_BF16)
+        ((uint16_t*)Y)[i] = (uint16_t)bf16_rne(s);
+      else
+        ((float*)Y)[i] = s;
+    }
+  }
+}
+
+hipError_t launch_reduce(const float* P, void* Y, int64_t N, int64_t V, int64_t groups, bool out_bf16,
+                         hipStream_t stream) {
+  const int64_t work = (V & 3) == 0 ? (N * V) / 4 : N * V;
+  int64_t blocks = (work + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  auto k = out_bf16 ? splitk_reduce_kernel<true> : splitk_reduce_kernel<false>;
+  hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(256), 0, stream, P, Y, N, V, (int)groups);
+  return hipGetLastError();
+}
+
+// Launch geometry of one panel configuration for a shape.
+struct PanelPlan {
+  int64_t npass, cpk, groups, grid;
+};
+
+// Splits the k range into groups when the (vocabulary block, token pass) work
+// items alone would leave CUs idle.  The group count (each group at least 4
+// chunks) minimises an estimate of the time: bytes moved (W once, plus the
+// fp32 partials written and read back) over the share of CU slots that the
+// rounds of blocks keep busy.
+PanelPlan plan_panel(int64_t N, int64_t d, int64_t V, int NT, int R, int NW, int KS, int cus) {
+  PanelPlan p{};
+  const int64_t ntiles = (V + 15) / 16, nvb = (ntiles + NW * R - 1) / (NW * R);
+  const int64_t nch = (d / 32 + KS - 1) / KS;
+  p.npass = (N + NT * 16 - 1) / (NT * 16);
+  const int64_t items = nvb * p.npass;
+  const double wbytes = 2.0 * (double)V * (double)d, pbytes = 8.0 * (double)N * (double)V;
+  int64_t best_groups = 1;
+  double best = -1.0;
+  for (int64_t gq = 1; gq == 1 || (gq <= 4 * ((cus + items - 1) / items) && gq <= nch / 4); ++gq) {
+    const int64_t cpk = (nch + gq - 1) / gq, real = (nch + cpk - 1) / cpk;
+    const int64_t total = items * real, rounds = (total + cus - 1) / cus;
+    const double fill = (double)total / (double)(rounds * cus) * ((double)nch / (double)(real * cpk));
+    const double t = (wbytes + (real > 1 ? pbytes * (double)real : 0.0)) / fill;
+    if (best < 0.0 || t < best * (1.0 - 1e-9)) {
+      best = t;
+      best_groups = real;
+    }
+  }
+  p.cpk = (nch + best_groups - 1) / best_groups;
+  p.groups = (nch + p.cpk - 1) / p.cpk;
+  p.grid = 8 * ((nvb * p.groups + 7) / 8) * p.npass;
+  return p;
 }
 
 template <int NT, int R, int NW, int KS>
@@ -304,34 +419,93 @@ constexpr size_t panel_lds_bytes() {
 }
 
 template <int NT, int R, int NW, int KS>
-hipError_t launch_panel(const uint16_t* X, const uint16_t* Wp, void* Y, int64_t N, int64_t d, int64_t V, bool out_bf16,
-                        hipStream_t stream) {
+hipError_t launch_panel(const PanelPlan& p, const uint16_t* X, const uint16_t* Wp, void* Y, int64_t N, int64_t d,
+                        int64_t V, bool out_bf16, hipStream_t stream) {
   constexpr size_t kLds = panel_lds_bytes<NT, R, NW, KS>();
   static_assert(kLds <= 160 * 1024, "panel LDS");
   auto k = out_bf16 ? panel_kernel<NT, R, NW, KS, true> : panel_kernel<NT, R, NW, KS, false>;
   hipError_t e = allow_lds(k, kLds);
   if (e != hipSuccess) return e;
-  const int64_t ntiles = (V + 15) / 16;
-  const int64_t nvb = (ntiles + NW * R - 1) / (NW * R);
-  const int64_t npass = (N + NT * 16 - 1) / (NT * 16);
-  const int64_t grid = 8 * ((nvb + 7) / 8) * npass;
-  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(NW * 64), kLds, stream, X, Wp, Y, (int)N, (int)d, (int)V,
-                     (int)npass);
+  hipLaunchKernelGGL(k, dim3((unsigned)p.grid), dim3(NW * 64), kLds, stream, X, Wp, Y, (int)N, (int)d, (int)V,
+                     (int)p.npass, (int)p.cpk);
   return hipGetLastError();
+}
+
+// The panel configurations the dispatcher uses, by N (chosen by measurement).
+struct PanelShape {
+  int NT, R, NW, KS;
+};
+PanelShape panel_shape(int64_t N) {
+  if (N <= 16) return {1, 2, 8, 4};
+  if (N <= 32) return {2, 2, 8, 4};
+  if (N <= 64) return {4, 4, 8, 2};
+  if (N <= 128) return {8, 2, 8, 4};
+  return {8, 4, 8, 2};
+}
+
+hipError_t launch_panel_shape(const PanelShape& s, const PanelPlan& p, const uint16_t* X, const uint16_t* Wp, void* Y,
+                              int64_t N, int64_t d, int64_t V, bool out_bf16, hipStream_t stream) {
+  if (s.NT == 1) return launch_panel<1, 2, 8, 4>(p, X, Wp, Y, N, d, V, out_bf16, stream);
+  if (s.NT == 2) return launch_panel<2, 2, 8, 4>(p, X, Wp, Y, N, d, V, out_bf16, stream);
+  if (s.NT == 4) return launch_panel<4, 4, 8, 2>(p, X, Wp, Y, N, d, V, out_bf16, stream);
+  if (s.R == 2) return launch_panel<8, 2, 8, 4>(p, X, Wp, Y, N, d, V, out_bf16, stream);
+  return launch_panel<8, 4, 8, 2>(p, X, Wp, Y, N, d, V, out_bf16, stream);
+}
+
+// What the dispatcher will run for a shape, and the workspace it needs.
+struct GemmPlan {
+  enum Kind { kSweep, kPanel, kTiled } kind;
+  SweepPlan sweep;
+  PanelShape shape;
+  PanelPlan panel;
+  size_t workspace;
+};
+
+GemmPlan plan_gemm(int64_t N, int64_t d, int64_t V, bool packed) {
+  GemmPlan g{};
+  const int cus = device_cus();
+  g.kind = GemmPlan::kTiled;
+  if (!packed) return g;
+  g.sweep = plan_sweep(N, d, V, cus);
+  if (g.sweep.ok) {
+    g.kind = GemmPlan::kSweep;
+    if (g.sweep.kgroups > 1) g.workspace = (size_t)g.sweep.kgroups * N * V * sizeof(float);
+    return g;
+  }
+  g.kind = GemmPlan::kPanel;
+  g.shape = panel_shape(N);
+  g.panel = plan_panel(N, d, V, g.shape.NT, g.shape.R, g.shape.NW, g.shape.KS, cus);
+  if (g.panel.groups > 1) g.workspace = (size_t)g.panel.groups * N * V * sizeof(float);
+  return g;
 }
 
 }  // namespace
 }  // namespace gemm
 
+size_t gemm_workspace_bytes(int64_t N, int64_t d, int64_t V, bool packed) {
+  return gemm::plan_gemm(N, d, V, packed).workspace;
+}
+
 hipError_t launch_skinny_gemm(const uint16_t* X, const uint16_t* W, void* Y, int64_t N, int64_t d, int64_t V,
-                              bool out_bf16, bool packed, hipStream_t stream) {
+                              bool out_bf16, bool packed, void* workspace, hipStream_t stream) {
   using namespace gemm;
-  // Shapes chosen by measurement on MI355X (streaming rate of W per N range).
-  if (packed) {
-    if (sweep_applies(N, d)) return launch_sweep(X, W, Y, N, d, V, out_bf16, stream);
-    if (N <= 32) return launch_tiled<4, 2, 64, 4, true, true>(X, W, Y, N, d, V, out_bf16, stream);
-    return launch_tiled<4, 1, 128, 8, true, true>(X, W, Y, N, d, V, out_bf16, stream);
+  const GemmPlan g = plan_gemm(N, d, V, packed);
+  if (g.workspace > 0 && !workspace) return hipErrorInvalidValue;
+  switch (g.kind) {
+    case GemmPlan::kSweep: {
+      if (g.sweep.kgroups == 1) return launch_sweep(g.sweep, X, W, Y, N, d, V, out_bf16, stream);
+      hipError_t e = launch_sweep(g.sweep, X, W, workspace, N, d, V, false, stream);
+      return e != hipSuccess ? e : launch_reduce((const float*)workspace, Y, N, V, g.sweep.kgroups, out_bf16, stream);
+    }
+    case GemmPlan::kPanel: {
+      if (g.panel.groups == 1) return launch_panel_shape(g.shape, g.panel, X, W, Y, N, d, V, out_bf16, stream);
+      hipError_t e = launch_panel_shape(g.shape, g.panel, X, W, workspace, N, d, V, false, stream);
+      return e != hipSuccess ? e : launch_reduce((const float*)workspace, Y, N, V, g.panel.groups, out_bf16, stream);
+    }
+    default:
+      break;
   }
+  // Row-major weights.
   if (N <= 16) return launch_tiled<1, 1, 256, 4, false, false>(X, W, Y, N, d, V, out_bf16, stream);
   if (N <= 32) return launch_tiled<2, 2, 128, 4, false, false>(X, W, Y, N, d, V, out_bf16, stream);
   return launch_tiled<4, 2, 128, 4, false, false>(X, W, Y, N, d, V, out_bf16, stream);

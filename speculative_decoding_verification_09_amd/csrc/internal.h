@@ -9,15 +9,27 @@ namespace specdec {
 
 // Y[n, v] = sum_k X[n, k] W[v, k]; X [N, d] bf16; W [V, d] bf16 row-major or
 // in the packed tile layout; Y fp32 or bf16.
+// The workspace must hold gemm_workspace_bytes(N, d, V, packed) bytes (may be
+// null when that is 0).
 hipError_t launch_skinny_gemm(const uint16_t* X, const uint16_t* W, void* Y, int64_t N, int64_t d, int64_t V,
-                              bool out_bf16, bool packed, hipStream_t stream);
+                              bool out_bf16, bool packed, void* workspace, hipStream_t stream);
 
 namespace gemm {
-// The sweep kernel (packed W, at most 8 positions, X held in LDS whole).
-bool sweep_applies(int64_t N, int64_t d);
-hipError_t launch_sweep(const uint16_t* X, const uint16_t* Wp, void* Y, int64_t N, int64_t d, int64_t V, bool out_bf16,
-                        hipStream_t stream);
+// The sweep kernel (packed W, at most 8 positions).  Its k range is split into
+// kgroups groups of spk k-steps when X does not fit in LDS whole or the tiles
+// are too few for the CUs; each group then writes fp32 partials [N, V] to its
+// own slice of the output pointer, to be summed in group order.
+struct SweepPlan {
+  bool ok;
+  int64_t spk, kgroups, grid;
+};
+SweepPlan plan_sweep(int64_t N, int64_t d, int64_t V, int cus);
+hipError_t launch_sweep(const SweepPlan& p, const uint16_t* X, const uint16_t* Wp, void* Y, int64_t N, int64_t d,
+                        int64_t V, bool out_bf16, hipStream_t stream);
 }  // namespace gemm
+
+// Bytes of device workspace the scoring GEMM needs for this shape (0: none).
+size_t gemm_workspace_bytes(int64_t N, int64_t d, int64_t V, bool packed);
 
 // Packed tile layout of W [V, d] (d % 32 == 0): ceil(V/16)*16*d elements.
 int64_t packed_weight_elems(int64_t V, int64_t d);
@@ -40,5 +52,33 @@ struct RejectArgs {
 
 size_t reject_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
 hipError_t launch_reject_sample(const RejectArgs& a, hipStream_t stream);
+
+// Softmax (or argmax) statistics formed by the scoring kernel itself, as an
+// epilogue: for every row, one partial per workgroup of that kernel, in the
+// reject workspace's partial slots.  Target rows are [0, B*(gamma+1)), draft
+// rows B*(gamma+1) + b*gamma + i.
+constexpr int64_t kFusedStatsMaxParts = 256;  // workgroups (partials per row)
+constexpr int64_t kFusedStatsMaxRows = 8;     // B*(gamma+1)
+struct FusedStats {
+  float* cmax;            // [row][pstride]: max of z/T (greedy: max of z)
+  double* csum;           // [row][pstride]: sum of exp(z/T - max)
+  int32_t* cidx;          // [row][pstride]: lowest index of the max (greedy)
+  float* zx;              // [row]: logit of the drafted token
+  int64_t pstride;
+  const float* draft;     // draft logits [B, gamma, V] to summarise, or null
+  const int32_t* tokens;  // [B, gamma]
+  int64_t B, gamma;
+  float inv_t;            // fl32(1/T); 1 when greedy
+  bool greedy;
+};
+// Points fs at the workspace of a; false when the shape cannot take fused statistics.
+bool reject_fused_stats(const RejectArgs& a, FusedStats* fs);
+// The stages after the statistics, reading nparts partials per row.
+hipError_t launch_reject_after_fused(const RejectArgs& a, int64_t nparts, hipStream_t stream);
+// The scoring GEMM with the statistics epilogue (packed W, sweep kernel without
+// k-groups, at most kFusedStatsMaxParts workgroups).  Returns
+// hipErrorNotSupported, launching nothing, for shapes it does not take.
+hipError_t launch_gemm_with_stats(const uint16_t* X, const uint16_t* Wp, float* Y, int64_t N, int64_t d, int64_t V,
+                                  const FusedStats& fs, int64_t* nparts, hipStream_t stream);
 
 }  // namespace specdec

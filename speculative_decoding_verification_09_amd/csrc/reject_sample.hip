@@ -47,6 +47,8 @@ constexpr int kDrawChunk = 1024;   // vocabulary entries per draw work item (one
 constexpr int kMergeBatch = 16;    // rows whose argmax partials one wave loads together
 constexpr int kWavesPerBlock = 4;
 constexpr float kQFloor = 1e-12f;
+constexpr int64_t kMaxFusedParts = kFusedStatsMaxParts;
+constexpr int64_t kMaxFusedRows = kFusedStatsMaxRows;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -63,19 +65,30 @@ struct DrawDesc {
   float pad[2];
 };
 
-// Workspace layout, every array 16-byte aligned.
+// Workspace layout, every array 16-byte aligned.  Each row has pstride slots
+// for softmax partials: one per statistics chunk, or, when the scoring kernel
+// forms them itself (at most kMaxFusedParts workgroups, B*(gamma+1) <= 8), one
+// per workgroup of that kernel.
 struct Layout {
-  size_t off_cmax, off_csum, off_cidx;      // per (row, statistics chunk)
+  size_t off_cmax, off_csum, off_cidx;      // per (row, partial slot)
   size_t off_zx;                            // per row
   size_t off_desc;                          // per sequence
   size_t off_sres, off_sp;                  // per (sequence, draw chunk)
+  int64_t pstride;
   size_t total;
 };
+
+__host__ __device__ inline int64_t partial_stride(int64_t B, int64_t gamma, int64_t V) {
+  const int64_t sc = stat_chunks(V);
+  const bool fusable = B * (gamma + 1) <= kMaxFusedRows;
+  return fusable && sc < kMaxFusedParts ? kMaxFusedParts : sc;
+}
 
 __host__ __device__ inline Layout make_layout(int64_t B, int64_t gamma, int64_t V) {
   Layout L;
   const size_t rows = (size_t)(B * (2 * gamma + 1));
-  const size_t rc = rows * (size_t)stat_chunks(V);
+  L.pstride = partial_stride(B, gamma, V);
+  const size_t rc = rows * (size_t)L.pstride;
   const size_t ndc = (size_t)(B * draw_chunks(V));
   size_t o = 0;
   L.off_cmax = o; o = align16(o + rc * sizeof(float));
@@ -90,19 +103,21 @@ __host__ __device__ inline Layout make_layout(int64_t B, int64_t gamma, int64_t 
 }
 
 struct Ws {
-  float* cmax;     // per (row, chunk): max of a = z / T (greedy: max of z)
-  double* csum;    // per (row, chunk): sum exp(a - chunk max)
-  int32_t* cidx;   // per (row, chunk): lowest index of the max (greedy)
+  float* cmax;     // per (row, slot): max of a = z / T (greedy: max of z)
+  double* csum;    // per (row, slot): sum exp(a - slot max)
+  int32_t* cidx;   // per (row, slot): lowest index of the max (greedy)
   float* zx;       // per drafted row: logit of the drafted token
   DrawDesc* desc;  // per sequence
   double* sres;    // per (sequence, draw chunk): sum of the residual weights
   double* sp;      // per (sequence, draw chunk): sum of p
+  int64_t pstride; // slots per row
+  int64_t nparts;  // slots in use per row
 };
 
-inline Ws bind(void* base, const Layout& L) {
+inline Ws bind(void* base, const Layout& L, int64_t nparts) {
   char* b = (char*)base;
   return Ws{(float*)(b + L.off_cmax), (double*)(b + L.off_csum), (int32_t*)(b + L.off_cidx), (float*)(b + L.off_zx),
-            (DrawDesc*)(b + L.off_desc), (double*)(b + L.off_sres), (double*)(b + L.off_sp)};
+            (DrawDesc*)(b + L.off_desc), (double*)(b + L.off_sres), (double*)(b + L.off_sp), L.pstride, nparts};
 }
 
 // ---------------------------------------------------------------------------
@@ -192,8 +207,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void stats_kernel(const float*
     }
     wave_argmax(bv, bi);
     if (lane == 0) {
-      ws.cmax[item] = bv;
-      ws.cidx[item] = bi;
+      ws.cmax[r * ws.pstride + c] = bv;
+      ws.cidx[r * ws.pstride + c] = bi;
     }
     return;
   }
@@ -217,28 +232,44 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void stats_kernel(const float*
   for (int e = 0; e < PL; ++e) sum += (double)expf(x[e] - mx);
   sum = wave_sum(sum);
   if (lane == 0) {
-    ws.cmax[item] = mx;
-    ws.csum[item] = sum;
+    ws.cmax[r * ws.pstride + c] = mx;
+    ws.csum[r * ws.pstride + c] = sum;
   }
 }
 
-// Merges the chunk partials of row r with one wave: M = max m_c, Z = sum s_c
+// Merges the partials of row r with one wave: M = max m_c, Z = sum s_c
 // exp(m_c - M) (fp64), and the probability of the drafted token exp(a_x - M)/Z
-// (fp64, rounded once to fp32; 0 for rows without a drafted token).
+// (fp64, rounded once to fp32; 0 for rows without a drafted token).  Partials
+// are read 256 at a time, all loads of a batch issued before any reduction.
 __device__ __forceinline__ void merge_row(const Ws& ws, int64_t r, bool drafted, int64_t nch, float inv_t, int lane,
                                           double& M_out, double& Z_out, float& px_out) {
-  const size_t base = (size_t)r * nch;
+  constexpr int kPer = 4;  // partials per lane and batch
+  const size_t base = (size_t)r * ws.pstride;
   const float zx = drafted ? ws.zx[r] : 0.0f;  // loaded with the partials
-  const float cm = lane < nch ? ws.cmax[base + lane] : -INFINITY;
-  const double cs = lane < nch ? ws.csum[base + lane] : 0.0;
-  float M = wave_max(cm);
-  for (int64_t c = lane + 64; c < nch; c += 64) M = fmaxf(M, wave_max(ws.cmax[base + c]));
-  double z = cs > 0.0 ? cs * exp((double)cm - (double)M) : 0.0;
-  for (int64_t c = lane + 64; c < nch; c += 64) {
-    const double sc = ws.csum[base + c];
-    if (sc > 0.0) z += sc * exp((double)ws.cmax[base + c] - (double)M);
+  float M = -INFINITY;
+  double z = 0.0;
+  for (int64_t c0 = 0; c0 < nch; c0 += 64 * kPer) {
+    float cm[kPer];
+    double cs[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int64_t c = c0 + 64 * j + lane;
+      cm[j] = c < nch ? ws.cmax[base + c] : -INFINITY;
+      cs[j] = c < nch ? ws.csum[base + c] : 0.0;
+    }
+    float bm = cm[0];
+#pragma unroll
+    for (int j = 1; j < kPer; ++j) bm = fmaxf(bm, cm[j]);
+    bm = wave_max(bm);
+    const float Mn = fmaxf(M, bm);
+    if (z > 0.0) z *= exp((double)M - (double)Mn);  // wave-uniform: every lane holds the same M
+    M = Mn;
+    double zb = 0.0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (cs[j] > 0.0) zb += cs[j] * exp((double)cm[j] - (double)M);
+    z += wave_sum(zb);
   }
-  z = wave_sum(z);
   M_out = (double)M;
   Z_out = z;
   px_out = drafted ? (float)(exp((double)(zx * inv_t) - (double)M) / z) : 0.0f;
@@ -319,15 +350,22 @@ __global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
   const int64_t c = (blockIdx.x - b * gps) * WB + wv;
   const int64_t g1 = gamma + 1;
   const bool q_probs = draft_kind == 1;
-  const int64_t nch = stat_chunks(V);
+  const int64_t nch = ws.nparts;
+  // Per-row inputs that do not depend on the statistics, loaded first (lane i <-> row i).
+  const bool has_row = lane < g1;
+  const bool drafted = lane < gamma;
+  const float u_acc = drafted ? uniforms[(b * g1 + lane) * 2 + 0] : 0.0f;
+  const float u_smp = has_row ? uniforms[(b * g1 + lane) * 2 + 1] : 0.0f;
+  const int xi = drafted ? clamp_token(tokens[b * gamma + lane], V) : 0;
+  const float q_given = drafted && q_probs ? draft[(size_t)(b * gamma + lane) * V + xi] : 0.0f;
   // Rows of the sequence: j < g1 target row j, then draft row j - g1 (draft logits).
   const int nrows = (int)(q_probs ? g1 : g1 + gamma);
   for (int j = wv; j < nrows; j += WB) {
     const int64_t r = j < g1 ? b * g1 + j : B * g1 + b * gamma + (j - g1);
-    const bool drafted = j < g1 ? j < gamma : true;
+    const bool row_drafted = j < g1 ? j < gamma : true;
     double M, Z;
     float px;
-    merge_row(ws, r, drafted, nch, inv_t, lane, M, Z, px);
+    merge_row(ws, r, row_drafted, nch, inv_t, lane, M, Z, px);
     if (lane == 0) {
       sh_m[j] = M;
       sh_z[j] = Z;
@@ -337,17 +375,11 @@ __global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
   __syncthreads();
   if (c >= ndc) return;  // no barrier below
   const int64_t item = b * ndc + c;
-  const bool has_row = lane < g1;
-  const bool drafted = lane < gamma;
   const double rmt = has_row ? sh_m[lane] : 0.0, rzt = has_row ? sh_z[lane] : 1.0;
   const float p_x = drafted ? sh_px[lane] : 0.0f;
   const bool ql = drafted && !q_probs;
   const double rmq = ql ? sh_m[g1 + lane] : 0.0, rzq = ql ? sh_z[g1 + lane] : 1.0;
-  float q_x = ql ? sh_px[g1 + lane] : 0.0f;
-  const float u_acc = drafted ? uniforms[(b * g1 + lane) * 2 + 0] : 0.0f;
-  const float u_smp = has_row ? uniforms[(b * g1 + lane) * 2 + 1] : 0.0f;
-  const int xi = drafted ? clamp_token(tokens[b * gamma + lane], V) : 0;
-  if (drafted && q_probs) q_x = draft[(size_t)(b * gamma + lane) * V + xi];
+  const float q_x = ql ? sh_px[g1 + lane] : q_given;
 
   bool reject = false;
   if (drafted) {
@@ -510,7 +542,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void greedy_kernel(const int32
   const int64_t b = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (b >= B) return;
   const int64_t g1 = gamma + 1;
-  const int64_t nch = stat_chunks(V);
+  const int64_t nch = ws.nparts;
   const bool drafted = lane < gamma;
   const int xi = drafted ? clamp_token(tokens[b * gamma + lane], V) : 0;
   int mine = 0;
@@ -522,7 +554,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void greedy_kernel(const int32
       cv[j] = -INFINITY;
       ci[j] = 0x7fffffff;
       if (r0 + j < g1) {
-        const size_t base = (size_t)(b * g1 + r0 + j) * nch;
+        const size_t base = (size_t)(b * g1 + r0 + j) * ws.pstride;
         for (int64_t c = lane; c < nch; c += 64) {
           const float v = ws.cmax[base + c];
           const int ix = ws.cidx[base + c];
@@ -553,27 +585,33 @@ inline unsigned blocks_for(int64_t items, int per) { return (unsigned)((items + 
 
 size_t reject_workspace_bytes(int64_t B, int64_t gamma, int64_t V) { return make_layout(B, gamma, V).total; }
 
-hipError_t launch_reject_sample(const RejectArgs& a, hipStream_t stream) {
+bool reject_fused_stats(const RejectArgs& a, FusedStats* fs) {
   const Layout L = make_layout(a.B, a.gamma, a.V);
-  const Ws ws = bind(a.workspace, L);
+  if (a.B * (a.gamma + 1) > kMaxFusedRows || L.pstride < kMaxFusedParts) return false;
+  const Ws ws = bind(a.workspace, L, 0);
+  const bool greedy = a.temperature == 0.0f;
+  fs->cmax = ws.cmax;
+  fs->csum = ws.csum;
+  fs->cidx = ws.cidx;
+  fs->zx = ws.zx;
+  fs->pstride = L.pstride;
+  fs->draft = (!greedy && a.draft_kind == 0 && a.gamma > 0) ? a.draft : nullptr;
+  fs->tokens = a.tokens;
+  fs->B = a.B;
+  fs->gamma = a.gamma;
+  fs->inv_t = greedy ? 1.0f : (float)(1.0 / (double)a.temperature);
+  fs->greedy = greedy;
+  return true;
+}
+
+namespace {
+
+// The stages after the statistics: the draw (T > 0) or the greedy rule.
+hipError_t launch_decide(const RejectArgs& a, const Ws& ws, hipStream_t stream) {
   const bool greedy = a.temperature == 0.0f;
   const bool vec = (a.V & 3) == 0;
   const float inv_t = greedy ? 1.0f : (float)(1.0 / (double)a.temperature);
-  const int64_t n_target = a.B * (a.gamma + 1);
-  const int64_t n_rows = n_target + ((!greedy && a.draft_kind == 0) ? a.B * a.gamma : 0);
   const dim3 blk(kWavesPerBlock * 64);
-  const dim3 g1(blocks_for(n_rows * stat_chunks(a.V), kWavesPerBlock));
-#define SPECDEC_STATS(V4, GR)                                                                                        \
-  hipLaunchKernelGGL((stats_kernel<V4, GR>), g1, blk, 0, stream, a.target, a.draft, a.tokens, n_target, n_rows, \
-                     a.gamma, a.V, inv_t, ws)
-  if (greedy) {
-    if (vec) SPECDEC_STATS(true, true); else SPECDEC_STATS(false, true);
-  } else {
-    if (vec) SPECDEC_STATS(true, false); else SPECDEC_STATS(false, false);
-  }
-#undef SPECDEC_STATS
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   if (greedy) {
     hipLaunchKernelGGL(greedy_kernel, dim3(blocks_for(a.B, kWavesPerBlock)), blk, 0, stream, a.tokens, a.B, a.gamma,
                        a.V, a.out_tokens, a.out_num, ws);
@@ -590,7 +628,7 @@ hipError_t launch_reject_sample(const RejectArgs& a, hipStream_t stream) {
     if (vec) SPECDEC_DRAW(4, true); else SPECDEC_DRAW(4, false);
   }
 #undef SPECDEC_DRAW
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 g3(blocks_for(a.B, kWavesPerBlock));
   if (vec)
@@ -600,6 +638,37 @@ hipError_t launch_reject_sample(const RejectArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((select_kernel<false>), g3, blk, 0, stream, a.target, a.draft, a.draft_kind, a.B, a.gamma,
                        a.V, inv_t, a.out_tokens, ws);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_reject_after_fused(const RejectArgs& a, int64_t nparts, hipStream_t stream) {
+  const Layout L = make_layout(a.B, a.gamma, a.V);
+  return launch_decide(a, bind(a.workspace, L, nparts), stream);
+}
+
+hipError_t launch_reject_sample(const RejectArgs& a, hipStream_t stream) {
+  const Layout L = make_layout(a.B, a.gamma, a.V);
+  const Ws ws = bind(a.workspace, L, stat_chunks(a.V));
+  const bool greedy = a.temperature == 0.0f;
+  const bool vec = (a.V & 3) == 0;
+  const float inv_t = greedy ? 1.0f : (float)(1.0 / (double)a.temperature);
+  const int64_t n_target = a.B * (a.gamma + 1);
+  const int64_t n_rows = n_target + ((!greedy && a.draft_kind == 0) ? a.B * a.gamma : 0);
+  const dim3 blk(kWavesPerBlock * 64);
+  const dim3 g1(blocks_for(n_rows * stat_chunks(a.V), kWavesPerBlock));
+#define SPECDEC_STATS(V4, GR)                                                                                        \
+  hipLaunchKernelGGL((stats_kernel<V4, GR>), g1, blk, 0, stream, a.target, a.draft, a.tokens, n_target, n_rows, \
+                     a.gamma, a.V, inv_t, ws)
+  if (greedy) {
+    if (vec) SPECDEC_STATS(true, true); else SPECDEC_STATS(false, true);
+  } else {
+    if (vec) SPECDEC_STATS(true, false); else SPECDEC_STATS(false, false);
+  }
+#undef SPECDEC_STATS
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_decide(a, ws, stream);
 }
 
 }  // namespace specdec

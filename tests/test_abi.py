@@ -36,7 +36,7 @@ def test_status_strings_and_version():
     for s in range(1, 8):
         assert sd.status_string(s) and sd.status_string(s) != "unknown status"
     assert sd.status_string(99) == "unknown status"
-    assert sd.version() == 10000
+    assert sd.version() == 10100
 
 
 def test_workspace_bytes():
@@ -59,8 +59,9 @@ A = 0x100000  # 16-byte aligned fake address
 P = ctypes.c_void_p
 
 
-def _logits(X=A, W=A, Y=A, N=5, d=64, V=128, dt=0, layout=0):
-    return sd.library().specdec_verify_logits(P(X), P(W), P(Y), N, d, V, dt, layout, None)
+def _logits(X=A, W=A, Y=A, N=5, d=64, V=128, dt=0, layout=0, ws=0, wsb=0):
+    return sd.library().specdec_verify_logits(P(X), P(W), P(Y), N, d, V, dt, layout, P(ws) if ws else None, wsb,
+                                              None)
 
 
 def _reject(target=A, draft=A, kind=0, tokens=A, T=1.0, u=A, B=2, g=3, V=128, ot=A, on=A, op=None, ws=A,
@@ -151,3 +152,31 @@ def test_python_binding_rejects_host_tensors():
     y = torch.zeros(5, 128)
     with pytest.raises(ValueError):
         sd.specdec_verify_logits(x, w, y)
+
+
+def test_workspace_size_queries():
+    """The scoring GEMM needs no workspace at the LM-head shapes; shapes with few output rows and a long k range
+    (the projection that maps 28672 inputs to 8192 outputs) split k and keep fp32 partials; the step's workspace
+    covers both stages."""
+    PK, RM = sd.SPECDEC_WEIGHTS_PACKED, sd.SPECDEC_WEIGHTS_ROW_MAJOR
+    assert sd.logits_workspace_bytes(5, 4096, 128256, PK) == 0
+    assert sd.logits_workspace_bytes(64, 8192, 128256, PK) == 0
+    assert sd.logits_workspace_bytes(5, 4096, 128256, RM) == 0
+    for N in (5, 8, 64):
+        need = sd.logits_workspace_bytes(N, 28672, 8192, PK)
+        assert need > 0 and need % (N * 8192 * 4) == 0
+    assert sd.logits_workspace_bytes(0, 4096, 100, PK) == 0
+    assert sd.logits_workspace_bytes(5, 4100, 100, PK) == 0  # packed needs d % 32 == 0
+    assert sd.step_workspace_bytes(1, 4, 4096, 128256, PK) == sd.workspace_bytes(1, 4, 128256)
+    big = sd.logits_workspace_bytes(56, 28672, 8192, PK)
+    assert sd.step_workspace_bytes(7, 7, 28672, 8192, PK) == max(big, sd.workspace_bytes(7, 7, 8192))
+    assert sd.step_workspace_bytes(0, 4, 4096, 100, PK) == 0
+
+
+@needs_no_gpu
+def test_logits_workspace_checks():
+    """A shape that splits k rejects a missing or short workspace before launching."""
+    need = sd.logits_workspace_bytes(64, 28672, 8192, sd.SPECDEC_WEIGHTS_PACKED)
+    assert _logits(N=64, d=28672, V=8192, layout=1) == 5
+    assert _logits(N=64, d=28672, V=8192, layout=1, ws=A, wsb=need - 1) == 5
+    assert _logits(N=64, d=28672, V=8192, layout=1, ws=A + 8, wsb=need) == 3

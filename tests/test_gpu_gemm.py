@@ -12,8 +12,9 @@ import numpy as np
 import pytest
 import torch
 
+import speculative_decoding_verification_09_amd as sd
 import synth
-from gpu_util import announce, gemm, host, weights
+from gpu_util import announce, dev_bf16, gemm, host, weights
 
 pytestmark = pytest.mark.gpu
 
@@ -104,6 +105,62 @@ def test_packed_bf16_output(orc, N, d, V):
     W = synth.normal_bf16((V, d), 0.02, 92, V)
     announce(f"gemm packed bf16-out N={N} d={d} V={V}")
     Yf = host(gemm(X, W, out_bf16=True, packed=True).float()).astype(np.float64)
+    ref = orc.linear(X, W)
+    bound = _bound(synth.bf16_to_f32(X), synth.bf16_to_f32(W), d)
+    assert np.all(np.abs(Yf - ref) <= 2.0**-8 * (np.abs(ref) + bound) + bound + 1e-30)
+
+
+# Packed shapes whose k range is split into groups (fp32 partials in the
+# workspace, added in group order): X too wide for LDS at small N (sweep), few
+# vocabulary tiles for the CUs (panel), vocabulary and k tails.
+SPLIT_SHAPES = [
+    (40, 2048, 300), (8, 9984, 100), (8, 9984, 5000), (17, 4096, 300), (100, 1024, 64), (3, 16384, 40),
+    (5, 28672, 77), (64, 8192, 1030), (130, 2048, 500),
+]
+
+
+def _gemm_ws(X_bits, W_bits, out_bf16=False):
+    """Packed GEMM with an explicit workspace poisoned with NaN bytes (every partial must be overwritten)."""
+    X = dev_bf16(X_bits)
+    W = weights(W_bits, True)
+    N, V, d = X.shape[0], W_bits.shape[0], X_bits.shape[1]
+    need = sd.logits_workspace_bytes(N, d, V, sd.SPECDEC_WEIGHTS_PACKED)
+    assert need > 0, "shape does not split k"
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    Y = torch.full((N, V), float("nan"), device="cuda", dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    sd.specdec_verify_logits(X, W, Y, sd.SPECDEC_OUT_BF16 if out_bf16 else sd.SPECDEC_OUT_F32, workspace=ws)
+    torch.cuda.synchronize()
+    return Y
+
+
+@pytest.mark.parametrize("N,d,V", SPLIT_SHAPES)
+def test_split_k_integer_bit_exact(orc, N, d, V):
+    X = synth.integer_bf16((N, d), 8, 61, N)
+    W = synth.integer_bf16((V, d), 8, 62, V)
+    announce(f"gemm split-k integer N={N} d={d} V={V}")
+    Y = host(_gemm_ws(X, W))
+    assert np.array_equal(Y.astype(np.float64), orc.linear(X, W))
+
+
+@pytest.mark.parametrize("N,d,V", SPLIT_SHAPES)
+def test_split_k_normal_within_fp32_bound(orc, N, d, V):
+    X = synth.normal_bf16((N, d), 1.0, 63, N)
+    W = synth.normal_bf16((V, d), 0.02, 64, V)
+    announce(f"gemm split-k normal N={N} d={d} V={V}")
+    Y = host(_gemm_ws(X, W)).astype(np.float64)
+    ref = orc.linear(X, W)
+    bound = _bound(synth.bf16_to_f32(X), synth.bf16_to_f32(W), d)
+    assert np.all(np.abs(Y - ref) <= bound + 1e-30)
+    rms = float(np.sqrt(np.mean(ref**2)))
+    assert np.all(np.abs(Y - ref) <= 2e-2 * np.maximum(np.abs(ref), 1e-3 * rms))
+
+
+@pytest.mark.parametrize("N,d,V", [(8, 9984, 5000), (40, 2048, 300)])
+def test_split_k_bf16_output(orc, N, d, V):
+    X = synth.normal_bf16((N, d), 1.0, 65, N)
+    W = synth.normal_bf16((V, d), 0.02, 66, V)
+    announce(f"gemm split-k bf16-out N={N} d={d} V={V}")
+    Yf = host(_gemm_ws(X, W, out_bf16=True).float()).astype(np.float64)
     ref = orc.linear(X, W)
     bound = _bound(synth.bf16_to_f32(X), synth.bf16_to_f32(W), d)
     assert np.all(np.abs(Yf - ref) <= 2.0**-8 * (np.abs(ref) + bound) + bound + 1e-30)

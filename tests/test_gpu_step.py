@@ -24,19 +24,21 @@ from gpu_util import abs_dot_bound, announce, compare_steps, dev, dev_bf16, host
 pytestmark = pytest.mark.gpu
 
 
-def run_step(X, W, draft, tokens, u, T, B, g, V, packed=True):
+def run_step(X, W, draft, tokens, u, T, B, g, V, packed=True, kind=sd.SPECDEC_DRAFT_LOGITS, probs=None):
     Xd, Wd = dev_bf16(X), weights(W, packed)
     logits = torch.full((B * (g + 1), V), float("nan"), device="cuda")
     ot = torch.full((B, g + 1), -7, dtype=torch.int32, device="cuda")
     on = torch.full((B,), -7, dtype=torch.int32, device="cuda")
-    ws = sd.new_workspace(B, g, V)
+    layout = sd.SPECDEC_WEIGHTS_PACKED if packed else sd.SPECDEC_WEIGHTS_ROW_MAJOR
+    ws = torch.full((sd.step_workspace_bytes(B, g, X.shape[1], V, layout),), 0xFF, dtype=torch.uint8, device="cuda")
     sd.specdec_verify_step(Xd, Wd, dev(draft) if draft is not None else None, dev(tokens), T,
-                           dev(u) if u is not None else None, logits, ot, on, ws)
+                           dev(u) if u is not None else None, logits, ot, on, ws, out_probs=probs, draft_kind=kind)
     torch.cuda.synchronize()
     return logits, host(ot), host(on)
 
 
-def check_sequences(orc, X, W, logits, tok, num, draft, tokens, u, T, g, V, seqs, greedy=False):
+def check_sequences(orc, X, W, logits, tok, num, draft, tokens, u, T, g, V, seqs, greedy=False,
+                    kind=sd.SPECDEC_DRAFT_LOGITS):
     rows = np.concatenate([np.arange(b * (g + 1), (b + 1) * (g + 1)) for b in seqs])
     Y64 = orc.linear(X[rows], W)
     got = host(logits[torch.from_numpy(rows).cuda()]).astype(np.float64)
@@ -46,7 +48,7 @@ def check_sequences(orc, X, W, logits, tok, num, draft, tokens, u, T, g, V, seqs
     max_dz = float(dz.max())
     target32 = Y64.astype(np.float32).reshape(len(seqs), g + 1, V)
     ora = orc.verify(target32, draft[seqs] if draft is not None else None, tokens[seqs],
-                     u[seqs] if u is not None else None, T)
+                     u[seqs] if u is not None else None, T, draft_kind=kind)
     if greedy:
         acc_band, draw_band = 4 * max_dz, 4 * max_dz
     else:
@@ -127,3 +129,51 @@ def test_greedy_b64_g4_sampled_sequences(orc):
     logits, tok, num = run_step(X, W, None, tokens, None, 0.0, w.B, w.gamma, w.V)
     check_sequences(orc, X, W, logits, tok, num, None, tokens, None, 0.0, w.gamma, w.V, seqs, greedy=True)
     assert np.all((num >= 1) & (num <= g1))
+
+
+# Shapes that take the fused path (packed weights, B*(gamma+1) <= 8): the
+# scoring kernel forms the softmax or argmax partials of every row itself.
+# Covers draft logits and probabilities, greedy, gamma = 0, vocabulary tails
+# (V % 4, V % 16 != 0), fewer tiles than workgroups, and tile counts that
+# leave some workgroups one tile more (those skip the draft rows).
+FUSED = [
+    ("logits", 1, 4, 256, 5000, 1.0), ("logits_tail", 2, 3, 512, 4099, 0.7), ("gamma0", 1, 0, 256, 3000, 1.0),
+    ("few_tiles", 1, 7, 128, 300, 1.3), ("probs", 4, 1, 256, 8191, 1.0), ("greedy", 1, 4, 256, 5000, 0.0),
+    ("greedy_tail", 2, 3, 96, 1025, 0.0), ("greedy_gamma0", 8, 0, 64, 1000, 0.0), ("rem_tiles", 1, 4, 4096, 70000, 1.0),
+]
+
+
+@pytest.mark.parametrize("name,B,g,d,V,T", FUSED, ids=[f[0] for f in FUSED])
+def test_fused_statistics_path(orc, name, B, g, d, V, T):
+    seed = 700 + V % 97
+    X = synth.normal_bf16((B * (g + 1), d), 1.0, seed, synth.STREAM_X)
+    W = synth.normal_bf16((V, d), 2.0 / np.sqrt(d), seed, synth.STREAM_W)
+    target32 = orc.linear(X, W).astype(np.float32).reshape(B, g + 1, V)
+    greedy = T == 0.0
+    kind = sd.SPECDEC_DRAFT_PROBS if name == "probs" else sd.SPECDEC_DRAFT_LOGITS
+    if greedy:
+        draft = None
+        am = np.array([[orc.argmax(target32[b, i])[0] for i in range(g)] for b in range(B)], np.int32).reshape(B, g)
+        rnd = synth.integers((B, g), 0, V, seed, synth.STREAM_REPLACE)
+        tokens = np.where(synth.bernoulli((B, g), 0.3, seed, synth.STREAM_REPLACE + 1), rnd, am).astype(np.int32)
+        u = None
+    else:
+        draft, tokens = _draft_and_tokens(orc, target32, g, 1.0, T if T > 0 else 1.0, seed)
+        if kind == sd.SPECDEC_DRAFT_PROBS:
+            draft = np.stack([orc.softmax(draft[b, i], T)[0] for b in range(B) for i in range(g)]).reshape(B, g, V)
+            draft = np.ascontiguousarray(draft, np.float32)
+        u = synth.uniforms((B, g + 1, 2), seed, synth.STREAM_STEP_UNIFORMS)
+    probs = torch.full((B, g, 2), float("nan"), device="cuda") if not greedy else None
+    announce(f"step fused {name} B={B} gamma={g} d={d} V={V} T={T}")
+    logits, tok, num = run_step(X, W, draft, tokens, u, T, B, g, V, packed=True, kind=kind, probs=probs)
+    check_sequences(orc, X, W, logits, tok, num, draft, tokens, u, T, g, V, list(range(B)), greedy=greedy, kind=kind)
+    if probs is not None and g > 0:
+        # p(x), q(x) against the oracle's fp32 probabilities on the GPU's own logits
+        z = host(logits).reshape(B, g + 1, V)
+        got = host(probs)
+        for b in range(B):
+            for i in range(g):
+                x = int(tokens[b, i])
+                p_x = orc.softmax(z[b, i], T)[0][x]
+                q_x = draft[b, i, x] if kind == sd.SPECDEC_DRAFT_PROBS else orc.softmax(draft[b, i], T)[0][x]
+                assert abs(got[b, i, 0] - p_x) <= 1e-5 and abs(got[b, i, 1] - q_x) <= 1e-5, (b, i, got[b, i], p_x, q_x)
