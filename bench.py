@@ -6,6 +6,7 @@ the rejection-sampling kernels.  Inputs are synthetic, seeded, and resident in
 HBM before timing starts.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --projection-sweep     (the decoder-projection GEMM sweep over N; one JSON line)
 """
 from __future__ import annotations
 
@@ -28,8 +29,8 @@ GEMM_SOURCES = [os.path.join(HERE, "speculative_decoding_verification_09_amd", "
 # FETCH_SIZE, 1.0 for WRITE_SIZE).  Keyed by workload, weight layout and the SHA-256 of the GEMM source the
 # counters were taken on: once that source changes, the record no longer describes the kernel and traffic is null.
 MEASURED_TRAFFIC = {
-    ("lmhead_b1_g4", "packed"): {"fetch_bytes": 1081605294, "write_bytes": 2565120,
-                                 "source_sha256": "a4b5529c0f358de8da1c4a8bcecfe32f71ac33e0dcc8cd1ee171be161823297f"},
+    ("lmhead_b1_g4", "packed"): {"fetch_bytes": 1051182331, "write_bytes": 2565120,
+                                 "source_sha256": "0081623de30eb1123662d03e456909cadd21e9ce09a1c73bf16c4b87c1645281"},
 }
 
 
@@ -66,7 +67,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="lmhead_b1_g4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-steps", type=int, default=8, help="oracle sequences timed for the CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="the CPU baseline times whole oracle sequences until this much time has passed")
+    ap.add_argument("--projection-sweep", action="store_true",
+                    help="time the scoring GEMM on the decoder projection shapes over N instead of the step")
     ap.add_argument("--layout", choices=["packed", "rowmajor"], default="packed", help="weight layout")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (a known byte count for hardware counters)")
@@ -84,6 +88,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.projection_sweep:
+        projection_sweep(args)
+        return
     w = synth.WORKLOADS[args.workload]
     if w.d == 0:
         print(f"workload {w.name} has no scoring GEMM; pick an LM-head workload", file=sys.stderr)
@@ -188,15 +195,16 @@ def main():
         orc = oracle.load()
         Xh, Wh = synth.lm_head_inputs(w)
         rows_per_seq = g + 1
-        reps = max(1, args.cpu_steps)
         uh = synth.step_uniforms(w)
         toks = tokens.cpu().numpy()
         dr = draft.cpu().numpy() if draft is not None else None
+        reps = 0
         t0 = time.perf_counter()
-        for r in range(reps):
-            b = r % B
+        while reps == 0 or time.perf_counter() - t0 < args.cpu_seconds:
+            b = reps % B
             zb = orc.linear(Xh[b * rows_per_seq:(b + 1) * rows_per_seq], Wh).astype(np.float32)
             orc.verify(zb[None], dr[b:b + 1] if dr is not None else None, toks[b:b + 1], uh[b:b + 1], T)
+            reps += 1
         cpu_s = time.perf_counter() - t0
         cpu = {"value": reps * rows_per_seq / cpu_s, "unit": "positions/s", "cores": 1, "kind": "oracle",
                "sample": f"{reps} sequence(s) of {rows_per_seq} positions (B={B}: "
@@ -227,6 +235,69 @@ def main():
                      "traffic": measured_traffic(w.name, args.layout), "bytes_per_launch": gemm_bytes,
                      "avg_launch_ms": gemm_ms},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
+
+
+def projection_sweep(args):
+    """The scoring GEMM on the decoder projection shapes [N x d_in] . [d_in x d_out] (W stored [d_out, d_in],
+    packed, bf16 out), for each N: K back-to-back launches between two events.  Reports achieved HBM GB/s
+    (algorithmic bytes: W once, X once, Y once) and MFMA utilisation (2 N d_in d_out flops against the dense bf16
+    peak)."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_verification_09_amd as sd
+    import synth
+
+    cfg = synth.PROJECTION_SWEEP
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    points = []
+    Nmax = max(cfg["N"])
+    for d_in, d_out in cfg["shapes"]:
+        seed = cfg["seed"] + d_in
+        W_rows = torch.from_numpy(synth.normal_bf16((d_out, d_in), cfg["w_std"], seed, synth.STREAM_W).view(np.int16))
+        W = sd.specdec_pack_weights(W_rows.to(dev).view(torch.bfloat16))
+        torch.cuda.synchronize()
+        del W_rows
+        Xall = torch.from_numpy(synth.normal_bf16((Nmax, d_in), cfg["x_std"], seed, synth.STREAM_X).view(np.int16))
+        Xall = Xall.to(dev).view(torch.bfloat16)
+        for N in cfg["N"]:
+            X = Xall[:N].contiguous()
+            Y = torch.empty((N, d_out), dtype=torch.bfloat16, device=dev)
+            need = sd.logits_workspace_bytes(N, d_in, d_out, sd.SPECDEC_WEIGHTS_PACKED)
+            ws = torch.empty(max(1, need), dtype=torch.uint8, device=dev)
+            for _ in range(args.warmup):
+                sd.specdec_verify_logits(X, W, Y, sd.SPECDEC_OUT_BF16, workspace=ws, stream=stream)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(args.steps):
+                sd.specdec_verify_logits(X, W, Y, sd.SPECDEC_OUT_BF16, workspace=ws, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            nbytes = 2 * d_in * d_out + 2 * N * d_in + 2 * N * d_out
+            flops = 2.0 * N * d_in * d_out
+            gbps = nbytes / (ms * 1e-3) / 1e9
+            tflops = flops / (ms * 1e-3) / 1e12
+            points.append({"d_in": d_in, "d_out": d_out, "N": N, "us": ms * 1e3, "gbps": gbps,
+                           "hbm_frac": gbps / HBM_PEAK_GBPS, "tflops": tflops,
+                           "mfma_util": tflops / MFMA_BF16_PEAK_TFLOPS, "k_groups": need // max(1, N * d_out * 4)})
+        del W, Xall
+    low = min(p["hbm_frac"] for p in points if p["N"] <= 64)
+    out = {
+        "metric": "projection GEMM sweep: lowest fraction of HBM peak over N <= 64 (per-N GB/s and MFMA use listed)",
+        "value": low, "unit": "fraction of 8 TB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": True, "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "projection_sweep", "shapes": cfg["shapes"], "N": cfg["N"], "weight_layout": "packed",
+                   "out_dtype": "bf16"},
+        "points": points,
     }
     print(json.dumps(out), flush=True)
 
