@@ -183,17 +183,17 @@ int specdec_verify_step(const void* X, const void* W, int weight_layout, const f
   const specdec::RejectArgs a = reject_args(logits, draft, draft_kind, draft_tokens, temperature, uniforms, B, gamma,
                                             V, out_tokens, out_num_emitted, out_probs, workspace, workspace_bytes);
   const hipStream_t s = (hipStream_t)stream;
-  // Packed weights and few positions: the scoring kernel also forms the
-  // softmax (or argmax) partials of every row, so the sampling stages start
-  // from them and no separate statistics pass reads the logits again.
+  // Packed weights: the scoring kernel also forms the softmax (or argmax)
+  // partials of every target row, so no separate statistics pass reads the
+  // logits again.
   specdec::FusedStats fs;
-  if (weight_layout == SPECDEC_WEIGHTS_PACKED && specdec::reject_fused_stats(a, &fs)) {
+  if (weight_layout == SPECDEC_WEIGHTS_PACKED && specdec::reject_fused_stats(a, &fs) &&
+      specdec::gemm_stats_parts(N, d, V, fs.pstride) > 0) {
     int64_t nparts = 0;
-    const hipError_t e =
-        specdec::launch_gemm_with_stats((const uint16_t*)X, (const uint16_t*)W, logits, N, d, V, fs, &nparts, s);
-    if (e == hipSuccess)
-      return specdec::launch_reject_after_fused(a, nparts, s) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
-    if (e != hipErrorNotSupported) return SPECDEC_ERR_LAUNCH;
+    if (specdec::launch_gemm_with_stats((const uint16_t*)X, (const uint16_t*)W, logits, N, d, V, fs, &nparts, s) !=
+        hipSuccess)
+      return SPECDEC_ERR_LAUNCH;
+    return specdec::launch_reject_after_fused(a, nparts, s) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
   }
   // The scoring pass finishes (stream order) before the sampling kernels reuse the workspace.
   if (specdec_verify_logits(X, W, logits, N, d, V, SPECDEC_OUT_F32, weight_layout, workspace, workspace_bytes,

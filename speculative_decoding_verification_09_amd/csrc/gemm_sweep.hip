@@ -69,7 +69,8 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
 // largest z with its lowest index), records the logit of each row's drafted
 // token from the tile that holds it, and at the end leaves one partial per
 // (row, workgroup).  With draft logits, the workgroups that have one tile
-// fewer (they finish first) also summarise a slice of every draft row.
+// fewer (they finish first) also summarise a slice of every draft row, one
+// wave per row (few rows here: B*(gamma+1) <= 8).
 template <int NW, int SPW, bool NTL, bool OUT_BF16, int EPI>
 __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp,
                                                         void* __restrict__ Y, int N, int d, int V, int spk,
@@ -314,12 +315,10 @@ hipError_t launch_sweep(const SweepPlan& p, const uint16_t* X, const uint16_t* W
 
 }  // namespace gemm
 
-hipError_t launch_gemm_with_stats(const uint16_t* X, const uint16_t* Wp, float* Y, int64_t N, int64_t d, int64_t V,
-                                  const FusedStats& fs, int64_t* nparts, hipStream_t stream) {
-  using namespace gemm;
-  const SweepPlan p = plan_sweep(N, d, V, device_cus());
-  if (!p.ok || p.kgroups != 1 || p.grid > kFusedStatsMaxParts || p.grid > fs.pstride || N > kFusedStatsMaxRows)
-    return hipErrorNotSupported;
+namespace gemm {
+
+hipError_t launch_sweep_with_stats(const SweepPlan& p, const uint16_t* X, const uint16_t* Wp, float* Y, int64_t N,
+                                   int64_t d, int64_t V, const FusedStats& fs, int64_t* nparts, hipStream_t stream) {
   const size_t lds = sweep_lds_bytes(N, p.spk);
   auto k = fs.greedy ? sweep_kernel<kSweepWaves, kSweepGroup, true, false, 2>
                      : sweep_kernel<kSweepWaves, kSweepGroup, true, false, 1>;
@@ -331,6 +330,8 @@ hipError_t launch_gemm_with_stats(const uint16_t* X, const uint16_t* Wp, float* 
   if (e == hipSuccess) *nparts = p.grid;
   return e;
 }
+
+}  // namespace gemm
 
 int64_t packed_weight_elems(int64_t V, int64_t d) { return ((V + 15) / 16) * 16 * d; }
 

@@ -195,6 +195,123 @@ hipError_t launch_tiled(const uint16_t* X, const uint16_t* W, void* Y, int64_t N
   return hipSuccess;
 }
 // ---------------------------------------------------------------------------
+// Statistics epilogue of the panel kernel (see below).  xs: the kernel's LDS,
+// free once the main loop has ended.
+template <int NT, int R, int NW, int EPI>
+__device__ __forceinline__ void panel_stats(const f32x4 (&acc)[R][NT], uint16_t* xs, const FusedStats& fs, int N,
+                                            int V, int n0, int ncols, int vt0, int vb, int wv, int lane) {
+  constexpr int kTok = NT * 16;
+  const int m = lane & 15, g = lane >> 4;
+  float* lm = (float*)xs;                                     // [NW][kTok] wave maxima
+  double* ls = (double*)((char*)xs + 4 * NW * kTok);          // [NW][kTok] wave sums (8-byte aligned)
+  int* li = (int*)((char*)xs + 12 * NW * kTok);               // [NW][kTok] argmax indices
+  const int g1 = (int)fs.gamma + 1;
+  __syncthreads();  // every wave is done with the X buffers
+  // Pass 1: per-token maxima (with the lowest index at T == 0) over the wave's rows.
+  float pm[NT];
+  int pi[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    pm[t] = -INFINITY;
+    pi[t] = 0x7fffffff;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int v = (vt0 + r) * 16 + 4 * g + j;
+        const float a = EPI == 1 ? acc[r][t][j] * fs.inv_t : acc[r][t][j];
+        if (v < V && (a > pm[t] || (EPI == 2 && a == pm[t] && v < pi[t]))) {
+          pm[t] = a;
+          pi[t] = v;
+        }
+      }
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const float om = __shfl_xor(pm[t], o);
+      const int oi = __shfl_xor(pi[t], o);
+      if (om > pm[t] || (om == pm[t] && oi < pi[t])) {
+        pm[t] = om;
+        pi[t] = oi;
+      }
+    }
+    if (g == 0) {
+      lm[wv * kTok + t * 16 + m] = pm[t];
+      if (EPI == 2) li[wv * kTok + t * 16 + m] = pi[t];
+    }
+    if (EPI == 1 && t * 16 + m < ncols) {  // the drafted token's logit, from the lane that holds it
+      const int n = n0 + t * 16 + m;
+      const int bq = n / g1, iq = n - bq * g1;
+      if (iq < fs.gamma) {
+        const int32_t x = fs.tokens[bq * fs.gamma + iq];
+        const int xc = x < 0 ? 0 : (x >= V ? V - 1 : x);
+        const int rel = xc - vt0 * 16 - 4 * g;  // = 16r + j when this lane holds it
+        bool hit = false;
+        float zv = 0.0f;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (rel == 16 * r + j) {  // static indices only: acc stays in registers
+              hit = true;
+              zv = acc[r][t][j];
+            }
+        if (hit) fs.zx[n] = zv;
+      }
+    }
+  }
+  __syncthreads();
+  if (EPI == 2) {
+    for (int tk = wv * 64 + lane; tk < kTok; tk += NW * 64) {
+      if (tk >= ncols) continue;
+      float M = -INFINITY;
+      int I = 0x7fffffff;
+      for (int w = 0; w < NW; ++w) {  // fixed order
+        const float om = lm[w * kTok + tk];
+        const int oi = li[w * kTok + tk];
+        if (om > M || (om == M && oi < I)) {
+          M = om;
+          I = oi;
+        }
+      }
+      const size_t slot = (size_t)(n0 + tk) * fs.pstride + vb;
+      fs.cmax[slot] = M;
+      fs.cidx[slot] = I;
+    }
+    return;
+  }
+  // Pass 2: fp32 exp(a - M) summed in fp64 against the workgroup maximum M of each token.
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    float M = lm[t * 16 + m];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, lm[w * kTok + t * 16 + m]);
+    double ps = 0.0;
+    if (M > -INFINITY) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if ((vt0 + r) * 16 + 4 * g + j < V) ps += (double)expf(acc[r][t][j] * fs.inv_t - M);
+    }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    if (g == 0) ls[wv * kTok + t * 16 + m] = ps;
+    pm[t] = M;
+  }
+  __syncthreads();
+  for (int tk = wv * 64 + lane; tk < kTok; tk += NW * 64) {
+    if (tk >= ncols) continue;
+    float M = lm[tk];
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, lm[w * kTok + tk]);
+    double S = 0.0;
+    for (int w = 0; w < NW; ++w) S += ls[w * kTok + tk];  // fixed order
+    const size_t slot = (size_t)(n0 + tk) * fs.pstride + vb;
+    fs.cmax[slot] = M;
+    fs.csum[slot] = S;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Panel kernel.  Work items are (vocabulary block, k-group, token pass): a
 // vocabulary block is NW*R 16-row tiles, a token pass NT*16 tokens, and a
 // k-group cpk chunks of KS MFMA k-steps (32 k each).  Block id i runs on XCD
@@ -202,9 +319,16 @@ hipError_t launch_tiled(const uint16_t* X, const uint16_t* W, void* Y, int64_t N
 // slots of one XCD, so the W rows they share are read from HBM once.  With one
 // k-group the block writes Y; otherwise it writes fp32 partials to slice
 // `group` of Y ([groups][N][V]), which are then summed in group order.
-template <int NT, int R, int NW, int KS, bool OUT_BF16>
+//
+// Statistics epilogue (EPI 1: softmax at temperature T, EPI 2: argmax; one
+// k-group only), for the whole verification step: every wave reduces its
+// 16*R vocabulary rows per token, the NW wave partials meet in LDS, and the
+// workgroup leaves one partial per (row, vocabulary block), plus the logit of
+// each drafted token from the lane that holds it.
+template <int NT, int R, int NW, int KS, bool OUT_BF16, int EPI>
 __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp,
-                                                        void* __restrict__ Y, int N, int d, int V, int npass, int cpk) {
+                                                        void* __restrict__ Y, int N, int d, int V, int npass, int cpk,
+                                                        FusedStats fs) {
   constexpr int kThreads = NW * 64;
   constexpr int kBlocks = NT * KS;                   // 1 KB X blocks per chunk
   constexpr int kXPT = (kBlocks * 64 + kThreads - 1) / kThreads;
@@ -255,15 +379,17 @@ __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restri
       if (kXPT * kThreads == kBlocks * 64 || u < kBlocks * 64) *(u32x4*)(xs + buf * kBufElems + u * 8) = xr[j];
     }
   };
+  // One wave-uniform row base per vocabulary tile (clamped into the buffer)
+  // and one lane offset: the loads take a scalar base and a 32-bit offset.
+  const uint16_t* wrow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) wrow[r] = Wp + (size_t)min(vt0 + r, ntiles - 1) * nsteps * 512;
   auto load_w = [&](u32x4(&dst)[KS][R], int c) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const int ks = min(c * KS + s, nsteps - 1);
+      const int off = min(c * KS + s, nsteps - 1) * 512 + lane * 8;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int vt = min(vt0 + r, ntiles - 1);
-        dst[s][r] = load_w16<true>(Wp + ((size_t)vt * nsteps + ks) * 512 + lane * 8);
-      }
+      for (int r = 0; r < R; ++r) dst[s][r] = load_w16<true>(wrow[r] + off);
     }
   };
 
@@ -318,6 +444,8 @@ __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restri
   } else {
     compute(wa, 0, c);
   }
+
+  if (EPI != 0) panel_stats<NT, R, NW, EPI>(acc, xs, fs, N, V, n0, ncols, vt0, vb, wv, lane);
 
   // Lane holds tokens n0 + 16t + m, vocabulary rows 16*(vt0 + r) + 4g .. +3.
   const bool split = ngroups > 1;
@@ -420,14 +548,18 @@ constexpr size_t panel_lds_bytes() {
 
 template <int NT, int R, int NW, int KS>
 hipError_t launch_panel(const PanelPlan& p, const uint16_t* X, const uint16_t* Wp, void* Y, int64_t N, int64_t d,
-                        int64_t V, bool out_bf16, hipStream_t stream) {
+                        int64_t V, bool out_bf16, hipStream_t stream, const FusedStats* fs = nullptr) {
   constexpr size_t kLds = panel_lds_bytes<NT, R, NW, KS>();
   static_assert(kLds <= 160 * 1024, "panel LDS");
-  auto k = out_bf16 ? panel_kernel<NT, R, NW, KS, true> : panel_kernel<NT, R, NW, KS, false>;
+  // The statistics epilogue reuses the X buffers: NW*NT*16 entries of 4 + 8 + 4 bytes.
+  static_assert((size_t)NW * NT * 16 * 16 <= kLds, "panel statistics LDS");
+  auto k = out_bf16 ? panel_kernel<NT, R, NW, KS, true, 0> : panel_kernel<NT, R, NW, KS, false, 0>;
+  if (fs) k = fs->greedy ? panel_kernel<NT, R, NW, KS, false, 2> : panel_kernel<NT, R, NW, KS, false, 1>;
   hipError_t e = allow_lds(k, kLds);
   if (e != hipSuccess) return e;
+  const FusedStats none{};
   hipLaunchKernelGGL(k, dim3((unsigned)p.grid), dim3(NW * 64), kLds, stream, X, Wp, Y, (int)N, (int)d, (int)V,
-                     (int)p.npass, (int)p.cpk);
+                     (int)p.npass, (int)p.cpk, fs ? *fs : none);
   return hipGetLastError();
 }
 
@@ -435,21 +567,29 @@ hipError_t launch_panel(const PanelPlan& p, const uint16_t* X, const uint16_t* W
 struct PanelShape {
   int NT, R, NW, KS;
 };
-PanelShape panel_shape(int64_t N) {
+// Large vocabularies (LM heads) have vocabulary blocks to spare and favour
+// 64 rows per wave; the projection shapes (few output rows, k split into
+// groups) favour more tokens per wave.  The 8x4 shape is the fastest at 512
+// positions on the projection shapes but does not fit its registers without
+// spilling, so the statistics epilogue never uses it.
+PanelShape panel_shape(int64_t N, int64_t V, bool with_stats) {
+  const bool big_v = V >= 65536;
   if (N <= 16) return {1, 2, 8, 4};
   if (N <= 32) return {2, 2, 8, 4};
-  if (N <= 64) return {4, 4, 8, 2};
-  if (N <= 128) return {8, 2, 8, 4};
-  return {8, 4, 8, 2};
+  if (N <= 64) return big_v ? PanelShape{4, 4, 8, 2} : PanelShape{8, 2, 8, 2};
+  if (N <= 128) return {8, 2, 8, 2};
+  return big_v || with_stats ? PanelShape{4, 4, 8, 2} : PanelShape{8, 4, 8, 2};
 }
 
 hipError_t launch_panel_shape(const PanelShape& s, const PanelPlan& p, const uint16_t* X, const uint16_t* Wp, void* Y,
-                              int64_t N, int64_t d, int64_t V, bool out_bf16, hipStream_t stream) {
-  if (s.NT == 1) return launch_panel<1, 2, 8, 4>(p, X, Wp, Y, N, d, V, out_bf16, stream);
-  if (s.NT == 2) return launch_panel<2, 2, 8, 4>(p, X, Wp, Y, N, d, V, out_bf16, stream);
-  if (s.NT == 4) return launch_panel<4, 4, 8, 2>(p, X, Wp, Y, N, d, V, out_bf16, stream);
-  if (s.R == 2) return launch_panel<8, 2, 8, 4>(p, X, Wp, Y, N, d, V, out_bf16, stream);
-  return launch_panel<8, 4, 8, 2>(p, X, Wp, Y, N, d, V, out_bf16, stream);
+                              int64_t N, int64_t d, int64_t V, bool out_bf16, hipStream_t stream,
+                              const FusedStats* fs = nullptr) {
+  if (s.NT == 1) return launch_panel<1, 2, 8, 4>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);
+  if (s.NT == 2) return launch_panel<2, 2, 8, 4>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);
+  if (s.NT == 4) return launch_panel<4, 4, 8, 2>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);
+  if (s.R == 2) return launch_panel<8, 2, 8, 2>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);
+  if (fs) return hipErrorNotSupported;
+  return launch_panel<8, 4, 8, 2>(p, X, Wp, Y, N, d, V, out_bf16, stream, nullptr);
 }
 
 // What the dispatcher will run for a shape, and the workspace it needs.
@@ -461,7 +601,7 @@ struct GemmPlan {
   size_t workspace;
 };
 
-GemmPlan plan_gemm(int64_t N, int64_t d, int64_t V, bool packed) {
+GemmPlan plan_gemm(int64_t N, int64_t d, int64_t V, bool packed, bool with_stats = false) {
   GemmPlan g{};
   const int cus = device_cus();
   g.kind = GemmPlan::kTiled;
@@ -473,7 +613,7 @@ GemmPlan plan_gemm(int64_t N, int64_t d, int64_t V, bool packed) {
     return g;
   }
   g.kind = GemmPlan::kPanel;
-  g.shape = panel_shape(N);
+  g.shape = panel_shape(N, V, with_stats);
   g.panel = plan_panel(N, d, V, g.shape.NT, g.shape.R, g.shape.NW, g.shape.KS, cus);
   if (g.panel.groups > 1) g.workspace = (size_t)g.panel.groups * N * V * sizeof(float);
   return g;
@@ -481,6 +621,43 @@ GemmPlan plan_gemm(int64_t N, int64_t d, int64_t V, bool packed) {
 
 }  // namespace
 }  // namespace gemm
+
+int64_t gemm_stats_parts(int64_t N, int64_t d, int64_t V, int64_t pstride) {
+  using namespace gemm;
+  if (N > kFusedStatsMaxRows) return 0;
+  const GemmPlan g = plan_gemm(N, d, V, true, true);
+  int64_t parts = 0;
+  if (g.kind == GemmPlan::kSweep && g.sweep.kgroups == 1) {
+    parts = g.sweep.grid;
+  } else if (g.kind == GemmPlan::kPanel && g.panel.groups == 1) {
+    const int64_t ntiles = (V + 15) / 16, rows = (int64_t)g.shape.NW * g.shape.R;
+    parts = (ntiles + rows - 1) / rows;
+  }
+  return parts > 0 && parts <= kFusedStatsMaxParts && parts <= pstride ? parts : 0;
+}
+
+hipError_t launch_gemm_with_stats(const uint16_t* X, const uint16_t* Wp, float* Y, int64_t N, int64_t d, int64_t V,
+                                  const FusedStats& fs, int64_t* nparts, hipStream_t stream) {
+  using namespace gemm;
+  const int64_t parts = gemm_stats_parts(N, d, V, fs.pstride);
+  if (parts == 0) return hipErrorNotSupported;
+  const GemmPlan g = plan_gemm(N, d, V, true, true);
+  if (g.kind == GemmPlan::kSweep) {
+    // The sweep kernel also summarises the (at most 7) draft rows itself.
+    const hipError_t e = launch_sweep_with_stats(g.sweep, X, Wp, Y, N, d, V, fs, nparts, stream);
+    if (e == hipSuccess) *nparts = parts;
+    return e;
+  }
+  // Many draft rows: their partials come from a kernel of their own, launched
+  // first on the same stream; the panel kernel forms the target rows' partials.
+  hipError_t e = launch_draft_parts(fs, N, V, parts, stream);
+  if (e != hipSuccess) return e;
+  FusedStats target_only = fs;
+  target_only.draft = nullptr;
+  e = launch_panel_shape(g.shape, g.panel, X, Wp, Y, N, d, V, false, stream, &target_only);
+  if (e == hipSuccess) *nparts = parts;
+  return e;
+}
 
 size_t gemm_workspace_bytes(int64_t N, int64_t d, int64_t V, bool packed) {
   return gemm::plan_gemm(N, d, V, packed).workspace;

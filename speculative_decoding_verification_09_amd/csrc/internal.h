@@ -27,6 +27,12 @@ SweepPlan plan_sweep(int64_t N, int64_t d, int64_t V, int cus);
 hipError_t launch_sweep(const SweepPlan& p, const uint16_t* X, const uint16_t* Wp, void* Y, int64_t N, int64_t d,
                         int64_t V, bool out_bf16, hipStream_t stream);
 }  // namespace gemm
+struct FusedStats;
+namespace gemm {
+// The sweep kernel with the statistics epilogue (one k-group, fp32 logits).
+hipError_t launch_sweep_with_stats(const SweepPlan& p, const uint16_t* X, const uint16_t* Wp, float* Y, int64_t N,
+                                   int64_t d, int64_t V, const FusedStats& fs, int64_t* nparts, hipStream_t stream);
+}  // namespace gemm
 
 // Bytes of device workspace the scoring GEMM needs for this shape (0: none).
 size_t gemm_workspace_bytes(int64_t N, int64_t d, int64_t V, bool packed);
@@ -57,8 +63,8 @@ hipError_t launch_reject_sample(const RejectArgs& a, hipStream_t stream);
 // epilogue: for every row, one partial per workgroup of that kernel, in the
 // reject workspace's partial slots.  Target rows are [0, B*(gamma+1)), draft
 // rows B*(gamma+1) + b*gamma + i.
-constexpr int64_t kFusedStatsMaxParts = 256;  // workgroups (partials per row)
-constexpr int64_t kFusedStatsMaxRows = 8;     // B*(gamma+1)
+constexpr int64_t kFusedStatsMaxParts = 512;  // workgroups (partials per row)
+constexpr int64_t kFusedStatsMaxRows = 512;   // B*(gamma+1)
 struct FusedStats {
   float* cmax;            // [row][pstride]: max of z/T (greedy: max of z)
   double* csum;           // [row][pstride]: sum of exp(z/T - max)
@@ -75,9 +81,16 @@ struct FusedStats {
 bool reject_fused_stats(const RejectArgs& a, FusedStats* fs);
 // The stages after the statistics, reading nparts partials per row.
 hipError_t launch_reject_after_fused(const RejectArgs& a, int64_t nparts, hipStream_t stream);
-// The scoring GEMM with the statistics epilogue (packed W, sweep kernel without
-// k-groups, at most kFusedStatsMaxParts workgroups).  Returns
-// hipErrorNotSupported, launching nothing, for shapes it does not take.
+// The draft rows' partials (nparts vocabulary slices per row) in the fused
+// slot layout; independent of the scoring kernel.  Nothing to do without draft
+// logits.
+hipError_t launch_draft_parts(const FusedStats& fs, int64_t n_target, int64_t V, int64_t nparts, hipStream_t stream);
+// Partials per row that launch_gemm_with_stats will produce for this shape
+// (0: the shape does not take the statistics epilogue).
+int64_t gemm_stats_parts(int64_t N, int64_t d, int64_t V, int64_t pstride);
+// The scoring GEMM with the statistics epilogue (packed W, sweep or panel
+// kernel without k-groups, at most kFusedStatsMaxParts partials per row).
+// Returns hipErrorNotSupported, launching nothing, for shapes it does not take.
 hipError_t launch_gemm_with_stats(const uint16_t* X, const uint16_t* Wp, float* Y, int64_t N, int64_t d, int64_t V,
                                   const FusedStats& fs, int64_t* nparts, hipStream_t stream);
 

@@ -579,6 +579,56 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void greedy_kernel(const int32
   if (lane == 0) out_num[b] = k + 1;
 }
 
+// 1'. Draft-row partials in the slot layout of the fused statistics: row j of
+//     the draft is cut into nparts slices of L entries (a multiple of 4), one
+//     wave per (row, slice): the slice max of a = z * fl32(1/T) and the fp64
+//     sum of fp32 exp(a - max), plus the drafted token's logit from the wave
+//     whose slice holds it.  Used beside the scoring kernel's own statistics
+//     epilogue when there are many draft rows.
+__global__ __launch_bounds__(kWavesPerBlock * 64) void draft_part_kernel(FusedStats fs, int64_t n_target, int64_t V,
+                                                                          int64_t nparts) {
+  constexpr int kPer = 8;  // entries per lane and load round
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int64_t nd = fs.B * fs.gamma;
+  if (item >= nd * nparts) return;
+  const int64_t j = item / nparts, p = item - j * nparts;
+  const int64_t L = (((V + nparts - 1) / nparts) + 3) & ~(int64_t)3;
+  const int64_t s0 = p * L < V ? p * L : V, s1 = s0 + L < V ? s0 + L : V;
+  const float* row = fs.draft + (size_t)j * V;
+  float M = -INFINITY;
+  double S = 0.0;
+  for (int64_t b0 = s0; b0 < s1; b0 += 64 * kPer) {
+    float x[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {  // clamped addresses, no branches: all loads in flight together
+      const int64_t v = b0 + lane + 64 * e;
+      x[e] = row[v < s1 ? v : s1 - 1];
+    }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+      if (b0 + lane + 64 * e < s1) bm = fmaxf(bm, x[e] * fs.inv_t);
+    bm = wave_max(bm);
+    const float Mn = fmaxf(M, bm);
+    if (S > 0.0) S *= exp((double)M - (double)Mn);  // wave-uniform
+    M = Mn;
+    double bs = 0.0;
+    if (M > -INFINITY)
+#pragma unroll
+      for (int e = 0; e < kPer; ++e)
+        if (b0 + lane + 64 * e < s1) bs += (double)expf(x[e] * fs.inv_t - M);
+    S += wave_sum(bs);
+  }
+  if (lane == 0) {
+    const size_t slot = (size_t)(n_target + j) * fs.pstride + p;
+    fs.cmax[slot] = M;
+    fs.csum[slot] = S;
+    const int xt = clamp_token(fs.tokens[j], V);
+    if (xt >= s0 && xt < s1) fs.zx[n_target + j] = row[xt];
+  }
+}
+
 inline unsigned blocks_for(int64_t items, int per) { return (unsigned)((items + per - 1) / per); }
 
 }  // namespace
@@ -641,6 +691,14 @@ hipError_t launch_decide(const RejectArgs& a, const Ws& ws, hipStream_t stream) 
 }
 
 }  // namespace
+
+hipError_t launch_draft_parts(const FusedStats& fs, int64_t n_target, int64_t V, int64_t nparts, hipStream_t stream) {
+  const int64_t items = fs.B * fs.gamma * nparts;
+  if (items == 0 || fs.draft == nullptr) return hipSuccess;
+  hipLaunchKernelGGL(draft_part_kernel, dim3(blocks_for(items, kWavesPerBlock)), dim3(kWavesPerBlock * 64), 0, stream,
+                     fs, n_target, V, nparts);
+  return hipGetLastError();
+}
 
 hipError_t launch_reject_after_fused(const RejectArgs& a, int64_t nparts, hipStream_t stream) {
   const Layout L = make_layout(a.B, a.gamma, a.V);

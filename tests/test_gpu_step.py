@@ -131,8 +131,9 @@ def test_greedy_b64_g4_sampled_sequences(orc):
     assert np.all((num >= 1) & (num <= g1))
 
 
-# Shapes that take the fused path (packed weights, B*(gamma+1) <= 8): the
-# scoring kernel forms the softmax or argmax partials of every row itself.
+# Shapes that take the fused path (packed weights, one k-group): the scoring
+# kernel (sweep for B*(gamma+1) <= 8, panel above) forms the softmax or argmax
+# partials of every row itself.
 # Covers draft logits and probabilities, greedy, gamma = 0, vocabulary tails
 # (V % 4, V % 16 != 0), fewer tiles than workgroups, and tile counts that
 # leave some workgroups one tile more (those skip the draft rows).
@@ -140,6 +141,9 @@ FUSED = [
     ("logits", 1, 4, 256, 5000, 1.0), ("logits_tail", 2, 3, 512, 4099, 0.7), ("gamma0", 1, 0, 256, 3000, 1.0),
     ("few_tiles", 1, 7, 128, 300, 1.3), ("probs", 4, 1, 256, 8191, 1.0), ("greedy", 1, 4, 256, 5000, 0.0),
     ("greedy_tail", 2, 3, 96, 1025, 0.0), ("greedy_gamma0", 8, 0, 64, 1000, 0.0), ("rem_tiles", 1, 4, 4096, 70000, 1.0),
+    # more positions: the panel kernel's epilogue (one or two token passes)
+    ("panel_probs", 6, 3, 128, 3001, 0.8), ("panel_greedy", 16, 3, 64, 2053, 0.0), ("panel_logits", 20, 4, 64, 1500, 1.0),
+    ("panel_passes_greedy", 40, 4, 64, 999, 0.0), ("panel_passes_logits", 32, 5, 96, 4100, 1.1),
 ]
 
 
