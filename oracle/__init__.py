@@ -23,6 +23,7 @@ LIBRARY = os.path.join(_HERE, "libspecdec_oracle.so")
 
 Q_LOGITS = 0
 Q_PROBS = 1
+Q_ONEHOT = 2
 
 # Planted mistakes compiled in with -DORACLE_PLANT=<n>; see specdec_oracle.c.
 PLANTS = {
@@ -40,6 +41,8 @@ PLANTS = {
     "row_offset": 12,
     "drop_last_term": 13,
     "accept_le": 14,
+    "tree_depth": 15,
+    "tree_self_argmax": 16,
 }
 
 
@@ -80,6 +83,10 @@ class Oracle:
         lib.oracle_residual.restype = _f64
         lib.oracle_draw.argtypes = [P, _i64, ctypes.c_float, P, P]
         lib.oracle_draw.restype = _i64
+        lib.oracle_tree_mask.argtypes = [P, _i64, P, P, P]
+        lib.oracle_tree_mask.restype = None
+        lib.oracle_tree_greedy.argtypes = [P, P, P, _i64, _i64, P, P, P]
+        lib.oracle_tree_greedy.restype = ctypes.c_int
         lib.oracle_verify_probs.argtypes = [P, P, P, P, _i64, _i64, _i64, P, P, P, P, P, P]
         lib.oracle_verify_probs.restype = ctypes.c_int
         lib.oracle_verify.argtypes = [P, P, ctypes.c_int, P, _f64, P, _i64, _i64, _i64, P, P, P, P, P, P]
@@ -216,6 +223,31 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"oracle_verify rejected its inputs (code {rc})")
         return out
+
+    # -- trees -----------------------------------------------------------
+    def tree_mask(self, parents):
+        """Returns (ancestor bit masks uint64 [M], depths int32 [M], additive mask fp32 [M, M] of 0 / -inf)."""
+        par = np.ascontiguousarray(parents, dtype=np.int32)
+        M = par.size
+        mask = np.empty(M, np.uint64)
+        depth = np.empty(M, np.int32)
+        add = np.empty((M, M), np.float32)
+        self.lib.oracle_tree_mask(par.ctypes.data, M, mask.ctypes.data, depth.ctypes.data, add.ctypes.data)
+        return mask, depth, add
+
+    def tree_greedy(self, z, parents, node_tokens):
+        """Greedy tree verification of one tree: z [M, V] fp32, parents [M], node_tokens [M].
+        Returns (tokens [M] (-1 padded), path nodes [M] (-1 padded), number emitted)."""
+        z = np.ascontiguousarray(z, dtype=np.float32)
+        M, V = z.shape
+        par = np.ascontiguousarray(parents, dtype=np.int32).reshape(M)
+        tok = np.ascontiguousarray(node_tokens, dtype=np.int32).reshape(M)
+        out_t = np.empty(M, np.int32)
+        out_n = np.empty(M, np.int32)
+        scratch = np.empty(3 * M, np.int32)
+        n = self.lib.oracle_tree_greedy(z.ctypes.data, par.ctypes.data, tok.ctypes.data, M, V, scratch.ctypes.data,
+                                        out_t.ctypes.data, out_n.ctypes.data)
+        return out_t, out_n, int(n)
 
     def sample_rows(self, z, u, T: float = 1.0) -> np.ndarray:
         """One inverse-CDF draw per row of softmax(z / T); z [R, V], u [R]."""

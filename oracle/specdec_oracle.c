@@ -51,11 +51,17 @@
 #define PLANT_ROW_OFFSET 12       /* draft row i+1 paired with target row i   */
 #define PLANT_DROP_LAST_TERM 13   /* dot product drops the last k term        */
 #define PLANT_ACCEPT_LE 14        /* accept when u <= ratio (boundary)        */
+#define PLANT_TREE_DEPTH 15       /* tree depth counts the root as depth 1    */
+#define PLANT_TREE_SELF_ARGMAX 16 /* tree node checked against its own row    */
 
 /* The draft is given either as logits (softmax at temperature T) or as
  * probabilities used as given. */
 #define ORACLE_Q_LOGITS 0
 #define ORACLE_Q_PROBS 1
+/* The draft is the one-hot distribution at the drafted token: a greedy draft,
+ * or prompt lookup ([LESS] "Where drafts come from": a lookup draft's q is
+ * one-hot; "Why the output is exactly p": so is a greedy draft's). */
+#define ORACLE_Q_ONEHOT 2
 
 /* q is clamped below at this value before dividing ([LLMI] section 2 listing). */
 static const float Q_FLOOR = 1e-12f;
@@ -378,7 +384,8 @@ static int verify_one_greedy(const float* z, const int32_t* x, int64_t gamma, in
 /* The full step from logits.
  *   target: [B, gamma+1, V] fp32 target logits
  *   draft:  [B, gamma, V] fp32 draft logits (draft_kind 0) or probabilities
- *           (draft_kind 1, used as given); ignored at T == 0
+ *           (draft_kind 1, used as given); not read for draft_kind 2 (q is
+ *           one-hot at the drafted token) or at T == 0
  *   x:      [B, gamma] drafted token ids
  *   T:      temperature; T == 0 selects the greedy rule, T > 0 sampling
  *   u:      [B, gamma+1, 2] uniforms in [0, 1); ignored at T == 0
@@ -412,11 +419,15 @@ int oracle_verify(const float* target, const float* draft, int draft_kind, const
     }
     for (int64_t i = 0; i <= gamma; ++i) oracle_softmax(zt + i * V, V, T, prow + i * V, 0, 0);
     for (int64_t i = 0; i < gamma; ++i) {
-      const float* dq = draft + (b * gamma + i) * V;
-      if (draft_kind == ORACLE_Q_PROBS)
+      const float* dq = draft_kind == ORACLE_Q_ONEHOT ? 0 : draft + (b * gamma + i) * V;
+      if (draft_kind == ORACLE_Q_ONEHOT) {
+        for (int64_t v = 0; v < V; ++v) qrow[i * V + v] = 0.0f;
+        qrow[i * V + xb[i]] = 1.0f;
+      } else if (draft_kind == ORACLE_Q_PROBS) {
         memcpy(qrow + i * V, dq, (size_t)V * sizeof(float));
-      else
+      } else {
         oracle_softmax(dq, V, T, qrow + i * V, 0, 0);
+      }
     }
     num_emitted[b] = verify_one_probs(prow, qrow, xb, u + b * (gamma + 1) * 2, gamma, V, work, tb, amb, dmb, dsb);
   }
@@ -463,6 +474,88 @@ double oracle_expected_tokens_rows(const double* alpha, int64_t gamma) {
     if (k < gamma) run *= alpha[k];
   }
   return e;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Tree verification ([LLMI] section 3, the tree attention mask and depth
+ * offsets; [MATH] "SpecInfer and Tree-Based Verification").  A tree of M
+ * nodes is flattened in an order where every parent comes before its
+ * children: parents[0] = -1 (node 0, the root, is the last token already in
+ * the text) and parents[i] is in [0, i) for i >= 1.  A node whose parent index
+ * is outside that range is taken as detached: it is its own only ancestor,
+ * has depth 0 and is never accepted. */
+
+/* Parent of node i if the link is well formed, else -1. */
+static int64_t tree_parent(const int32_t* parents, int64_t i) {
+  if (i == 0) return -1;
+  const int64_t p = parents[i];
+  return (p >= 0 && p < i) ? p : -1;
+}
+
+/* Depth of every node (edges from the root) and its ancestor set as a bit mask
+ * (bit j set iff node j is an ancestor of i or i itself; M <= 64), found by
+ * walking the parent links up from each node.  Optionally the additive mask
+ * the pages use, [M, M] with 0 where attention is allowed and -inf elsewhere. */
+void oracle_tree_mask(const int32_t* parents, int64_t M, uint64_t* mask, int32_t* depth, float* additive) {
+  for (int64_t i = 0; i < M; ++i) {
+    uint64_t bits = 0;
+    int32_t dpt = 0;
+    for (int64_t cur = i; cur != -1; cur = tree_parent(parents, cur)) {
+      bits |= (uint64_t)1 << cur;
+      if (tree_parent(parents, cur) != -1) ++dpt;
+    }
+#if ORACLE_PLANT == PLANT_TREE_DEPTH
+    dpt += 1;
+#endif
+    if (mask) mask[i] = bits;
+    if (depth) depth[i] = dpt;
+    if (additive)
+      for (int64_t j = 0; j < M; ++j) additive[i * M + j] = ((bits >> j) & 1) ? 0.0f : -INFINITY;
+  }
+}
+
+/* Greedy verification of one tree (T == 0).  z: [M, V] target logits, row i
+ * scoring the position after node i along its path.  Node i >= 1 is accepted
+ * iff its parent is accepted and its token equals the argmax of the parent's
+ * row (lowest index on ties); the root always is.  The accepted nodes form
+ * paths from the root; the deepest accepted node a (lowest index among equals)
+ * ends the path that is kept.  Emits the tokens of the path after the root,
+ * then the argmax of row a.  nodes receives the path root .. a (the positions
+ * whose keys and values survive).  Returns the number of emitted tokens,
+ * depth(a) + 1.  scratch: 3*M ints. */
+int oracle_tree_greedy(const float* z, const int32_t* parents, const int32_t* node_tokens, int64_t M, int64_t V,
+                       int32_t* scratch, int32_t* tokens, int32_t* nodes) {
+  int32_t* best = scratch;          /* argmax of each row */
+  int32_t* accepted = scratch + M;
+  int32_t* depth = scratch + 2 * M;
+  oracle_tree_mask(parents, M, 0, depth, 0);
+  for (int64_t i = 0; i < M; ++i) best[i] = (int32_t)oracle_argmax(z + i * V, V, 0);
+  int64_t a = 0;
+  for (int64_t i = 0; i < M; ++i) {
+    const int64_t p = tree_parent(parents, i);
+    if (i == 0) {
+      accepted[i] = 1;
+    } else {
+#if ORACLE_PLANT == PLANT_TREE_SELF_ARGMAX
+      accepted[i] = p >= 0 && accepted[p] && node_tokens[i] == best[i];
+#else
+      accepted[i] = p >= 0 && accepted[p] && node_tokens[i] == best[p];
+#endif
+    }
+    if (accepted[i] && depth[i] > depth[a]) a = i;
+  }
+  /* the path root .. a, root first */
+  const int64_t n = depth[a] + 1;
+  int64_t cur = a;
+  for (int64_t j = n - 1; j >= 0; --j) {
+    nodes[j] = (int32_t)cur;
+    cur = cur >= 0 ? tree_parent(parents, cur) : -1;
+  }
+  for (int64_t j = n; j < M; ++j) nodes[j] = -1;
+  for (int64_t j = 1; j < n; ++j) tokens[j - 1] = nodes[j] >= 0 ? node_tokens[nodes[j]] : -1;
+  tokens[n - 1] = best[a];
+  for (int64_t j = n; j < M; ++j) tokens[j] = -1;
+  return (int)n;
 }
 
 /* Which mistake (if any) this build carries; 0 for the real oracle. */

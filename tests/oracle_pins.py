@@ -18,6 +18,7 @@ import os
 import numpy as np
 from scipy import stats
 
+import oracle as oracle_mod
 import synth
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -302,6 +303,23 @@ def pin_special_cases(o):
     assert np.all(rej != 1)
     freq = np.bincount(rej, minlength=4) / rej.size
     assert np.allclose(freq, [0.25, 0, 0.5, 0.25], atol=1e-12)
+    # The same from logits with the one-hot draft kind (no draft array: q = e_x by construction).
+    z = np.log(p.astype(np.float64)).astype(np.float32)
+    out1 = o.verify(np.broadcast_to(z, (n, 2, 4)), None, np.ones((n, 1), np.int32), u, 1.0,
+                    draft_kind=oracle_mod.Q_ONEHOT)
+    kept1 = out1["num_emitted"] == 2
+    assert abs(kept1.mean() - 0.5) < 1e-12
+    freq1 = np.bincount(out1["tokens"][~kept1, 0], minlength=4) / (~kept1).sum()
+    assert np.allclose(freq1, [0.25, 0, 0.5, 0.25], atol=1e-12)
+    # and equals the probability kind fed an explicit one-hot q, step for step
+    zz = synth.normal_f32((300, 3, V), 1.5, 51, 0)
+    xx = synth.integers((300, 2), 0, V, 51, 1)
+    uu = synth.uniforms((300, 3, 2), 51, 2)
+    qq = np.zeros((300, 2, V), np.float32)
+    np.put_along_axis(qq, xx[..., None].astype(np.int64), 1.0, axis=2)
+    a1 = o.verify(zz, None, xx, uu, 0.9, draft_kind=oracle_mod.Q_ONEHOT)
+    a2 = o.verify(zz, qq, xx, uu, 0.9, draft_kind=oracle_mod.Q_PROBS)
+    assert np.array_equal(a1["tokens"], a2["tokens"]) and np.array_equal(a1["num_emitted"], a2["num_emitted"])
     # gamma = 0: one inverse-CDF draw from p.
     p = _dyadic_simplex(rng, V)
     us = synth.uniforms((500,), 41, 0)
@@ -417,6 +435,82 @@ def pin_llmi_toy(o):
     assert abs(n.mean() - e) < 4 * n.std() / math.sqrt(trials), (n.mean(), e)
 
 
+# ---------------------------------------------------------------------------
+# Tree verification ([LLMI] section 3; [MATH] "SpecInfer and Tree-Based
+# Verification").
+
+def _tree_paths_bruteforce(parents, node_tokens, best):
+    """Every root-to-node path, taken whole: a path is kept iff each of its nodes after the root carries the argmax of
+    the previous node's row.  Returns (deepest kept path (lowest end index among equals), its end)."""
+    M = len(parents)
+    kept = []
+    for end in range(M):
+        path, cur, ok = [], end, True
+        while True:
+            path.append(cur)
+            if cur == 0:
+                break
+            p = parents[cur]
+            if not (0 <= p < cur):
+                ok = False
+                break
+            cur = p
+        if not ok:
+            continue
+        path = path[::-1]
+        if all(node_tokens[path[j]] == best[path[j - 1]] for j in range(1, len(path))):
+            kept.append(path)
+    return max(kept, key=lambda pth: (len(pth), -pth[-1]))
+
+
+def pin_tree(o):
+    g = golden("llmi_tree_and_paged_kv.json")
+    mask, depth, add = o.tree_mask(g["tree_parents"])
+    assert depth.tolist() == g["tree_depths_asserted"]
+    # ancestors-or-self of [-1, 0, 0, 1, 1, 2]: {0}, {0,1}, {0,2}, {0,1,3}, {0,1,4}, {0,2,5}
+    assert mask.tolist() == [0b1, 0b11, 0b101, 0b1011, 0b10011, 0b100101]
+    assert np.array_equal(add == 0, ((mask[:, None] >> np.arange(6, dtype=np.uint64)[None, :]) & 1) == 1)
+    assert np.all(np.isneginf(add[add != 0]))
+    # A worked tree: root 0; children 1 (token 7) and 2 (token 3); 3 under 2 (token 5); 4 under 1 (token 9).
+    V = 16
+    z = np.zeros((5, V), np.float32)
+    z[0, 3] = z[1, 9] = z[2, 5] = z[3, 11] = z[4, 2] = 4.0
+    tok, nodes, n = o.tree_greedy(z, [-1, 0, 0, 2, 1], [0, 7, 3, 5, 9])
+    assert n == 3 and tok[:3].tolist() == [3, 5, 11] and nodes[:3].tolist() == [0, 2, 3]
+    assert np.all(tok[3:] == -1) and np.all(nodes[3:] == -1)
+    # Two siblings carrying the same right token: the lower index is kept.
+    tok, nodes, n = o.tree_greedy(z[:3], [-1, 0, 0], [0, 3, 3])
+    assert n == 2 and nodes[:2].tolist() == [0, 1] and tok[:2].tolist() == [3, 9]
+    # A detached node (parent not before it) is never kept and has depth 0.
+    _, dep, _ = o.tree_mask([-1, 0, 5, 1])
+    assert dep.tolist() == [0, 1, 0, 2]
+    tok, nodes, n = o.tree_greedy(z[:3], [-1, 7, 0], [0, 3, 3])  # node 1 detached although its token is right
+    assert n == 2 and nodes[:2].tolist() == [0, 2] and tok[:2].tolist() == [3, 5]
+    # A chain is the linear greedy rule: node i carries draft i-1, row i scores the position after it.
+    rng = np.random.default_rng(71)
+    for _ in range(20):
+        M, V = int(rng.integers(2, 9)), 12
+        zz = synth.normal_f32((M, V), 1.0, int(rng.integers(1 << 30)), 0)
+        best = zz.argmax(axis=1)
+        x = np.where(rng.random(M - 1) < 0.7, best[:-1], rng.integers(0, V, M - 1)).astype(np.int32)
+        tok, nodes, n = o.tree_greedy(zz, [-1] + list(range(M - 1)), np.concatenate([[0], x]))
+        lin = o.verify(zz[None], None, x[None], None, 0.0)
+        assert n == lin["num_emitted"][0] and np.array_equal(tok[:n], lin["tokens"][0][:n])
+        assert nodes[:n].tolist() == list(range(n))
+    # Brute force over random small trees: every path checked whole.
+    for trial in range(200):
+        M, V = int(rng.integers(1, 12)), 4
+        parents = [-1] + [int(rng.integers(-1, i + 1)) if rng.random() < 0.1 else int(rng.integers(0, i))
+                          for i in range(1, M)]
+        zz = synth.integers((M, V), 0, 3, trial, 9).astype(np.float32)  # many ties: lowest index wins
+        best = [min(np.flatnonzero(zz[i] == zz[i].max())) for i in range(M)]
+        node_tokens = [0] + [int(rng.integers(0, V)) for _ in range(1, M)]
+        path = _tree_paths_bruteforce(parents, node_tokens, best)
+        tok, nodes, n = o.tree_greedy(zz, parents, node_tokens)
+        assert n == len(path) and nodes[:n].tolist() == path
+        assert tok[:n].tolist() == [node_tokens[j] for j in path[1:]] + [best[path[-1]]]
+
+
 def toy_config_inputs(o, w: synth.Workload, independent_rows: bool = False):
     """The reject-only toy workload: target logits z ~ N(0, target_std) for one row (or one per position),
     draft logits z + N(0, noise_std), replicated over B trials; drafted tokens follow q (drawn with the oracle)."""
@@ -470,5 +564,5 @@ def pin_config_toy(o):
 
 ALL_PINS = [
     pin_identity, pin_prep_residual, pin_expected_tokens, pin_softmax, pin_argmax, pin_draw, pin_accept,
-    pin_bruteforce, pin_special_cases, pin_greedy, pin_linear, pin_prep_tv, pin_llmi_toy, pin_config_toy,
+    pin_bruteforce, pin_special_cases, pin_greedy, pin_linear, pin_prep_tv, pin_llmi_toy, pin_config_toy, pin_tree,
 ]
