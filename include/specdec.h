@@ -58,6 +58,9 @@ typedef enum {
 /* How the draft distribution is given. */
 #define SPECDEC_DRAFT_LOGITS 0 /* q = softmax(draft / T), formed on the device      */
 #define SPECDEC_DRAFT_PROBS 1  /* q used as given (one-hot, lookup or any vector)   */
+#define SPECDEC_DRAFT_ONEHOT 2 /* q = e_x, one-hot at each drafted token (greedy or
+                                  prompt-lookup drafts, [LESS] "Where drafts come
+                                  from"); no draft array is read                  */
 
 /* Element type of the scores written by specdec_verify_logits. */
 #define SPECDEC_OUT_F32 0
@@ -69,6 +72,9 @@ typedef enum {
 
 /* Largest number of drafted tokens per sequence. */
 #define SPECDEC_MAX_GAMMA 63
+
+/* Largest number of nodes of one draft tree (the root included). */
+#define SPECDEC_MAX_TREE_NODES 64
 
 /* Human-readable name of a status code; never NULL. */
 const char* specdec_status_string(int status);
@@ -140,7 +146,9 @@ int specdec_verify_logits(const void* X, const void* W, void* Y, int64_t N, int6
  *                 the i-th drafted token; row gamma is the bonus row
  *   draft         device fp32 [B, gamma, V]: draft logits (draft_kind
  *                 SPECDEC_DRAFT_LOGITS) or probabilities (SPECDEC_DRAFT_PROBS);
- *                 unused (may be NULL) when temperature == 0 or gamma == 0
+ *                 unused (may be NULL) when temperature == 0, gamma == 0 or
+ *                 draft_kind is SPECDEC_DRAFT_ONEHOT (then row i keeps x_i
+ *                 iff u < p_i(x_i), and a rejection draws from p_i without x_i)
  *   draft_tokens  device int32 [B, gamma]: the drafted ids x_i
  *   temperature   T >= 0.  T > 0: p = softmax(target / T) and, for logits,
  *                 q = softmax(draft / T) ([LESS] "First: what an output
@@ -182,6 +190,61 @@ int specdec_verify_step(const void* X, const void* W, int weight_layout, const f
                         int64_t gamma, int64_t d, int64_t V, float* logits, int32_t* out_tokens,
                         int32_t* out_num_emitted, float* out_probs, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Tree verification ([LLMI] section 3, multi-draft tree speculation: the tree
+ * attention mask and depth offsets; [MATH] "SpecInfer and Tree-Based
+ * Verification": every node of the tree is scored in one pass and the longest
+ * accepted path is kept).  A tree of M nodes is flattened so that every parent
+ * comes before its children: node 0 is the root (the last token already in the
+ * text; its parent entry is ignored) and node i >= 1 has parents[i] in
+ * [0, i).  A node whose parent entry is outside [0, i) is detached: it is its
+ * own only ancestor, has depth 0 and is never accepted.  M <= 64. */
+
+/* Ancestor masks and depths of B trees.
+ *   parents       device int32 [B, M]
+ *   out_mask      device uint64 [B, M]: bit j of [b, i] set iff node j is an
+ *                 ancestor of node i or i itself (the attention pattern)
+ *   out_depth     device int32 [B, M]: edges from the root (the RoPE position
+ *                 offset of the node)
+ *   out_additive  optional device fp32 [B, M, M]: 0 where node i may attend
+ *                 to node j, -inf elsewhere (NULL to skip) */
+int specdec_tree_mask(const int32_t* parents, int64_t B, int64_t M, uint64_t* out_mask, int32_t* out_depth,
+                      float* out_additive, void* stream);
+
+/* Bytes of device workspace for specdec_tree_verify_greedy (0 for invalid sizes). */
+size_t specdec_tree_workspace_bytes(int64_t B, int64_t M, int64_t V);
+
+/* Greedy (T = 0) verification of B trees on given logits.
+ *   target_logits device fp32 [B, M, V]: row i scores the position after
+ *                 node i along its path from the root
+ *   parents, node_tokens  device int32 [B, M]: node i's parent and token
+ *                 (ids outside [0, V) never match an argmax)
+ *   out_tokens    device int32 [B, M]: the tokens of the kept path after the
+ *                 root, then the argmax of the last kept node's row, then -1
+ *   out_num_emitted device int32 [B]: length of the kept path (root
+ *                 excluded) + 1, in 1 .. M
+ *   out_nodes     device int32 [B, M]: the kept path's node indices from the
+ *                 root (the positions whose keys and values survive), then -1
+ * Node i >= 1 is accepted iff its parent is and node_tokens[i] is the argmax
+ * of its parent's row (lowest index on ties); the deepest accepted node
+ * (lowest index among equals) ends the kept path.  With a chain (parents[i] =
+ * i - 1) this is the greedy rule of specdec_reject_sample. */
+int specdec_tree_verify_greedy(const float* target_logits, const int32_t* parents, const int32_t* node_tokens,
+                               int64_t B, int64_t M, int64_t V, int32_t* out_tokens, int32_t* out_num_emitted,
+                               int32_t* out_nodes, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace for specdec_tree_verify_step (0 for invalid sizes). */
+size_t specdec_tree_step_workspace_bytes(int64_t B, int64_t M, int64_t d, int64_t V, int weight_layout);
+
+/* The whole tree step: scores of all B*M nodes (X [B*M, d] bf16, row b*M + i
+ * the hidden state of node i of tree b; W as in specdec_verify_logits) into
+ * `logits` fp32 [B*M, V], then specdec_tree_verify_greedy on them.  With
+ * packed weights the scoring kernel forms the rows' argmax partials itself. */
+int specdec_tree_verify_step(const void* X, const void* W, int weight_layout, const int32_t* parents,
+                             const int32_t* node_tokens, int64_t B, int64_t M, int64_t d, int64_t V, float* logits,
+                             int32_t* out_tokens, int32_t* out_num_emitted, int32_t* out_nodes, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -20,11 +20,13 @@ LIBRARY = os.path.join(_HERE, "libspecdec.so")
 SPECDEC_OK = 0
 SPECDEC_DRAFT_LOGITS = 0
 SPECDEC_DRAFT_PROBS = 1
+SPECDEC_DRAFT_ONEHOT = 2
 SPECDEC_OUT_F32 = 0
 SPECDEC_OUT_BF16 = 1
 SPECDEC_WEIGHTS_ROW_MAJOR = 0
 SPECDEC_WEIGHTS_PACKED = 1
 SPECDEC_MAX_GAMMA = 63
+SPECDEC_MAX_TREE_NODES = 64
 
 EXPORTED = [
     "specdec_status_string",
@@ -37,6 +39,11 @@ EXPORTED = [
     "specdec_verify_logits",
     "specdec_reject_sample",
     "specdec_verify_step",
+    "specdec_tree_mask",
+    "specdec_tree_workspace_bytes",
+    "specdec_tree_verify_greedy",
+    "specdec_tree_step_workspace_bytes",
+    "specdec_tree_verify_step",
 ]
 
 
@@ -71,6 +78,16 @@ def _load() -> ctypes.CDLL:
     lib.specdec_verify_step.argtypes = [P, P, I, P, I, P, ctypes.c_float, P, I64, I64, I64, I64, P, P, P, P, P,
                                         ctypes.c_size_t, P]
     lib.specdec_verify_step.restype = I
+    lib.specdec_tree_mask.argtypes = [P, I64, I64, P, P, P, P]
+    lib.specdec_tree_mask.restype = I
+    lib.specdec_tree_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.specdec_tree_workspace_bytes.restype = ctypes.c_size_t
+    lib.specdec_tree_verify_greedy.argtypes = [P, P, P, I64, I64, I64, P, P, P, P, ctypes.c_size_t, P]
+    lib.specdec_tree_verify_greedy.restype = I
+    lib.specdec_tree_step_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
+    lib.specdec_tree_step_workspace_bytes.restype = ctypes.c_size_t
+    lib.specdec_tree_verify_step.argtypes = [P, P, I, P, P, I64, I64, I64, I64, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.specdec_tree_verify_step.restype = I
     return lib
 
 
@@ -250,3 +267,65 @@ def new_workspace(B: int, gamma: int, V: int, device="cuda") -> torch.Tensor:
 def new_step_workspace(B: int, gamma: int, d: int, V: int, weight_layout: int, device="cuda") -> torch.Tensor:
     """A device byte buffer of the size specdec_verify_step needs."""
     return torch.empty(step_workspace_bytes(B, gamma, d, V, weight_layout), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+# Trees
+
+def tree_workspace_bytes(B: int, M: int, V: int) -> int:
+    return int(_lib.specdec_tree_workspace_bytes(int(B), int(M), int(V)))
+
+
+def tree_step_workspace_bytes(B: int, M: int, d: int, V: int, weight_layout: int) -> int:
+    return int(_lib.specdec_tree_step_workspace_bytes(int(B), int(M), int(d), int(V), int(weight_layout)))
+
+
+def specdec_tree_mask(parents, out_mask, out_depth, out_additive=None, stream=None):
+    """parents int32 [B, M]; out_mask int64 [B, M] (ancestor bit masks); out_depth int32 [B, M];
+    out_additive fp32 [B, M, M] (0 / -inf) or None."""
+    B, M = parents.shape
+    _expect(parents, torch.int32, (B, M), "parents")
+    _expect(out_mask, torch.int64, (B, M), "out_mask")
+    _expect(out_depth, torch.int32, (B, M), "out_depth")
+    if out_additive is not None:
+        _expect(out_additive, torch.float32, (B, M, M), "out_additive")
+    _check(_lib.specdec_tree_mask(_ptr(parents), B, M, _ptr(out_mask), _ptr(out_depth), _ptr(out_additive),
+                                  _stream(stream)), "specdec_tree_mask")
+    return out_mask, out_depth
+
+
+def specdec_tree_verify_greedy(target_logits, parents, node_tokens, out_tokens, out_num_emitted, out_nodes, workspace,
+                               stream=None):
+    """target_logits fp32 [B, M, V]; parents, node_tokens int32 [B, M]; outputs int32 [B, M], [B], [B, M]."""
+    B, M, V = target_logits.shape
+    _expect(target_logits, torch.float32, (B, M, V), "target_logits")
+    for t, n in ((parents, "parents"), (node_tokens, "node_tokens"), (out_tokens, "out_tokens"),
+                 (out_nodes, "out_nodes")):
+        _expect(t, torch.int32, (B, M), n)
+    _expect(out_num_emitted, torch.int32, (B,), "out_num_emitted")
+    _check(_lib.specdec_tree_verify_greedy(_ptr(target_logits), _ptr(parents), _ptr(node_tokens), B, M, V,
+                                           _ptr(out_tokens), _ptr(out_num_emitted), _ptr(out_nodes), _ptr(workspace),
+                                           workspace.numel(), _stream(stream)), "specdec_tree_verify_greedy")
+    return out_tokens, out_num_emitted, out_nodes
+
+
+def specdec_tree_verify_step(X, W, parents, node_tokens, logits, out_tokens, out_num_emitted, out_nodes, workspace,
+                             stream=None):
+    """X bf16 [B*M, d]; W bf16 [V, d] or PackedWeights; logits fp32 [B*M, V] (written); others as
+    specdec_tree_verify_greedy."""
+    B, M = parents.shape
+    N, d = X.shape
+    wp, V, dw, layout = _weights(W)
+    if dw != d or N != B * M:
+        raise ValueError("X must be [B*M, d] with the weights' d")
+    _expect(X, torch.bfloat16, (N, d), "X")
+    _expect(logits, torch.float32, (N, V), "logits")
+    for t, n in ((parents, "parents"), (node_tokens, "node_tokens"), (out_tokens, "out_tokens"),
+                 (out_nodes, "out_nodes")):
+        _expect(t, torch.int32, (B, M), n)
+    _expect(out_num_emitted, torch.int32, (B,), "out_num_emitted")
+    _check(_lib.specdec_tree_verify_step(_ptr(X), wp, layout, _ptr(parents), _ptr(node_tokens), B, M, d, V,
+                                         _ptr(logits), _ptr(out_tokens), _ptr(out_num_emitted), _ptr(out_nodes),
+                                         _ptr(workspace), workspace.numel(), _stream(stream)),
+           "specdec_tree_verify_step")
+    return out_tokens, out_num_emitted, out_nodes

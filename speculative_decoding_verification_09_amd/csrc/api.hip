@@ -47,13 +47,14 @@ int check_reject_args(const float* target, const float* draft, int draft_kind, c
   if (B < 1 || B > kMaxRows || gamma < 0 || gamma > SPECDEC_MAX_GAMMA || V < 1 || V > kMaxDim)
     return SPECDEC_ERR_SHAPE;
   if ((size_t)B * (size_t)(gamma + 1) * (size_t)V > ((size_t)1 << 40)) return SPECDEC_ERR_SHAPE;
-  if (draft_kind != SPECDEC_DRAFT_LOGITS && draft_kind != SPECDEC_DRAFT_PROBS) return SPECDEC_ERR_ARG;
+  if (draft_kind != SPECDEC_DRAFT_LOGITS && draft_kind != SPECDEC_DRAFT_PROBS && draft_kind != SPECDEC_DRAFT_ONEHOT)
+    return SPECDEC_ERR_ARG;
   if (isnan(T) || T < 0.0f || isinf(T)) return SPECDEC_ERR_TEMPERATURE;
   const bool greedy = T == 0.0f;
   if (!target || !out_tokens || !out_num) return SPECDEC_ERR_NULL;
   if (gamma > 0 && !tokens) return SPECDEC_ERR_NULL;
   if (!greedy && !uniforms) return SPECDEC_ERR_NULL;
-  if (!greedy && gamma > 0 && !draft) return SPECDEC_ERR_NULL;
+  if (!greedy && gamma > 0 && draft_kind != SPECDEC_DRAFT_ONEHOT && !draft) return SPECDEC_ERR_NULL;
   if (!aligned16(target) || (draft && !aligned16(draft))) return SPECDEC_ERR_ALIGN;
   if (((uintptr_t)out_tokens & 3) || ((uintptr_t)out_num & 3) || (tokens && ((uintptr_t)tokens & 3)) ||
       (uniforms && ((uintptr_t)uniforms & 3)) || (out_probs && ((uintptr_t)out_probs & 3)))
@@ -200,6 +201,106 @@ int specdec_verify_step(const void* X, const void* W, int weight_layout, const f
                             stream) != SPECDEC_OK)
     return SPECDEC_ERR_LAUNCH;
   return specdec::launch_reject_sample(a, s) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
+}
+
+size_t specdec_tree_workspace_bytes(int64_t B, int64_t M, int64_t V) {
+  if (B < 1 || B > kMaxRows || M < 1 || M > SPECDEC_MAX_TREE_NODES || V < 1 || V > kMaxDim) return 0;
+  return specdec::tree_workspace_bytes(B, M, V);
+}
+
+int specdec_tree_mask(const int32_t* parents, int64_t B, int64_t M, uint64_t* out_mask, int32_t* out_depth,
+                      float* out_additive, void* stream) {
+  if (!parents || !out_mask || !out_depth) return SPECDEC_ERR_NULL;
+  if (B < 1 || B > kMaxRows || M < 1 || M > SPECDEC_MAX_TREE_NODES) return SPECDEC_ERR_SHAPE;
+  if (((uintptr_t)parents & 3) || ((uintptr_t)out_mask & 7) || ((uintptr_t)out_depth & 3) ||
+      ((uintptr_t)out_additive & 3))
+    return SPECDEC_ERR_ALIGN;
+  return specdec::launch_tree_mask(parents, B, M, out_mask, out_depth, out_additive, (hipStream_t)stream) ==
+                 hipSuccess
+             ? SPECDEC_OK
+             : SPECDEC_ERR_LAUNCH;
+}
+
+namespace {
+int check_tree_args(const void* logits, const int32_t* parents, const int32_t* node_tokens, int64_t B, int64_t M,
+                    int64_t V, const int32_t* out_tokens, const int32_t* out_num, const int32_t* out_nodes,
+                    const void* ws, size_t ws_bytes) {
+  if (!logits || !parents || !node_tokens || !out_tokens || !out_num || !out_nodes) return SPECDEC_ERR_NULL;
+  if (B < 1 || B > kMaxRows || M < 1 || M > SPECDEC_MAX_TREE_NODES || V < 1 || V > kMaxDim) return SPECDEC_ERR_SHAPE;
+  if ((size_t)B * (size_t)M * (size_t)V > ((size_t)1 << 40)) return SPECDEC_ERR_SHAPE;
+  if (!aligned16(logits) || ((uintptr_t)parents & 3) || ((uintptr_t)node_tokens & 3) || ((uintptr_t)out_tokens & 3) ||
+      ((uintptr_t)out_num & 3) || ((uintptr_t)out_nodes & 3))
+    return SPECDEC_ERR_ALIGN;
+  if (!ws || ws_bytes < specdec::tree_workspace_bytes(B, M, V)) return SPECDEC_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SPECDEC_ERR_ALIGN;
+  return SPECDEC_OK;
+}
+
+specdec::TreeArgs tree_args(const float* logits, const int32_t* parents, const int32_t* node_tokens, int64_t B,
+                            int64_t M, int64_t V, int32_t* out_tokens, int32_t* out_num, int32_t* out_nodes,
+                            void* ws) {
+  specdec::TreeArgs t;
+  t.logits = logits;
+  t.parents = parents;
+  t.node_tokens = node_tokens;
+  t.B = B;
+  t.M = M;
+  t.V = V;
+  t.out_tokens = out_tokens;
+  t.out_num = out_num;
+  t.out_nodes = out_nodes;
+  t.workspace = ws;
+  return t;
+}
+}  // namespace
+
+int specdec_tree_verify_greedy(const float* target_logits, const int32_t* parents, const int32_t* node_tokens,
+                               int64_t B, int64_t M, int64_t V, int32_t* out_tokens, int32_t* out_num_emitted,
+                               int32_t* out_nodes, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_tree_args(target_logits, parents, node_tokens, B, M, V, out_tokens, out_num_emitted, out_nodes,
+                                 workspace, workspace_bytes);
+  if (st != SPECDEC_OK) return st;
+  const specdec::TreeArgs t =
+      tree_args(target_logits, parents, node_tokens, B, M, V, out_tokens, out_num_emitted, out_nodes, workspace);
+  return specdec::launch_tree_greedy(t, 0, (hipStream_t)stream) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
+}
+
+size_t specdec_tree_step_workspace_bytes(int64_t B, int64_t M, int64_t d, int64_t V, int weight_layout) {
+  if (B < 1 || B > kMaxRows || M < 1 || M > SPECDEC_MAX_TREE_NODES || V < 1 || V > kMaxDim) return 0;
+  if (check_logits_shape(B * M, d, V, weight_layout) != SPECDEC_OK) return 0;
+  const size_t r = specdec::tree_workspace_bytes(B, M, V);
+  const size_t g = specdec::gemm_workspace_bytes(B * M, d, V, weight_layout == SPECDEC_WEIGHTS_PACKED);
+  return r > g ? r : g;
+}
+
+int specdec_tree_verify_step(const void* X, const void* W, int weight_layout, const int32_t* parents,
+                             const int32_t* node_tokens, int64_t B, int64_t M, int64_t d, int64_t V, float* logits,
+                             int32_t* out_tokens, int32_t* out_num_emitted, int32_t* out_nodes, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (B < 1 || B > kMaxRows || M < 1 || M > SPECDEC_MAX_TREE_NODES) return SPECDEC_ERR_SHAPE;
+  const int64_t N = B * M;
+  int st = check_logits_args(X, W, logits, N, d, V, SPECDEC_OUT_F32, weight_layout);
+  if (st != SPECDEC_OK) return st;
+  st = check_tree_args(logits, parents, node_tokens, B, M, V, out_tokens, out_num_emitted, out_nodes, workspace,
+                       workspace_bytes);
+  if (st != SPECDEC_OK) return st;
+  if (workspace_bytes < specdec_tree_step_workspace_bytes(B, M, d, V, weight_layout)) return SPECDEC_ERR_WORKSPACE;
+  const specdec::TreeArgs t =
+      tree_args(logits, parents, node_tokens, B, M, V, out_tokens, out_num_emitted, out_nodes, workspace);
+  const hipStream_t s = (hipStream_t)stream;
+  specdec::FusedStats fs;
+  if (weight_layout == SPECDEC_WEIGHTS_PACKED && specdec::tree_fused_stats(t, &fs) &&
+      specdec::gemm_stats_parts(N, d, V, fs.pstride) > 0) {
+    int64_t nparts = 0;
+    if (specdec::launch_gemm_with_stats((const uint16_t*)X, (const uint16_t*)W, logits, N, d, V, fs, &nparts, s) !=
+        hipSuccess)
+      return SPECDEC_ERR_LAUNCH;
+    return specdec::launch_tree_greedy(t, nparts, s) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
+  }
+  if (specdec_verify_logits(X, W, logits, N, d, V, SPECDEC_OUT_F32, weight_layout, workspace, workspace_bytes,
+                            stream) != SPECDEC_OK)
+    return SPECDEC_ERR_LAUNCH;
+  return specdec::launch_tree_greedy(t, 0, s) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restri
   double st_s = 0.0;
   int st_i = 0x7fffffff;
   int st_x = -1;  // drafted token of this lane's row, if any
-  if (EPI != 0 && live) {
+  if (EPI == 1 && live) {
     const int g1 = (int)fs.gamma + 1;
     const int bq = m / g1, iq = m - bq * g1;
     if (iq < fs.gamma) {

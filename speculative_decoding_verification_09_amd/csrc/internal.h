@@ -94,4 +94,24 @@ int64_t gemm_stats_parts(int64_t N, int64_t d, int64_t V, int64_t pstride);
 hipError_t launch_gemm_with_stats(const uint16_t* X, const uint16_t* Wp, float* Y, int64_t N, int64_t d, int64_t V,
                                   const FusedStats& fs, int64_t* nparts, hipStream_t stream);
 
+// Tree verification (greedy), M <= 64 nodes per tree.
+struct TreeArgs {
+  const float* logits;       // [B, M, V]
+  const int32_t* parents;    // [B, M]
+  const int32_t* node_tokens;  // [B, M]
+  int64_t B, M, V;
+  int32_t* out_tokens;       // [B, M]
+  int32_t* out_num;          // [B]
+  int32_t* out_nodes;        // [B, M]
+  void* workspace;
+};
+size_t tree_workspace_bytes(int64_t B, int64_t M, int64_t V);
+hipError_t launch_tree_mask(const int32_t* parents, int64_t B, int64_t M, uint64_t* out_mask, int32_t* out_depth,
+                            float* out_additive, hipStream_t stream);
+// Points fs at the tree workspace for the scoring kernel's argmax epilogue; false if the shape cannot take it.
+bool tree_fused_stats(const TreeArgs& t, FusedStats* fs);
+// The greedy tree rule; nparts > 0: argmax partials already in the workspace
+// (from the scoring kernel), else a statistics pass over t.logits first.
+hipError_t launch_tree_greedy(const TreeArgs& t, int64_t nparts, hipStream_t stream);
+
 }  // namespace specdec

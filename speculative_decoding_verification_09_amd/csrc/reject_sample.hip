@@ -62,7 +62,8 @@ struct DrawDesc {
   float mp, ip;    // target row: max of a and 1/Z
   float mq, iq;    // draft row (draft logits only)
   float u;         // the uniform that drives the draw
-  float pad[2];
+  int32_t xk;      // drafted token of row k (one-hot drafts), -1 on the bonus row
+  float pad;
 };
 
 // Workspace layout, every array 16-byte aligned.  Each row has pstride slots
@@ -275,18 +276,22 @@ __device__ __forceinline__ void merge_row(const Ws& ws, int64_t r, bool drafted,
   px_out = drafted ? (float)(exp((double)(zx * inv_t) - (double)M) / z) : 0.0f;
 }
 
-// Weights of the draw at one entry: p_v and r_v = max(0, p_v - q_v), fp32.
+// Weights of the draw at entry v: p_v and r_v = max(0, p_v - q_v), fp32.
+// q is read (draft logits or probabilities), or, for a one-hot draft, 1 at the
+// drafted token and 0 elsewhere.
 struct DrawRow {
   const float* zp;  // target logits of the row
-  const float* zq;  // draft logits or probabilities of the row (null on the bonus row)
+  const float* zq;  // draft logits or probabilities of the row (null on the bonus row and for one-hot drafts)
   float mp, ip, mq, iq, inv_t;
-  bool q_probs;
+  int kind;         // draft kind: 0 logits, 1 probabilities, 2 one-hot
+  bool has_q;       // the step ends on a drafted row (a residual), not on the bonus row
+  int xk;           // the drafted token of that row (one-hot drafts)
 };
 
-__device__ __forceinline__ void weights(const DrawRow& R, float zp, float zq, float& p, float& r) {
+__device__ __forceinline__ void weights(const DrawRow& R, int64_t v, float zp, float zq, float& p, float& r) {
   p = expf(zp * R.inv_t - R.mp) * R.ip;
-  if (R.zq) {
-    const float q = R.q_probs ? zq : expf(zq * R.inv_t - R.mq) * R.iq;
+  if (R.has_q) {
+    const float q = R.kind == 2 ? (v == R.xk ? 1.0f : 0.0f) : (R.kind == 1 ? zq : expf(zq * R.inv_t - R.mq) * R.iq);
     const float dlt = p - q;
     r = dlt > 0.0f ? dlt : 0.0f;
   } else {
@@ -299,13 +304,15 @@ __device__ __forceinline__ DrawRow make_row(const float* __restrict__ target, co
                                             float inv_t) {
   DrawRow R;
   R.zp = target + (size_t)(b * (gamma + 1) + D.k) * V;
-  R.zq = D.k < gamma ? draft + (size_t)(b * gamma + D.k) * V : nullptr;
+  R.has_q = D.k < gamma;
+  R.zq = R.has_q && draft_kind != 2 ? draft + (size_t)(b * gamma + D.k) * V : nullptr;
   R.mp = D.mp;
   R.ip = D.ip;
   R.mq = D.mq;
   R.iq = D.iq;
   R.inv_t = inv_t;
-  R.q_probs = draft_kind == 1;
+  R.kind = draft_kind;
+  R.xk = D.xk;
   return R;
 }
 
@@ -350,6 +357,7 @@ __global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
   const int64_t c = (blockIdx.x - b * gps) * WB + wv;
   const int64_t g1 = gamma + 1;
   const bool q_probs = draft_kind == 1;
+  const bool q_onehot = draft_kind == 2;
   const int64_t nch = ws.nparts;
   // Per-row inputs that do not depend on the statistics, loaded first (lane i <-> row i).
   const bool has_row = lane < g1;
@@ -357,9 +365,9 @@ __global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
   const float u_acc = drafted ? uniforms[(b * g1 + lane) * 2 + 0] : 0.0f;
   const float u_smp = has_row ? uniforms[(b * g1 + lane) * 2 + 1] : 0.0f;
   const int xi = drafted ? clamp_token(tokens[b * gamma + lane], V) : 0;
-  const float q_given = drafted && q_probs ? draft[(size_t)(b * gamma + lane) * V + xi] : 0.0f;
+  const float q_given = drafted && q_probs ? draft[(size_t)(b * gamma + lane) * V + xi] : (q_onehot ? 1.0f : 0.0f);
   // Rows of the sequence: j < g1 target row j, then draft row j - g1 (draft logits).
-  const int nrows = (int)(q_probs ? g1 : g1 + gamma);
+  const int nrows = (int)(draft_kind != 0 ? g1 : g1 + gamma);
   for (int j = wv; j < nrows; j += WB) {
     const int64_t r = j < g1 ? b * g1 + j : B * g1 + b * gamma + (j - g1);
     const bool row_drafted = j < g1 ? j < gamma : true;
@@ -377,7 +385,7 @@ __global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
   const int64_t item = b * ndc + c;
   const double rmt = has_row ? sh_m[lane] : 0.0, rzt = has_row ? sh_z[lane] : 1.0;
   const float p_x = drafted ? sh_px[lane] : 0.0f;
-  const bool ql = drafted && !q_probs;
+  const bool ql = drafted && draft_kind == 0;
   const double rmq = ql ? sh_m[g1 + lane] : 0.0, rzq = ql ? sh_z[g1 + lane] : 1.0;
   const float q_x = ql ? sh_px[g1 + lane] : q_given;
 
@@ -397,7 +405,8 @@ __global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
   D.mq = (float)__shfl(rmq, kq);
   D.iq = (float)(1.0 / __shfl(rzq, kq));
   D.u = __shfl(u_smp, k);
-  D.pad[0] = D.pad[1] = 0.0f;
+  D.xk = k < gamma ? __shfl(xi, k) : -1;
+  D.pad = 0.0f;
 
   if (c == 0) {
     if (has_row && lane != k) out_tokens[b * g1 + lane] = lane < k ? xi : -1;
@@ -419,7 +428,7 @@ __global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     float p, r;
-    weights(R, zp[e], R.zq ? zq[e] : 0.0f, p, r);
+    weights(R, c0 + 256 * (e >> 2) + 4 * lane + (e & 3), zp[e], R.zq ? zq[e] : 0.0f, p, r);
     sr += (double)r;
     sp += (double)p;
   }
@@ -450,7 +459,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void select_kernel(
   const double pj_p = lane < ndc ? pp[lane] : 0.0;
   const DrawRow R = make_row(target, draft, draft_kind, b, gamma, V, D, inv_t);
   double tot = 0.0;
-  if (R.zq) {
+  if (R.has_q) {
     tot = wave_sum(pj_r);
     for (int64_t j0 = 64; j0 < ndc; j0 += 64) tot += wave_sum(j0 + lane < ndc ? pr[j0 + lane] : 0.0);
   }
@@ -502,13 +511,13 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void select_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         ap[e] = v + e < V ? R.zp[v + e] : -INFINITY;
-        if (R.zq) aq[e] = v + e < V ? R.zq[v + e] : (R.q_probs ? 0.0f : -INFINITY);
+        if (R.zq) aq[e] = v + e < V ? R.zq[v + e] : (R.kind == 1 ? 0.0f : -INFINITY);
       }
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float p, r;
-      weights(R, ap[e], R.zq ? aq[e] : 0.0f, p, r);
+      weights(R, v + e, ap[e], R.zq ? aq[e] : 0.0f, p, r);
       w[4 * j + e] = use_p ? p : r;
       lsum += (double)w[4 * j + e];
     }
@@ -629,6 +638,135 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void draft_part_kernel(FusedSt
   }
 }
 
+// ---------------------------------------------------------------------------
+// Tree verification ([LLMI] section 3, tree attention mask and depth offsets;
+// [MATH] "SpecInfer and Tree-Based Verification").  One wave per tree of
+// M <= 64 nodes, lane i <-> node i.  parents[0] is ignored (node 0 is the
+// root); a node whose parent is not in [0, i) is detached: its own only
+// ancestor, depth 0, never accepted.
+
+// Parent of lane i's node if its link is well formed, else -1.
+__device__ __forceinline__ int tree_link(const int32_t* __restrict__ parents, int64_t base, int i, int M) {
+  if (i >= M || i == 0) return -1;
+  const int p = parents[base + i];
+  return (p >= 0 && p < i) ? p : -1;
+}
+
+// Ancestor-or-self bit mask and depth of lane i's node: every lane climbs one
+// link per round, reading its current node's parent from the lane that holds
+// it (M rounds bound every path).
+__device__ __forceinline__ void tree_walk(int par, int i, int M, uint64_t& bits, int& depth) {
+  bits = 0;
+  depth = 0;
+  int cur = i < M ? i : -1;
+  for (int step = 0; step < M; ++step) {
+    const int pc = __shfl(par, cur < 0 ? 0 : cur);
+    if (cur >= 0) {
+      bits |= (uint64_t)1 << cur;
+      if (pc >= 0) ++depth;
+      cur = pc;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kWavesPerBlock * 64) void tree_mask_kernel(const int32_t* __restrict__ parents, int64_t B,
+                                                                         int M, uint64_t* __restrict__ out_mask,
+                                                                         int32_t* __restrict__ out_depth,
+                                                                         float* __restrict__ out_additive) {
+  const int lane = threadIdx.x & 63;
+  const int64_t b = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (b >= B) return;
+  const int64_t base = b * M;
+  const int par = tree_link(parents, base, lane, M);
+  uint64_t bits;
+  int depth;
+  tree_walk(par, lane, M, bits, depth);
+  if (lane >= M) return;
+  out_mask[base + lane] = bits;
+  out_depth[base + lane] = depth;
+  if (out_additive) {
+    float* row = out_additive + (size_t)(base + lane) * M;
+    for (int j = 0; j < M; ++j) row[j] = ((bits >> j) & 1) ? 0.0f : -INFINITY;
+  }
+}
+
+// Greedy tree rule on the argmax partials of the B*M rows (row b*M + i scores
+// the position after node i).  Node i >= 1 is accepted iff its parent is and
+// its token is the parent row's argmax (lowest index on ties); the deepest
+// accepted node a (lowest index among equals) ends the kept path.  Its
+// ancestors, in index order, are the path from the root.
+__global__ __launch_bounds__(kWavesPerBlock * 64) void tree_greedy_kernel(
+    const int32_t* __restrict__ parents, const int32_t* __restrict__ node_tokens, int64_t B, int M, int64_t V,
+    int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_num, int32_t* __restrict__ out_nodes, Ws ws) {
+  const int lane = threadIdx.x & 63;
+  const int64_t b = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (b >= B) return;
+  const int64_t base = b * M;
+  const int64_t nch = ws.nparts;
+  const int par = tree_link(parents, base, lane, M);
+  const int tok = lane < M ? node_tokens[base + lane] : -1;
+  // Row argmaxes: lanes run over the partials of a batch of rows, then lane i keeps row i's.
+  int best = 0;
+  for (int r0 = 0; r0 < M; r0 += kMergeBatch) {
+    float cv[kMergeBatch];
+    int ci[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      cv[j] = -INFINITY;
+      ci[j] = 0x7fffffff;
+      if (r0 + j < M) {
+        const size_t rb = (size_t)(base + r0 + j) * ws.pstride;
+        for (int64_t c = lane; c < nch; c += 64) {
+          const float v = ws.cmax[rb + c];
+          const int ix = ws.cidx[rb + c];
+          if (v > cv[j] || (v == cv[j] && ix < ci[j])) {
+            cv[j] = v;
+            ci[j] = ix;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      if (r0 + j >= M) break;
+      wave_argmax(cv[j], ci[j]);
+      if (lane == r0 + j) best = (ci[j] >= 0 && ci[j] < V) ? ci[j] : 0;  // all-NaN row: any in-range id
+    }
+  }
+  uint64_t bits;
+  int depth;
+  tree_walk(par, lane, M, bits, depth);
+  // Acceptance, one level per round (parents come before children).
+  bool acc = lane == 0;
+  for (int step = 0; step < M; ++step) {
+    const bool pacc = __shfl(acc ? 1 : 0, par < 0 ? 0 : par) != 0;
+    const int pbest = __shfl(best, par < 0 ? 0 : par);
+    if (lane > 0 && lane < M) acc = par >= 0 && pacc && tok == pbest;
+  }
+  // Deepest accepted node, lowest index among equals.
+  const int key = acc && lane < M ? depth * 64 + (63 - lane) : -1;
+  const int kmax = wave_max_i(key);
+  const int a = 63 - (kmax & 63);
+  const uint64_t path = __shfl((unsigned long long)bits, a);
+  const int n = __shfl(depth, a) + 1;
+  const int a_best = __shfl(best, a);
+  if (lane < M) {
+    if ((path >> lane) & 1) {
+      const int rank = __builtin_popcountll(path & (((uint64_t)1 << lane) - 1));
+      out_nodes[base + rank] = lane;
+      if (rank > 0) out_tokens[base + rank - 1] = tok;
+    }
+    if (lane >= n) {
+      out_nodes[base + lane] = -1;
+      out_tokens[base + lane] = -1;
+    }
+    if (lane == 0) {
+      out_tokens[base + n - 1] = a_best;
+      out_num[b] = n;
+    }
+  }
+}
+
 inline unsigned blocks_for(int64_t items, int per) { return (unsigned)((items + per - 1) / per); }
 
 }  // namespace
@@ -703,6 +841,58 @@ hipError_t launch_draft_parts(const FusedStats& fs, int64_t n_target, int64_t V,
 hipError_t launch_reject_after_fused(const RejectArgs& a, int64_t nparts, hipStream_t stream) {
   const Layout L = make_layout(a.B, a.gamma, a.V);
   return launch_decide(a, bind(a.workspace, L, nparts), stream);
+}
+
+size_t tree_workspace_bytes(int64_t B, int64_t M, int64_t V) { return make_layout(B, M - 1, V).total; }
+
+hipError_t launch_tree_mask(const int32_t* parents, int64_t B, int64_t M, uint64_t* out_mask, int32_t* out_depth,
+                            float* out_additive, hipStream_t stream) {
+  hipLaunchKernelGGL(tree_mask_kernel, dim3(blocks_for(B, kWavesPerBlock)), dim3(kWavesPerBlock * 64), 0, stream,
+                     parents, B, (int)M, out_mask, out_depth, out_additive);
+  return hipGetLastError();
+}
+
+bool tree_fused_stats(const TreeArgs& t, FusedStats* fs) {
+  const Layout L = make_layout(t.B, t.M - 1, t.V);
+  if (t.B * t.M > kMaxFusedRows || L.pstride < kMaxFusedParts) return false;
+  const Ws ws = bind(t.workspace, L, 0);
+  *fs = FusedStats{};
+  fs->cmax = ws.cmax;
+  fs->csum = ws.csum;
+  fs->cidx = ws.cidx;
+  fs->zx = ws.zx;
+  fs->pstride = L.pstride;
+  fs->draft = nullptr;
+  fs->tokens = nullptr;
+  fs->B = t.B;
+  fs->gamma = t.M - 1;
+  fs->inv_t = 1.0f;
+  fs->greedy = true;
+  return true;
+}
+
+hipError_t launch_tree_greedy(const TreeArgs& t, int64_t nparts, hipStream_t stream) {
+  const Layout L = make_layout(t.B, t.M - 1, t.V);
+  const dim3 blk(kWavesPerBlock * 64);
+  Ws ws;
+  if (nparts <= 0) {  // argmax partials from the statistics pass over the given logits
+    ws = bind(t.workspace, L, stat_chunks(t.V));
+    const int64_t rows = t.B * t.M;
+    const dim3 g1(blocks_for(rows * stat_chunks(t.V), kWavesPerBlock));
+    if ((t.V & 3) == 0)
+      hipLaunchKernelGGL((stats_kernel<true, true>), g1, blk, 0, stream, t.logits, nullptr, nullptr, rows, rows,
+                         (int64_t)0, t.V, 1.0f, ws);
+    else
+      hipLaunchKernelGGL((stats_kernel<false, true>), g1, blk, 0, stream, t.logits, nullptr, nullptr, rows, rows,
+                         (int64_t)0, t.V, 1.0f, ws);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else {
+    ws = bind(t.workspace, L, nparts);
+  }
+  hipLaunchKernelGGL(tree_greedy_kernel, dim3(blocks_for(t.B, kWavesPerBlock)), blk, 0, stream, t.parents,
+                     t.node_tokens, t.B, (int)t.M, t.V, t.out_tokens, t.out_num, t.out_nodes, ws);
+  return hipGetLastError();
 }
 
 hipError_t launch_reject_sample(const RejectArgs& a, hipStream_t stream) {

@@ -117,7 +117,8 @@ def test_reject_argument_checks():
     assert _reject(g=-1) == 2
     assert _reject(g=64) == 2
     assert _reject(V=0) == 2
-    assert _reject(kind=2) == 7
+    assert _reject(kind=3) == 7
+    assert _reject(kind=2, draft=0) not in (1, 7)  # one-hot drafts need no draft array
     assert _reject(T=-0.5) == 4
     assert _reject(T=float("nan")) == 4
     assert _reject(T=float("inf")) == 4
@@ -180,3 +181,27 @@ def test_logits_workspace_checks():
     assert _logits(N=64, d=28672, V=8192, layout=1) == 5
     assert _logits(N=64, d=28672, V=8192, layout=1, ws=A, wsb=need - 1) == 5
     assert _logits(N=64, d=28672, V=8192, layout=1, ws=A + 8, wsb=need) == 3
+
+
+@needs_no_gpu
+def test_tree_argument_checks():
+    lib = sd.library()
+    # mask: null, size and alignment checks
+    assert lib.specdec_tree_mask(None, 2, 6, P(A), P(A), None, None) == 1
+    assert lib.specdec_tree_mask(P(A), 2, 65, P(A), P(A), None, None) == 2
+    assert lib.specdec_tree_mask(P(A), 0, 6, P(A), P(A), None, None) == 2
+    assert lib.specdec_tree_mask(P(A), 2, 6, P(A + 4), P(A), None, None) == 3
+    ws = sd.tree_workspace_bytes(2, 6, 100)
+    assert ws > 0 and sd.tree_workspace_bytes(2, 65, 100) == 0
+
+    def tv(logits=A, par=A, tok=A, B=2, M=6, V=100, ot=A, on=A, nodes=A, w=A, wb=ws):
+        return lib.specdec_tree_verify_greedy(P(logits), P(par), P(tok), B, M, V, P(ot), P(on), P(nodes), P(w), wb,
+                                              None)
+    assert tv(logits=0) == 1
+    assert tv(nodes=0) == 1
+    assert tv(M=0) == 2
+    assert tv(M=65) == 2
+    assert tv(logits=A + 4) == 3
+    assert tv(wb=ws - 1) == 5
+    assert sd.tree_step_workspace_bytes(1, 16, 4096, 128256, sd.SPECDEC_WEIGHTS_PACKED) == \
+        sd.tree_workspace_bytes(1, 16, 128256)

@@ -188,6 +188,25 @@ def test_probs_one_hot_draft(orc):
     assert np.all(tok[rejected, k] != x[rejected, k])
 
 
+@pytest.mark.parametrize("V", [64, 4099])
+def test_onehot_kind(orc, V):
+    """The one-hot draft kind (no draft array read) gives the same steps as explicit one-hot probability rows,
+    bit for bit, and matches the oracle's one-hot kind."""
+    B, g = 3000 if V == 64 else 200, 3
+    zt = synth.normal_f32((B, g + 1, V), 2.0, 305, 0)
+    x = synth.integers((B, g), 0, V, 305, 1)
+    q = np.zeros((B, g, V), np.float32)
+    q[np.arange(B)[:, None], np.arange(g)[None, :], x] = 1.0
+    u = synth.uniforms((B, g + 1, 2), 305, 2)
+    announce(f"reject one-hot kind V={V}")
+    tok1, num1, pr1 = reject(zt, None, x, u, 0.8, kind=sd.SPECDEC_DRAFT_ONEHOT)
+    tok2, num2, pr2 = reject(zt, q, x, u, 0.8, kind=sd.SPECDEC_DRAFT_PROBS)
+    assert np.array_equal(tok1, tok2) and np.array_equal(num1, num2) and np.array_equal(pr1, pr2)
+    ora = orc.verify(zt, None, x, u, 0.8, draft_kind=2)
+    _check(tok1, num1, ora)
+    assert np.all(pr1[:, :, 1] == 1.0)
+
+
 def test_q_equals_p_always_accepts(orc):
     B, g, V = 500, 5, 3000
     zt = synth.normal_f32((B, g + 1, V), 1.3, 311, 0)

@@ -144,6 +144,8 @@ FUSED = [
     # more positions: the panel kernel's epilogue (one or two token passes)
     ("panel_probs", 6, 3, 128, 3001, 0.8), ("panel_greedy", 16, 3, 64, 2053, 0.0), ("panel_logits", 20, 4, 64, 1500, 1.0),
     ("panel_passes_greedy", 40, 4, 64, 999, 0.0), ("panel_passes_logits", 32, 5, 96, 4100, 1.1),
+    # one-hot (greedy or lookup) drafts: no draft array
+    ("onehot", 2, 3, 256, 5000, 1.0), ("panel_onehot", 12, 4, 128, 3001, 0.9),
 ]
 
 
@@ -154,7 +156,8 @@ def test_fused_statistics_path(orc, name, B, g, d, V, T):
     W = synth.normal_bf16((V, d), 2.0 / np.sqrt(d), seed, synth.STREAM_W)
     target32 = orc.linear(X, W).astype(np.float32).reshape(B, g + 1, V)
     greedy = T == 0.0
-    kind = sd.SPECDEC_DRAFT_PROBS if name == "probs" else sd.SPECDEC_DRAFT_LOGITS
+    kind = {"probs": sd.SPECDEC_DRAFT_PROBS}.get(name, sd.SPECDEC_DRAFT_ONEHOT if "onehot" in name
+                                                  else sd.SPECDEC_DRAFT_LOGITS)
     if greedy:
         draft = None
         am = np.array([[orc.argmax(target32[b, i])[0] for i in range(g)] for b in range(B)], np.int32).reshape(B, g)
@@ -166,6 +169,10 @@ def test_fused_statistics_path(orc, name, B, g, d, V, T):
         if kind == sd.SPECDEC_DRAFT_PROBS:
             draft = np.stack([orc.softmax(draft[b, i], T)[0] for b in range(B) for i in range(g)]).reshape(B, g, V)
             draft = np.ascontiguousarray(draft, np.float32)
+        elif kind == sd.SPECDEC_DRAFT_ONEHOT:  # a greedy draft: its argmax tokens, q one-hot
+            tokens = np.array([[orc.argmax(draft[b, i])[0] for i in range(g)] for b in range(B)],
+                              np.int32).reshape(B, g)
+            draft = None
         u = synth.uniforms((B, g + 1, 2), seed, synth.STREAM_STEP_UNIFORMS)
     probs = torch.full((B, g, 2), float("nan"), device="cuda") if not greedy else None
     announce(f"step fused {name} B={B} gamma={g} d={d} V={V} T={T}")
@@ -179,5 +186,10 @@ def test_fused_statistics_path(orc, name, B, g, d, V, T):
             for i in range(g):
                 x = int(tokens[b, i])
                 p_x = orc.softmax(z[b, i], T)[0][x]
-                q_x = draft[b, i, x] if kind == sd.SPECDEC_DRAFT_PROBS else orc.softmax(draft[b, i], T)[0][x]
+                if kind == sd.SPECDEC_DRAFT_ONEHOT:
+                    q_x = 1.0
+                elif kind == sd.SPECDEC_DRAFT_PROBS:
+                    q_x = draft[b, i, x]
+                else:
+                    q_x = orc.softmax(draft[b, i], T)[0][x]
                 assert abs(got[b, i, 0] - p_x) <= 1e-5 and abs(got[b, i, 1] - q_x) <= 1e-5, (b, i, got[b, i], p_x, q_x)
