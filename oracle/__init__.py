@@ -43,6 +43,8 @@ PLANTS = {
     "accept_le": 14,
     "tree_depth": 15,
     "tree_self_argmax": 16,
+    "kv_free_order": 17,
+    "kv_offset": 18,
 }
 
 
@@ -87,6 +89,14 @@ class Oracle:
         lib.oracle_tree_mask.restype = None
         lib.oracle_tree_greedy.argtypes = [P, P, P, _i64, _i64, P, P, P]
         lib.oracle_tree_greedy.restype = ctypes.c_int
+        lib.oracle_kv_init.argtypes = [P, P, P, _i64, _i64]
+        lib.oracle_kv_init.restype = None
+        lib.oracle_kv_append.argtypes = [P, P, P, P, P, P, P, P, _i64, _i64, _i64, _i64, _i64, _i64, _i64]
+        lib.oracle_kv_append.restype = ctypes.c_int
+        lib.oracle_kv_rollback.argtypes = [P, P, P, P, P, _i64, _i64, _i64]
+        lib.oracle_kv_rollback.restype = ctypes.c_int
+        lib.oracle_kv_gather.argtypes = [P, P, P, P, _i64, _i64, _i64, _i64, _i64, _i64, P, P]
+        lib.oracle_kv_gather.restype = None
         lib.oracle_verify_probs.argtypes = [P, P, P, P, _i64, _i64, _i64, P, P, P, P, P, P]
         lib.oracle_verify_probs.restype = ctypes.c_int
         lib.oracle_verify.argtypes = [P, P, ctypes.c_int, P, _f64, P, _i64, _i64, _i64, P, P, P, P, P, P]
@@ -249,6 +259,10 @@ class Oracle:
                                         out_t.ctypes.data, out_n.ctypes.data)
         return out_t, out_n, int(n)
 
+    # -- paged KV cache --------------------------------------------------
+    def kv_cache(self, R, num_blocks, block_size, heads, head_dim, max_blocks, dtype=np.float32):
+        return OracleKV(self, R, num_blocks, block_size, heads, head_dim, max_blocks, dtype)
+
     def sample_rows(self, z, u, T: float = 1.0) -> np.ndarray:
         """One inverse-CDF draw per row of softmax(z / T); z [R, V], u [R]."""
         z = np.ascontiguousarray(z, dtype=np.float32)
@@ -271,6 +285,46 @@ class Oracle:
 
 
 _DEFAULT: Oracle | None = None
+
+
+class OracleKV:
+    """State of the oracle's paged KV cache (numpy arrays) and its operations."""
+
+    def __init__(self, o, R, num_blocks, block_size, heads, head_dim, max_blocks, dtype=np.float32):
+        self.o, self.R, self.nb, self.bs, self.H, self.D, self.mb = o, R, num_blocks, block_size, heads, head_dim, max_blocks
+        self.dtype = np.dtype(dtype)
+        self.k = np.zeros((num_blocks, heads, block_size, head_dim), self.dtype)
+        self.v = np.zeros_like(self.k)
+        self.tables = np.full((R, max_blocks), -1, np.int32)
+        self.lens = np.zeros(R, np.int32)
+        self.stack = np.zeros(num_blocks, np.int32)
+        self.top = np.zeros(1, np.int32)
+        o.lib.oracle_kv_init(self.stack.ctypes.data, self.top.ctypes.data, self.lens.ctypes.data, R, num_blocks)
+
+    def append(self, knew, vnew) -> int:
+        """knew, vnew: [R, heads, n_new, head_dim].  Returns the status (0 ok)."""
+        knew = np.ascontiguousarray(knew, self.dtype)
+        vnew = np.ascontiguousarray(vnew, self.dtype)
+        n_new = knew.shape[2]
+        return int(self.o.lib.oracle_kv_append(self.k.ctypes.data, self.v.ctypes.data, self.tables.ctypes.data,
+                                               self.lens.ctypes.data, self.stack.ctypes.data, self.top.ctypes.data,
+                                               knew.ctypes.data, vnew.ctypes.data, self.R, n_new, self.H, self.bs,
+                                               self.D, self.dtype.itemsize, self.mb))
+
+    def rollback(self, keep_lens) -> int:
+        keep = np.ascontiguousarray(keep_lens, np.int32)
+        return int(self.o.lib.oracle_kv_rollback(self.tables.ctypes.data, self.lens.ctypes.data,
+                                                 self.stack.ctypes.data, self.top.ctypes.data, keep.ctypes.data,
+                                                 self.R, self.bs, self.mb))
+
+    def gather(self, r):
+        n = int(self.lens[r])
+        ko = np.zeros((self.H, n, self.D), self.dtype)
+        vo = np.zeros_like(ko)
+        self.o.lib.oracle_kv_gather(self.k.ctypes.data, self.v.ctypes.data, self.tables.ctypes.data,
+                                    self.lens.ctypes.data, r, self.H, self.bs, self.D, self.dtype.itemsize, self.mb,
+                                    ko.ctypes.data, vo.ctypes.data)
+        return ko, vo
 
 
 def load(build_if_missing: bool = True) -> Oracle:

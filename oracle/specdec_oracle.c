@@ -53,6 +53,8 @@
 #define PLANT_ACCEPT_LE 14        /* accept when u <= ratio (boundary)        */
 #define PLANT_TREE_DEPTH 15       /* tree depth counts the root as depth 1    */
 #define PLANT_TREE_SELF_ARGMAX 16 /* tree node checked against its own row    */
+#define PLANT_KV_FREE_ORDER 17    /* rollback frees blocks front to back      */
+#define PLANT_KV_OFFSET 18        /* in-block offset taken as t / block_size  */
 
 /* The draft is given either as logits (softmax at temperature T) or as
  * probabilities used as given. */
@@ -556,6 +558,102 @@ int oracle_tree_greedy(const float* z, const int32_t* parents, const int32_t* no
   tokens[n - 1] = best[a];
   for (int64_t j = n; j < M; ++j) tokens[j] = -1;
   return (int)n;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Paged KV cache ([LLMI] section 1, paged block allocation and instant
+ * speculative rollback).  Keys and values live in a pool of fixed-size
+ * physical blocks, [num_blocks][heads][block_size][head_dim] elements of
+ * elem bytes.  Request r keeps a block table (its logical blocks in order)
+ * and a length; token position t lives in logical block t / block_size at
+ * offset t % block_size.  Free blocks form a stack: it starts as
+ * num_blocks-1, ..., 1, 0 (so the first block handed out is 0), allocation
+ * takes from its top, and rollback pushes a request's trailing blocks back,
+ * the last logical block first.  A batch is served request by request in
+ * index order.  tables: [R][max_blocks]; stack: [num_blocks]; *top: number
+ * of free blocks. */
+
+void oracle_kv_init(int32_t* stack, int32_t* top, int32_t* seq_lens, int64_t R, int64_t num_blocks) {
+  for (int64_t i = 0; i < num_blocks; ++i) stack[i] = (int32_t)(num_blocks - 1 - i);
+  *top = (int32_t)num_blocks;
+  for (int64_t r = 0; r < R; ++r) seq_lens[r] = 0;
+}
+
+static int64_t blocks_for_len(int64_t len, int64_t block_size) { return (len + block_size - 1) / block_size; }
+
+/* Appends n_new tokens to every request: new keys/values [R][heads][n_new][head_dim].
+ * Returns 0, or 1 (changing nothing) when the free blocks do not cover the
+ * batch, or 2 (changing nothing) when a request would need more than
+ * max_blocks blocks. */
+int oracle_kv_append(uint8_t* kpool, uint8_t* vpool, int32_t* tables, int32_t* seq_lens, int32_t* stack, int32_t* top,
+                     const uint8_t* knew, const uint8_t* vnew, int64_t R, int64_t n_new, int64_t heads,
+                     int64_t block_size, int64_t head_dim, int64_t elem, int64_t max_blocks) {
+  int64_t need = 0;
+  for (int64_t r = 0; r < R; ++r) {
+    const int64_t nb = blocks_for_len(seq_lens[r] + n_new, block_size);
+    if (nb > max_blocks) return 2;
+    need += nb - blocks_for_len(seq_lens[r], block_size);
+  }
+  if (need > *top) return 1;
+  const int64_t row = head_dim * elem;  /* bytes of one token of one head */
+  for (int64_t r = 0; r < R; ++r) {
+    for (int64_t i = 0; i < n_new; ++i) {
+      const int64_t pos = seq_lens[r] + i;
+      const int64_t logical = pos / block_size;
+#if ORACLE_PLANT == PLANT_KV_OFFSET
+      const int64_t off = (pos / block_size) % block_size;
+#else
+      const int64_t off = pos % block_size;
+#endif
+      if (pos % block_size == 0) tables[r * max_blocks + logical] = stack[--*top]; /* a new logical block */
+      const int64_t phys = tables[r * max_blocks + logical];
+      for (int64_t h = 0; h < heads; ++h) {
+        const int64_t dst = ((phys * heads + h) * block_size + off) * row;
+        const int64_t src = ((r * heads + h) * n_new + i) * row;
+        memcpy(kpool + dst, knew + src, (size_t)row);
+        memcpy(vpool + dst, vnew + src, (size_t)row);
+      }
+    }
+    seq_lens[r] += (int32_t)n_new;
+  }
+  return 0;
+}
+
+/* Rolls request r back to keep_lens[r] tokens, freeing the blocks it no
+ * longer needs (the last logical block first).  No key or value moves.  A
+ * request asked to grow is left as it is; returns the number of such. */
+int oracle_kv_rollback(int32_t* tables, int32_t* seq_lens, int32_t* stack, int32_t* top, const int32_t* keep_lens,
+                       int64_t R, int64_t block_size, int64_t max_blocks) {
+  int bad = 0;
+  for (int64_t r = 0; r < R; ++r) {
+    const int64_t keep = keep_lens[r];
+    if (keep < 0 || keep > seq_lens[r]) {
+      ++bad;
+      continue;
+    }
+    const int64_t have = blocks_for_len(seq_lens[r], block_size), needed = blocks_for_len(keep, block_size);
+#if ORACLE_PLANT == PLANT_KV_FREE_ORDER
+    for (int64_t j = needed; j < have; ++j) stack[(*top)++] = tables[r * max_blocks + j];
+#else
+    for (int64_t j = have - 1; j >= needed; --j) stack[(*top)++] = tables[r * max_blocks + j];
+#endif
+    seq_lens[r] = (int32_t)keep;
+  }
+  return bad;
+}
+
+/* Contiguous keys and values of request r, [heads][seq_len][head_dim]. */
+void oracle_kv_gather(const uint8_t* kpool, const uint8_t* vpool, const int32_t* tables, const int32_t* seq_lens,
+                      int64_t r, int64_t heads, int64_t block_size, int64_t head_dim, int64_t elem, int64_t max_blocks,
+                      uint8_t* kout, uint8_t* vout) {
+  const int64_t len = seq_lens[r], row = head_dim * elem;
+  for (int64_t h = 0; h < heads; ++h)
+    for (int64_t t = 0; t < len; ++t) {
+      const int64_t phys = tables[r * max_blocks + t / block_size];
+      const int64_t src = ((phys * heads + h) * block_size + t % block_size) * row;
+      memcpy(kout + (h * len + t) * row, kpool + src, (size_t)row);
+      memcpy(vout + (h * len + t) * row, vpool + src, (size_t)row);
+    }
 }
 
 /* Which mistake (if any) this build carries; 0 for the real oracle. */

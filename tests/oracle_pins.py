@@ -511,6 +511,62 @@ def pin_tree(o):
         assert tok[:n].tolist() == [node_tokens[j] for j in path[1:]] + [best[path[-1]]]
 
 
+# ---------------------------------------------------------------------------
+# Paged KV cache ([LLMI] section 1; the section 5 script's rollback check).
+
+def pin_paged_kv(o):
+    g = golden("llmi_tree_and_paged_kv.json")["paged_kv"]
+    kv = o.kv_cache(1, g["num_blocks"], g["block_size"], g["n_kv_heads"], g["head_dim"], max_blocks=8)
+    k = synth.normal_f32((1, g["n_kv_heads"], g["appended_tokens"], g["head_dim"]), 1.0, 81, 0)
+    v = synth.normal_f32(k.shape, 1.0, 81, 1)
+    assert kv.append(k, v) == 0
+    assert kv.tables[0, :3].tolist() == [0, 1, 2]  # the free list starts reversed, so blocks come out 0, 1, 2
+    kv.rollback([g["rollback_to"]])
+    kg, vg = kv.gather(0)
+    n = g["gather_equals_first"]
+    assert np.array_equal(kg, k[0, :, :n]) and np.array_equal(vg, v[0, :, :n])
+    assert kv.lens[0] == 6 and kv.top[0] == g["num_blocks"] - 2
+    # the freed block is the first one handed out again
+    assert kv.append(k[:, :, :3], v[:, :, :3]) == 0 and kv.tables[0, 2] == 2
+    # several trailing blocks go back last-logical-first: the earlier one is on top
+    kv2 = o.kv_cache(1, 8, 4, 1, 4, max_blocks=8)
+    z = synth.normal_f32((1, 1, 12, 4), 1.0, 82, 0)
+    kv2.append(z, z)
+    kv2.rollback([1])
+    assert kv2.stack[kv2.top[0] - 1] == 1 and kv2.stack[kv2.top[0] - 2] == 2
+    # not enough free blocks, or a table too short: nothing changes
+    snap = (kv2.lens.copy(), kv2.top.copy(), kv2.tables.copy())
+    big = synth.normal_f32((1, 1, 40, 4), 1.0, 83, 0)
+    assert kv2.append(big, big) == 2
+    kv3 = o.kv_cache(2, 3, 4, 1, 4, max_blocks=8)
+    zz = synth.normal_f32((2, 1, 8, 4), 1.0, 84, 0)
+    assert kv3.append(zz, zz) == 1 and kv3.lens.tolist() == [0, 0] and kv3.top[0] == 3
+    assert np.array_equal(kv2.lens, snap[0]) and np.array_equal(kv2.top, snap[1])
+    # a request asked to grow is left as it is
+    assert kv2.rollback([5]) == 1 and kv2.lens[0] == 1
+    # Random batches of appends and rollbacks against a plain list of tokens per request.
+    rng = np.random.default_rng(85)
+    R, NB, BS, H, D = 5, 64, 4, 2, 8
+    kv = o.kv_cache(R, NB, BS, H, D, max_blocks=12)
+    plain = [np.zeros((H, 0, D), np.float32) for _ in range(R)]
+    for step in range(40):
+        if rng.random() < 0.6:
+            n_new = int(rng.integers(1, 6))
+            kn = synth.normal_f32((R, H, n_new, D), 1.0, 900 + step, 0)
+            vn = synth.normal_f32((R, H, n_new, D), 1.0, 900 + step, 1)
+            if all(plain[r].shape[1] + n_new <= 12 * BS for r in range(R)) and kv.append(kn, vn) == 0:
+                plain = [np.concatenate([plain[r], kn[r]], axis=1) for r in range(R)]
+        else:
+            keep = [int(rng.integers(0, plain[r].shape[1] + 1)) for r in range(R)]
+            assert kv.rollback(keep) == 0
+            plain = [plain[r][:, :keep[r]] for r in range(R)]
+        used = [int(b) for r in range(R) for b in kv.tables[r, :(kv.lens[r] + BS - 1) // BS]]
+        assert sorted(used + kv.stack[:kv.top[0]].tolist()) == list(range(NB))  # every block exactly once
+        for r in range(R):
+            kg, _ = kv.gather(r)
+            assert np.array_equal(kg, plain[r])
+
+
 def toy_config_inputs(o, w: synth.Workload, independent_rows: bool = False):
     """The reject-only toy workload: target logits z ~ N(0, target_std) for one row (or one per position),
     draft logits z + N(0, noise_std), replicated over B trials; drafted tokens follow q (drawn with the oracle)."""
@@ -565,4 +621,5 @@ def pin_config_toy(o):
 ALL_PINS = [
     pin_identity, pin_prep_residual, pin_expected_tokens, pin_softmax, pin_argmax, pin_draw, pin_accept,
     pin_bruteforce, pin_special_cases, pin_greedy, pin_linear, pin_prep_tv, pin_llmi_toy, pin_config_toy, pin_tree,
+    pin_paged_kv,
 ]
