@@ -246,6 +246,71 @@ int specdec_tree_verify_step(const void* X, const void* W, int weight_layout, co
                              int32_t* out_tokens, int32_t* out_num_emitted, int32_t* out_nodes, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Paged KV cache with speculative rollback ([LLMI] section 1, paged block
+ * allocation: keys and values in fixed-size physical blocks reached through a
+ * per-request block table, so rejected speculative tokens are dropped by
+ * shortening a length and returning blocks, without moving data; [LESS] "The
+ * KV cache has to forget": after a round the cache is cut back to the true
+ * text).  All state is caller-owned device memory:
+ *   k_pool, v_pool  [num_blocks][heads][block_size][head_dim] elements of
+ *                   elem_bytes (2 or 4) each; head_dim * elem_bytes % 16 == 0
+ *   block_tables    int32 [R][max_blocks]: physical block of each logical block
+ *   seq_lens        int32 [R]: tokens held; request r uses
+ *                   ceil(seq_lens[r] / block_size) logical blocks, token t sits
+ *                   in logical block t / block_size at offset t % block_size
+ *   free_stack      int32 [num_blocks] and free_top int32 [1]: the free blocks
+ *                   are free_stack[0 .. free_top-1], the top of the stack last
+ *   status          int32 [1], written by append (0 ok; 1 not enough free
+ *                   blocks; 2 a request would exceed max_blocks; on 1 or 2
+ *                   nothing changes) and by rollback (0 ok; 3 some request was
+ *                   asked to grow or to go below 0 and was left as it is)
+ * A batch is served in request order, exactly as one request after another
+ * would be: allocation takes blocks from the top of the free stack, rollback
+ * pushes a request's trailing blocks back, its last logical block first.
+ * Block ids read from a table are checked against num_blocks: an
+ * inconsistent table never makes a kernel access outside the pool. */
+
+/* Fresh state: free_stack = num_blocks-1, ..., 1, 0 (the first block handed
+ * out is 0), free_top = num_blocks, seq_lens = 0. */
+int specdec_kv_init(int32_t* free_stack, int32_t* free_top, int32_t* seq_lens, int64_t R, int64_t num_blocks,
+                    void* stream);
+
+/* Bytes of device workspace for specdec_kv_append (0 for invalid sizes). */
+size_t specdec_kv_workspace_bytes(int64_t R);
+
+/* Appends n_new tokens to every request: k_new, v_new device
+ * [R][heads][n_new][head_dim] (16-byte aligned).  Allocates the logical
+ * blocks the new lengths need, then writes the keys and values through the
+ * tables; all or nothing (see status). */
+int specdec_kv_append(void* k_pool, void* v_pool, int32_t* block_tables, int32_t* seq_lens, int32_t* free_stack,
+                      int32_t* free_top, int32_t* status, const void* k_new, const void* v_new, int64_t R,
+                      int64_t n_new, int64_t num_blocks, int64_t heads, int64_t block_size, int64_t head_dim,
+                      int64_t elem_bytes, int64_t max_blocks, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Rolls request r back to keep_lens[r] tokens (device int32 [R]), returning
+ * the blocks it no longer needs.  No key or value moves. */
+int specdec_kv_rollback(int32_t* block_tables, int32_t* seq_lens, int32_t* free_stack, int32_t* free_top,
+                        int32_t* status, const int32_t* keep_lens, int64_t R, int64_t num_blocks, int64_t block_size,
+                        int64_t max_blocks, void* stream);
+
+/* The rollback after a verification step, driven by its num_emitted (device
+ * int32 [R]): the step appended the gamma+1 positions it scored (the last
+ * token of the text and the gamma drafts); the text grew by num_emitted
+ * tokens, of which the last (correction or bonus) is not yet in the cache.
+ * So request r keeps seq_lens[r] - (gamma + 1) + num_emitted[r] tokens. */
+int specdec_kv_rollback_after_verify(int32_t* block_tables, int32_t* seq_lens, int32_t* free_stack,
+                                     int32_t* free_top, int32_t* status, const int32_t* num_emitted, int64_t gamma,
+                                     int64_t R, int64_t num_blocks, int64_t block_size, int64_t max_blocks,
+                                     void* stream);
+
+/* Contiguous keys and values: k_out, v_out device [R][heads][max_len][head_dim];
+ * entries t < min(seq_lens[r], max_len) are written, the rest left as they are. */
+int specdec_kv_gather(const void* k_pool, const void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
+                      int64_t R, int64_t num_blocks, int64_t heads, int64_t block_size, int64_t head_dim,
+                      int64_t elem_bytes, int64_t max_blocks, int64_t max_len, void* k_out, void* v_out,
+                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

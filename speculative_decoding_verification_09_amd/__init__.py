@@ -44,6 +44,12 @@ EXPORTED = [
     "specdec_tree_verify_greedy",
     "specdec_tree_step_workspace_bytes",
     "specdec_tree_verify_step",
+    "specdec_kv_init",
+    "specdec_kv_workspace_bytes",
+    "specdec_kv_append",
+    "specdec_kv_rollback",
+    "specdec_kv_rollback_after_verify",
+    "specdec_kv_gather",
 ]
 
 
@@ -88,6 +94,19 @@ def _load() -> ctypes.CDLL:
     lib.specdec_tree_step_workspace_bytes.restype = ctypes.c_size_t
     lib.specdec_tree_verify_step.argtypes = [P, P, I, P, P, I64, I64, I64, I64, P, P, P, P, P, ctypes.c_size_t, P]
     lib.specdec_tree_verify_step.restype = I
+    lib.specdec_kv_init.argtypes = [P, P, P, I64, I64, P]
+    lib.specdec_kv_init.restype = I
+    lib.specdec_kv_workspace_bytes.argtypes = [I64]
+    lib.specdec_kv_workspace_bytes.restype = ctypes.c_size_t
+    lib.specdec_kv_append.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, P,
+                                      ctypes.c_size_t, P]
+    lib.specdec_kv_append.restype = I
+    lib.specdec_kv_rollback.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
+    lib.specdec_kv_rollback.restype = I
+    lib.specdec_kv_rollback_after_verify.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64, P]
+    lib.specdec_kv_rollback_after_verify.restype = I
+    lib.specdec_kv_gather.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, P, P, P]
+    lib.specdec_kv_gather.restype = I
     return lib
 
 
@@ -329,3 +348,66 @@ def specdec_tree_verify_step(X, W, parents, node_tokens, logits, out_tokens, out
                                          _ptr(workspace), workspace.numel(), _stream(stream)),
            "specdec_tree_verify_step")
     return out_tokens, out_num_emitted, out_nodes
+
+
+# ---------------------------------------------------------------------------
+# Paged KV cache
+
+class PagedKVCache:
+    """Device state of a paged KV cache (torch tensors) and the C calls on it: append, rollback (to given lengths or
+    after a verification step) and gather.  Pools are [num_blocks, heads, block_size, head_dim] of `dtype`
+    (bfloat16 or float32)."""
+
+    def __init__(self, R, num_blocks, heads, block_size, head_dim, max_blocks, dtype=torch.bfloat16, device="cuda",
+                 stream=None):
+        self.R, self.num_blocks, self.heads, self.block_size = int(R), int(num_blocks), int(heads), int(block_size)
+        self.head_dim, self.max_blocks, self.dtype = int(head_dim), int(max_blocks), dtype
+        self.elem = torch.empty((), dtype=dtype).element_size()
+        shape = (num_blocks, heads, block_size, head_dim)
+        self.k_pool = torch.zeros(shape, dtype=dtype, device=device)
+        self.v_pool = torch.zeros(shape, dtype=dtype, device=device)
+        self.tables = torch.full((R, max_blocks), -1, dtype=torch.int32, device=device)
+        self.lens = torch.zeros((R,), dtype=torch.int32, device=device)
+        self.stack = torch.empty((num_blocks,), dtype=torch.int32, device=device)
+        self.top = torch.empty((1,), dtype=torch.int32, device=device)
+        self.status = torch.zeros((1,), dtype=torch.int32, device=device)
+        self.workspace = torch.empty((_lib.specdec_kv_workspace_bytes(self.R),), dtype=torch.uint8, device=device)
+        _check(_lib.specdec_kv_init(_ptr(self.stack), _ptr(self.top), _ptr(self.lens), self.R, self.num_blocks,
+                                    _stream(stream)), "specdec_kv_init")
+
+    def append(self, k_new, v_new, stream=None):
+        """k_new, v_new: [R, heads, n_new, head_dim] of the pool dtype."""
+        R, H, n, D = k_new.shape
+        _expect(k_new, self.dtype, (self.R, self.heads, n, self.head_dim), "k_new")
+        _expect(v_new, self.dtype, (self.R, self.heads, n, self.head_dim), "v_new")
+        _check(_lib.specdec_kv_append(_ptr(self.k_pool), _ptr(self.v_pool), _ptr(self.tables), _ptr(self.lens),
+                                      _ptr(self.stack), _ptr(self.top), _ptr(self.status), _ptr(k_new), _ptr(v_new),
+                                      self.R, n, self.num_blocks, self.heads, self.block_size, self.head_dim,
+                                      self.elem, self.max_blocks, _ptr(self.workspace), self.workspace.numel(),
+                                      _stream(stream)), "specdec_kv_append")
+
+    def rollback(self, keep_lens, stream=None):
+        _expect(keep_lens, torch.int32, (self.R,), "keep_lens")
+        _check(_lib.specdec_kv_rollback(_ptr(self.tables), _ptr(self.lens), _ptr(self.stack), _ptr(self.top),
+                                        _ptr(self.status), _ptr(keep_lens), self.R, self.num_blocks, self.block_size,
+                                        self.max_blocks, _stream(stream)), "specdec_kv_rollback")
+
+    def rollback_after_verify(self, num_emitted, gamma: int, stream=None):
+        _expect(num_emitted, torch.int32, (self.R,), "num_emitted")
+        _check(_lib.specdec_kv_rollback_after_verify(_ptr(self.tables), _ptr(self.lens), _ptr(self.stack),
+                                                     _ptr(self.top), _ptr(self.status), _ptr(num_emitted), int(gamma),
+                                                     self.R, self.num_blocks, self.block_size, self.max_blocks,
+                                                     _stream(stream)), "specdec_kv_rollback_after_verify")
+
+    def gather(self, max_len: int, k_out=None, v_out=None, stream=None):
+        """[R, heads, max_len, head_dim] views of every request (entries past its length untouched)."""
+        shape = (self.R, self.heads, int(max_len), self.head_dim)
+        if k_out is None:
+            k_out = torch.zeros(shape, dtype=self.dtype, device=self.k_pool.device)
+        if v_out is None:
+            v_out = torch.zeros(shape, dtype=self.dtype, device=self.k_pool.device)
+        _check(_lib.specdec_kv_gather(_ptr(self.k_pool), _ptr(self.v_pool), _ptr(self.tables), _ptr(self.lens),
+                                      self.R, self.num_blocks, self.heads, self.block_size, self.head_dim, self.elem,
+                                      self.max_blocks, int(max_len), _ptr(k_out), _ptr(v_out), _stream(stream)),
+               "specdec_kv_gather")
+        return k_out, v_out

@@ -303,4 +303,131 @@ int specdec_tree_verify_step(const void* X, const void* W, int weight_layout, co
   return specdec::launch_tree_greedy(t, 0, s) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
 }
 
+/* ---- paged KV cache ---- */
+
+namespace {
+int check_kv(const void* kpool, const void* vpool, const int32_t* tables, const int32_t* lens, const int32_t* stack,
+             const int32_t* top, const int32_t* status, int64_t R, int64_t num_blocks, int64_t heads,
+             int64_t block_size, int64_t head_dim, int64_t elem, int64_t max_blocks, bool need_pools) {
+  if ((need_pools && (!kpool || !vpool)) || !tables || !lens || !stack || !top || !status) return SPECDEC_ERR_NULL;
+  if (R < 1 || R > kMaxRows || num_blocks < 1 || num_blocks > ((int64_t)1 << 30) || heads < 1 || heads > 4096 ||
+      block_size < 1 || block_size > 4096 || head_dim < 1 || head_dim > 65536 || max_blocks < 1 ||
+      max_blocks > ((int64_t)1 << 24) || (elem != 2 && elem != 4))
+    return SPECDEC_ERR_SHAPE;
+  if ((head_dim * elem) % 16 != 0) return SPECDEC_ERR_SHAPE;
+  if ((size_t)R * (size_t)max_blocks > ((size_t)1 << 31) ||
+      (size_t)num_blocks * heads * block_size * head_dim * elem > ((size_t)1 << 44))
+    return SPECDEC_ERR_SHAPE;
+  if ((need_pools && (!aligned16(kpool) || !aligned16(vpool))) || ((uintptr_t)tables & 3) || ((uintptr_t)lens & 3) ||
+      ((uintptr_t)stack & 3) || ((uintptr_t)top & 3) || ((uintptr_t)status & 3))
+    return SPECDEC_ERR_ALIGN;
+  return SPECDEC_OK;
+}
+
+specdec::KvArgs kv_args(void* kpool, void* vpool, int32_t* tables, int32_t* lens, int32_t* stack, int32_t* top,
+                        int32_t* status, int64_t R, int64_t num_blocks, int64_t heads, int64_t block_size,
+                        int64_t head_dim, int64_t elem, int64_t max_blocks) {
+  specdec::KvArgs a;
+  a.kpool = kpool;
+  a.vpool = vpool;
+  a.tables = tables;
+  a.lens = lens;
+  a.stack = stack;
+  a.top = top;
+  a.status = status;
+  a.R = R;
+  a.num_blocks = num_blocks;
+  a.heads = heads;
+  a.block_size = block_size;
+  a.head_dim = head_dim;
+  a.elem = elem;
+  a.max_blocks = max_blocks;
+  return a;
+}
+}  // namespace
+
+int specdec_kv_init(int32_t* free_stack, int32_t* free_top, int32_t* seq_lens, int64_t R, int64_t num_blocks,
+                    void* stream) {
+  if (!free_stack || !free_top || !seq_lens) return SPECDEC_ERR_NULL;
+  if (R < 1 || R > kMaxRows || num_blocks < 1 || num_blocks > ((int64_t)1 << 30)) return SPECDEC_ERR_SHAPE;
+  if (((uintptr_t)free_stack & 3) || ((uintptr_t)free_top & 3) || ((uintptr_t)seq_lens & 3)) return SPECDEC_ERR_ALIGN;
+  return specdec::launch_kv_init(free_stack, free_top, seq_lens, R, num_blocks, (hipStream_t)stream) == hipSuccess
+             ? SPECDEC_OK
+             : SPECDEC_ERR_LAUNCH;
+}
+
+size_t specdec_kv_workspace_bytes(int64_t R) {
+  if (R < 1 || R > kMaxRows) return 0;
+  return ((size_t)R * sizeof(int32_t) + 15) & ~(size_t)15;
+}
+
+int specdec_kv_append(void* k_pool, void* v_pool, int32_t* block_tables, int32_t* seq_lens, int32_t* free_stack,
+                      int32_t* free_top, int32_t* status, const void* k_new, const void* v_new, int64_t R,
+                      int64_t n_new, int64_t num_blocks, int64_t heads, int64_t block_size, int64_t head_dim,
+                      int64_t elem_bytes, int64_t max_blocks, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_kv(k_pool, v_pool, block_tables, seq_lens, free_stack, free_top, status, R, num_blocks, heads,
+                    block_size, head_dim, elem_bytes, max_blocks, true);
+  if (st != SPECDEC_OK) return st;
+  if (!k_new || !v_new) return SPECDEC_ERR_NULL;
+  if (n_new < 1 || n_new > ((int64_t)1 << 20)) return SPECDEC_ERR_SHAPE;
+  if (!aligned16(k_new) || !aligned16(v_new)) return SPECDEC_ERR_ALIGN;
+  if (!workspace || workspace_bytes < specdec_kv_workspace_bytes(R)) return SPECDEC_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 3)) return SPECDEC_ERR_ALIGN;
+  const specdec::KvArgs a = kv_args(k_pool, v_pool, block_tables, seq_lens, free_stack, free_top, status, R,
+                                    num_blocks, heads, block_size, head_dim, elem_bytes, max_blocks);
+  return specdec::launch_kv_append(a, k_new, v_new, n_new, (int32_t*)workspace, (hipStream_t)stream) == hipSuccess
+             ? SPECDEC_OK
+             : SPECDEC_ERR_LAUNCH;
+}
+
+int specdec_kv_rollback(int32_t* block_tables, int32_t* seq_lens, int32_t* free_stack, int32_t* free_top,
+                        int32_t* status, const int32_t* keep_lens, int64_t R, int64_t num_blocks, int64_t block_size,
+                        int64_t max_blocks, void* stream) {
+  int st = check_kv(nullptr, nullptr, block_tables, seq_lens, free_stack, free_top, status, R, num_blocks, 1,
+                    block_size, 4, 4, max_blocks, false);
+  if (st != SPECDEC_OK) return st;
+  if (!keep_lens) return SPECDEC_ERR_NULL;
+  if (((uintptr_t)keep_lens & 3)) return SPECDEC_ERR_ALIGN;
+  const specdec::KvArgs a = kv_args(nullptr, nullptr, block_tables, seq_lens, free_stack, free_top, status, R,
+                                    num_blocks, 1, block_size, 4, 4, max_blocks);
+  return specdec::launch_kv_rollback(a, keep_lens, nullptr, 0, (hipStream_t)stream) == hipSuccess
+             ? SPECDEC_OK
+             : SPECDEC_ERR_LAUNCH;
+}
+
+int specdec_kv_rollback_after_verify(int32_t* block_tables, int32_t* seq_lens, int32_t* free_stack,
+                                     int32_t* free_top, int32_t* status, const int32_t* num_emitted, int64_t gamma,
+                                     int64_t R, int64_t num_blocks, int64_t block_size, int64_t max_blocks,
+                                     void* stream) {
+  int st = check_kv(nullptr, nullptr, block_tables, seq_lens, free_stack, free_top, status, R, num_blocks, 1,
+                    block_size, 4, 4, max_blocks, false);
+  if (st != SPECDEC_OK) return st;
+  if (!num_emitted) return SPECDEC_ERR_NULL;
+  if (gamma < 0 || gamma > SPECDEC_MAX_GAMMA) return SPECDEC_ERR_SHAPE;
+  if (((uintptr_t)num_emitted & 3)) return SPECDEC_ERR_ALIGN;
+  const specdec::KvArgs a = kv_args(nullptr, nullptr, block_tables, seq_lens, free_stack, free_top, status, R,
+                                    num_blocks, 1, block_size, 4, 4, max_blocks);
+  return specdec::launch_kv_rollback(a, nullptr, num_emitted, gamma, (hipStream_t)stream) == hipSuccess
+             ? SPECDEC_OK
+             : SPECDEC_ERR_LAUNCH;
+}
+
+int specdec_kv_gather(const void* k_pool, const void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
+                      int64_t R, int64_t num_blocks, int64_t heads, int64_t block_size, int64_t head_dim,
+                      int64_t elem_bytes, int64_t max_blocks, int64_t max_len, void* k_out, void* v_out,
+                      void* stream) {
+  // The stack pointers are not used here: pass the tables for the null checks.
+  int st = check_kv(k_pool, v_pool, block_tables, seq_lens, (const int32_t*)block_tables, (const int32_t*)seq_lens,
+                    (const int32_t*)seq_lens, R, num_blocks, heads, block_size, head_dim, elem_bytes, max_blocks, true);
+  if (st != SPECDEC_OK) return st;
+  if (!k_out || !v_out) return SPECDEC_ERR_NULL;
+  if (max_len < 1 || max_len > ((int64_t)1 << 24)) return SPECDEC_ERR_SHAPE;
+  if (!aligned16(k_out) || !aligned16(v_out)) return SPECDEC_ERR_ALIGN;
+  const specdec::KvArgs a = kv_args((void*)k_pool, (void*)v_pool, (int32_t*)block_tables, (int32_t*)seq_lens, nullptr,
+                                    nullptr, nullptr, R, num_blocks, heads, block_size, head_dim, elem_bytes,
+                                    max_blocks);
+  return specdec::launch_kv_gather(a, max_len, k_out, v_out, (hipStream_t)stream) == hipSuccess ? SPECDEC_OK
+                                                                                                : SPECDEC_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -114,4 +114,24 @@ bool tree_fused_stats(const TreeArgs& t, FusedStats* fs);
 // (from the scoring kernel), else a statistics pass over t.logits first.
 hipError_t launch_tree_greedy(const TreeArgs& t, int64_t nparts, hipStream_t stream);
 
+// Paged KV cache (see paged_kv.hip).
+struct KvArgs {
+  void* kpool;           // [num_blocks][heads][block_size][head_dim] elements of elem bytes
+  void* vpool;
+  int32_t* tables;       // [R][max_blocks]
+  int32_t* lens;         // [R]
+  int32_t* stack;        // [num_blocks] free blocks
+  int32_t* top;          // [1] number of free blocks
+  int32_t* status;       // [1]
+  int64_t R, num_blocks, heads, block_size, head_dim, elem, max_blocks;
+};
+hipError_t launch_kv_init(int32_t* stack, int32_t* top, int32_t* lens, int64_t R, int64_t num_blocks,
+                          hipStream_t stream);
+// old_lens: [R] int32 scratch (the lengths before the append).
+hipError_t launch_kv_append(const KvArgs& a, const void* knew, const void* vnew, int64_t n_new, int32_t* old_lens,
+                            hipStream_t stream);
+hipError_t launch_kv_rollback(const KvArgs& a, const int32_t* keep_lens, const int32_t* num_emitted, int64_t gamma,
+                              hipStream_t stream);
+hipError_t launch_kv_gather(const KvArgs& a, int64_t max_len, void* kout, void* vout, hipStream_t stream);
+
 }  // namespace specdec
