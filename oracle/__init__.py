@@ -45,6 +45,8 @@ PLANTS = {
     "tree_self_argmax": 16,
     "kv_free_order": 17,
     "kv_offset": 18,
+    "topk_tie_high": 19,
+    "topp_strict": 20,
 }
 
 
@@ -97,6 +99,11 @@ class Oracle:
         lib.oracle_kv_rollback.restype = ctypes.c_int
         lib.oracle_kv_gather.argtypes = [P, P, P, P, _i64, _i64, _i64, _i64, _i64, _i64, P, P]
         lib.oracle_kv_gather.restype = None
+        lib.oracle_warp.argtypes = [P, _i64, ctypes.c_double, _i64, ctypes.c_double, P, P, P]
+        lib.oracle_warp.restype = _i64
+        lib.oracle_verify_warped.argtypes = [P, P, ctypes.c_int, P, ctypes.c_double, P, _i64, _i64, _i64, _i64,
+                                             ctypes.c_double, P, P, P, P, P, P, P, P]
+        lib.oracle_verify_warped.restype = ctypes.c_int
         lib.oracle_verify_probs.argtypes = [P, P, P, P, _i64, _i64, _i64, P, P, P, P, P, P]
         lib.oracle_verify_probs.restype = ctypes.c_int
         lib.oracle_verify.argtypes = [P, P, ctypes.c_int, P, _f64, P, _i64, _i64, _i64, P, P, P, P, P, P]
@@ -232,6 +239,45 @@ class Oracle:
                                     out["draw_margin"].ctypes.data, out["draw_mass"].ctypes.data)
         if rc != 0:
             raise ValueError(f"oracle_verify rejected its inputs (code {rc})")
+        return out
+
+    # -- top-k / top-p warping -------------------------------------------
+    def warp(self, z, T: float, top_k: int = 0, top_p: float = 1.0):
+        """Warped probabilities of one row of logits: returns (p fp32 [V], number kept, top-p margin)."""
+        z = np.ascontiguousarray(z, dtype=np.float32)
+        p = np.empty_like(z)
+        order = np.empty(z.size, np.int32)
+        mg = np.zeros(1)
+        n = self.lib.oracle_warp(z.ctypes.data, z.size, float(T), int(top_k), float(top_p), p.ctypes.data,
+                                 order.ctypes.data, mg.ctypes.data)
+        return p, int(n), float(mg[0])
+
+    def verify_warped(self, target_logits, draft, draft_tokens, uniforms, temperature: float, top_k: int = 0,
+                      top_p: float = 1.0, draft_kind: int = Q_LOGITS):
+        """The step with top-k/top-p warping of p (and of q given as logits).  Returns as verify, plus
+        warp_margin [B]."""
+        z = np.ascontiguousarray(target_logits, dtype=np.float32)
+        B, g1, V = z.shape
+        g = g1 - 1
+        if draft is None:
+            draft = np.zeros((B, g, V), dtype=np.float32)
+        d = np.ascontiguousarray(draft, dtype=np.float32).reshape(B, g, V)
+        x = np.ascontiguousarray(draft_tokens, dtype=np.int32).reshape(B, g)
+        if uniforms is None:
+            uniforms = np.zeros((B, g1, 2), dtype=np.float32)
+        u = np.ascontiguousarray(uniforms, dtype=np.float32).reshape(B, g1, 2)
+        out = self._outputs(B, g)
+        out["warp_margin"] = np.empty(B, np.float64)
+        scratch = np.empty(2 * g1 * V, dtype=np.float32)
+        order = np.empty(V, np.int32)
+        rc = self.lib.oracle_verify_warped(z.ctypes.data, d.ctypes.data, int(draft_kind), x.ctypes.data,
+                                           float(temperature), u.ctypes.data, B, g, V, int(top_k), float(top_p),
+                                           scratch.ctypes.data, order.ctypes.data, out["tokens"].ctypes.data,
+                                           out["num_emitted"].ctypes.data, out["accept_margin"].ctypes.data,
+                                           out["draw_margin"].ctypes.data, out["draw_mass"].ctypes.data,
+                                           out["warp_margin"].ctypes.data)
+        if rc != 0:
+            raise ValueError(f"oracle_verify_warped rejected its inputs (code {rc})")
         return out
 
     # -- trees -----------------------------------------------------------

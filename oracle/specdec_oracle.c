@@ -30,6 +30,7 @@
  * that the pins catch each kind of mistake.  The default build has none.
  */
 #include <math.h>
+#include <stdlib.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -55,6 +56,8 @@
 #define PLANT_TREE_SELF_ARGMAX 16 /* tree node checked against its own row    */
 #define PLANT_KV_FREE_ORDER 17    /* rollback frees blocks front to back      */
 #define PLANT_KV_OFFSET 18        /* in-block offset taken as t / block_size  */
+#define PLANT_TOPK_TIE_HIGH 19    /* top-k ties broken towards higher indices */
+#define PLANT_TOPP_STRICT 20      /* top-p stops only when the mass exceeds p */
 
 /* The draft is given either as logits (softmax at temperature T) or as
  * probabilities used as given. */
@@ -432,6 +435,121 @@ int oracle_verify(const float* target, const float* draft, int draft_kind, const
       }
     }
     num_emitted[b] = verify_one_probs(prow, qrow, xb, u + b * (gamma + 1) * 2, gamma, V, work, tb, amb, dmb, dsb);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Warping of a distribution by top-k and top-p before the rule ([LESS] "Why
+ * the output is exactly p": temperature, top-k and top-p are applied to p
+ * before the rule, and to q before drafting; [PREP] "Correctness": the rule
+ * reproduces whatever p it is given).  The pages fix no details; the reading
+ * taken here: temperature first, then top-k, then top-p; entries are ranked
+ * by logit (larger first), ties by index (lower first); top-k keeps the first
+ * k of that ranking (k <= 0 or k >= V: all); top-p keeps the shortest prefix
+ * of the top-k survivors whose probabilities (fp32, the softmax over the
+ * survivors) sum (fp64) to at least top_p, and at least one entry (top_p >= 1:
+ * all); the kept entries are renormalised. */
+
+static const float* g_rank_z; /* ranking key for qsort (the oracle is single-threaded) */
+
+static int rank_cmp(const void* pa, const void* pb) {
+  const int32_t a = *(const int32_t*)pa, b = *(const int32_t*)pb;
+  const float za = g_rank_z[a], zb = g_rank_z[b];
+  if (za > zb) return -1;
+  if (za < zb) return 1;
+#if ORACLE_PLANT == PLANT_TOPK_TIE_HIGH
+  return a < b ? 1 : (a > b ? -1 : 0);
+#else
+  return a < b ? -1 : (a > b ? 1 : 0);
+#endif
+}
+
+/* Warped probabilities p [V] (fp32, 0 outside the kept set) of logits z at
+ * temperature T > 0.  order: V ints of scratch.  margin (optional): the
+ * distance of top_p from the cumulative sums just before and at the top-p cut
+ * (infinite without top-p), for counting near ties.  Returns the number kept. */
+int64_t oracle_warp(const float* z, int64_t V, double T, int64_t top_k, double top_p, float* p, int32_t* order,
+                    double* margin) {
+  for (int64_t v = 0; v < V; ++v) order[v] = (int32_t)v;
+  g_rank_z = z;
+  qsort(order, (size_t)V, sizeof(int32_t), rank_cmp);
+  const int64_t n1 = (top_k > 0 && top_k < V) ? top_k : V;
+  const double m = (double)z[order[0]] / T;
+  double Z1 = 0.0;
+  for (int64_t j = 0; j < n1; ++j) Z1 += exp((double)z[order[j]] / T - m);
+  int64_t n2 = n1;
+  if (margin) *margin = INFINITY;
+  if (top_p < 1.0) {
+    double cum = 0.0;
+    for (int64_t j = 0; j < n1; ++j) {
+      const double before = cum;
+      cum += (double)(float)(exp((double)z[order[j]] / T - m) / Z1);
+#if ORACLE_PLANT == PLANT_TOPP_STRICT
+      if (cum > top_p) {
+#else
+      if (cum >= top_p) {
+#endif
+        n2 = j + 1;
+        if (margin) *margin = fmin(cum - top_p, fabs(top_p - before));
+        break;
+      }
+    }
+  }
+  double Z2 = 0.0;
+  for (int64_t j = 0; j < n2; ++j) Z2 += exp((double)z[order[j]] / T - m);
+  for (int64_t v = 0; v < V; ++v) p[v] = 0.0f;
+  for (int64_t j = 0; j < n2; ++j) p[order[j]] = (float)(exp((double)z[order[j]] / T - m) / Z2);
+  return n2;
+}
+
+/* The step with warping (T > 0): the target rows, and the draft rows given as
+ * logits, are warped with the same top_k and top_p before the rule; draft
+ * probabilities and one-hot drafts are used as given.  At T == 0 the greedy
+ * rule ignores the warping (it keeps the argmax).  warp_margin [B]: the
+ * smallest top-p margin over the rows of the sequence.  scratch: 2*(gamma+1)*V
+ * floats; order: V ints.  Returns as oracle_verify. */
+int oracle_verify_warped(const float* target, const float* draft, int draft_kind, const int32_t* x, double T,
+                         const float* u, int64_t B, int64_t gamma, int64_t V, int64_t top_k, double top_p,
+                         float* scratch, int32_t* order, int32_t* tokens, int32_t* num_emitted, double* accept_margin,
+                         double* draw_margin, double* draw_mass, double* warp_margin) {
+  if (!(T >= 0.0)) return -2;
+  if (T == 0.0) {
+    for (int64_t b = 0; b < B && warp_margin; ++b) warp_margin[b] = INFINITY;
+    return oracle_verify(target, draft, draft_kind, x, T, u, B, gamma, V, scratch, tokens, num_emitted, accept_margin,
+                         draw_margin, draw_mass);
+  }
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t i = 0; i < gamma; ++i)
+      if (x[b * gamma + i] < 0 || x[b * gamma + i] >= V) return -1;
+  float* prow = scratch;
+  float* qrow = scratch + (gamma + 1) * V;
+  float* work = qrow + gamma * V;
+  for (int64_t b = 0; b < B; ++b) {
+    double wm = INFINITY, mg;
+    for (int64_t i = 0; i <= gamma; ++i) {
+      oracle_warp(target + (b * (gamma + 1) + i) * V, V, T, top_k, top_p, prow + i * V, order, &mg);
+      wm = fmin(wm, mg);
+    }
+    for (int64_t i = 0; i < gamma; ++i) {
+      const int32_t xi = x[b * gamma + i];
+      if (draft_kind == ORACLE_Q_ONEHOT) {
+        for (int64_t v = 0; v < V; ++v) qrow[i * V + v] = 0.0f;
+        qrow[i * V + xi] = 1.0f;
+      } else if (draft_kind == ORACLE_Q_PROBS) {
+        memcpy(qrow + i * V, draft + (b * gamma + i) * V, (size_t)V * sizeof(float));
+      } else {
+        oracle_warp(draft + (b * gamma + i) * V, V, T, top_k, top_p, qrow + i * V, order, &mg);
+        wm = fmin(wm, mg);
+      }
+    }
+    if (accept_margin)
+      for (int64_t i = 0; i < gamma; ++i) accept_margin[b * gamma + i] = NAN;
+    if (draw_mass) draw_mass[b] = 0.0;
+    num_emitted[b] = verify_one_probs(prow, qrow, x + b * gamma, u + b * (gamma + 1) * 2, gamma, V, work,
+                                      tokens + b * (gamma + 1), accept_margin ? accept_margin + b * gamma : 0,
+                                      draw_margin ? draw_margin + b : 0, draw_mass ? draw_mass + b : 0);
+    if (warp_margin) warp_margin[b] = wm;
   }
   return 0;
 }

@@ -567,6 +567,59 @@ def pin_paged_kv(o):
             assert np.array_equal(kg, plain[r])
 
 
+# ---------------------------------------------------------------------------
+# top-k / top-p warping before the rule ([LESS] "Why the output is exactly p";
+# [PREP] "Correctness").
+
+def pin_warp(o):
+    # top-k on a worked row: ranking by logit, ties to the lower index.
+    z = np.array([3.0, 1.0, 2.0, 2.0, 0.0], np.float32)
+    p, n, _ = o.warp(z, 1.0, top_k=2)
+    assert n == 2 and np.flatnonzero(p).tolist() == [0, 2]
+    e = np.exp(np.array([3.0, 2.0]) - 3.0)
+    assert np.allclose(p[[0, 2]], e / e.sum(), rtol=1e-7, atol=0)
+    # top-p on dyadic probabilities [1/2, 1/4, 1/8, 1/8]: the shortest prefix reaching p; reaching it exactly counts
+    z = np.log(np.array([0.5, 0.25, 0.125, 0.125])).astype(np.float32)
+    for top_p, kept in ((0.7, 2), (0.75, 2), (0.76, 3), (0.5, 1), (0.1, 1), (0.999, 4)):
+        p, n, _ = o.warp(z, 1.0, top_p=top_p)
+        assert n == kept, (top_p, n)
+        assert abs(float(p.astype(np.float64).sum()) - 1.0) < 1e-6
+    # top-p after top-k: the mass is that of the top-k survivors
+    p, n, _ = o.warp(z, 1.0, top_k=2, top_p=0.7)  # survivors [2/3, 1/3]: 2/3 < 0.7
+    assert n == 2
+    p, n, _ = o.warp(z, 1.0, top_k=2, top_p=0.6)
+    assert n == 1 and p[0] == 1.0
+    # no warping reproduces the plain rule
+    zz = synth.normal_f32((200, 4, 64), 1.5, 61, 0)
+    dd = zz[:, :3] + synth.normal_f32((200, 3, 64), 1.0, 61, 1)
+    xx = synth.integers((200, 3), 0, 64, 61, 2)
+    uu = synth.uniforms((200, 4, 2), 61, 3)
+    a = o.verify(zz, dd, xx, uu, 0.8)
+    b = o.verify_warped(zz, dd, xx, uu, 0.8, top_k=0, top_p=1.0)
+    c = o.verify_warped(zz, dd, xx, uu, 0.8, top_k=64, top_p=1.5)
+    for r in (b, c):
+        assert np.array_equal(a["tokens"], r["tokens"]) and np.array_equal(a["num_emitted"], r["num_emitted"])
+    # the rule reproduces the warped p: exact distribution of the first emitted token over a lattice of uniforms
+    V = 6
+    zt = np.array([2.0, 1.5, 1.0, 0.2, -0.5, 0.1], np.float32)
+    zd = np.array([0.5, 2.0, 0.0, 1.0, 0.3, -1.0], np.float32)
+    for top_k, top_p in ((3, 1.0), (0, 0.8), (4, 0.9)):
+        pw, _, _ = o.warp(zt, 1.0, top_k, top_p)
+        qw, _, _ = o.warp(zd, 1.0, top_k, top_p)
+        G = 512
+        lat = ((np.arange(G) + 0.5) / G).astype(np.float32)
+        tot = np.zeros(V)
+        for x in np.flatnonzero(qw):  # the draft's token, weighted by q
+            uu = np.zeros((G * G, 2, 2), np.float32)
+            ua, us = np.meshgrid(lat, lat, indexing="ij")
+            uu[:, 0, 0] = ua.ravel()
+            uu[:, :, 1] = us.ravel()[:, None]
+            out = o.verify_warped(np.broadcast_to(zt, (G * G, 2, V)), np.broadcast_to(zd, (G * G, 1, V)),
+                                  np.full((G * G, 1), x, np.int32), uu, 1.0, top_k, top_p)
+            tot += float(qw[x]) * np.bincount(out["tokens"][:, 0], minlength=V) / (G * G)
+        assert np.abs(tot - pw).max() < 4.0 / G, (top_k, top_p, tot, pw)
+
+
 def toy_config_inputs(o, w: synth.Workload, independent_rows: bool = False):
     """The reject-only toy workload: target logits z ~ N(0, target_std) for one row (or one per position),
     draft logits z + N(0, noise_std), replicated over B trials; drafted tokens follow q (drawn with the oracle)."""
@@ -621,5 +674,5 @@ def pin_config_toy(o):
 ALL_PINS = [
     pin_identity, pin_prep_residual, pin_expected_tokens, pin_softmax, pin_argmax, pin_draw, pin_accept,
     pin_bruteforce, pin_special_cases, pin_greedy, pin_linear, pin_prep_tv, pin_llmi_toy, pin_config_toy, pin_tree,
-    pin_paged_kv,
+    pin_paged_kv, pin_warp,
 ]
