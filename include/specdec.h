@@ -191,6 +191,36 @@ int specdec_verify_step(const void* X, const void* W, int weight_layout, const f
                         int32_t* out_num_emitted, float* out_probs, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/* Top-k / top-p warping before the rule ([LESS] "Why the output is exactly p":
+ * the sampling settings reshape p, and q before drafting, and the rule then
+ * reproduces the reshaped p; [PREP] "Correctness").  At T > 0 every target row
+ * and every draft-logits row is warped after temperature: entries are ranked
+ * by logit (larger first, ties by lower index); top-k keeps the first top_k;
+ * top-p then keeps the shortest prefix of those whose probability mass reaches
+ * top_p (at least one entry); the kept entries are renormalised and the rest
+ * have probability 0.  Draft probabilities and one-hot drafts are used as
+ * given.  At T == 0 the settings are ignored (the argmax is always kept).
+ *   top_k  >= 0; 0 (or >= V) turns top-k off
+ *   top_p  in (0, 1]; 1 turns top-p off.  Masses are summed exactly as
+ *          integers with 40 fraction bits (fp32 exp(z/T - max)), so the top-p
+ *          cut may differ from an fp64 one only where the cumulative mass is
+ *          within about 1e-6 of top_p.  Requires V <= 2^23 when top_p < 1.
+ * Other arguments, the workspace and the rule as in specdec_reject_sample
+ * (SPECDEC_ERR_ARG for settings out of range).  Logits must not be NaN. */
+int specdec_reject_sample_warped(const float* target_logits, const float* draft, int draft_kind,
+                                 const int32_t* draft_tokens, float temperature, int64_t top_k, float top_p,
+                                 const float* uniforms, int64_t B, int64_t gamma, int64_t V, int32_t* out_tokens,
+                                 int32_t* out_num_emitted, float* out_probs, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/* specdec_verify_step with top-k / top-p warping as in
+ * specdec_reject_sample_warped (same workspace size as specdec_verify_step). */
+int specdec_verify_step_warped(const void* X, const void* W, int weight_layout, const float* draft, int draft_kind,
+                               const int32_t* draft_tokens, float temperature, int64_t top_k, float top_p,
+                               const float* uniforms, int64_t B, int64_t gamma, int64_t d, int64_t V, float* logits,
+                               int32_t* out_tokens, int32_t* out_num_emitted, float* out_probs, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Tree verification ([LLMI] section 3, multi-draft tree speculation: the tree
  * attention mask and depth offsets; [MATH] "SpecInfer and Tree-Based

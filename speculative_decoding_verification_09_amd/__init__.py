@@ -39,6 +39,8 @@ EXPORTED = [
     "specdec_verify_logits",
     "specdec_reject_sample",
     "specdec_verify_step",
+    "specdec_reject_sample_warped",
+    "specdec_verify_step_warped",
     "specdec_tree_mask",
     "specdec_tree_workspace_bytes",
     "specdec_tree_verify_greedy",
@@ -84,6 +86,12 @@ def _load() -> ctypes.CDLL:
     lib.specdec_verify_step.argtypes = [P, P, I, P, I, P, ctypes.c_float, P, I64, I64, I64, I64, P, P, P, P, P,
                                         ctypes.c_size_t, P]
     lib.specdec_verify_step.restype = I
+    lib.specdec_reject_sample_warped.argtypes = [P, P, I, P, ctypes.c_float, I64, ctypes.c_float, P, I64, I64, I64, P,
+                                                 P, P, P, ctypes.c_size_t, P]
+    lib.specdec_reject_sample_warped.restype = I
+    lib.specdec_verify_step_warped.argtypes = [P, P, I, P, I, P, ctypes.c_float, I64, ctypes.c_float, P, I64, I64,
+                                               I64, I64, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.specdec_verify_step_warped.restype = I
     lib.specdec_tree_mask.argtypes = [P, I64, I64, P, P, P, P]
     lib.specdec_tree_mask.restype = I
     lib.specdec_tree_workspace_bytes.argtypes = [I64, I64, I64]
@@ -223,12 +231,7 @@ def specdec_verify_logits(X: torch.Tensor, W, Y: torch.Tensor, out_dtype: int = 
     return Y
 
 
-def specdec_reject_sample(target_logits, draft, draft_tokens, temperature: float, uniforms, out_tokens,
-                          out_num_emitted, workspace, out_probs=None, draft_kind: int = SPECDEC_DRAFT_LOGITS,
-                          stream=None):
-    """The rejection-sampling rule; see include/specdec.h.  Shapes: target [B, g+1, V] fp32, draft [B, g, V]
-    fp32 (or None at T == 0), draft_tokens [B, g] int32, uniforms [B, g+1, 2] fp32 (or None at T == 0),
-    out_tokens [B, g+1] int32, out_num_emitted [B] int32, workspace uint8 >= workspace_bytes(B, g, V)."""
+def _reject_shapes(target_logits, draft, draft_tokens, uniforms, out_tokens, out_num_emitted, out_probs):
     B, g1, V = target_logits.shape
     g = g1 - 1
     _expect(target_logits, torch.float32, (B, g1, V), "target_logits")
@@ -241,6 +244,16 @@ def specdec_reject_sample(target_logits, draft, draft_tokens, temperature: float
     _expect(out_num_emitted, torch.int32, (B,), "out_num_emitted")
     if out_probs is not None:
         _expect(out_probs, torch.float32, (B, g, 2), "out_probs")
+    return B, g, V
+
+
+def specdec_reject_sample(target_logits, draft, draft_tokens, temperature: float, uniforms, out_tokens,
+                          out_num_emitted, workspace, out_probs=None, draft_kind: int = SPECDEC_DRAFT_LOGITS,
+                          stream=None):
+    """The rejection-sampling rule; see include/specdec.h.  Shapes: target [B, g+1, V] fp32, draft [B, g, V]
+    fp32 (or None at T == 0), draft_tokens [B, g] int32, uniforms [B, g+1, 2] fp32 (or None at T == 0),
+    out_tokens [B, g+1] int32, out_num_emitted [B] int32, workspace uint8 >= workspace_bytes(B, g, V)."""
+    B, g, V = _reject_shapes(target_logits, draft, draft_tokens, uniforms, out_tokens, out_num_emitted, out_probs)
     _check(_lib.specdec_reject_sample(_ptr(target_logits), _ptr(draft), int(draft_kind), _ptr(draft_tokens),
                                       float(temperature), _ptr(uniforms), B, g, V, _ptr(out_tokens),
                                       _ptr(out_num_emitted), _ptr(out_probs), _ptr(workspace), workspace.numel(),
@@ -248,11 +261,20 @@ def specdec_reject_sample(target_logits, draft, draft_tokens, temperature: float
     return out_tokens, out_num_emitted
 
 
-def specdec_verify_step(X, W, draft, draft_tokens, temperature: float, uniforms, logits, out_tokens,
-                        out_num_emitted, workspace, out_probs=None, draft_kind: int = SPECDEC_DRAFT_LOGITS,
-                        stream=None):
-    """specdec_verify_logits into `logits` [B*(g+1), V] fp32, then specdec_reject_sample on it.
-    W is a bf16 [V, d] tensor or a PackedWeights handle."""
+def specdec_reject_sample_warped(target_logits, draft, draft_tokens, temperature: float, top_k: int, top_p: float,
+                                 uniforms, out_tokens, out_num_emitted, workspace, out_probs=None,
+                                 draft_kind: int = SPECDEC_DRAFT_LOGITS, stream=None):
+    """specdec_reject_sample after top-k (0: off) / top-p (1: off) warping of the rows; see include/specdec.h."""
+    B, g, V = _reject_shapes(target_logits, draft, draft_tokens, uniforms, out_tokens, out_num_emitted, out_probs)
+    _check(_lib.specdec_reject_sample_warped(_ptr(target_logits), _ptr(draft), int(draft_kind), _ptr(draft_tokens),
+                                             float(temperature), int(top_k), float(top_p), _ptr(uniforms), B, g, V,
+                                             _ptr(out_tokens), _ptr(out_num_emitted), _ptr(out_probs),
+                                             _ptr(workspace), workspace.numel(), _stream(stream)),
+           "specdec_reject_sample_warped")
+    return out_tokens, out_num_emitted
+
+
+def _step_shapes(X, W, draft, draft_tokens, uniforms, logits, out_tokens, out_num_emitted, out_probs):
     B, g = draft_tokens.shape
     N, d = X.shape
     wp, V, dw, layout = _weights(W)
@@ -271,10 +293,34 @@ def specdec_verify_step(X, W, draft, draft_tokens, temperature: float, uniforms,
     _expect(out_num_emitted, torch.int32, (B,), "out_num_emitted")
     if out_probs is not None:
         _expect(out_probs, torch.float32, (B, g, 2), "out_probs")
+    return B, g, d, V, wp, layout
+
+
+def specdec_verify_step(X, W, draft, draft_tokens, temperature: float, uniforms, logits, out_tokens,
+                        out_num_emitted, workspace, out_probs=None, draft_kind: int = SPECDEC_DRAFT_LOGITS,
+                        stream=None):
+    """specdec_verify_logits into `logits` [B*(g+1), V] fp32, then specdec_reject_sample on it.
+    W is a bf16 [V, d] tensor or a PackedWeights handle."""
+    B, g, d, V, wp, layout = _step_shapes(X, W, draft, draft_tokens, uniforms, logits, out_tokens, out_num_emitted,
+                                          out_probs)
     _check(_lib.specdec_verify_step(_ptr(X), wp, layout, _ptr(draft), int(draft_kind), _ptr(draft_tokens),
                                     float(temperature), _ptr(uniforms), B, g, d, V, _ptr(logits), _ptr(out_tokens),
                                     _ptr(out_num_emitted), _ptr(out_probs), _ptr(workspace), workspace.numel(),
                                     _stream(stream)), "specdec_verify_step")
+    return out_tokens, out_num_emitted
+
+
+def specdec_verify_step_warped(X, W, draft, draft_tokens, temperature: float, top_k: int, top_p: float, uniforms,
+                               logits, out_tokens, out_num_emitted, workspace, out_probs=None,
+                               draft_kind: int = SPECDEC_DRAFT_LOGITS, stream=None):
+    """specdec_verify_step with top-k / top-p warping; see include/specdec.h."""
+    B, g, d, V, wp, layout = _step_shapes(X, W, draft, draft_tokens, uniforms, logits, out_tokens, out_num_emitted,
+                                          out_probs)
+    _check(_lib.specdec_verify_step_warped(_ptr(X), wp, layout, _ptr(draft), int(draft_kind), _ptr(draft_tokens),
+                                           float(temperature), int(top_k), float(top_p), _ptr(uniforms), B, g, d, V,
+                                           _ptr(logits), _ptr(out_tokens), _ptr(out_num_emitted), _ptr(out_probs),
+                                           _ptr(workspace), workspace.numel(), _stream(stream)),
+           "specdec_verify_step_warped")
     return out_tokens, out_num_emitted
 
 

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(HERE, "_build")
 LIBRARY = os.path.join(HERE, "libspecdec.so")
-SOURCES = ["api.hip", "gemm_sweep.hip", "gemm_tiled.hip", "reject_sample.hip", "paged_kv.hip"]
+SOURCES = ["api.hip", "gemm_sweep.hip", "gemm_tiled.hip", "reject_sample.hip", "paged_kv.hip", "warp.hip"]
 ARCH = "gfx950"
 
 # -ffp-contract=off: the draw kernel recomputes the same fp32 weights in two

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kVersion = 10100;  // 1.1.0
+constexpr int kVersion = 10200;  // 1.2.0
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -83,7 +83,17 @@ specdec::RejectArgs reject_args(const float* target, const float* draft, int dra
   a.out_probs = T == 0.0f ? nullptr : out_probs;
   a.workspace = ws;
   a.workspace_bytes = ws_bytes;
+  a.top_k = 0;
+  a.top_p = 1.0f;
   return a;
+}
+
+// top_k >= 0 (0: off); 0 < top_p <= 1.  Top-p sums fixed-point masses that
+// stay exact for V <= 2^23.
+int check_warp_args(int64_t top_k, float top_p, int64_t V) {
+  if (top_k < 0 || !(top_p > 0.0f && top_p <= 1.0f)) return SPECDEC_ERR_ARG;
+  if (top_p < 1.0f && V > ((int64_t)1 << 23)) return SPECDEC_ERR_SHAPE;
+  return SPECDEC_OK;
 }
 
 }  // namespace
@@ -166,6 +176,55 @@ int specdec_reject_sample(const float* target_logits, const float* draft, int dr
                                             workspace_bytes);
   const hipError_t e = specdec::launch_reject_sample(a, (hipStream_t)stream);
   return e == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
+}
+
+int specdec_reject_sample_warped(const float* target_logits, const float* draft, int draft_kind,
+                                 const int32_t* draft_tokens, float temperature, int64_t top_k, float top_p,
+                                 const float* uniforms, int64_t B, int64_t gamma, int64_t V, int32_t* out_tokens,
+                                 int32_t* out_num_emitted, float* out_probs, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  int st = check_reject_args(target_logits, draft, draft_kind, draft_tokens, temperature, uniforms, B, gamma, V,
+                             out_tokens, out_num_emitted, out_probs, workspace, workspace_bytes);
+  if (st != SPECDEC_OK) return st;
+  st = check_warp_args(top_k, top_p, V);
+  if (st != SPECDEC_OK) return st;
+  specdec::RejectArgs a = reject_args(target_logits, draft, draft_kind, draft_tokens, temperature, uniforms, B, gamma,
+                                      V, out_tokens, out_num_emitted, out_probs, workspace, workspace_bytes);
+  a.top_k = top_k;
+  a.top_p = top_p;
+  const hipError_t e = specdec::launch_reject_sample(a, (hipStream_t)stream);
+  return e == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
+}
+
+int specdec_verify_step_warped(const void* X, const void* W, int weight_layout, const float* draft, int draft_kind,
+                               const int32_t* draft_tokens, float temperature, int64_t top_k, float top_p,
+                               const float* uniforms, int64_t B, int64_t gamma, int64_t d, int64_t V, float* logits,
+                               int32_t* out_tokens, int32_t* out_num_emitted, float* out_probs, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (B < 1 || B > kMaxRows || gamma < 0 || gamma > SPECDEC_MAX_GAMMA) return SPECDEC_ERR_SHAPE;
+  const int64_t N = B * (gamma + 1);
+  int st = check_logits_args(X, W, logits, N, d, V, SPECDEC_OUT_F32, weight_layout);
+  if (st != SPECDEC_OK) return st;
+  st = check_reject_args(logits, draft, draft_kind, draft_tokens, temperature, uniforms, B, gamma, V, out_tokens,
+                         out_num_emitted, out_probs, workspace, workspace_bytes);
+  if (st != SPECDEC_OK) return st;
+  st = check_warp_args(top_k, top_p, V);
+  if (st != SPECDEC_OK) return st;
+  if (workspace_bytes < specdec_step_workspace_bytes(B, gamma, d, V, weight_layout)) return SPECDEC_ERR_WORKSPACE;
+  specdec::RejectArgs a = reject_args(logits, draft, draft_kind, draft_tokens, temperature, uniforms, B, gamma, V,
+                                      out_tokens, out_num_emitted, out_probs, workspace, workspace_bytes);
+  a.top_k = top_k;
+  a.top_p = top_p;
+  if (!specdec::warp_active(a))  // nothing to warp (T == 0, or both settings off): the plain step
+    return specdec_verify_step(X, W, weight_layout, draft, draft_kind, draft_tokens, temperature, uniforms, B, gamma,
+                               d, V, logits, out_tokens, out_num_emitted, out_probs, workspace, workspace_bytes,
+                               stream);
+  // The cuts need whole rows, so the scores are written first and the
+  // statistics pass reads them back.
+  if (specdec_verify_logits(X, W, logits, N, d, V, SPECDEC_OUT_F32, weight_layout, workspace, workspace_bytes,
+                            stream) != SPECDEC_OK)
+    return SPECDEC_ERR_LAUNCH;
+  return specdec::launch_reject_sample(a, (hipStream_t)stream) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
 }
 
 int specdec_verify_step(const void* X, const void* W, int weight_layout, const float* draft, int draft_kind,

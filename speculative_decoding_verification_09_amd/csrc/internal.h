@@ -54,10 +54,35 @@ struct RejectArgs {
   float* out_probs;        // [B, gamma, 2] or null
   void* workspace;
   size_t workspace_bytes;
+  int64_t top_k = 0;       // keep the top_k largest logits of a row; <= 0 or >= V: no top-k
+  float top_p = 1.0f;      // then the shortest prefix with mass >= top_p; >= 1: no top-p
 };
 
+// True when the step warps its rows (T > 0 with an active top-k or top-p).
+inline bool warp_active(const RejectArgs& a) {
+  return a.temperature > 0.0f && ((a.top_k > 0 && a.top_k < a.V) || a.top_p < 1.0f);
+}
+
 size_t reject_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
+// Statistics pass over a.target (and draft logits), then the draw or the
+// greedy rule; with warping, the per-row cuts are found first.
 hipError_t launch_reject_sample(const RejectArgs& a, hipStream_t stream);
+
+// Order-preserving integer image of an fp32 logit (larger value, larger key;
+// -0 and +0 map to one key).  A warped row keeps entry v iff
+// key(z_v) > cut_key, or key(z_v) == cut_key and v <= cut_idx: the entries
+// ranked by logit, ties by lower index, cut after one of them.
+__device__ __forceinline__ uint32_t order_key(float z) {
+  uint32_t u = __float_as_uint(z == 0.0f ? 0.0f : z);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ bool warp_kept(uint32_t key, int64_t v, uint32_t cut_key, int32_t cut_idx) {
+  return key > cut_key || (key == cut_key && v <= (int64_t)cut_idx);
+}
+// One workgroup per row: rows [0, n_target) of target, then rows of draft.
+hipError_t launch_warp_cuts(const float* target, const float* draft, int64_t n_target, int64_t n_rows, int64_t V,
+                            float inv_t, int64_t top_k, float top_p, uint32_t* cut_key, int32_t* cut_idx,
+                            hipStream_t stream);
 
 // Softmax (or argmax) statistics formed by the scoring kernel itself, as an
 // epilogue: for every row, one partial per workgroup of that kernel, in the

@@ -75,6 +75,7 @@ struct Layout {
   size_t off_zx;                            // per row
   size_t off_desc;                          // per sequence
   size_t off_sres, off_sp;                  // per (sequence, draw chunk)
+  size_t off_wkey, off_widx;                // per row: warp cut
   int64_t pstride;
   size_t total;
 };
@@ -99,6 +100,8 @@ __host__ __device__ inline Layout make_layout(int64_t B, int64_t gamma, int64_t 
   L.off_desc = o; o = align16(o + (size_t)B * sizeof(DrawDesc));
   L.off_sres = o; o = align16(o + ndc * sizeof(double));
   L.off_sp = o;   o = align16(o + ndc * sizeof(double));
+  L.off_wkey = o; o = align16(o + rows * sizeof(uint32_t));
+  L.off_widx = o; o = align16(o + rows * sizeof(int32_t));
   L.total = o;
   return L;
 }
@@ -111,6 +114,8 @@ struct Ws {
   DrawDesc* desc;  // per sequence
   double* sres;    // per (sequence, draw chunk): sum of the residual weights
   double* sp;      // per (sequence, draw chunk): sum of p
+  uint32_t* wkey;  // per row: warp cut key (read only by the warped kernels)
+  int32_t* widx;   // per row: warp cut index
   int64_t pstride; // slots per row
   int64_t nparts;  // slots in use per row
 };
@@ -118,7 +123,8 @@ struct Ws {
 inline Ws bind(void* base, const Layout& L, int64_t nparts) {
   char* b = (char*)base;
   return Ws{(float*)(b + L.off_cmax), (double*)(b + L.off_csum), (int32_t*)(b + L.off_cidx), (float*)(b + L.off_zx),
-            (DrawDesc*)(b + L.off_desc), (double*)(b + L.off_sres), (double*)(b + L.off_sp), L.pstride, nparts};
+            (DrawDesc*)(b + L.off_desc), (double*)(b + L.off_sres), (double*)(b + L.off_sp),
+            (uint32_t*)(b + L.off_wkey), (int32_t*)(b + L.off_widx), L.pstride, nparts};
 }
 
 // ---------------------------------------------------------------------------
@@ -164,8 +170,9 @@ __device__ __forceinline__ int clamp_token(int32_t t, int64_t V) { return t < 0 
 // 1. Chunk statistics.  Target rows are [0, B*(gamma+1)) (row b*(gamma+1) + i),
 //    draft rows [B*(gamma+1), B*(2*gamma+1)) (row B*(gamma+1) + b*gamma + i).
 //    Lane l of a wave takes the 32 entries 256*j + 4*l + e (j < 8, e < 4) of
-//    its 2048-entry chunk (1 KB per load instruction).
-template <bool VEC, bool GREEDY>
+//    its 2048-entry chunk (1 KB per load instruction).  WARP: entries the
+//    row's warp cut drops count as -inf (so does a dropped drafted token).
+template <bool VEC, bool GREEDY, bool WARP>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void stats_kernel(const float* __restrict__ target,
                                                                      const float* __restrict__ draft,
                                                                      const int32_t* __restrict__ tokens,
@@ -213,13 +220,25 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void stats_kernel(const float*
     }
     return;
   }
+  uint32_t wk = 0;
+  int32_t wi = 0x7fffffff;
+  if (WARP) {
+    wk = ws.wkey[r];
+    wi = ws.widx[r];
+#pragma unroll
+    for (int e = 0; e < PL; ++e)
+      if (!warp_kept(order_key(x[e]), c0 + 256 * (e >> 2) + 4 * lane + (e & 3), wk, wi)) x[e] = -INFINITY;
+  }
   // The drafted token of this row, if it falls in this chunk.
   const int64_t g1 = gamma + 1;
   const int64_t b = is_target ? r / g1 : (r - n_target_rows) / gamma;
   const int64_t i = is_target ? r - b * g1 : (r - n_target_rows) - b * gamma;
   if (i < gamma && lane == 0) {
     const int xt = clamp_token(tokens[b * gamma + i], V);
-    if (xt >= c0 && xt < c0 + kStatChunk) ws.zx[r] = row[xt];
+    if (xt >= c0 && xt < c0 + kStatChunk) {
+      const float zx = row[xt];
+      ws.zx[r] = (!WARP || warp_kept(order_key(zx), xt, wk, wi)) ? zx : -INFINITY;
+    }
   }
   float mx = -INFINITY;
 #pragma unroll
@@ -229,8 +248,9 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void stats_kernel(const float*
   }
   mx = wave_max(mx);
   double sum = 0.0;
+  if (mx > -INFINITY)  // a chunk the warp cut drops whole has no mass
 #pragma unroll
-  for (int e = 0; e < PL; ++e) sum += (double)expf(x[e] - mx);
+    for (int e = 0; e < PL; ++e) sum += (double)expf(x[e] - mx);
   sum = wave_sum(sum);
   if (lane == 0) {
     ws.cmax[r * ws.pstride + c] = mx;
@@ -286,12 +306,18 @@ struct DrawRow {
   int kind;         // draft kind: 0 logits, 1 probabilities, 2 one-hot
   bool has_q;       // the step ends on a drafted row (a residual), not on the bonus row
   int xk;           // the drafted token of that row (one-hot drafts)
+  uint32_t pk, qk;  // warp cuts of the two rows (WARP only)
+  int32_t pi, qi;
 };
 
+// WARP: p_v (and q_v of draft logits) is 0 where the row's warp cut drops v.
+template <bool WARP>
 __device__ __forceinline__ void weights(const DrawRow& R, int64_t v, float zp, float zq, float& p, float& r) {
   p = expf(zp * R.inv_t - R.mp) * R.ip;
+  if (WARP && !warp_kept(order_key(zp), v, R.pk, R.pi)) p = 0.0f;
   if (R.has_q) {
-    const float q = R.kind == 2 ? (v == R.xk ? 1.0f : 0.0f) : (R.kind == 1 ? zq : expf(zq * R.inv_t - R.mq) * R.iq);
+    float q = R.kind == 2 ? (v == R.xk ? 1.0f : 0.0f) : (R.kind == 1 ? zq : expf(zq * R.inv_t - R.mq) * R.iq);
+    if (WARP && R.kind == 0 && !warp_kept(order_key(zq), v, R.qk, R.qi)) q = 0.0f;
     const float dlt = p - q;
     r = dlt > 0.0f ? dlt : 0.0f;
   } else {
@@ -299,9 +325,10 @@ __device__ __forceinline__ void weights(const DrawRow& R, int64_t v, float zp, f
   }
 }
 
+template <bool WARP>
 __device__ __forceinline__ DrawRow make_row(const float* __restrict__ target, const float* __restrict__ draft,
-                                            int draft_kind, int64_t b, int64_t gamma, int64_t V, const DrawDesc& D,
-                                            float inv_t) {
+                                            int draft_kind, int64_t B, int64_t b, int64_t gamma, int64_t V,
+                                            const DrawDesc& D, float inv_t, const Ws& ws) {
   DrawRow R;
   R.zp = target + (size_t)(b * (gamma + 1) + D.k) * V;
   R.has_q = D.k < gamma;
@@ -313,6 +340,18 @@ __device__ __forceinline__ DrawRow make_row(const float* __restrict__ target, co
   R.inv_t = inv_t;
   R.kind = draft_kind;
   R.xk = D.xk;
+  R.pk = R.qk = 0u;
+  R.pi = R.qi = 0x7fffffff;
+  if (WARP) {
+    const int64_t rt = b * (gamma + 1) + D.k;
+    R.pk = ws.wkey[rt];
+    R.pi = ws.widx[rt];
+    if (R.zq && draft_kind == 0) {
+      const int64_t rd = B * (gamma + 1) + b * gamma + D.k;
+      R.qk = ws.wkey[rd];
+      R.qi = ws.widx[rd];
+    }
+  }
   return R;
 }
 
@@ -342,7 +381,7 @@ __device__ __forceinline__ void load_chunk16(const float* __restrict__ row, int6
 //    row per wave at a time) into LDS; after one barrier every wave reads the
 //    statistics of all rows from LDS, lane i <-> row i.
 constexpr int kMaxRows = 2 * 63 + 1;
-template <int WB, bool VEC>
+template <int WB, bool VEC, bool WARP>
 __global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
     const float* __restrict__ target, const float* __restrict__ draft, int draft_kind,
     const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, int64_t B, int64_t gamma, int64_t V,
@@ -419,7 +458,7 @@ __global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
       ws.desc[b] = D;
     }
   }
-  const DrawRow R = make_row(target, draft, draft_kind, b, gamma, V, D, inv_t);
+  const DrawRow R = make_row<WARP>(target, draft, draft_kind, B, b, gamma, V, D, inv_t, ws);
   const int64_t c0 = c * kDrawChunk;
   float zp[16], zq[16];
   load_chunk16<VEC>(R.zp, V, c0, lane, -INFINITY, zp);
@@ -428,7 +467,7 @@ __global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     float p, r;
-    weights(R, c0 + 256 * (e >> 2) + 4 * lane + (e & 3), zp[e], R.zq ? zq[e] : 0.0f, p, r);
+    weights<WARP>(R, c0 + 256 * (e >> 2) + 4 * lane + (e & 3), zp[e], R.zq ? zq[e] : 0.0f, p, r);
     sr += (double)r;
     sp += (double)p;
   }
@@ -442,7 +481,7 @@ __global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
 
 // 3. Select (T > 0): one wave per sequence.  The residual's weights, or p
 //    when the residual has no mass or the step ends on the bonus row.
-template <bool VEC>
+template <bool VEC, bool WARP>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void select_kernel(
     const float* __restrict__ target, const float* __restrict__ draft, int draft_kind, int64_t B, int64_t gamma,
     int64_t V, float inv_t, int32_t* __restrict__ out_tokens, Ws ws) {
@@ -457,7 +496,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void select_kernel(
   const double* pp = ws.sp + b * ndc;
   const double pj_r = lane < ndc ? pr[lane] : 0.0;
   const double pj_p = lane < ndc ? pp[lane] : 0.0;
-  const DrawRow R = make_row(target, draft, draft_kind, b, gamma, V, D, inv_t);
+  const DrawRow R = make_row<WARP>(target, draft, draft_kind, B, b, gamma, V, D, inv_t, ws);
   double tot = 0.0;
   if (R.has_q) {
     tot = wave_sum(pj_r);
@@ -517,7 +556,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void select_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float p, r;
-      weights(R, v + e, ap[e], R.zq ? aq[e] : 0.0f, p, r);
+      weights<WARP>(R, v + e, ap[e], R.zq ? aq[e] : 0.0f, p, r);
       w[4 * j + e] = use_p ? p : r;
       lsum += (double)w[4 * j + e];
     }
@@ -775,7 +814,7 @@ size_t reject_workspace_bytes(int64_t B, int64_t gamma, int64_t V) { return make
 
 bool reject_fused_stats(const RejectArgs& a, FusedStats* fs) {
   const Layout L = make_layout(a.B, a.gamma, a.V);
-  if (a.B * (a.gamma + 1) > kMaxFusedRows || L.pstride < kMaxFusedParts) return false;
+  if (a.B * (a.gamma + 1) > kMaxFusedRows || L.pstride < kMaxFusedParts || warp_active(a)) return false;
   const Ws ws = bind(a.workspace, L, 0);
   const bool greedy = a.temperature == 0.0f;
   fs->cmax = ws.cmax;
@@ -806,25 +845,35 @@ hipError_t launch_decide(const RejectArgs& a, const Ws& ws, hipStream_t stream) 
     return hipGetLastError();
   }
   const int64_t ndc = draw_chunks(a.V);
-#define SPECDEC_DRAW(WB, V4)                                                                                    \
-  hipLaunchKernelGGL((draw_sum_kernel<WB, V4>), dim3((unsigned)(a.B * ((ndc + WB - 1) / WB))), dim3(WB * 64), 0, \
-                     stream, a.target, a.draft, a.draft_kind, a.tokens, a.uniforms, a.B, a.gamma, a.V, inv_t,      \
+  const bool warp = warp_active(a);
+#define SPECDEC_DRAW(WB, V4, WP)                                                                                    \
+  hipLaunchKernelGGL((draw_sum_kernel<WB, V4, WP>), dim3((unsigned)(a.B * ((ndc + WB - 1) / WB))), dim3(WB * 64), 0, \
+                     stream, a.target, a.draft, a.draft_kind, a.tokens, a.uniforms, a.B, a.gamma, a.V, inv_t,          \
                      a.out_tokens, a.out_num, a.out_probs, ws)
-  if (ndc >= 16) {
-    if (vec) SPECDEC_DRAW(16, true); else SPECDEC_DRAW(16, false);
+  if (warp) {
+    if (ndc >= 16) {
+      if (vec) SPECDEC_DRAW(16, true, true); else SPECDEC_DRAW(16, false, true);
+    } else {
+      if (vec) SPECDEC_DRAW(4, true, true); else SPECDEC_DRAW(4, false, true);
+    }
+  } else if (ndc >= 16) {
+    if (vec) SPECDEC_DRAW(16, true, false); else SPECDEC_DRAW(16, false, false);
   } else {
-    if (vec) SPECDEC_DRAW(4, true); else SPECDEC_DRAW(4, false);
+    if (vec) SPECDEC_DRAW(4, true, false); else SPECDEC_DRAW(4, false, false);
   }
 #undef SPECDEC_DRAW
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 g3(blocks_for(a.B, kWavesPerBlock));
-  if (vec)
-    hipLaunchKernelGGL((select_kernel<true>), g3, blk, 0, stream, a.target, a.draft, a.draft_kind, a.B, a.gamma, a.V,
-                       inv_t, a.out_tokens, ws);
-  else
-    hipLaunchKernelGGL((select_kernel<false>), g3, blk, 0, stream, a.target, a.draft, a.draft_kind, a.B, a.gamma,
-                       a.V, inv_t, a.out_tokens, ws);
+#define SPECDEC_SELECT(V4, WP)                                                                                  \
+  hipLaunchKernelGGL((select_kernel<V4, WP>), g3, blk, 0, stream, a.target, a.draft, a.draft_kind, a.B, a.gamma, \
+                     a.V, inv_t, a.out_tokens, ws)
+  if (warp) {
+    if (vec) SPECDEC_SELECT(true, true); else SPECDEC_SELECT(false, true);
+  } else {
+    if (vec) SPECDEC_SELECT(true, false); else SPECDEC_SELECT(false, false);
+  }
+#undef SPECDEC_SELECT
   return hipGetLastError();
 }
 
@@ -880,10 +929,10 @@ hipError_t launch_tree_greedy(const TreeArgs& t, int64_t nparts, hipStream_t str
     const int64_t rows = t.B * t.M;
     const dim3 g1(blocks_for(rows * stat_chunks(t.V), kWavesPerBlock));
     if ((t.V & 3) == 0)
-      hipLaunchKernelGGL((stats_kernel<true, true>), g1, blk, 0, stream, t.logits, nullptr, nullptr, rows, rows,
+      hipLaunchKernelGGL((stats_kernel<true, true, false>), g1, blk, 0, stream, t.logits, nullptr, nullptr, rows, rows,
                          (int64_t)0, t.V, 1.0f, ws);
     else
-      hipLaunchKernelGGL((stats_kernel<false, true>), g1, blk, 0, stream, t.logits, nullptr, nullptr, rows, rows,
+      hipLaunchKernelGGL((stats_kernel<false, true, false>), g1, blk, 0, stream, t.logits, nullptr, nullptr, rows, rows,
                          (int64_t)0, t.V, 1.0f, ws);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -905,13 +954,21 @@ hipError_t launch_reject_sample(const RejectArgs& a, hipStream_t stream) {
   const int64_t n_rows = n_target + ((!greedy && a.draft_kind == 0) ? a.B * a.gamma : 0);
   const dim3 blk(kWavesPerBlock * 64);
   const dim3 g1(blocks_for(n_rows * stat_chunks(a.V), kWavesPerBlock));
-#define SPECDEC_STATS(V4, GR)                                                                                        \
-  hipLaunchKernelGGL((stats_kernel<V4, GR>), g1, blk, 0, stream, a.target, a.draft, a.tokens, n_target, n_rows, \
+  const bool warp = warp_active(a);
+  if (warp) {  // the per-row cuts, read by every later kernel
+    const hipError_t ew = launch_warp_cuts(a.target, a.draft, n_target, n_rows, a.V, inv_t, a.top_k, a.top_p,
+                                           ws.wkey, ws.widx, stream);
+    if (ew != hipSuccess) return ew;
+  }
+#define SPECDEC_STATS(V4, GR, WP)                                                                                        \
+  hipLaunchKernelGGL((stats_kernel<V4, GR, WP>), g1, blk, 0, stream, a.target, a.draft, a.tokens, n_target, n_rows, \
                      a.gamma, a.V, inv_t, ws)
   if (greedy) {
-    if (vec) SPECDEC_STATS(true, true); else SPECDEC_STATS(false, true);
+    if (vec) SPECDEC_STATS(true, true, false); else SPECDEC_STATS(false, true, false);
+  } else if (warp) {
+    if (vec) SPECDEC_STATS(true, false, true); else SPECDEC_STATS(false, false, true);
   } else {
-    if (vec) SPECDEC_STATS(true, false); else SPECDEC_STATS(false, false);
+    if (vec) SPECDEC_STATS(true, false, false); else SPECDEC_STATS(false, false, false);
   }
 #undef SPECDEC_STATS
   const hipError_t e = hipGetLastError();

@@ -118,3 +118,21 @@ def abs_dot_bound(X_bits: np.ndarray, W_bits: np.ndarray, chunk: int = 16384) ->
         Wa = np.abs(synth.bf16_to_f32(W_bits[v0:v0 + chunk]))
         out[:, v0:v0 + chunk] = Xa @ Wa.T
     return 1.01 * g * out
+
+
+def reject_warped(target, draft, tokens, uniforms, T, top_k, top_p, kind=sd.SPECDEC_DRAFT_LOGITS, probs=True):
+    """Runs specdec_reject_sample_warped on host arrays; returns (tokens, num_emitted, probs)."""
+    target = np.ascontiguousarray(target, np.float32)
+    B, g1, V = target.shape
+    g = g1 - 1
+    t_d = dev(target)
+    d_d = dev(np.ascontiguousarray(draft, np.float32)) if draft is not None else None
+    x_d = dev(np.ascontiguousarray(tokens, np.int32).reshape(B, g))
+    u_d = dev(np.ascontiguousarray(uniforms, np.float32)) if uniforms is not None else None
+    ot = torch.full((B, g1), -7, dtype=torch.int32, device="cuda")
+    on = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    op = torch.full((B, g, 2), float("nan"), device="cuda") if probs else None
+    ws = torch.full((sd.workspace_bytes(B, g, V),), 0xFF, dtype=torch.uint8, device="cuda")
+    sd.specdec_reject_sample_warped(t_d, d_d, x_d, T, top_k, top_p, u_d, ot, on, ws, out_probs=op, draft_kind=kind)
+    torch.cuda.synchronize()
+    return host(ot), host(on), (host(op) if probs else None)

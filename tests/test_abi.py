@@ -36,7 +36,7 @@ def test_status_strings_and_version():
     for s in range(1, 8):
         assert sd.status_string(s) and sd.status_string(s) != "unknown status"
     assert sd.status_string(99) == "unknown status"
-    assert sd.version() == 10100
+    assert sd.version() == 10200
 
 
 def test_workspace_bytes():
@@ -127,6 +127,35 @@ def test_reject_argument_checks():
     assert _reject(target=A + 4) == 3
     assert _reject(ws=A + 8) == 3
     assert _reject(ot=A + 2) == 3
+
+
+def _warped(kind=0, T=1.0, k=0, p=1.0, B=2, g=3, V=128, ws=A, wsb=1 << 30, draft=A):
+    return sd.library().specdec_reject_sample_warped(P(A), P(draft), kind, P(A), T, k, p, P(A), B, g, V, P(A), P(A),
+                                                     None, P(ws), wsb, None)
+
+
+@needs_no_gpu
+def test_warp_argument_checks():
+    assert _warped(k=-1) == 7
+    assert _warped(p=0.0) == 7
+    assert _warped(p=-0.25) == 7
+    assert _warped(p=1.5) == 7
+    assert _warped(p=float("nan")) == 7
+    assert _warped(k=5, p=0.9, V=(1 << 23) + 1, B=1, g=0) == 2  # top-p masses are exact up to 2^23 entries
+    assert _warped(k=5, p=1.0, V=(1 << 23) + 1, B=1, g=0) not in (2, 7)  # top-k alone has no such limit
+    assert _warped(kind=3, k=5) == 7
+    assert _warped(T=-1.0, k=5) == 4
+    assert _warped(ws=0, k=5) == 5
+    assert _warped(draft=0, k=5, p=0.5) == 1
+    lib = sd.library()
+
+    def step(k=0, p=1.0, wsb=1 << 30):
+        return lib.specdec_verify_step_warped(P(A), P(A), 0, P(A), 0, P(A), 1.0, k, p, P(A), 1, 4, 64, 128, P(A),
+                                              P(A), P(A), None, P(A), wsb, None)
+
+    assert step(k=-3) == 7
+    assert step(p=2.0) == 7
+    assert step(k=3, wsb=16) == 5
 
 
 @needs_no_gpu
