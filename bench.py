@@ -7,6 +7,7 @@ HBM before timing starts.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --projection-sweep     (the decoder-projection GEMM sweep over N; one JSON line)
+    python bench.py --extensions           (warping, one-hot drafts, tree verification, paged KV; one JSON line)
 """
 from __future__ import annotations
 
@@ -74,6 +75,8 @@ def main():
     ap.add_argument("--layout", choices=["packed", "rowmajor"], default="packed", help="weight layout")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (a known byte count for hardware counters)")
+    ap.add_argument("--extensions", action="store_true",
+                    help="time the extensions (warping, one-hot drafts, tree verification, paged KV) instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -91,6 +94,9 @@ def main():
     if args.projection_sweep:
         projection_sweep(args)
         return
+    if args.extensions:
+        extensions(args)
+        return
     w = synth.WORKLOADS[args.workload]
     if w.d == 0:
         print(f"workload {w.name} has no scoring GEMM; pick an LM-head workload", file=sys.stderr)
@@ -98,48 +104,8 @@ def main():
     B, g, V, d, T = w.B, w.gamma, w.V, w.d, w.temperature
     N = B * (g + 1)
     dev = torch.device("cuda")
-
-    # ---- inputs (untimed): hidden states and weights from the seeded generator
-    Xb, Wb = synth.lm_head_inputs(w)
-    X = torch.from_numpy(Xb.view(np.int16)).to(dev).view(torch.bfloat16)
-    W_rows = torch.from_numpy(Wb.view(np.int16)).to(dev).view(torch.bfloat16)
-    del Xb, Wb
-    # One-time weight preparation, as at model load: the packed tile layout.  Every step still reads all of it.
-    W = sd.specdec_pack_weights(W_rows) if args.layout == "packed" else W_rows
-    torch.cuda.synchronize()
-    if args.layout == "packed":
-        del W_rows
-    logits = torch.empty((N, V), dtype=torch.float32, device=dev)
-    out_tok = torch.empty((B, g + 1), dtype=torch.int32, device=dev)
-    out_num = torch.empty((B,), dtype=torch.int32, device=dev)
+    X, W, logits, out_tok, out_num, ws, gemm_ws, uni, draft, tokens = step_inputs(w, args.layout)
     layout = sd.SPECDEC_WEIGHTS_PACKED if args.layout == "packed" else sd.SPECDEC_WEIGHTS_ROW_MAJOR
-    ws = sd.new_step_workspace(B, g, d, V, layout)
-    gemm_ws = torch.empty(max(1, sd.logits_workspace_bytes(N, d, V, layout)), dtype=torch.uint8, device=dev)
-    uni = torch.from_numpy(synth.step_uniforms(w)).to(dev)
-    # Draft logits = target logits + N(0, noise) and drafted tokens ~ q: built with the library itself
-    # (one scoring pass, then one draw per drafted row as gamma = 0 steps), outside the timed region.
-    sd.specdec_verify_logits(X, W, logits, workspace=gemm_ws)
-    if T > 0:
-        tl = logits.view(B, g + 1, V)[:, :g]
-        noise = torch.from_numpy(synth.normal_f32((B, g, V), w.noise_std, w.seed, synth.STREAM_DRAFT_NOISE)).to(dev)
-        draft = (tl + noise).contiguous()
-        du = torch.zeros((B * g, 1, 2), dtype=torch.float32, device=dev)
-        du[:, 0, 1] = torch.from_numpy(synth.draft_sample_uniforms(w).reshape(-1)).to(dev)
-        dt = torch.empty((B * g, 1), dtype=torch.int32, device=dev)
-        dn = torch.empty((B * g,), dtype=torch.int32, device=dev)
-        dws = sd.new_workspace(B * g, 0, V)
-        sd.specdec_reject_sample(draft.view(B * g, 1, V), None, torch.empty((B * g, 0), dtype=torch.int32, device=dev),
-                                 T, du, dt, dn, dws)
-        tokens = dt.view(B, g).contiguous()
-        del noise, dws
-    else:
-        draft = None
-        am = logits.view(B, g + 1, V)[:, :g].argmax(dim=2).to(torch.int32)
-        rep = torch.from_numpy(synth.bernoulli((B, g), w.replace_prob, w.seed, synth.STREAM_REPLACE)).to(dev)
-        rnd = torch.from_numpy(synth.integers((B, g), 0, V, w.seed, synth.STREAM_REPLACE + 10)).to(dev)
-        tokens = torch.where(rep, rnd, am).contiguous()
-    torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream()
     probs = None
     if args.copy_calibration:
@@ -235,6 +201,204 @@ def main():
                      "traffic": measured_traffic(w.name, args.layout), "bytes_per_launch": gemm_bytes,
                      "avg_launch_ms": gemm_ms},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def step_inputs(w, layout_name: str):
+    """Device inputs of one verify step of workload w (untimed): X, W (packed or row-major), logits, outputs, the step
+    and scoring workspaces, uniforms, draft logits (T > 0) and drafted tokens."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_verification_09_amd as sd
+    import synth
+
+    B, g, V, d, T = w.B, w.gamma, w.V, w.d, w.temperature
+    N = B * (g + 1)
+    dev = torch.device("cuda")
+
+    # ---- inputs (untimed): hidden states and weights from the seeded generator
+    Xb, Wb = synth.lm_head_inputs(w)
+    X = torch.from_numpy(Xb.view(np.int16)).to(dev).view(torch.bfloat16)
+    W_rows = torch.from_numpy(Wb.view(np.int16)).to(dev).view(torch.bfloat16)
+    del Xb, Wb
+    # One-time weight preparation, as at model load: the packed tile layout.  Every step still reads all of it.
+    W = sd.specdec_pack_weights(W_rows) if layout_name == "packed" else W_rows
+    torch.cuda.synchronize()
+    if layout_name == "packed":
+        del W_rows
+    logits = torch.empty((N, V), dtype=torch.float32, device=dev)
+    out_tok = torch.empty((B, g + 1), dtype=torch.int32, device=dev)
+    out_num = torch.empty((B,), dtype=torch.int32, device=dev)
+    layout = sd.SPECDEC_WEIGHTS_PACKED if layout_name == "packed" else sd.SPECDEC_WEIGHTS_ROW_MAJOR
+    ws = sd.new_step_workspace(B, g, d, V, layout)
+    gemm_ws = torch.empty(max(1, sd.logits_workspace_bytes(N, d, V, layout)), dtype=torch.uint8, device=dev)
+    uni = torch.from_numpy(synth.step_uniforms(w)).to(dev)
+    # Draft logits = target logits + N(0, noise) and drafted tokens ~ q: built with the library itself
+    # (one scoring pass, then one draw per drafted row as gamma = 0 steps), outside the timed region.
+    sd.specdec_verify_logits(X, W, logits, workspace=gemm_ws)
+    if T > 0:
+        tl = logits.view(B, g + 1, V)[:, :g]
+        noise = torch.from_numpy(synth.normal_f32((B, g, V), w.noise_std, w.seed, synth.STREAM_DRAFT_NOISE)).to(dev)
+        draft = (tl + noise).contiguous()
+        du = torch.zeros((B * g, 1, 2), dtype=torch.float32, device=dev)
+        du[:, 0, 1] = torch.from_numpy(synth.draft_sample_uniforms(w).reshape(-1)).to(dev)
+        dt = torch.empty((B * g, 1), dtype=torch.int32, device=dev)
+        dn = torch.empty((B * g,), dtype=torch.int32, device=dev)
+        dws = sd.new_workspace(B * g, 0, V)
+        sd.specdec_reject_sample(draft.view(B * g, 1, V), None, torch.empty((B * g, 0), dtype=torch.int32, device=dev),
+                                 T, du, dt, dn, dws)
+        tokens = dt.view(B, g).contiguous()
+        del noise, dws
+    else:
+        draft = None
+        am = logits.view(B, g + 1, V)[:, :g].argmax(dim=2).to(torch.int32)
+        rep = torch.from_numpy(synth.bernoulli((B, g), w.replace_prob, w.seed, synth.STREAM_REPLACE)).to(dev)
+        rnd = torch.from_numpy(synth.integers((B, g), 0, V, w.seed, synth.STREAM_REPLACE + 10)).to(dev)
+        tokens = torch.where(rep, rnd, am).contiguous()
+    torch.cuda.synchronize()
+
+    return X, W, logits, out_tok, out_num, ws, gemm_ws, uni, draft, tokens
+
+
+def _time_launches(fn, K: int, warmup: int, stream) -> float:
+    """Average ms of fn() over K back-to-back calls on one stream, between two events, after warmup calls."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / K
+
+
+def extensions(args):
+    """Times each extension on its synthetic workload (inputs resident in HBM, K back-to-back calls between two
+    events on the launch stream): top-k / top-p warping and one-hot drafts on the larger LM-head step (each beside
+    the plain step on the same inputs), greedy tree verification with its scoring GEMM, and the paged KV cache
+    operations around a verify step."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_verification_09_amd as sd
+    import synth
+
+    K, Wm = args.steps, args.warmup
+    stream = torch.cuda.current_stream()
+    dev = torch.device("cuda")
+    res = {}
+
+    # ---- warping and one-hot drafts on the larger LM-head step
+    cfg = synth.EXTENSIONS["warp"]
+    w = synth.WORKLOADS[cfg["workload"]]
+    B, g, V, d, T = w.B, w.gamma, w.V, w.d, w.temperature
+    N = B * (g + 1)
+    X, W, logits, out_tok, out_num, ws, gemm_ws, uni, draft, tokens = step_inputs(w, "packed")
+    k, p = cfg["top_k"], cfg["top_p"]
+    plain = _time_launches(lambda: sd.specdec_verify_step(X, W, draft, tokens, T, uni, logits, out_tok, out_num, ws,
+                                                          stream=stream), K, Wm, stream)
+    warped = _time_launches(lambda: sd.specdec_verify_step_warped(X, W, draft, tokens, T, k, p, uni, logits, out_tok,
+                                                                  out_num, ws, stream=stream), K, Wm, stream)
+    emitted_w = int(out_num.sum().item())
+    rws = sd.new_workspace(B, g, V)
+    tl = logits.view(B, g + 1, V)
+    rej = _time_launches(lambda: sd.specdec_reject_sample(tl, draft, tokens, T, uni, out_tok, out_num, rws,
+                                                          stream=stream), K, Wm, stream)
+    rej_w = _time_launches(lambda: sd.specdec_reject_sample_warped(tl, draft, tokens, T, k, p, uni, out_tok, out_num,
+                                                                   rws, stream=stream), K, Wm, stream)
+    rows = B * (g + 1) + B * g
+    res["warp"] = {"workload": w.name, "top_k": k, "top_p": p, "plain_step_ms": plain, "warped_step_ms": warped,
+                   "warped_positions_per_s": N / (warped * 1e-3), "warped_emitted_per_step": emitted_w,
+                   "plain_rule_ms": rej, "warped_rule_ms": rej_w, "warp_overhead_ms": rej_w - rej,
+                   "rows_warped": rows, "row_bytes_read_once": rows * V * 4}
+    onehot = _time_launches(lambda: sd.specdec_verify_step(X, W, None, tokens, T, uni, logits, out_tok, out_num, ws,
+                                                           draft_kind=sd.SPECDEC_DRAFT_ONEHOT, stream=stream),
+                            K, Wm, stream)
+    res["onehot"] = {"workload": w.name, "plain_step_ms": plain, "onehot_step_ms": onehot,
+                     "onehot_positions_per_s": N / (onehot * 1e-3),
+                     "draft_bytes_not_read": B * g * V * 4}
+    del X, W, logits, ws, gemm_ws, draft, rws
+    torch.cuda.empty_cache()
+
+    # ---- greedy tree verification
+    c = synth.EXTENSIONS["tree"]
+    B, M, V, d = c["B"], c["M"], c["V"], c["d"]
+    N = B * M
+    X = torch.from_numpy(synth.normal_bf16((N, d), c["x_std"], c["seed"], synth.STREAM_X).view(np.int16))
+    X = X.to(dev).view(torch.bfloat16)
+    W_rows = torch.from_numpy(synth.normal_bf16((V, d), c["w_std"], c["seed"], synth.STREAM_W).view(np.int16))
+    W = sd.specdec_pack_weights(W_rows.to(dev).view(torch.bfloat16))
+    del W_rows
+    parents = torch.from_numpy(np.tile((np.arange(M, dtype=np.int32) - 1) // 2, (B, 1))).to(dev)
+    logits = torch.empty((N, V), dtype=torch.float32, device=dev)
+    gws = torch.empty(max(1, sd.logits_workspace_bytes(N, d, V, sd.SPECDEC_WEIGHTS_PACKED)), dtype=torch.uint8,
+                      device=dev)
+    sd.specdec_verify_logits(X, W, logits, workspace=gws)
+    am = logits.view(B, M, V).argmax(dim=2).to(torch.int32)
+    par_l = parents.long().clamp(min=0)
+    right = torch.from_numpy(synth.bernoulli((B, M), c["right"], c["seed"], synth.STREAM_REPLACE)).to(dev)
+    rnd = torch.from_numpy(synth.integers((B, M), 0, V, c["seed"], synth.STREAM_REPLACE + 10)).to(dev)
+    node_tok = torch.where(right, torch.gather(am, 1, par_l), rnd).to(torch.int32).contiguous()
+    ot = torch.empty((B, M), dtype=torch.int32, device=dev)
+    on = torch.empty((B,), dtype=torch.int32, device=dev)
+    nd = torch.empty((B, M), dtype=torch.int32, device=dev)
+    tws = torch.empty(sd.tree_step_workspace_bytes(B, M, d, V, sd.SPECDEC_WEIGHTS_PACKED), dtype=torch.uint8,
+                      device=dev)
+    tree_ms = _time_launches(lambda: sd.specdec_tree_verify_step(X, W, parents, node_tok, logits, ot, on, nd, tws,
+                                                                 stream=stream), K, Wm, stream)
+    gemm_ms = _time_launches(lambda: sd.specdec_verify_logits(X, W, logits, workspace=gws, stream=stream), K, Wm,
+                             stream)
+    gemm_bytes = V * d * 2 + N * d * 2 + N * V * 4
+    res["tree"] = {"B": B, "M": M, "V": V, "d": d, "tree_step_ms": tree_ms, "positions_per_s": N / (tree_ms * 1e-3),
+                   "mean_emitted": float(on.float().mean().item()), "gemm_ms": gemm_ms,
+                   "gemm_hbm_gbps": gemm_bytes / (gemm_ms * 1e-3) / 1e9,
+                   "gemm_hbm_frac": gemm_bytes / (gemm_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    del X, W, logits, gws, tws
+    torch.cuda.empty_cache()
+
+    # ---- paged KV cache around a verify step
+    c = synth.EXTENSIONS["paged_kv"]
+    R, H, D, bs, ctx, g = c["R"], c["heads"], c["head_dim"], c["block_size"], c["ctx"], c["gamma"]
+    max_len = ctx + (K + Wm + 2) * (g + 1)
+    mb = (max_len + bs - 1) // bs
+    kv = sd.PagedKVCache(R, R * mb, H, bs, D, max_blocks=mb, dtype=torch.bfloat16)
+    k0 = torch.from_numpy(synth.normal_bf16((R, H, ctx, D), 1.0, c["seed"], 0).view(np.int16)).to(dev)
+    kv.append(k0.view(torch.bfloat16), k0.view(torch.bfloat16))
+    del k0
+    kn = torch.from_numpy(synth.normal_bf16((R, H, g + 1, D), 1.0, c["seed"], 1).view(np.int16)).to(dev)
+    kn = kn.view(torch.bfloat16)
+    num = torch.from_numpy(synth.integers((R,), 1, g + 2, c["seed"], 2)).to(dev)
+
+    def kv_step():
+        kv.append(kn, kn, stream=stream)
+        kv.rollback_after_verify(num, g, stream=stream)
+
+    kv_ms = _time_launches(kv_step, K, Wm, stream)
+    torch.cuda.synchronize()
+    assert int(kv.status.item()) == 0
+    cur = int(kv.lens.max().item())
+    kout = torch.empty((R, H, cur, D), dtype=torch.bfloat16, device=dev)
+    vout = torch.empty_like(kout)
+    gather_ms = _time_launches(lambda: kv.gather(cur, kout, vout, stream=stream), K, Wm, stream)
+    gather_bytes = 2 * 2 * int(kv.lens.sum().item()) * H * D * 2
+    res["paged_kv"] = {"R": R, "heads": H, "head_dim": D, "block_size": bs, "gamma": g,
+                       "append_and_rollback_us": kv_ms * 1e3,
+                       "append_bytes": 2 * 2 * R * H * (g + 1) * D * 2,
+                       "gather_ms": gather_ms, "gather_hbm_gbps": gather_bytes / (gather_ms * 1e-3) / 1e9,
+                       "gather_hbm_frac": gather_bytes / (gather_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+
+    out = {
+        "metric": "extensions: warped / one-hot / tree verify steps and paged-KV operations (times per call)",
+        "value": res["warp"]["warped_positions_per_s"], "unit": "positions/s (warped step)", "n_gpus": 1,
+        "steps": K, "warmup": Wm, "higher_is_better": True, "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic", "config": {"workload": "extensions"}, "results": res,
     }
     print(json.dumps(out), flush=True)
 

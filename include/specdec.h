@@ -202,9 +202,10 @@ int specdec_verify_step(const void* X, const void* W, int weight_layout, const f
  * given.  At T == 0 the settings are ignored (the argmax is always kept).
  *   top_k  >= 0; 0 (or >= V) turns top-k off
  *   top_p  in (0, 1]; 1 turns top-p off.  Masses are summed exactly as
- *          integers with 40 fraction bits (fp32 exp(z/T - max)), so the top-p
- *          cut may differ from an fp64 one only where the cumulative mass is
- *          within about 1e-6 of top_p.  Requires V <= 2^23 when top_p < 1.
+ *          integers with 40 fraction bits (fp32 exp((z - max z) / T)), so the
+ *          top-p cut may differ from an fp64 one only where the cumulative
+ *          mass is within a few 1e-6 of top_p.
+ * Requires V <= 2^23 when either setting is active (SPECDEC_ERR_SHAPE).
  * Other arguments, the workspace and the rule as in specdec_reject_sample
  * (SPECDEC_ERR_ARG for settings out of range).  Logits must not be NaN. */
 int specdec_reject_sample_warped(const float* target_logits, const float* draft, int draft_kind,

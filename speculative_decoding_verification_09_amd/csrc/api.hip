@@ -88,11 +88,12 @@ specdec::RejectArgs reject_args(const float* target, const float* draft, int dra
   return a;
 }
 
-// top_k >= 0 (0: off); 0 < top_p <= 1.  Top-p sums fixed-point masses that
-// stay exact for V <= 2^23.
+// top_k >= 0 (0: off); 0 < top_p <= 1.  The cut kernel ranks entries by a
+// composite of key and index and sums fixed-point masses, both exact for
+// V <= 2^23.
 int check_warp_args(int64_t top_k, float top_p, int64_t V) {
   if (top_k < 0 || !(top_p > 0.0f && top_p <= 1.0f)) return SPECDEC_ERR_ARG;
-  if (top_p < 1.0f && V > ((int64_t)1 << 23)) return SPECDEC_ERR_SHAPE;
+  if (((top_k > 0 && top_k < V) || top_p < 1.0f) && V > ((int64_t)1 << 23)) return SPECDEC_ERR_SHAPE;
   return SPECDEC_OK;
 }
 

@@ -8,38 +8,73 @@
 // top_p (at least one entry); the sampling kernels renormalise what is kept.
 //
 // Every kept set is a prefix of that ranking, so a row's warping is one cut
-// (cut_key, cut_idx) in the order of order_key and index.  One workgroup per
+// (cut_key, cut_idx).  Ranking entries by the 55-bit composite
+// (order_key(z) << 23) | (2^23 - 1 - index), larger first, is exactly that
+// order, and the cut is the entry at which the running weight (1 per entry
+// for top-k; for top-p the mass) first reaches a target.  One workgroup per
 // row finds it:
-//   top-k: a radix select over the 32-bit keys, 8 bits a level, each level a
-//     histogram of the digit under the prefix found so far (LDS integer
-//     atomics into 16 padded copies, lane l using copy l % 16, so lanes of one
-//     wave that hit the same digit mostly hit different addresses), then the
-//     tie at the cut resolved in index order with a workgroup prefix sum;
-//   top-p: the same select weighted by the masses of the top-k survivors.  The
-//     mass of v is fp32 exp((z_v - max z) * fl32(1/T)) (the difference first,
-//     so the error stays near (1 + |z_v - max z| / T) * 2^-23 relative however
-//     large the logits are) held as an integer with 40 fraction bits, so every
-//     sum is exact and independent of the order of the atomics; the cut is the
-//     first entry at which the running mass reaches ceil(top_p * total), at
-//     least one entry.
-// Totals stay below 2^64 for V <= 2^23.  The row is read from L2 after the
-// first pass (a 128K-entry row is 512 KB).
+//   * the 12 high bits of the key (sign, exponent, 3 mantissa bits) split the
+//     row into 4096 buckets: one coalesced pass histograms them in LDS (with
+//     the row maximum), and a workgroup scan from the top bucket finds the
+//     bucket of the cut;
+//   * a second pass copies the candidates into LDS: for top-k every entry at
+//     or above that bucket when they are at most kCap (top-p then runs on the
+//     same candidates, with no further pass), else that bucket alone;
+//   * in LDS the cut is the crossing of the running weight in composite order:
+//     a single wave ranks up to 64 candidates directly, more take radix levels
+//     of 12 bits over the composite;
+//   * a bucket with more than kCap entries is split by a second global level
+//     on the next 12 key bits, and one still too full (runs of equal logits)
+//     by the last 8 bits; equal keys are then cut in index order by an
+//     ordered scan over wave-contiguous ranges.
+// The mass of v is fp32 exp((z_v - max z) * fl32(1/T)) (the difference first,
+// so its error stays near (1 + |z_v - max z| / T) * 2^-23 relative however
+// large the logits are) as an integer with 40 fraction bits: every sum is
+// exact and independent of the order of the atomics.  The top-p target is
+// ceil(top_p * total), at least 1.  Totals stay below 2^64 and indices fit
+// the composite for V <= 2^23.
 #include "internal.h"
 
 namespace specdec {
 namespace {
 
-constexpr int kWarpThreads = 1024;
-constexpr int kWaves = kWarpThreads / 64;
-constexpr int kCopies = 16;
-constexpr int kBinPitch = 257;  // padded so copies start on different banks
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int kBins = 4096;  // 12-bit digits
+constexpr int kCap = 2048;   // candidates held in LDS
+constexpr int kIdxBits = 23;
+constexpr uint32_t kIdxMask = (1u << kIdxBits) - 1;
 constexpr double kFix = 1099511627776.0;  // 2^40
 
 typedef unsigned long long u64;
 
+struct Cut {
+  uint32_t key;
+  int32_t idx;
+};
+
+struct Shared {
+  u64 mass[kBins];      // per-bin masses (top-p)
+  uint32_t cnt[kBins];  // per-bin counts
+  u64 comp[kCap];       // candidates: composite
+  u64 cw[kCap];         // candidates: mass (top-p)
+  u64 red[kWaves];
+  float redf[kWaves];
+  u64 above;
+  uint32_t ncand;
+  uint32_t bin;
+  int found;
+};
+
 __device__ __forceinline__ u64 mass_fixed(float z, float inv_t, float zmax) {
   const float e = expf((z - zmax) * inv_t);
-  return e > 0.0f ? (u64)((double)e * kFix) : 0ull;  // 0 for -inf logits and NaN
+  return e > 0.0f ? (u64)((double)e * kFix) : 0ull;  // 0 for -inf logits
+}
+__device__ __forceinline__ u64 composite(uint32_t key, int v) {
+  return ((u64)key << kIdxBits) | (u64)(kIdxMask - (uint32_t)v);
+}
+__device__ __forceinline__ float key_value(uint32_t key) {  // inverse of order_key
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
 __device__ __forceinline__ float block_max(float v, float* lds) {
@@ -83,150 +118,353 @@ __device__ __forceinline__ u64 block_exclusive(u64 v, u64* lds) {
   return before + x - v;
 }
 
-struct Shared {
-  u64 hist[kCopies * kBinPitch];
-  u64 tot[256];
-  u64 red[kWaves];
-  float redf[kWaves];
-  u64 above;
-  uint32_t digit;
-  int idx;
-};
-
-// One radix level: among entries whose key matches `prefix` under `mask` and
-// that the cut (lk, li) keeps, weigh the digit at `shift` (count, or mass when
-// MASS); scanning digits from 255 down, take the one where the running weight
-// first reaches `need`, and lower `need` by the weight of the digits above it.
+// Bins nb-1 down to 0 (thread t holds nb-1-4t .. nb-4-4t): the bin where the
+// running weight first reaches `need`, and the weight of the bins above it.
 template <bool MASS>
-__device__ void radix_level(const float* __restrict__ row, int V, uint32_t& prefix, uint32_t& mask, int shift,
-                            u64& need, uint32_t lk, int li, float inv_t, float zmax, Shared& sh) {
-  for (int b = threadIdx.x; b < kCopies * kBinPitch; b += kWarpThreads) sh.hist[b] = 0;
-  __syncthreads();
-  u64* mine = sh.hist + (threadIdx.x & (kCopies - 1)) * kBinPitch;
-  for (int v = threadIdx.x; v < V; v += kWarpThreads) {
-    const float z = row[v];
-    const uint32_t k = order_key(z);
-    if ((k & mask) == prefix && warp_kept(k, v, lk, li))
-      atomicAdd(mine + ((k >> shift) & 0xffu), MASS ? mass_fixed(z, inv_t, zmax) : 1ull);
+__device__ void scan_bins(int nb, u64 need, Shared& sh, uint32_t& bin, u64& above) {
+  u64 h[4], local = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int d = nb - 1 - 4 * (int)threadIdx.x - j;
+    h[j] = d >= 0 ? (MASS ? sh.mass[d] : (u64)sh.cnt[d]) : 0ull;
+    local += h[j];
+  }
+  if (threadIdx.x == 0) {  // kept if no bin crosses (need above the total)
+    sh.bin = 0;
+    sh.above = 0;
+  }
+  const u64 before = block_exclusive(local, sh.red);
+  if (before < need && before + local >= need) {
+    u64 run = before;
+    int sel = 3;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {  // static indices: h stays in registers
+      if (sel == 3 && run + h[j] >= need) sel = j;
+      if (sel == 3) run += h[j];
+    }
+    sh.bin = (uint32_t)(nb - 1 - 4 * (int)threadIdx.x - sel);
+    sh.above = run;
   }
   __syncthreads();
-  if (threadIdx.x < 256) {
-    u64 t = 0;
-#pragma unroll
-    for (int c = 0; c < kCopies; ++c) t += sh.hist[c * kBinPitch + threadIdx.x];
-    sh.tot[threadIdx.x] = t;
-  }
-  __syncthreads();
-  if (threadIdx.x < 64) {  // wave 0: lane l holds digits 255-4l down to 252-4l
-    const int lane = threadIdx.x;
-    u64 h[4], local = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      h[j] = sh.tot[255 - 4 * lane - j];
-      local += h[j];
-    }
-    u64 incl = local;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const u64 y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    const u64 before = incl - local;
-    const u64 hit = __ballot(before < need && incl >= need);
-    const int l = hit ? __builtin_ctzll(hit) : 63;  // none: only if need exceeds the total
-    if (lane == l) {
-      u64 run = before;
-      int j = 0;
-      while (j < 3 && run + h[j] < need) run += h[j++];
-      sh.digit = (uint32_t)(255 - 4 * lane - j);
-      sh.above = run;
-    }
-  }
-  __syncthreads();
-  prefix |= sh.digit << shift;
-  mask |= 0xffu << shift;
-  need = need > sh.above ? need - sh.above : 0;
+  bin = sh.bin;
+  above = sh.above;
   __syncthreads();
 }
 
-// Among entries with key == ck that the cut (lk, li) keeps, in index order,
-// the index at which the running weight first reaches `need` (thread t takes a
-// contiguous slice, so thread order is index order).
-template <bool MASS>
-__device__ int tie_index(const float* __restrict__ row, int V, uint32_t ck, u64 need, uint32_t lk, int li,
-                         float inv_t, float zmax, Shared& sh) {
-  const int chunk = (V + kWarpThreads - 1) / kWarpThreads;
-  const int v0 = min((int)threadIdx.x * chunk, V), v1 = min(v0 + chunk, V);
-  u64 w = 0;
-  for (int v = v0; v < v1; ++v) {
-    const float z = row[v];
-    const uint32_t k = order_key(z);
-    if (k == ck && warp_kept(k, v, lk, li)) w += MASS ? mass_fixed(z, inv_t, zmax) : 1ull;
+__device__ __forceinline__ void clear_bins(Shared& sh, bool mass) {
+  for (int b = threadIdx.x; b < kBins; b += kThreads) {
+    sh.cnt[b] = 0;
+    if (mass) sh.mass[b] = 0;
   }
-  const u64 before = block_exclusive(w, sh.red);
-  if (threadIdx.x == 0) sh.idx = -1;
   __syncthreads();
-  if (before < need && before + w >= need) {  // exactly one thread, unless need exceeds the total
-    u64 run = before;
-    for (int v = v0; v < v1; ++v) {
-      const float z = row[v];
-      const uint32_t k = order_key(z);
-      if (k == ck && warp_kept(k, v, lk, li)) {
-        run += MASS ? mass_fixed(z, inv_t, zmax) : 1ull;
-        if (run >= need) {
-          sh.idx = v;
-          break;
+}
+
+// Calls f(v, z) for every entry of the row; wave w takes the contiguous range
+// [w*R, (w+1)*R) (R a multiple of 256) in steps of 256 entries, lane l the 4
+// entries at 4l, two steps' loads issued together.
+template <bool VEC, class F>
+__device__ __forceinline__ void for_row(const float* __restrict__ row, int V, int R, F&& f) {
+  constexpr int U = 2;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int b0 = w * R, b1 = min(b0 + R, V);
+  for (int base = b0; base < b1; base += U * 256) {
+    float z[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = base + 256 * u + 4 * lane;
+      if (VEC && v + 3 < b1) {
+        const float4 t = *(const float4*)(row + v);
+        z[u][0] = t.x;
+        z[u][1] = t.y;
+        z[u][2] = t.z;
+        z[u][3] = t.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[u][e] = v + e < b1 ? row[v + e] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = base + 256 * u + 4 * lane + e;
+        if (v < b1) f(v, z[u][e]);
+      }
+  }
+}
+
+// The cut among the n candidates in LDS: the candidate (those with composite >=
+// floor only) at which the running weight in composite order first reaches
+// need.  Returns its composite, or 0 if the weights never reach need.
+template <bool MASS>
+__device__ u64 lds_select(int n, u64 need, u64 floor, Shared& sh) {
+  if (n <= 64) {  // one wave ranks every candidate directly
+    if (threadIdx.x == 0) sh.found = -1;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      const int i = threadIdx.x;
+      const u64 ci = i < n ? sh.comp[i] : 0ull;
+      const u64 wi = (i < n && ci >= floor) ? (MASS ? sh.cw[i] : 1ull) : 0ull;
+      u64 before = 0;
+      for (int j = 0; j < n; ++j) {
+        const u64 cj = sh.comp[j];
+        if (cj > ci && cj >= floor) before += MASS ? sh.cw[j] : 1ull;
+      }
+      if (wi > 0 && before < need && before + wi >= need) sh.found = i;
+    }
+    __syncthreads();
+    const int f = sh.found;
+    const u64 r = f >= 0 ? sh.comp[f] : 0ull;
+    __syncthreads();
+    return r;
+  }
+  u64 prefix = 0;
+  int hi = 32 + kIdxBits;  // composite bits [0, hi) still open
+  while (hi > 0) {
+    const int width = hi < 12 ? hi : 12, lo = hi - width;
+    clear_bins(sh, MASS);
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+      const u64 c = sh.comp[i];
+      if (c >= floor && (c >> hi) == (prefix >> hi)) {
+        const uint32_t d = (uint32_t)((c >> lo) & ((1ull << width) - 1));
+        atomicAdd(&sh.cnt[d], 1u);
+        if (MASS) atomicAdd(&sh.mass[d], sh.cw[i]);
+      }
+    }
+    __syncthreads();
+    uint32_t d;
+    u64 above;
+    scan_bins<MASS>(1 << width, need, sh, d, above);
+    need = need > above ? need - above : 0;
+    prefix |= (u64)d << lo;
+    hi = lo;
+  }
+  return prefix;
+}
+
+// Copies into LDS the entries kept by `lim` (positive mass when MASS) whose
+// key has `prefix` in the bits under `mask`.  Returns how many there are.
+template <bool MASS, bool VEC>
+__device__ int compact(const float* __restrict__ row, int V, int R, uint32_t mask, uint32_t prefix, bool at_or_above,
+                       Cut lim, float inv_t, float zmax, Shared& sh) {
+  if (threadIdx.x == 0) sh.ncand = 0;
+  __syncthreads();
+  for_row<VEC>(row, V, R, [&](int v, float z) {
+    const uint32_t k = order_key(z);
+    const bool in = at_or_above ? (k & mask) >= prefix : (k & mask) == prefix;
+    if (in && warp_kept(k, v, lim.key, lim.idx)) {
+      const u64 m = MASS ? mass_fixed(z, inv_t, zmax) : 1ull;
+      if (m > 0) {
+        const uint32_t s = atomicAdd(&sh.ncand, 1u);
+        if (s < (uint32_t)kCap) {
+          sh.comp[s] = composite(k, v);
+          if (MASS) sh.cw[s] = m;
         }
       }
     }
-  }
+  });
   __syncthreads();
-  const int r = sh.idx;
+  const int n = (int)min(sh.ncand, (uint32_t)kCap);
   __syncthreads();
-  return r < 0 ? V - 1 : r;
+  return n;
 }
 
-__global__ __launch_bounds__(kWarpThreads) void warp_cut_kernel(const float* __restrict__ target,
-                                                                const float* __restrict__ draft, int64_t n_target,
-                                                                int64_t V64, float inv_t, int64_t top_k, float top_p,
-                                                                uint32_t* __restrict__ cut_key,
-                                                                int32_t* __restrict__ cut_idx) {
+// The r-th (1-based) entry in index order among those with key == ck kept by
+// lim: each wave counts its contiguous range, the waves' counts are scanned,
+// and the wave holding the crossing walks its range in order with ballots.
+template <bool VEC>
+__device__ int ordered_tie(const float* __restrict__ row, int V, int R, uint32_t ck, u64 r, Cut lim, Shared& sh) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  u64 c = 0;
+  for_row<VEC>(row, V, R, [&](int v, float z) {
+    const uint32_t k = order_key(z);
+    if (k == ck && warp_kept(k, v, lim.key, lim.idx)) ++c;
+  });
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+  const u64 before = block_exclusive(lane == 0 ? c : 0ull, sh.red);  // lane 0 of each wave carries its count
+  const u64 wb = __shfl(before, 0);
+  if (threadIdx.x == 0) sh.found = V - 1;
+  __syncthreads();
+  if (wb < r && wb + c >= r) {  // wave-uniform
+    const int b0 = w * R, b1 = min(b0 + R, V);
+    u64 run = wb;
+    for (int base = b0; base < b1; base += 256) {
+      const int v = base + 4 * lane;
+      int cnt = 0;
+      bool hit[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hit[e] = false;
+        if (v + e < b1) {
+          const uint32_t k = order_key(row[v + e]);
+          hit[e] = k == ck && warp_kept(k, v + e, lim.key, lim.idx);
+        }
+        cnt += hit[e];
+      }
+      u64 incl = (u64)cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const u64 y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      const u64 total = __shfl(incl, 63);
+      if (run + total >= r) {
+        const u64 lb = run + incl - (u64)cnt;  // matches before this lane's four
+        if (lb < r && lb + (u64)cnt >= r) {
+          u64 q = lb;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (hit[e] && ++q == r) sh.found = v + e;
+        }
+        break;
+      }
+      run += total;
+    }
+  }
+  __syncthreads();
+  const int f = sh.found;
+  __syncthreads();
+  return f;
+}
+
+// The cut at which the running weight over the entries kept by lim (in rank
+// order) first reaches need, given the 12-bit level-1 histograms in sh of
+// those entries (counts, and masses when MASS).
+template <bool MASS, bool VEC>
+__device__ Cut select_cut(const float* __restrict__ row, int V, int R, u64 need, Cut lim, float inv_t, float zmax,
+                          Shared& sh) {
+  uint32_t b;
+  u64 above;
+  scan_bins<MASS>(kBins, need, sh, b, above);
+  need -= above;
+  uint32_t prefix = b << 20, mask = 0xfff00000u;
+  int n = (int)sh.cnt[b];
+  __syncthreads();
+  if (n > kCap) {  // level 2: key bits 19..8 of the bucket's entries
+    clear_bins(sh, MASS);
+    for_row<VEC>(row, V, R, [&](int v, float z) {
+      const uint32_t k = order_key(z);
+      if ((k & mask) == prefix && warp_kept(k, v, lim.key, lim.idx)) {
+        const u64 m = MASS ? mass_fixed(z, inv_t, zmax) : 1ull;
+        if (m > 0) {
+          atomicAdd(&sh.cnt[(k >> 8) & 0xfffu], 1u);
+          if (MASS) atomicAdd(&sh.mass[(k >> 8) & 0xfffu], m);
+        }
+      }
+    });
+    __syncthreads();
+    scan_bins<MASS>(kBins, need, sh, b, above);
+    need -= above;
+    prefix |= b << 8;
+    mask = 0xffffff00u;
+    n = (int)sh.cnt[b];
+    __syncthreads();
+    if (n > kCap) {  // level 3: the last 8 bits, then equal keys in index order
+      clear_bins(sh, MASS);
+      for_row<VEC>(row, V, R, [&](int v, float z) {
+        const uint32_t k = order_key(z);
+        if ((k & mask) == prefix && warp_kept(k, v, lim.key, lim.idx)) {
+          const u64 m = MASS ? mass_fixed(z, inv_t, zmax) : 1ull;
+          if (m > 0) {
+            atomicAdd(&sh.cnt[k & 0xffu], 1u);
+            if (MASS) atomicAdd(&sh.mass[k & 0xffu], m);
+          }
+        }
+      });
+      __syncthreads();
+      scan_bins<MASS>(256, need, sh, b, above);
+      need -= above;
+      const uint32_t ck = prefix | b;
+      u64 r = need;
+      if (MASS) {  // every entry with this key weighs the same
+        const u64 m = mass_fixed(key_value(ck), inv_t, zmax);
+        r = m > 0 ? (need + m - 1) / m : 1;
+      }
+      return Cut{ck, ordered_tie<VEC>(row, V, R, ck, r, lim, sh)};
+    }
+  }
+  n = compact<MASS, VEC>(row, V, R, mask, prefix, false, lim, inv_t, zmax, sh);
+  const u64 c = lds_select<MASS>(n, need, 0ull, sh);
+  return Cut{(uint32_t)(c >> kIdxBits), (int32_t)(kIdxMask - (uint32_t)(c & kIdxMask))};
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void warp_cut_kernel(const float* __restrict__ target,
+                                                            const float* __restrict__ draft, int64_t n_target,
+                                                            int64_t V64, float inv_t, int64_t top_k, float top_p,
+                                                            uint32_t* __restrict__ cut_key,
+                                                            int32_t* __restrict__ cut_idx) {
   __shared__ Shared sh;
   const int V = (int)V64;
   const int64_t r = blockIdx.x;
   const float* row = r < n_target ? target + (size_t)r * V : draft + (size_t)(r - n_target) * V;
-  uint32_t ck = 0u;  // (0, INT_MAX) keeps every entry
-  int ci = 0x7fffffff;
+  const int R = ((V + kWaves * 256 - 1) / (kWaves * 256)) * 256;
+  const bool tk = top_k > 0 && top_k < V, tp = top_p < 1.0f;
+  Cut cut{0u, 0x7fffffff};  // keeps every entry
+  // Pass 1: the row maximum, and the top-k level-1 histogram.
+  if (tk) clear_bins(sh, false);
   float zm = -INFINITY;
-  for (int v = threadIdx.x; v < V; v += kWarpThreads) zm = fmaxf(zm, row[v]);
-  const float zmax = block_max(zm, sh.redf);  // the top entry's mass is 1, every other <= 1
-  if (top_k > 0 && top_k < V) {
-    uint32_t prefix = 0, mask = 0;
-    u64 need = (u64)top_k;
-    for (int shift = 24; shift >= 0; shift -= 8)
-      radix_level<false>(row, V, prefix, mask, shift, need, ck, ci, inv_t, zmax, sh);
-    ci = tie_index<false>(row, V, prefix, need, ck, ci, inv_t, zmax, sh);
-    ck = prefix;
-  }
-  if (top_p < 1.0f) {
-    u64 total = 0;
-    for (int v = threadIdx.x; v < V; v += kWarpThreads) {
-      const float z = row[v];
-      if (warp_kept(order_key(z), v, ck, ci)) total += mass_fixed(z, inv_t, zmax);
+  for_row<VEC>(row, V, R, [&](int v, float z) {
+    zm = fmaxf(zm, z);
+    if (tk) atomicAdd(&sh.cnt[order_key(z) >> 20], 1u);
+  });
+  const float zmax = block_max(zm, sh.redf);
+  bool done_p = false;
+  if (tk) {
+    uint32_t b;
+    u64 above;
+    scan_bins<false>(kBins, (u64)top_k, sh, b, above);
+    const u64 held = above + sh.cnt[b];
+    __syncthreads();
+    if (held <= (u64)kCap) {
+      // Every entry at or above the cut's bucket fits in LDS: both cuts from there.
+      const int n = compact<false, VEC>(row, V, R, 0xfff00000u, b << 20, true, cut, inv_t, zmax, sh);
+      const u64 ck = lds_select<false>(n, (u64)top_k, 0ull, sh);
+      cut = Cut{(uint32_t)(ck >> kIdxBits), (int32_t)(kIdxMask - (uint32_t)(ck & kIdxMask))};
+      if (tp) {
+        u64 part = 0;
+        for (int i = threadIdx.x; i < n; i += kThreads) {
+          const u64 c = sh.comp[i];
+          const u64 m = c >= ck ? mass_fixed(key_value((uint32_t)(c >> kIdxBits)), inv_t, zmax) : 0ull;
+          sh.cw[i] = m;
+          part += m;
+        }
+        const u64 total = block_sum(part, sh.red);
+        const double t = ceil((double)top_p * (double)total);
+        u64 need = t < 1.0 ? 1ull : (u64)t;
+        if (need > total) need = total;
+        const u64 cp = need > 0 ? lds_select<true>(n, need, ck, sh) : 0ull;
+        if (cp != 0ull) cut = Cut{(uint32_t)(cp >> kIdxBits), (int32_t)(kIdxMask - (uint32_t)(cp & kIdxMask))};
+        done_p = true;
+      }
+    } else {
+      cut = select_cut<false, VEC>(row, V, R, (u64)top_k, cut, inv_t, zmax, sh);
     }
-    total = block_sum(total, sh.red);
+  }
+  if (tp && !done_p) {
+    clear_bins(sh, true);
+    u64 part = 0;
+    for_row<VEC>(row, V, R, [&](int v, float z) {
+      const uint32_t k = order_key(z);
+      if (warp_kept(k, v, cut.key, cut.idx)) {
+        const u64 m = mass_fixed(z, inv_t, zmax);
+        if (m > 0) {
+          atomicAdd(&sh.cnt[k >> 20], 1u);
+          atomicAdd(&sh.mass[k >> 20], m);
+          part += m;
+        }
+      }
+    });
+    const u64 total = block_sum(part, sh.red);  // its barriers also order the atomics before the scan
     const double t = ceil((double)top_p * (double)total);
     u64 need = t < 1.0 ? 1ull : (u64)t;
     if (need > total) need = total;
-    uint32_t prefix = 0, mask = 0;
-    for (int shift = 24; shift >= 0; shift -= 8)
-      radix_level<true>(row, V, prefix, mask, shift, need, ck, ci, inv_t, zmax, sh);
-    ci = tie_index<true>(row, V, prefix, need, ck, ci, inv_t, zmax, sh);
-    ck = prefix;
+    if (need > 0) cut = select_cut<true, VEC>(row, V, R, need, cut, inv_t, zmax, sh);
   }
   if (threadIdx.x == 0) {
-    cut_key[r] = ck;
-    cut_idx[r] = ci;
+    cut_key[r] = cut.key;
+    cut_idx[r] = cut.idx;
   }
 }
 
@@ -236,8 +474,12 @@ hipError_t launch_warp_cuts(const float* target, const float* draft, int64_t n_t
                             float inv_t, int64_t top_k, float top_p, uint32_t* cut_key, int32_t* cut_idx,
                             hipStream_t stream) {
   if (n_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(warp_cut_kernel, dim3((unsigned)n_rows), dim3(kWarpThreads), 0, stream, target, draft, n_target,
-                     V, inv_t, top_k, top_p, cut_key, cut_idx);
+  if ((V & 3) == 0)
+    hipLaunchKernelGGL(warp_cut_kernel<true>, dim3((unsigned)n_rows), dim3(kThreads), 0, stream, target, draft,
+                       n_target, V, inv_t, top_k, top_p, cut_key, cut_idx);
+  else
+    hipLaunchKernelGGL(warp_cut_kernel<false>, dim3((unsigned)n_rows), dim3(kThreads), 0, stream, target, draft,
+                       n_target, V, inv_t, top_k, top_p, cut_key, cut_idx);
   return hipGetLastError();
 }
 

@@ -160,6 +160,20 @@ WORKLOADS = {
                               temperature=0.0, replace_prob=0.3),
 }
 
+# Workloads of the extensions beyond the plain step, each timed on its own.
+EXTENSIONS = {
+    # Top-k / top-p warping of every target and draft row of the larger LM-head step.
+    "warp": {"workload": "lmhead_b8_g7", "top_k": 50, "top_p": 0.95},
+    # The same step with one-hot drafts (greedy or prompt-lookup drafters): no draft array is read.
+    "onehot": {"workload": "lmhead_b8_g7"},
+    # Greedy verification of 8 binary trees of 16 nodes (parent of node i is (i - 1) // 2) on a Llama-8B head;
+    # a node carries its parent row's argmax with probability `right`, else a random id.
+    "tree": {"seed": 6000, "B": 8, "M": 16, "V": 128256, "d": 4096, "x_std": 1.0, "w_std": 0.02, "right": 0.7},
+    # Paged KV cache around a verify step: 64 requests with 1000-token contexts, 8 KV heads of 128 (bf16), 16-token
+    # blocks; each step appends gamma + 1 = 8 positions and rolls back to the emitted ones (uniform in 1 .. 8).
+    "paged_kv": {"seed": 6100, "R": 64, "heads": 8, "head_dim": 128, "block_size": 16, "ctx": 1000, "gamma": 7},
+}
+
 # Decoder-layer projection stack in the verify pass: [N x d_in] . [d_in x d_out].
 PROJECTION_SWEEP = {
     "seed": 4000,

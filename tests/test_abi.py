@@ -141,8 +141,9 @@ def test_warp_argument_checks():
     assert _warped(p=-0.25) == 7
     assert _warped(p=1.5) == 7
     assert _warped(p=float("nan")) == 7
-    assert _warped(k=5, p=0.9, V=(1 << 23) + 1, B=1, g=0) == 2  # top-p masses are exact up to 2^23 entries
-    assert _warped(k=5, p=1.0, V=(1 << 23) + 1, B=1, g=0) not in (2, 7)  # top-k alone has no such limit
+    assert _warped(k=5, p=0.9, V=(1 << 23) + 1, B=1, g=0) == 2  # ranks and masses are exact up to 2^23 entries
+    assert _warped(k=5, p=1.0, V=(1 << 23) + 1, B=1, g=0) == 2
+    assert _warped(k=0, p=1.0, V=(1 << 23) + 1, B=1, g=0) not in (2, 7)  # no warping: no such limit
     assert _warped(kind=3, k=5) == 7
     assert _warped(T=-1.0, k=5) == 4
     assert _warped(ws=0, k=5) == 5

@@ -41,12 +41,17 @@ def _sample_warped(orc, z, us, T, top_k, top_p):
 
 
 def _inputs(orc, B, g, V, std, T, top_k, top_p, kind, ties, seed):
-    """Target logits ~ N(0, std) (or integers in [0, 4) when ties), draft = target + N(0, 1) (or, for ties, a
-    fresh integer row), drafted tokens drawn from the draft's warped distribution (logits), its unwarped one
-    (probabilities) or uniformly over the vocabulary (one-hot)."""
-    if ties:
+    """Target logits ~ N(0, std), or integers in [0, 4) (ties="ties": long runs of equal logits), or uniform in
+    [1, 1.125) (ties="narrow": one octave-eighth, so distinct values crowd one 12-bit key bucket); draft = target
+    + N(0, 1), or a fresh row of the same kind; drafted tokens drawn from the draft's warped distribution (logits),
+    its unwarped one (probabilities) or uniformly over the vocabulary (one-hot)."""
+    if ties in (True, "ties"):
         zt = synth.integers((B, g + 1, V), 0, 4, seed, synth.STREAM_TARGET).astype(np.float32)
         zd = synth.integers((B, g, V), 0, 4, seed, synth.STREAM_DRAFT_NOISE).astype(np.float32)
+    elif ties == "narrow":
+        zt = 1.0 + np.float32(0.125) * synth.uniforms((B, g + 1, V), seed, synth.STREAM_TARGET)
+        zd = 1.0 + np.float32(0.125) * synth.uniforms((B, g, V), seed, synth.STREAM_DRAFT_NOISE)
+        zt, zd = zt.astype(np.float32), zd.astype(np.float32)
     else:
         zt = synth.normal_f32((B, g + 1, V), std, seed, synth.STREAM_TARGET)
         zd = zt[:, :g] + synth.normal_f32((B, g, V), 1.0, seed, synth.STREAM_DRAFT_NOISE)
@@ -92,6 +97,12 @@ CASES = [
     (100, 4, 3000, 0.0, 1.0, 900, 0.3, 2, True, 0.02),     # both, ties, one-hot
     (16, 0, 5000, 2.0, 1.0, 10, 0.9, 0, False, 0.02),      # gamma = 0: the bonus row alone
     (8, 7, 128256, 2.5, 0.8, 50, 0.95, 0, False, 0.02),    # a 128K vocabulary
+    (24, 3, 32000, 2.0, 1.0, 5000, 1.0, 0, False, 0.02),   # top-k survivors beyond what LDS holds
+    (24, 3, 32000, 0.0, 1.0, 100, 1.0, 0, "narrow", 0.02),  # the cut's bucket over capacity: a second level
+    (24, 3, 32000, 0.0, 0.05, 0, 0.5, 0, "narrow", 0.1),   # the same for the top-p cut (broad: T over the range)
+    (24, 3, 32000, 0.0, 1.0, 100, 1.0, 2, "ties", 0.02),   # runs of equal keys past capacity: index-order scan
+    (24, 3, 32000, 0.0, 1.0, 0, 0.5, 2, "ties", 0.05),     # the same for top-p
+    (24, 3, 32000, 0.0, 1.0, 3000, 0.9, 0, "ties", 0.05),  # both, over capacity
 ]
 
 
