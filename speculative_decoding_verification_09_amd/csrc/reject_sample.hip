@@ -733,45 +733,51 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void tree_mask_kernel(const in
 // the position after node i).  Node i >= 1 is accepted iff its parent is and
 // its token is the parent row's argmax (lowest index on ties); the deepest
 // accepted node a (lowest index among equals) ends the kept path.  Its
-// ancestors, in index order, are the path from the root.
-__global__ __launch_bounds__(kWavesPerBlock * 64) void tree_greedy_kernel(
+// ancestors, in index order, are the path from the root.  One workgroup per
+// tree: its waves merge the rows' partials in parallel (row i by wave i % 16,
+// four partials per lane in flight), then wave 0 applies the rule.
+constexpr int kTreeWaves = 16;
+__global__ __launch_bounds__(kTreeWaves * 64) void tree_greedy_kernel(
     const int32_t* __restrict__ parents, const int32_t* __restrict__ node_tokens, int64_t B, int M, int64_t V,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_num, int32_t* __restrict__ out_nodes, Ws ws) {
-  const int lane = threadIdx.x & 63;
-  const int64_t b = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (b >= B) return;
+  __shared__ int sh_best[64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t b = blockIdx.x;
   const int64_t base = b * M;
   const int64_t nch = ws.nparts;
-  const int par = tree_link(parents, base, lane, M);
-  const int tok = lane < M ? node_tokens[base + lane] : -1;
-  // Row argmaxes: lanes run over the partials of a batch of rows, then lane i keeps row i's.
-  int best = 0;
-  for (int r0 = 0; r0 < M; r0 += kMergeBatch) {
-    float cv[kMergeBatch];
-    int ci[kMergeBatch];
+  for (int i = wv; i < M; i += kTreeWaves) {
+    const size_t rb = (size_t)(base + i) * ws.pstride;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int64_t c0 = 0; c0 < nch; c0 += 4 * 64) {
+      float v[4];
+      int ix[4];
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      cv[j] = -INFINITY;
-      ci[j] = 0x7fffffff;
-      if (r0 + j < M) {
-        const size_t rb = (size_t)(base + r0 + j) * ws.pstride;
-        for (int64_t c = lane; c < nch; c += 64) {
-          const float v = ws.cmax[rb + c];
-          const int ix = ws.cidx[rb + c];
-          if (v > cv[j] || (v == cv[j] && ix < ci[j])) {
-            cv[j] = v;
-            ci[j] = ix;
-          }
+      for (int j = 0; j < 4; ++j) {  // clamped addresses: the four loads go out together
+        const int64_t c = c0 + 64 * j + lane;
+        const int64_t cc = c < nch ? c : nch - 1;
+        v[j] = ws.cmax[rb + cc];
+        ix[j] = ws.cidx[rb + cc];
+        if (c >= nch) {
+          v[j] = -INFINITY;
+          ix[j] = 0x7fffffff;
         }
       }
-    }
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      if (r0 + j >= M) break;
-      wave_argmax(cv[j], ci[j]);
-      if (lane == r0 + j) best = (ci[j] >= 0 && ci[j] < V) ? ci[j] : 0;  // all-NaN row: any in-range id
+      for (int j = 0; j < 4; ++j)
+        if (v[j] > bv || (v[j] == bv && ix[j] < bi)) {
+          bv = v[j];
+          bi = ix[j];
+        }
     }
+    wave_argmax(bv, bi);
+    if (lane == 0) sh_best[i] = (bi >= 0 && bi < V) ? bi : 0;  // all-NaN row: any in-range id
   }
+  __syncthreads();
+  if (wv != 0) return;  // no barrier below
+  const int par = tree_link(parents, base, lane, M);
+  const int tok = lane < M ? node_tokens[base + lane] : -1;
+  const int best = lane < M ? sh_best[lane] : 0;
   uint64_t bits;
   int depth;
   tree_walk(par, lane, M, bits, depth);
@@ -939,7 +945,7 @@ hipError_t launch_tree_greedy(const TreeArgs& t, int64_t nparts, hipStream_t str
   } else {
     ws = bind(t.workspace, L, nparts);
   }
-  hipLaunchKernelGGL(tree_greedy_kernel, dim3(blocks_for(t.B, kWavesPerBlock)), blk, 0, stream, t.parents,
+  hipLaunchKernelGGL(tree_greedy_kernel, dim3((unsigned)t.B), dim3(kTreeWaves * 64), 0, stream, t.parents,
                      t.node_tokens, t.B, (int)t.M, t.V, t.out_tokens, t.out_num, t.out_nodes, ws);
   return hipGetLastError();
 }
