@@ -250,11 +250,12 @@ int specdec_verify_step(const void* X, const void* W, int weight_layout, const f
   specdec::FusedStats fs;
   if (weight_layout == SPECDEC_WEIGHTS_PACKED && specdec::reject_fused_stats(a, &fs) &&
       specdec::gemm_stats_parts(N, d, V, fs.pstride) > 0) {
-    int64_t nparts = 0;
-    if (specdec::launch_gemm_with_stats((const uint16_t*)X, (const uint16_t*)W, logits, N, d, V, fs, &nparts, s) !=
-        hipSuccess)
+    int64_t nparts = 0, nparts_draft = 0;
+    if (specdec::launch_gemm_with_stats((const uint16_t*)X, (const uint16_t*)W, logits, N, d, V, fs, &nparts,
+                                        &nparts_draft, s) != hipSuccess)
       return SPECDEC_ERR_LAUNCH;
-    return specdec::launch_reject_after_fused(a, nparts, s) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
+    return specdec::launch_reject_after_fused(a, nparts, nparts_draft, s) == hipSuccess ? SPECDEC_OK
+                                                                                         : SPECDEC_ERR_LAUNCH;
   }
   // The scoring pass finishes (stream order) before the sampling kernels reuse the workspace.
   if (specdec_verify_logits(X, W, logits, N, d, V, SPECDEC_OUT_F32, weight_layout, workspace, workspace_bytes,
@@ -351,9 +352,9 @@ int specdec_tree_verify_step(const void* X, const void* W, int weight_layout, co
   specdec::FusedStats fs;
   if (weight_layout == SPECDEC_WEIGHTS_PACKED && specdec::tree_fused_stats(t, &fs) &&
       specdec::gemm_stats_parts(N, d, V, fs.pstride) > 0) {
-    int64_t nparts = 0;
-    if (specdec::launch_gemm_with_stats((const uint16_t*)X, (const uint16_t*)W, logits, N, d, V, fs, &nparts, s) !=
-        hipSuccess)
+    int64_t nparts = 0, nparts_draft = 0;
+    if (specdec::launch_gemm_with_stats((const uint16_t*)X, (const uint16_t*)W, logits, N, d, V, fs, &nparts,
+                                        &nparts_draft, s) != hipSuccess)
       return SPECDEC_ERR_LAUNCH;
     return specdec::launch_tree_greedy(t, nparts, s) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
   }

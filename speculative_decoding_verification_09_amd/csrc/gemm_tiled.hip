@@ -637,25 +637,32 @@ int64_t gemm_stats_parts(int64_t N, int64_t d, int64_t V, int64_t pstride) {
 }
 
 hipError_t launch_gemm_with_stats(const uint16_t* X, const uint16_t* Wp, float* Y, int64_t N, int64_t d, int64_t V,
-                                  const FusedStats& fs, int64_t* nparts, hipStream_t stream) {
+                                  const FusedStats& fs, int64_t* nparts, int64_t* nparts_draft, hipStream_t stream) {
   using namespace gemm;
   const int64_t parts = gemm_stats_parts(N, d, V, fs.pstride);
   if (parts == 0) return hipErrorNotSupported;
   const GemmPlan g = plan_gemm(N, d, V, true, true);
   if (g.kind == GemmPlan::kSweep) {
-    // The sweep kernel also summarises the (at most 7) draft rows itself.
+    // The sweep kernel also summarises the (at most 7) draft rows itself, in
+    // the same slots as the target rows.
     const hipError_t e = launch_sweep_with_stats(g.sweep, X, Wp, Y, N, d, V, fs, nparts, stream);
-    if (e == hipSuccess) *nparts = parts;
+    if (e == hipSuccess) *nparts = *nparts_draft = parts;
     return e;
   }
-  // Many draft rows: their partials come from a kernel of their own, launched
-  // first on the same stream; the panel kernel forms the target rows' partials.
-  hipError_t e = launch_draft_parts(fs, N, V, parts, stream);
-  if (e != hipSuccess) return e;
+  // Many draft rows: the statistics kernel summarises them first, one
+  // partial per 2048-entry chunk; the panel kernel forms the target rows'.
+  int64_t dparts = parts;
+  if (fs.draft != nullptr) {
+    const hipError_t e = launch_draft_stats(fs, N, V, &dparts, stream);
+    if (e != hipSuccess) return e;
+  }
   FusedStats target_only = fs;
   target_only.draft = nullptr;
-  e = launch_panel_shape(g.shape, g.panel, X, Wp, Y, N, d, V, false, stream, &target_only);
-  if (e == hipSuccess) *nparts = parts;
+  const hipError_t e = launch_panel_shape(g.shape, g.panel, X, Wp, Y, N, d, V, false, stream, &target_only);
+  if (e == hipSuccess) {
+    *nparts = parts;
+    *nparts_draft = dparts;
+  }
   return e;
 }
 

@@ -104,20 +104,22 @@ struct FusedStats {
 };
 // Points fs at the workspace of a; false when the shape cannot take fused statistics.
 bool reject_fused_stats(const RejectArgs& a, FusedStats* fs);
-// The stages after the statistics, reading nparts partials per row.
-hipError_t launch_reject_after_fused(const RejectArgs& a, int64_t nparts, hipStream_t stream);
-// The draft rows' partials (nparts vocabulary slices per row) in the fused
-// slot layout; independent of the scoring kernel.  Nothing to do without draft
-// logits.
-hipError_t launch_draft_parts(const FusedStats& fs, int64_t n_target, int64_t V, int64_t nparts, hipStream_t stream);
+// The stages after the statistics, reading nparts partials per target row and
+// nparts_draft per draft row.
+hipError_t launch_reject_after_fused(const RejectArgs& a, int64_t nparts, int64_t nparts_draft, hipStream_t stream);
+// The draft rows' partials in the fused slot layout, one per 2048-entry chunk
+// (their count in *nparts); independent of the scoring kernel.
+hipError_t launch_draft_stats(const FusedStats& fs, int64_t n_target, int64_t V, int64_t* nparts, hipStream_t stream);
 // Partials per row that launch_gemm_with_stats will produce for this shape
 // (0: the shape does not take the statistics epilogue).
 int64_t gemm_stats_parts(int64_t N, int64_t d, int64_t V, int64_t pstride);
 // The scoring GEMM with the statistics epilogue (packed W, sweep or panel
-// kernel without k-groups, at most kFusedStatsMaxParts partials per row).
-// Returns hipErrorNotSupported, launching nothing, for shapes it does not take.
+// kernel without k-groups, at most kFusedStatsMaxParts partials per row); the
+// same launch summarises the draft rows.  Returns the partial counts of target
+// and draft rows, or hipErrorNotSupported, launching nothing, for shapes it
+// does not take.
 hipError_t launch_gemm_with_stats(const uint16_t* X, const uint16_t* Wp, float* Y, int64_t N, int64_t d, int64_t V,
-                                  const FusedStats& fs, int64_t* nparts, hipStream_t stream);
+                                  const FusedStats& fs, int64_t* nparts, int64_t* nparts_draft, hipStream_t stream);
 
 // Tree verification (greedy), M <= 64 nodes per tree.
 struct TreeArgs {

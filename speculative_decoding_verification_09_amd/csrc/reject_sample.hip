@@ -117,14 +117,16 @@ struct Ws {
   uint32_t* wkey;  // per row: warp cut key (read only by the warped kernels)
   int32_t* widx;   // per row: warp cut index
   int64_t pstride; // slots per row
-  int64_t nparts;  // slots in use per row
+  int64_t nparts;  // slots in use per target row
+  int64_t nparts_d;  // slots in use per draft row
 };
 
-inline Ws bind(void* base, const Layout& L, int64_t nparts) {
+inline Ws bind(void* base, const Layout& L, int64_t nparts, int64_t nparts_d = -1) {
   char* b = (char*)base;
   return Ws{(float*)(b + L.off_cmax), (double*)(b + L.off_csum), (int32_t*)(b + L.off_cidx), (float*)(b + L.off_zx),
             (DrawDesc*)(b + L.off_desc), (double*)(b + L.off_sres), (double*)(b + L.off_sp),
-            (uint32_t*)(b + L.off_wkey), (int32_t*)(b + L.off_widx), L.pstride, nparts};
+            (uint32_t*)(b + L.off_wkey), (int32_t*)(b + L.off_widx), L.pstride, nparts,
+            nparts_d < 0 ? nparts : nparts_d};
 }
 
 // ---------------------------------------------------------------------------
@@ -170,20 +172,22 @@ __device__ __forceinline__ int clamp_token(int32_t t, int64_t V) { return t < 0 
 // 1. Chunk statistics.  Target rows are [0, B*(gamma+1)) (row b*(gamma+1) + i),
 //    draft rows [B*(gamma+1), B*(2*gamma+1)) (row B*(gamma+1) + b*gamma + i).
 //    Lane l of a wave takes the 32 entries 256*j + 4*l + e (j < 8, e < 4) of
-//    its 2048-entry chunk (1 KB per load instruction).  WARP: entries the
-//    row's warp cut drops count as -inf (so does a dropped drafted token).
+//    its 2048-entry chunk (1 KB per load instruction).  Rows [row0, n_rows)
+//    are summarised.  WARP: entries the row's warp cut drops count as -inf (so
+//    does a dropped drafted token).
 template <bool VEC, bool GREEDY, bool WARP>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void stats_kernel(const float* __restrict__ target,
                                                                      const float* __restrict__ draft,
                                                                      const int32_t* __restrict__ tokens,
-                                                                     int64_t n_target_rows, int64_t n_rows,
-                                                                     int64_t gamma, int64_t V, float inv_t, Ws ws) {
+                                                                     int64_t n_target_rows, int64_t row0,
+                                                                     int64_t n_rows, int64_t gamma, int64_t V,
+                                                                     float inv_t, Ws ws) {
   constexpr int PL = kStatChunk / 64;
   const int lane = threadIdx.x & 63;
   const int64_t nch = stat_chunks(V);
   const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (item >= n_rows * nch) return;
-  const int64_t r = item / nch, c = item - r * nch;
+  if (item >= (n_rows - row0) * nch) return;
+  const int64_t r = row0 + item / nch, c = item - (r - row0) * nch;
   const bool is_target = r < n_target_rows;
   const float* row = is_target ? target + (size_t)r * V : draft + (size_t)(r - n_target_rows) * V;
   const int64_t c0 = c * kStatChunk;
@@ -412,7 +416,7 @@ __global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
     const bool row_drafted = j < g1 ? j < gamma : true;
     double M, Z;
     float px;
-    merge_row(ws, r, row_drafted, nch, inv_t, lane, M, Z, px);
+    merge_row(ws, r, row_drafted, j < g1 ? nch : ws.nparts_d, inv_t, lane, M, Z, px);
     if (lane == 0) {
       sh_m[j] = M;
       sh_z[j] = Z;
@@ -627,56 +631,6 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void greedy_kernel(const int32
   if (lane == 0) out_num[b] = k + 1;
 }
 
-// 1'. Draft-row partials in the slot layout of the fused statistics: row j of
-//     the draft is cut into nparts slices of L entries (a multiple of 4), one
-//     wave per (row, slice): the slice max of a = z * fl32(1/T) and the fp64
-//     sum of fp32 exp(a - max), plus the drafted token's logit from the wave
-//     whose slice holds it.  Used beside the scoring kernel's own statistics
-//     epilogue when there are many draft rows.
-__global__ __launch_bounds__(kWavesPerBlock * 64) void draft_part_kernel(FusedStats fs, int64_t n_target, int64_t V,
-                                                                          int64_t nparts) {
-  constexpr int kPer = 8;  // entries per lane and load round
-  const int lane = threadIdx.x & 63;
-  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  const int64_t nd = fs.B * fs.gamma;
-  if (item >= nd * nparts) return;
-  const int64_t j = item / nparts, p = item - j * nparts;
-  const int64_t L = (((V + nparts - 1) / nparts) + 3) & ~(int64_t)3;
-  const int64_t s0 = p * L < V ? p * L : V, s1 = s0 + L < V ? s0 + L : V;
-  const float* row = fs.draft + (size_t)j * V;
-  float M = -INFINITY;
-  double S = 0.0;
-  for (int64_t b0 = s0; b0 < s1; b0 += 64 * kPer) {
-    float x[kPer];
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {  // clamped addresses, no branches: all loads in flight together
-      const int64_t v = b0 + lane + 64 * e;
-      x[e] = row[v < s1 ? v : s1 - 1];
-    }
-    float bm = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < kPer; ++e)
-      if (b0 + lane + 64 * e < s1) bm = fmaxf(bm, x[e] * fs.inv_t);
-    bm = wave_max(bm);
-    const float Mn = fmaxf(M, bm);
-    if (S > 0.0) S *= exp((double)M - (double)Mn);  // wave-uniform
-    M = Mn;
-    double bs = 0.0;
-    if (M > -INFINITY)
-#pragma unroll
-      for (int e = 0; e < kPer; ++e)
-        if (b0 + lane + 64 * e < s1) bs += (double)expf(x[e] * fs.inv_t - M);
-    S += wave_sum(bs);
-  }
-  if (lane == 0) {
-    const size_t slot = (size_t)(n_target + j) * fs.pstride + p;
-    fs.cmax[slot] = M;
-    fs.csum[slot] = S;
-    const int xt = clamp_token(fs.tokens[j], V);
-    if (xt >= s0 && xt < s1) fs.zx[n_target + j] = row[xt];
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Tree verification ([LLMI] section 3, tree attention mask and depth offsets;
 // [MATH] "SpecInfer and Tree-Based Verification").  One wave per tree of
@@ -885,17 +839,31 @@ hipError_t launch_decide(const RejectArgs& a, const Ws& ws, hipStream_t stream) 
 
 }  // namespace
 
-hipError_t launch_draft_parts(const FusedStats& fs, int64_t n_target, int64_t V, int64_t nparts, hipStream_t stream) {
-  const int64_t items = fs.B * fs.gamma * nparts;
-  if (items == 0 || fs.draft == nullptr) return hipSuccess;
-  hipLaunchKernelGGL(draft_part_kernel, dim3(blocks_for(items, kWavesPerBlock)), dim3(kWavesPerBlock * 64), 0, stream,
-                     fs, n_target, V, nparts);
+hipError_t launch_draft_stats(const FusedStats& fs, int64_t n_target, int64_t V, int64_t* nparts, hipStream_t stream) {
+  const int64_t nd = fs.B * fs.gamma, nch = stat_chunks(V);
+  *nparts = nch;
+  if (nd == 0 || fs.draft == nullptr) return hipSuccess;
+  if (nch > fs.pstride) return hipErrorNotSupported;
+  Ws ws{};
+  ws.cmax = fs.cmax;
+  ws.csum = fs.csum;
+  ws.cidx = fs.cidx;
+  ws.zx = fs.zx;
+  ws.pstride = fs.pstride;
+  ws.nparts = ws.nparts_d = nch;
+  const dim3 grid(blocks_for(nd * nch, kWavesPerBlock)), blk(kWavesPerBlock * 64);
+  if ((V & 3) == 0)
+    hipLaunchKernelGGL((stats_kernel<true, false, false>), grid, blk, 0, stream, nullptr, fs.draft, fs.tokens,
+                       n_target, n_target, n_target + nd, fs.gamma, V, fs.inv_t, ws);
+  else
+    hipLaunchKernelGGL((stats_kernel<false, false, false>), grid, blk, 0, stream, nullptr, fs.draft, fs.tokens,
+                       n_target, n_target, n_target + nd, fs.gamma, V, fs.inv_t, ws);
   return hipGetLastError();
 }
 
-hipError_t launch_reject_after_fused(const RejectArgs& a, int64_t nparts, hipStream_t stream) {
+hipError_t launch_reject_after_fused(const RejectArgs& a, int64_t nparts, int64_t nparts_draft, hipStream_t stream) {
   const Layout L = make_layout(a.B, a.gamma, a.V);
-  return launch_decide(a, bind(a.workspace, L, nparts), stream);
+  return launch_decide(a, bind(a.workspace, L, nparts, nparts_draft), stream);
 }
 
 size_t tree_workspace_bytes(int64_t B, int64_t M, int64_t V) { return make_layout(B, M - 1, V).total; }
@@ -935,10 +903,10 @@ hipError_t launch_tree_greedy(const TreeArgs& t, int64_t nparts, hipStream_t str
     const int64_t rows = t.B * t.M;
     const dim3 g1(blocks_for(rows * stat_chunks(t.V), kWavesPerBlock));
     if ((t.V & 3) == 0)
-      hipLaunchKernelGGL((stats_kernel<true, true, false>), g1, blk, 0, stream, t.logits, nullptr, nullptr, rows, rows,
+      hipLaunchKernelGGL((stats_kernel<true, true, false>), g1, blk, 0, stream, t.logits, nullptr, nullptr, rows, 0, rows,
                          (int64_t)0, t.V, 1.0f, ws);
     else
-      hipLaunchKernelGGL((stats_kernel<false, true, false>), g1, blk, 0, stream, t.logits, nullptr, nullptr, rows, rows,
+      hipLaunchKernelGGL((stats_kernel<false, true, false>), g1, blk, 0, stream, t.logits, nullptr, nullptr, rows, 0, rows,
                          (int64_t)0, t.V, 1.0f, ws);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -967,7 +935,7 @@ hipError_t launch_reject_sample(const RejectArgs& a, hipStream_t stream) {
     if (ew != hipSuccess) return ew;
   }
 #define SPECDEC_STATS(V4, GR, WP)                                                                                        \
-  hipLaunchKernelGGL((stats_kernel<V4, GR, WP>), g1, blk, 0, stream, a.target, a.draft, a.tokens, n_target, n_rows, \
+  hipLaunchKernelGGL((stats_kernel<V4, GR, WP>), g1, blk, 0, stream, a.target, a.draft, a.tokens, n_target, 0, n_rows, \
                      a.gamma, a.V, inv_t, ws)
   if (greedy) {
     if (vec) SPECDEC_STATS(true, true, false); else SPECDEC_STATS(false, true, false);
