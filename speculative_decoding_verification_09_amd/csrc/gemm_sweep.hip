@@ -1,5 +1,5 @@
 // Packed weight layout and the sweep kernel: the scoring GEMM
-// Y[n, v] = sum_k X[n, k] * W[v, k] for few positions (N <= 8).
+// Y[n, v] = sum_k X[n, k] * W[v, k] for few positions (N <= 16: one MFMA column tile).
 //
 // The verification pass scores N = B*(gamma+1) positions with one read of the
 // output-layer weights ("LLM Inference & Speculative Decoding", section 0: a
@@ -47,11 +47,12 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Sweep kernel (packed W, small N).  The k range may be split into groups of
-// spk k-steps (KG = ceil(nsteps / spk) groups): block b takes group b % KG of
-// the tiles t = b / KG + j * (gridDim.x / KG), holds only that slice of X in
-// LDS, and writes its partial sums to slice b % KG of Y (fp32 [KG][N][V]),
-// which the caller then sums in group order.  With one group Y is the output.
+// Sweep kernel (packed W, small N).  The kernel can split the k range into
+// groups of spk k-steps (KG = ceil(nsteps / spk) groups): block b takes group
+// b % KG of the tiles t = b / KG + j * (gridDim.x / KG), holds only that slice
+// of X in LDS, and writes its partial sums to slice b % KG of Y (fp32
+// [KG][N][V]).  The planner runs it with one group (spk = nsteps), where Y is
+// the output.
 // Inside a block, wave w owns k-steps [w*spw, (w+1)*spw) of the group, taken
 // SPW at a time; a work unit u is (tile u / ngroups, register group
 // u % ngroups).
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
 // token from the tile that holds it, and at the end leaves one partial per
 // (row, workgroup).  With draft logits, the workgroups that have one tile
 // fewer (they finish first) also summarise a slice of every draft row, one
-// wave per row (few rows here: B*(gamma+1) <= 8).
+// wave per row (few rows here: B*(gamma+1) <= 16).
 template <int NW, int SPW, bool NTL, bool OUT_BF16, int EPI>
 __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp,
                                                         void* __restrict__ Y, int N, int d, int V, int spk,
@@ -283,20 +284,12 @@ size_t sweep_lds_bytes(int64_t N, int64_t spk) {
 SweepPlan plan_sweep(int64_t N, int64_t d, int64_t V, int cus) {
   SweepPlan p{};
   const int64_t nsteps = d / 32, ntiles = (V + 15) / 16;
-  if (N > 8 || nsteps < 1) return p;
-  // Fewest k-groups whose X slice fits in LDS and that give every CU a tile.
-  for (int64_t kgs = 1; kgs <= nsteps; ++kgs) {
-    const int64_t spk = (nsteps + kgs - 1) / kgs;
-    const int64_t groups = (nsteps + spk - 1) / spk;
-    if (sweep_lds_bytes(N, spk) > kSweepLdsLimit) continue;
-    if (ntiles * groups < cus && spk > 16) continue;
-    p.ok = true;
-    p.spk = spk;
-    p.kgroups = groups;
-    const int64_t streams = ntiles * groups < cus ? ntiles : (cus / groups > 0 ? cus / groups : 1);
-    p.grid = (streams < ntiles ? streams : ntiles) * groups;
-    return p;
-  }
+  // One k-group: X whole in LDS (the dispatcher takes the panel kernel otherwise).
+  if (N > 16 || nsteps < 1 || sweep_lds_bytes(N, nsteps) > kSweepLdsLimit) return p;
+  p.ok = true;
+  p.spk = nsteps;
+  p.kgroups = 1;
+  p.grid = ntiles < cus ? ntiles : cus;
   return p;
 }
 

@@ -511,31 +511,22 @@ struct PanelPlan {
   int64_t npass, cpk, groups, grid;
 };
 
-// Splits the k range into groups when the (vocabulary block, token pass) work
-// items alone would leave CUs idle.  The group count (each group at least 4
-// chunks) minimises an estimate of the time: bytes moved (W once, plus the
-// fp32 partials written and read back) over the share of CU slots that the
-// rounds of blocks keep busy.
+// Splits the k range into groups only when the (vocabulary block, token pass)
+// work items would leave more than 15% of the CUs idle: the fewest groups
+// (each at least 4 chunks) that reach 85% of the CUs in one round.  Measured
+// on the projection shapes, a CU streams well over its share of the HBM
+// bandwidth, so a partly idle round still saturates HBM, while every extra
+// group writes and reads back fp32 partials N x V and adds a reduction.
 PanelPlan plan_panel(int64_t N, int64_t d, int64_t V, int NT, int R, int NW, int KS, int cus) {
   PanelPlan p{};
   const int64_t ntiles = (V + 15) / 16, nvb = (ntiles + NW * R - 1) / (NW * R);
   const int64_t nch = (d / 32 + KS - 1) / KS;
   p.npass = (N + NT * 16 - 1) / (NT * 16);
-  const int64_t items = nvb * p.npass;
-  const double wbytes = 2.0 * (double)V * (double)d, pbytes = 8.0 * (double)N * (double)V;
-  int64_t best_groups = 1;
-  double best = -1.0;
-  for (int64_t gq = 1; gq == 1 || (gq <= 4 * ((cus + items - 1) / items) && gq <= nch / 4); ++gq) {
-    const int64_t cpk = (nch + gq - 1) / gq, real = (nch + cpk - 1) / cpk;
-    const int64_t total = items * real, rounds = (total + cus - 1) / cus;
-    const double fill = (double)total / (double)(rounds * cus) * ((double)nch / (double)(real * cpk));
-    const double t = (wbytes + (real > 1 ? pbytes * (double)real : 0.0)) / fill;
-    if (best < 0.0 || t < best * (1.0 - 1e-9)) {
-      best = t;
-      best_groups = real;
-    }
-  }
-  p.cpk = (nch + best_groups - 1) / best_groups;
+  const int64_t items = nvb * p.npass, want = (cus * 85 + 99) / 100;
+  int64_t gq = items >= want ? 1 : (want + items - 1) / items;
+  const int64_t gmax = nch / 4 > 1 ? nch / 4 : 1;
+  if (gq > gmax) gq = gmax;
+  p.cpk = (nch + gq - 1) / gq;
   p.groups = (nch + p.cpk - 1) / p.cpk;
   p.grid = 8 * ((nvb * p.groups + 7) / 8) * p.npass;
   return p;
@@ -567,25 +558,29 @@ hipError_t launch_panel(const PanelPlan& p, const uint16_t* X, const uint16_t* W
 struct PanelShape {
   int NT, R, NW, KS;
 };
-// Large vocabularies (LM heads) have vocabulary blocks to spare and favour
-// 64 rows per wave; the projection shapes (few output rows, k split into
-// groups) favour more tokens per wave.  The 8x4 shape is the fastest at 512
-// positions on the projection shapes but does not fit its registers without
-// spilling, so the statistics epilogue never uses it.
-PanelShape panel_shape(int64_t N, int64_t V, bool with_stats) {
+// Shapes (token tiles x vocabulary tiles per wave, waves, k-steps per chunk)
+// chosen from timings of every candidate on the LM heads (V = 128256 and
+// 152064, d = 4096 to 8192) and the decoder projections (8192 <-> 28672):
+// short vocabularies take narrow vocabulary blocks so that one round of
+// blocks covers the CUs without splitting k; long ones take 64 rows per wave.
+// Past 64 positions the work turns MFMA-bound and more token tiles per wave
+// win.  The 8x4 shape does not fit its registers without spilling (it is
+// still the fastest there), so the statistics epilogue never uses it.
+PanelShape panel_shape(int64_t N, int64_t d, int64_t V, bool with_stats) {
   const bool big_v = V >= 65536;
-  if (N <= 16) return {1, 2, 8, 4};
-  if (N <= 32) return {2, 2, 8, 4};
-  if (N <= 64) return big_v ? PanelShape{4, 4, 8, 2} : PanelShape{8, 2, 8, 2};
-  if (N <= 128) return {8, 2, 8, 2};
+  if (N <= 64) {
+    if (!big_v) return N <= 32 ? PanelShape{4, 1, 8, 4} : PanelShape{4, 2, 8, 2};
+    return d <= 4096 ? PanelShape{4, 2, 8, 2} : PanelShape{4, 4, 8, 2};
+  }
+  if (N <= 128) return big_v && !with_stats ? PanelShape{8, 4, 8, 2} : PanelShape{8, 2, 8, 2};
   return big_v || with_stats ? PanelShape{4, 4, 8, 2} : PanelShape{8, 4, 8, 2};
 }
 
 hipError_t launch_panel_shape(const PanelShape& s, const PanelPlan& p, const uint16_t* X, const uint16_t* Wp, void* Y,
                               int64_t N, int64_t d, int64_t V, bool out_bf16, hipStream_t stream,
                               const FusedStats* fs = nullptr) {
-  if (s.NT == 1) return launch_panel<1, 2, 8, 4>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);
-  if (s.NT == 2) return launch_panel<2, 2, 8, 4>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);
+  if (s.NT == 4 && s.R == 1) return launch_panel<4, 1, 8, 4>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);
+  if (s.NT == 4 && s.R == 2) return launch_panel<4, 2, 8, 2>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);
   if (s.NT == 4) return launch_panel<4, 4, 8, 2>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);
   if (s.R == 2) return launch_panel<8, 2, 8, 2>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);
   if (fs) return hipErrorNotSupported;
@@ -606,14 +601,15 @@ GemmPlan plan_gemm(int64_t N, int64_t d, int64_t V, bool packed, bool with_stats
   const int cus = device_cus();
   g.kind = GemmPlan::kTiled;
   if (!packed) return g;
+  // The sweep kernel wins on long vocabularies with X whole in LDS (d up to
+  // 4096 at 16 positions); elsewhere the panel kernel streams W faster.
   g.sweep = plan_sweep(N, d, V, cus);
-  if (g.sweep.ok) {
+  if (g.sweep.ok && V >= 65536 && d <= 4096) {
     g.kind = GemmPlan::kSweep;
-    if (g.sweep.kgroups > 1) g.workspace = (size_t)g.sweep.kgroups * N * V * sizeof(float);
     return g;
   }
   g.kind = GemmPlan::kPanel;
-  g.shape = panel_shape(N, V, with_stats);
+  g.shape = panel_shape(N, d, V, with_stats);
   g.panel = plan_panel(N, d, V, g.shape.NT, g.shape.R, g.shape.NW, g.shape.KS, cus);
   if (g.panel.groups > 1) g.workspace = (size_t)g.panel.groups * N * V * sizeof(float);
   return g;
@@ -627,7 +623,7 @@ int64_t gemm_stats_parts(int64_t N, int64_t d, int64_t V, int64_t pstride) {
   if (N > kFusedStatsMaxRows) return 0;
   const GemmPlan g = plan_gemm(N, d, V, true, true);
   int64_t parts = 0;
-  if (g.kind == GemmPlan::kSweep && g.sweep.kgroups == 1) {
+  if (g.kind == GemmPlan::kSweep) {
     parts = g.sweep.grid;
   } else if (g.kind == GemmPlan::kPanel && g.panel.groups == 1) {
     const int64_t ntiles = (V + 15) / 16, rows = (int64_t)g.shape.NW * g.shape.R;
@@ -677,9 +673,7 @@ hipError_t launch_skinny_gemm(const uint16_t* X, const uint16_t* W, void* Y, int
   if (g.workspace > 0 && !workspace) return hipErrorInvalidValue;
   switch (g.kind) {
     case GemmPlan::kSweep: {
-      if (g.sweep.kgroups == 1) return launch_sweep(g.sweep, X, W, Y, N, d, V, out_bf16, stream);
-      hipError_t e = launch_sweep(g.sweep, X, W, workspace, N, d, V, false, stream);
-      return e != hipSuccess ? e : launch_reduce((const float*)workspace, Y, N, V, g.sweep.kgroups, out_bf16, stream);
+      return launch_sweep(g.sweep, X, W, Y, N, d, V, out_bf16, stream);
     }
     case GemmPlan::kPanel: {
       if (g.panel.groups == 1) return launch_panel_shape(g.shape, g.panel, X, W, Y, N, d, V, out_bf16, stream);

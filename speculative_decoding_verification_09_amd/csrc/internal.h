@@ -15,10 +15,8 @@ hipError_t launch_skinny_gemm(const uint16_t* X, const uint16_t* W, void* Y, int
                               bool out_bf16, bool packed, void* workspace, hipStream_t stream);
 
 namespace gemm {
-// The sweep kernel (packed W, at most 8 positions).  Its k range is split into
-// kgroups groups of spk k-steps when X does not fit in LDS whole or the tiles
-// are too few for the CUs; each group then writes fp32 partials [N, V] to its
-// own slice of the output pointer, to be summed in group order.
+// The sweep kernel (packed W, at most 16 positions, X whole in LDS: one
+// k-group of spk = d/32 k-steps; ok is false when X does not fit).
 struct SweepPlan {
   bool ok;
   int64_t spk, kgroups, grid;

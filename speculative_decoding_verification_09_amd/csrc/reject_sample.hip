@@ -68,7 +68,7 @@ struct DrawDesc {
 
 // Workspace layout, every array 16-byte aligned.  Each row has pstride slots
 // for softmax partials: one per statistics chunk, or, when the scoring kernel
-// forms them itself (at most kMaxFusedParts workgroups, B*(gamma+1) <= 8), one
+// forms them itself (at most kMaxFusedParts workgroups, B*(gamma+1) <= kMaxFusedRows), one
 // per workgroup of that kernel.
 struct Layout {
   size_t off_cmax, off_csum, off_cidx;      // per (row, partial slot)

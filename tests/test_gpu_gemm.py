@@ -25,13 +25,16 @@ SHAPES = [
     (1, 8, 1), (5, 64, 37), (16, 256, 128), (17, 264, 1000), (33, 512, 777), (64, 520, 1030),
     (100, 1024, 2053), (200, 320, 515), (320, 136, 300), (513, 96, 129), (1, 4104, 4099),
 ]
-# Packed weights (d % 32 == 0).  Covers the sweep kernel (N <= 16 with X in
-# LDS): one and several k-groups per wave, k-step counts that leave waves idle
-# or partly filled (d = 96, 5120), vocabulary tails; and the tiled kernels.
+# Packed weights (d % 32 == 0).  Covers the sweep kernel (long vocabularies,
+# N <= 16, X whole in LDS: up to 16 positions, vocabulary tails), and every
+# panel shape (4x1, 4x2, 4x4, 8x2, 8x4 token x vocabulary tiles per wave) with
+# and without k-groups, k-step counts that leave waves idle or partly filled
+# (d = 96, 5120), vocabulary tails.
 PACKED_SHAPES = [
     (1, 64, 17), (5, 4096, 1000), (5, 8192, 515), (3, 5120, 513), (7, 96, 50), (16, 4096, 300),
     (16, 32, 16), (8, 28672, 40), (17, 256, 1000), (33, 512, 777), (64, 1024, 1030), (100, 512, 2053),
-    (200, 320, 515), (513, 96, 129),
+    (200, 320, 515), (513, 96, 129), (16, 256, 65541), (9, 4096, 65536), (12, 1024, 70001),
+    (40, 1024, 66000), (8, 4128, 65536), (120, 256, 65541), (130, 128, 65536),
 ]
 
 
@@ -111,8 +114,8 @@ def test_packed_bf16_output(orc, N, d, V):
 
 
 # Packed shapes whose k range is split into groups (fp32 partials in the
-# workspace, added in group order): X too wide for LDS at small N (sweep), few
-# vocabulary tiles for the CUs (panel), vocabulary and k tails.
+# workspace, added in group order): short vocabularies whose blocks would
+# leave CUs idle, at every token count; vocabulary and k tails.
 SPLIT_SHAPES = [
     (40, 2048, 300), (8, 9984, 100), (8, 9984, 5000), (17, 4096, 300), (100, 1024, 64), (3, 16384, 40),
     (5, 28672, 77), (64, 8192, 1030), (130, 2048, 500),

@@ -146,6 +146,9 @@ FUSED = [
     ("panel_passes_greedy", 40, 4, 64, 999, 0.0), ("panel_passes_logits", 32, 5, 96, 4100, 1.1),
     # one-hot (greedy or lookup) drafts: no draft array
     ("onehot", 2, 3, 256, 5000, 1.0), ("panel_onehot", 12, 4, 128, 3001, 0.9),
+    # long vocabularies, up to 16 positions: the sweep kernel's epilogue (draft rows in its spare workgroups)
+    ("sweep_logits", 1, 4, 256, 65600, 1.0), ("sweep_16", 2, 7, 128, 66001, 0.9), ("sweep_greedy", 3, 4, 64, 65536, 0.0),
+    ("sweep_probs", 2, 3, 128, 65541, 1.0), ("sweep_onehot", 2, 5, 128, 65600, 1.0),
 ]
 
 
@@ -156,8 +159,8 @@ def test_fused_statistics_path(orc, name, B, g, d, V, T):
     W = synth.normal_bf16((V, d), 2.0 / np.sqrt(d), seed, synth.STREAM_W)
     target32 = orc.linear(X, W).astype(np.float32).reshape(B, g + 1, V)
     greedy = T == 0.0
-    kind = {"probs": sd.SPECDEC_DRAFT_PROBS}.get(name, sd.SPECDEC_DRAFT_ONEHOT if "onehot" in name
-                                                  else sd.SPECDEC_DRAFT_LOGITS)
+    kind = (sd.SPECDEC_DRAFT_PROBS if "probs" in name else
+            sd.SPECDEC_DRAFT_ONEHOT if "onehot" in name else sd.SPECDEC_DRAFT_LOGITS)
     if greedy:
         draft = None
         am = np.array([[orc.argmax(target32[b, i])[0] for i in range(g)] for b in range(B)], np.int32).reshape(B, g)
