@@ -430,6 +430,16 @@ def projection_sweep(args):
         del W_rows
         Xall = torch.from_numpy(synth.normal_bf16((Nmax, d_in), cfg["x_std"], seed, synth.STREAM_X).view(np.int16))
         Xall = Xall.to(dev).view(torch.bfloat16)
+        # Sustained load first (about 0.1 s): after the host-side setup the GPU needs tens of milliseconds of work
+        # before its clocks settle, and each point below is only a few milliseconds long.
+        Xw = Xall[:64].contiguous()
+        Yw = torch.empty((64, d_out), dtype=torch.bfloat16, device=dev)
+        wsw = torch.empty(max(1, sd.logits_workspace_bytes(64, d_in, d_out, sd.SPECDEC_WEIGHTS_PACKED)),
+                          dtype=torch.uint8, device=dev)
+        for _ in range(1200):
+            sd.specdec_verify_logits(Xw, W, Yw, sd.SPECDEC_OUT_BF16, workspace=wsw, stream=stream)
+        torch.cuda.synchronize()
+        del Xw, Yw, wsw
         for N in cfg["N"]:
             X = Xall[:N].contiguous()
             Y = torch.empty((N, d_out), dtype=torch.bfloat16, device=dev)
