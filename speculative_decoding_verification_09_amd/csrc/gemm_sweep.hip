@@ -78,6 +78,10 @@ __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restri
                                                         FusedStats fs) {
   extern __shared__ __align__(16) uint16_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, g = lane >> 4;
+  if (EPI == 1 && fs.done != nullptr) {  // the draw kernel's counters, for the step that follows
+    const int64_t gid = (int64_t)blockIdx.x * (NW * 64) + tid;
+    if (gid < fs.B) fs.done[gid] = 0u;
+  }
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int nsteps = d >> 5;
   const int ntiles = (V + 15) >> 4;

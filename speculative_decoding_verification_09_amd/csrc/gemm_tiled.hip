@@ -341,6 +341,10 @@ __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restri
   const int nch_all = (nsteps + KS - 1) / KS;
   const int ngroups = (nch_all + cpk - 1) / cpk;
   const int id = (int)blockIdx.x;
+  if (EPI == 1 && fs.done != nullptr) {  // the draw kernel's counters, for the step that follows
+    const int64_t gid = (int64_t)id * kThreads + threadIdx.x;
+    if (gid < fs.B) fs.done[gid] = 0u;
+  }
   const int slot = id >> 3;
   const int gi = (id & 7) + 8 * (slot / npass);
   if (gi >= nvb * ngroups) return;

@@ -99,6 +99,7 @@ struct FusedStats {
   int64_t B, gamma;
   float inv_t;            // fl32(1/T); 1 when greedy
   bool greedy;
+  uint32_t* done;         // [B]: the draw kernel's per-sequence counters, zeroed by the softmax epilogue (or null)
 };
 // Points fs at the workspace of a; false when the shape cannot take fused statistics.
 bool reject_fused_stats(const RejectArgs& a, FusedStats* fs);

@@ -76,6 +76,7 @@ struct Layout {
   size_t off_desc;                          // per sequence
   size_t off_sres, off_sp;                  // per (sequence, draw chunk)
   size_t off_wkey, off_widx;                // per row: warp cut
+  size_t off_done;                          // per sequence: draw workgroups finished
   int64_t pstride;
   size_t total;
 };
@@ -102,6 +103,7 @@ __host__ __device__ inline Layout make_layout(int64_t B, int64_t gamma, int64_t 
   L.off_sp = o;   o = align16(o + ndc * sizeof(double));
   L.off_wkey = o; o = align16(o + rows * sizeof(uint32_t));
   L.off_widx = o; o = align16(o + rows * sizeof(int32_t));
+  L.off_done = o; o = align16(o + (size_t)B * sizeof(uint32_t));
   L.total = o;
   return L;
 }
@@ -116,6 +118,7 @@ struct Ws {
   double* sp;      // per (sequence, draw chunk): sum of p
   uint32_t* wkey;  // per row: warp cut key (read only by the warped kernels)
   int32_t* widx;   // per row: warp cut index
+  uint32_t* done;  // per sequence: draw workgroups finished (zeroed by the statistics pass)
   int64_t pstride; // slots per row
   int64_t nparts;  // slots in use per target row
   int64_t nparts_d;  // slots in use per draft row
@@ -125,8 +128,8 @@ inline Ws bind(void* base, const Layout& L, int64_t nparts, int64_t nparts_d = -
   char* b = (char*)base;
   return Ws{(float*)(b + L.off_cmax), (double*)(b + L.off_csum), (int32_t*)(b + L.off_cidx), (float*)(b + L.off_zx),
             (DrawDesc*)(b + L.off_desc), (double*)(b + L.off_sres), (double*)(b + L.off_sp),
-            (uint32_t*)(b + L.off_wkey), (int32_t*)(b + L.off_widx), L.pstride, nparts,
-            nparts_d < 0 ? nparts : nparts_d};
+            (uint32_t*)(b + L.off_wkey), (int32_t*)(b + L.off_widx), (uint32_t*)(b + L.off_done), L.pstride,
+            nparts, nparts_d < 0 ? nparts : nparts_d};
 }
 
 // ---------------------------------------------------------------------------
@@ -174,16 +177,19 @@ __device__ __forceinline__ int clamp_token(int32_t t, int64_t V) { return t < 0 
 //    Lane l of a wave takes the 32 entries 256*j + 4*l + e (j < 8, e < 4) of
 //    its 2048-entry chunk (1 KB per load instruction).  Rows [row0, n_rows)
 //    are summarised.  WARP: entries the row's warp cut drops count as -inf (so
-//    does a dropped drafted token).
+//    does a dropped drafted token).  The first n_done threads also zero the
+//    draw kernel's per-sequence counters.
 template <bool VEC, bool GREEDY, bool WARP>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void stats_kernel(const float* __restrict__ target,
                                                                      const float* __restrict__ draft,
                                                                      const int32_t* __restrict__ tokens,
                                                                      int64_t n_target_rows, int64_t row0,
                                                                      int64_t n_rows, int64_t gamma, int64_t V,
-                                                                     float inv_t, Ws ws) {
+                                                                     float inv_t, Ws ws, int64_t n_done) {
   constexpr int PL = kStatChunk / 64;
   const int lane = threadIdx.x & 63;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid < n_done) ws.done[gid] = 0u;
   const int64_t nch = stat_chunks(V);
   const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (item >= (n_rows - row0) * nch) return;
@@ -380,122 +386,16 @@ __device__ __forceinline__ void load_chunk16(const float* __restrict__ row, int6
   }
 }
 
-// 2. Draw sums (T > 0).  A workgroup of WB waves takes WB consecutive chunks of
-//    one sequence.  Its waves first merge the sequence's rows in parallel (one
-//    row per wave at a time) into LDS; after one barrier every wave reads the
-//    statistics of all rows from LDS, lane i <-> row i.
-constexpr int kMaxRows = 2 * 63 + 1;
-template <int WB, bool VEC, bool WARP>
-__global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
-    const float* __restrict__ target, const float* __restrict__ draft, int draft_kind,
-    const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, int64_t B, int64_t gamma, int64_t V,
-    float inv_t, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_num, float* __restrict__ out_probs,
-    Ws ws) {
-  __shared__ double sh_m[kMaxRows], sh_z[kMaxRows];
-  __shared__ float sh_px[kMaxRows];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int64_t ndc = draw_chunks(V);
-  const int64_t gps = (ndc + WB - 1) / WB;  // workgroups per sequence
-  const int64_t b = blockIdx.x / gps;
-  const int64_t c = (blockIdx.x - b * gps) * WB + wv;
-  const int64_t g1 = gamma + 1;
-  const bool q_probs = draft_kind == 1;
-  const bool q_onehot = draft_kind == 2;
-  const int64_t nch = ws.nparts;
-  // Per-row inputs that do not depend on the statistics, loaded first (lane i <-> row i).
-  const bool has_row = lane < g1;
-  const bool drafted = lane < gamma;
-  const float u_acc = drafted ? uniforms[(b * g1 + lane) * 2 + 0] : 0.0f;
-  const float u_smp = has_row ? uniforms[(b * g1 + lane) * 2 + 1] : 0.0f;
-  const int xi = drafted ? clamp_token(tokens[b * gamma + lane], V) : 0;
-  const float q_given = drafted && q_probs ? draft[(size_t)(b * gamma + lane) * V + xi] : (q_onehot ? 1.0f : 0.0f);
-  // Rows of the sequence: j < g1 target row j, then draft row j - g1 (draft logits).
-  const int nrows = (int)(draft_kind != 0 ? g1 : g1 + gamma);
-  for (int j = wv; j < nrows; j += WB) {
-    const int64_t r = j < g1 ? b * g1 + j : B * g1 + b * gamma + (j - g1);
-    const bool row_drafted = j < g1 ? j < gamma : true;
-    double M, Z;
-    float px;
-    merge_row(ws, r, row_drafted, j < g1 ? nch : ws.nparts_d, inv_t, lane, M, Z, px);
-    if (lane == 0) {
-      sh_m[j] = M;
-      sh_z[j] = Z;
-      sh_px[j] = px;
-    }
-  }
-  __syncthreads();
-  if (c >= ndc) return;  // no barrier below
-  const int64_t item = b * ndc + c;
-  const double rmt = has_row ? sh_m[lane] : 0.0, rzt = has_row ? sh_z[lane] : 1.0;
-  const float p_x = drafted ? sh_px[lane] : 0.0f;
-  const bool ql = drafted && draft_kind == 0;
-  const double rmq = ql ? sh_m[g1 + lane] : 0.0, rzq = ql ? sh_z[g1 + lane] : 1.0;
-  const float q_x = ql ? sh_px[g1 + lane] : q_given;
-
-  bool reject = false;
-  if (drafted) {
-    const float ratio = p_x / (q_x > kQFloor ? q_x : kQFloor);
-    const float thr = ratio < 1.0f ? ratio : 1.0f;
-    reject = !(u_acc < thr);
-  }
-  const uint64_t rej = ballot(reject);
-  const int k = rej ? (int)__builtin_ctzll(rej) : (int)gamma;
-  DrawDesc D;
-  D.k = k;
-  D.mp = (float)__shfl(rmt, k);
-  D.ip = (float)(1.0 / __shfl(rzt, k));
-  const int kq = k < gamma ? k : 0;
-  D.mq = (float)__shfl(rmq, kq);
-  D.iq = (float)(1.0 / __shfl(rzq, kq));
-  D.u = __shfl(u_smp, k);
-  D.xk = k < gamma ? __shfl(xi, k) : -1;
-  D.pad = 0.0f;
-
-  if (c == 0) {
-    if (has_row && lane != k) out_tokens[b * g1 + lane] = lane < k ? xi : -1;
-    if (drafted && out_probs) {
-      out_probs[(b * gamma + lane) * 2 + 0] = p_x;
-      out_probs[(b * gamma + lane) * 2 + 1] = q_x;
-    }
-    if (lane == 0) {
-      out_num[b] = k + 1;
-      ws.desc[b] = D;
-    }
-  }
-  const DrawRow R = make_row<WARP>(target, draft, draft_kind, B, b, gamma, V, D, inv_t, ws);
-  const int64_t c0 = c * kDrawChunk;
-  float zp[16], zq[16];
-  load_chunk16<VEC>(R.zp, V, c0, lane, -INFINITY, zp);
-  if (R.zq) load_chunk16<VEC>(R.zq, V, c0, lane, q_probs ? 0.0f : -INFINITY, zq);
-  double sr = 0.0, sp = 0.0;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    float p, r;
-    weights<WARP>(R, c0 + 256 * (e >> 2) + 4 * lane + (e & 3), zp[e], R.zq ? zq[e] : 0.0f, p, r);
-    sr += (double)r;
-    sp += (double)p;
-  }
-  sr = wave_sum(sr);
-  sp = wave_sum(sp);
-  if (lane == 0) {
-    ws.sres[item] = sr;
-    ws.sp[item] = sp;
-  }
-}
-
-// 3. Select (T > 0): one wave per sequence.  The residual's weights, or p
-//    when the residual has no mass or the step ends on the bonus row.
+// 3. Select (T > 0), by one wave of the last draw workgroup of sequence b to
+//    finish: the residual's weights, or p when the residual has no mass or the
+//    step ends on the bonus row.
 template <bool VEC, bool WARP>
-__global__ __launch_bounds__(kWavesPerBlock * 64) void select_kernel(
-    const float* __restrict__ target, const float* __restrict__ draft, int draft_kind, int64_t B, int64_t gamma,
-    int64_t V, float inv_t, int32_t* __restrict__ out_tokens, Ws ws) {
-  const int lane = threadIdx.x & 63;
-  const int64_t b = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (b >= B) return;
+__device__ void select_seq(const float* __restrict__ target, const float* __restrict__ draft, int draft_kind,
+                           int64_t B, int64_t b, int64_t gamma, int64_t V, float inv_t,
+                           int32_t* __restrict__ out_tokens, const Ws& ws, const DrawDesc& D, int lane) {
   const int64_t ndc = draw_chunks(V);
   const int64_t g1 = gamma + 1;
-  // Descriptor and the first 64 chunk totals in one round of loads.
-  const DrawDesc D = ws.desc[b];
+  // The first 64 chunk totals in one round of loads.
   const double* pr = ws.sres + b * ndc;
   const double* pp = ws.sp + b * ndc;
   const double pj_r = lane < ndc ? pr[lane] : 0.0;
@@ -581,6 +481,125 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void select_kernel(
   int tok = hits ? __shfl(hit, __builtin_ctzll(hits)) : lastpos;
   if (tok < 0 || tok >= V) tok = 0;  // no positive weight anywhere (non-finite inputs)
   if (lane == 0) out_tokens[b * g1 + D.k] = tok;
+}
+
+// 2. Draw sums (T > 0).  A workgroup of WB waves takes WB consecutive chunks of
+//    one sequence.  Its waves first merge the sequence's rows in parallel (one
+//    row per wave at a time) into LDS; after one barrier every wave reads the
+//    statistics of all rows from LDS, lane i <-> row i.  Each workgroup then
+//    counts itself done on the sequence's counter (a device-scope atomic after
+//    a device-scope fence, so its chunk totals are visible first); the last of
+//    them runs the select (3) with one wave.  No workgroup waits for another.
+constexpr int kMaxRows = 2 * 63 + 1;
+template <int WB, bool VEC, bool WARP>
+__global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
+    const float* __restrict__ target, const float* __restrict__ draft, int draft_kind,
+    const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, int64_t B, int64_t gamma, int64_t V,
+    float inv_t, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_num, float* __restrict__ out_probs,
+    Ws ws) {
+  __shared__ double sh_m[kMaxRows], sh_z[kMaxRows];
+  __shared__ float sh_px[kMaxRows];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t ndc = draw_chunks(V);
+  const int64_t gps = (ndc + WB - 1) / WB;  // workgroups per sequence
+  const int64_t b = blockIdx.x / gps;
+  const int64_t c = (blockIdx.x - b * gps) * WB + wv;
+  const int64_t g1 = gamma + 1;
+  const bool q_probs = draft_kind == 1;
+  const bool q_onehot = draft_kind == 2;
+  const int64_t nch = ws.nparts;
+  // Per-row inputs that do not depend on the statistics, loaded first (lane i <-> row i).
+  const bool has_row = lane < g1;
+  const bool drafted = lane < gamma;
+  const float u_acc = drafted ? uniforms[(b * g1 + lane) * 2 + 0] : 0.0f;
+  const float u_smp = has_row ? uniforms[(b * g1 + lane) * 2 + 1] : 0.0f;
+  const int xi = drafted ? clamp_token(tokens[b * gamma + lane], V) : 0;
+  const float q_given = drafted && q_probs ? draft[(size_t)(b * gamma + lane) * V + xi] : (q_onehot ? 1.0f : 0.0f);
+  // Rows of the sequence: j < g1 target row j, then draft row j - g1 (draft logits).
+  const int nrows = (int)(draft_kind != 0 ? g1 : g1 + gamma);
+  for (int j = wv; j < nrows; j += WB) {
+    const int64_t r = j < g1 ? b * g1 + j : B * g1 + b * gamma + (j - g1);
+    const bool row_drafted = j < g1 ? j < gamma : true;
+    double M, Z;
+    float px;
+    merge_row(ws, r, row_drafted, j < g1 ? nch : ws.nparts_d, inv_t, lane, M, Z, px);
+    if (lane == 0) {
+      sh_m[j] = M;
+      sh_z[j] = Z;
+      sh_px[j] = px;
+    }
+  }
+  __syncthreads();
+  const bool active = c < ndc;  // waves past the last chunk only take part in the barriers
+  const int64_t item = b * ndc + c;
+  const double rmt = has_row ? sh_m[lane] : 0.0, rzt = has_row ? sh_z[lane] : 1.0;
+  const float p_x = drafted ? sh_px[lane] : 0.0f;
+  const bool ql = drafted && draft_kind == 0;
+  const double rmq = ql ? sh_m[g1 + lane] : 0.0, rzq = ql ? sh_z[g1 + lane] : 1.0;
+  const float q_x = ql ? sh_px[g1 + lane] : q_given;
+
+  bool reject = false;
+  if (drafted) {
+    const float ratio = p_x / (q_x > kQFloor ? q_x : kQFloor);
+    const float thr = ratio < 1.0f ? ratio : 1.0f;
+    reject = !(u_acc < thr);
+  }
+  const uint64_t rej = ballot(reject);
+  const int k = rej ? (int)__builtin_ctzll(rej) : (int)gamma;
+  DrawDesc D;
+  D.k = k;
+  D.mp = (float)__shfl(rmt, k);
+  D.ip = (float)(1.0 / __shfl(rzt, k));
+  const int kq = k < gamma ? k : 0;
+  D.mq = (float)__shfl(rmq, kq);
+  D.iq = (float)(1.0 / __shfl(rzq, kq));
+  D.u = __shfl(u_smp, k);
+  D.xk = k < gamma ? __shfl(xi, k) : -1;
+  D.pad = 0.0f;
+
+  if (c == 0) {
+    if (has_row && lane != k) out_tokens[b * g1 + lane] = lane < k ? xi : -1;
+    if (drafted && out_probs) {
+      out_probs[(b * gamma + lane) * 2 + 0] = p_x;
+      out_probs[(b * gamma + lane) * 2 + 1] = q_x;
+    }
+    if (lane == 0) {
+      out_num[b] = k + 1;
+      ws.desc[b] = D;
+    }
+  }
+  const DrawRow R = make_row<WARP>(target, draft, draft_kind, B, b, gamma, V, D, inv_t, ws);
+  if (active) {
+    const int64_t c0 = c * kDrawChunk;
+    float zp[16], zq[16];
+    load_chunk16<VEC>(R.zp, V, c0, lane, -INFINITY, zp);
+    if (R.zq) load_chunk16<VEC>(R.zq, V, c0, lane, q_probs ? 0.0f : -INFINITY, zq);
+    double sr = 0.0, sp = 0.0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float p, r;
+      weights<WARP>(R, c0 + 256 * (e >> 2) + 4 * lane + (e & 3), zp[e], R.zq ? zq[e] : 0.0f, p, r);
+      sr += (double)r;
+      sp += (double)p;
+    }
+    sr = wave_sum(sr);
+    sp = wave_sum(sp);
+    if (lane == 0) {
+      ws.sres[item] = sr;
+      ws.sp[item] = sp;
+    }
+  }
+  __shared__ int sh_last;
+  __syncthreads();  // every wave's chunk totals are written
+  if (threadIdx.x == 0) {
+    __threadfence();  // release them before counting this workgroup
+    sh_last = atomicAdd(&ws.done[b], 1u) == (unsigned)(gps - 1);
+  }
+  __syncthreads();
+  if (sh_last && wv == 0) {
+    __threadfence();  // acquire the other workgroups' totals
+    select_seq<VEC, WARP>(target, draft, draft_kind, B, b, gamma, V, inv_t, out_tokens, ws, D, lane);
+  }
 }
 
 // 2'. Greedy decide (T == 0): one wave per sequence; lanes run over the chunk
@@ -783,6 +802,7 @@ bool reject_fused_stats(const RejectArgs& a, FusedStats* fs) {
   fs->zx = ws.zx;
   fs->pstride = L.pstride;
   fs->draft = (!greedy && a.draft_kind == 0 && a.gamma > 0) ? a.draft : nullptr;
+  fs->done = greedy ? nullptr : ws.done;
   fs->tokens = a.tokens;
   fs->B = a.B;
   fs->gamma = a.gamma;
@@ -822,18 +842,6 @@ hipError_t launch_decide(const RejectArgs& a, const Ws& ws, hipStream_t stream) 
     if (vec) SPECDEC_DRAW(4, true, false); else SPECDEC_DRAW(4, false, false);
   }
 #undef SPECDEC_DRAW
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 g3(blocks_for(a.B, kWavesPerBlock));
-#define SPECDEC_SELECT(V4, WP)                                                                                  \
-  hipLaunchKernelGGL((select_kernel<V4, WP>), g3, blk, 0, stream, a.target, a.draft, a.draft_kind, a.B, a.gamma, \
-                     a.V, inv_t, a.out_tokens, ws)
-  if (warp) {
-    if (vec) SPECDEC_SELECT(true, true); else SPECDEC_SELECT(false, true);
-  } else {
-    if (vec) SPECDEC_SELECT(true, false); else SPECDEC_SELECT(false, false);
-  }
-#undef SPECDEC_SELECT
   return hipGetLastError();
 }
 
@@ -854,10 +862,10 @@ hipError_t launch_draft_stats(const FusedStats& fs, int64_t n_target, int64_t V,
   const dim3 grid(blocks_for(nd * nch, kWavesPerBlock)), blk(kWavesPerBlock * 64);
   if ((V & 3) == 0)
     hipLaunchKernelGGL((stats_kernel<true, false, false>), grid, blk, 0, stream, nullptr, fs.draft, fs.tokens,
-                       n_target, n_target, n_target + nd, fs.gamma, V, fs.inv_t, ws);
+                       n_target, n_target, n_target + nd, fs.gamma, V, fs.inv_t, ws, (int64_t)0);
   else
     hipLaunchKernelGGL((stats_kernel<false, false, false>), grid, blk, 0, stream, nullptr, fs.draft, fs.tokens,
-                       n_target, n_target, n_target + nd, fs.gamma, V, fs.inv_t, ws);
+                       n_target, n_target, n_target + nd, fs.gamma, V, fs.inv_t, ws, (int64_t)0);
   return hipGetLastError();
 }
 
@@ -904,10 +912,10 @@ hipError_t launch_tree_greedy(const TreeArgs& t, int64_t nparts, hipStream_t str
     const dim3 g1(blocks_for(rows * stat_chunks(t.V), kWavesPerBlock));
     if ((t.V & 3) == 0)
       hipLaunchKernelGGL((stats_kernel<true, true, false>), g1, blk, 0, stream, t.logits, nullptr, nullptr, rows, 0, rows,
-                         (int64_t)0, t.V, 1.0f, ws);
+                         (int64_t)0, t.V, 1.0f, ws, (int64_t)0);
     else
       hipLaunchKernelGGL((stats_kernel<false, true, false>), g1, blk, 0, stream, t.logits, nullptr, nullptr, rows, 0, rows,
-                         (int64_t)0, t.V, 1.0f, ws);
+                         (int64_t)0, t.V, 1.0f, ws, (int64_t)0);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   } else {
@@ -936,7 +944,7 @@ hipError_t launch_reject_sample(const RejectArgs& a, hipStream_t stream) {
   }
 #define SPECDEC_STATS(V4, GR, WP)                                                                                        \
   hipLaunchKernelGGL((stats_kernel<V4, GR, WP>), g1, blk, 0, stream, a.target, a.draft, a.tokens, n_target, 0, n_rows, \
-                     a.gamma, a.V, inv_t, ws)
+                     a.gamma, a.V, inv_t, ws, greedy ? (int64_t)0 : a.B)
   if (greedy) {
     if (vec) SPECDEC_STATS(true, true, false); else SPECDEC_STATS(false, true, false);
   } else if (warp) {
