@@ -47,6 +47,7 @@ constexpr int kDrawChunk = 1024;   // vocabulary entries per draw work item (one
 constexpr int kMergeBatch = 16;    // rows whose argmax partials one wave loads together
 constexpr int kWavesPerBlock = 4;
 constexpr float kQFloor = 1e-12f;
+constexpr float kLog2e = 1.4426950408889634f;
 constexpr int64_t kMaxFusedParts = kFusedStatsMaxParts;
 constexpr int64_t kMaxFusedRows = kFusedStatsMaxRows;
 
@@ -250,17 +251,25 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void stats_kernel(const float*
       ws.zx[r] = (!WARP || warp_kept(order_key(zx), xt, wk, wi)) ? zx : -INFINITY;
     }
   }
-  float mx = -INFINITY;
+  // The chunk max of a = z * fl32(1/T) is fl32(max z * fl32(1/T)) (the product
+  // is monotonic in z).  Each term exp(a - max) is formed as 2^(z * c1 - c2)
+  // with c1 = fl32(1/T) * log2(e), c2 = max * log2(e): one FMA into the
+  // hardware base-2 exponential, its argument rounded about as much as
+  // fl32(z / T) - max is.  Four fp32 terms are added before each fp64 add.
+  float zm = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < PL; ++e) {
-    x[e] = x[e] * inv_t;
-    mx = fmaxf(mx, x[e]);
-  }
-  mx = wave_max(mx);
+  for (int e = 0; e < PL; ++e) zm = fmaxf(zm, x[e]);
+  const float mx = wave_max(zm) * inv_t;
   double sum = 0.0;
-  if (mx > -INFINITY)  // a chunk the warp cut drops whole has no mass
+  if (mx > -INFINITY) {  // a chunk the warp cut drops whole has no mass
+    const float c1 = inv_t * kLog2e, c2 = mx * kLog2e;
 #pragma unroll
-    for (int e = 0; e < PL; ++e) sum += (double)expf(x[e] - mx);
+    for (int e = 0; e < PL; e += 4) {
+      const float s4 = (__builtin_amdgcn_exp2f(fmaf(x[e], c1, -c2)) + __builtin_amdgcn_exp2f(fmaf(x[e + 1], c1, -c2))) +
+                       (__builtin_amdgcn_exp2f(fmaf(x[e + 2], c1, -c2)) + __builtin_amdgcn_exp2f(fmaf(x[e + 3], c1, -c2)));
+      sum += (double)s4;
+    }
+  }
   sum = wave_sum(sum);
   if (lane == 0) {
     ws.cmax[r * ws.pstride + c] = mx;
@@ -269,9 +278,12 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void stats_kernel(const float*
 }
 
 // Merges the partials of row r with one wave: M = max m_c, Z = sum s_c
-// exp(m_c - M) (fp64), and the probability of the drafted token exp(a_x - M)/Z
-// (fp64, rounded once to fp32; 0 for rows without a drafted token).  Partials
-// are read 256 at a time, all loads of a batch issued before any reduction.
+// exp(m_c - M) (fp64 sum; each rescale factor is the hardware base-2
+// exponential of fp32 (m_c - M) * log2(e), relative error about 1e-7 where a
+// partial carries weight), and the probability of the drafted token
+// exp(a_x - M)/Z (fp64, rounded once to fp32; 0 for rows without a drafted
+// token).  Partials are read 256 at a time, all loads of a batch issued before
+// any reduction.
 __device__ __forceinline__ void merge_row(const Ws& ws, int64_t r, bool drafted, int64_t nch, float inv_t, int lane,
                                           double& M_out, double& Z_out, float& px_out) {
   constexpr int kPer = 4;  // partials per lane and batch
@@ -298,7 +310,7 @@ __device__ __forceinline__ void merge_row(const Ws& ws, int64_t r, bool drafted,
     double zb = 0.0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
-      if (cs[j] > 0.0) zb += cs[j] * exp((double)cm[j] - (double)M);
+      if (cs[j] > 0.0) zb += cs[j] * (double)__builtin_amdgcn_exp2f((cm[j] - M) * kLog2e);
     z += wave_sum(zb);
   }
   M_out = (double)M;
@@ -487,9 +499,10 @@ __device__ void select_seq(const float* __restrict__ target, const float* __rest
 //    one sequence.  Its waves first merge the sequence's rows in parallel (one
 //    row per wave at a time) into LDS; after one barrier every wave reads the
 //    statistics of all rows from LDS, lane i <-> row i.  Each workgroup then
-//    counts itself done on the sequence's counter (a device-scope atomic after
-//    a device-scope fence, so its chunk totals are visible first); the last of
-//    them runs the select (3) with one wave.  No workgroup waits for another.
+//    counts itself done on the sequence's counter (a device-scope atomic with
+//    release order, so its chunk totals are visible first); the last of them
+//    acquires and runs the select (3) with one wave.  No workgroup waits for
+//    another.
 constexpr int kMaxRows = 2 * 63 + 1;
 template <int WB, bool VEC, bool WARP>
 __global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
@@ -591,13 +604,12 @@ __global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
   }
   __shared__ int sh_last;
   __syncthreads();  // every wave's chunk totals are written
-  if (threadIdx.x == 0) {
-    __threadfence();  // release them before counting this workgroup
-    sh_last = atomicAdd(&ws.done[b], 1u) == (unsigned)(gps - 1);
-  }
+  if (threadIdx.x == 0)  // counted with release order: the totals are visible before the count
+    sh_last = __hip_atomic_fetch_add(&ws.done[b], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) ==
+              (unsigned)(gps - 1);
   __syncthreads();
   if (sh_last && wv == 0) {
-    __threadfence();  // acquire the other workgroups' totals
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other workgroups' totals
     select_seq<VEC, WARP>(target, draft, draft_kind, B, b, gamma, V, inv_t, out_tokens, ws, D, lane);
   }
 }
