@@ -163,20 +163,23 @@ __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restri
           store4<OUT_BF16>(Y, (size_t)m * V + v0, v0, V, sum);
         else
           store4<false>(part, (size_t)m * V + v0, v0, V, sum);
-        if (EPI == 1) {
-          float a[4], mt = -INFINITY;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            a[j] = sum[j] * fs.inv_t;
-            if (v0 + j < V) mt = fmaxf(mt, a[j]);
-          }
-          if (mt > st_m) {
-            if (st_s > 0.0) st_s *= exp((double)st_m - (double)mt);
-            st_m = mt;
-          }
+        if (EPI == 1) {  // terms 2^(z * c1 - max * log2(e)), c1 = fl32(1/T) * log2(e)
+          constexpr float kLog2e = 1.4426950408889634f;
+          float zt = -INFINITY;
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (v0 + j < V) st_s += (double)expf(a[j] - st_m);
+            if (v0 + j < V) zt = fmaxf(zt, sum[j]);
+          const float mt = zt * fs.inv_t;  // = max of fl32(z * fl32(1/T)) over the four
+          if (mt > st_m) {
+            if (st_s > 0.0) st_s *= (double)__builtin_amdgcn_exp2f((st_m - mt) * kLog2e);
+            st_m = mt;
+          }
+          const float c1 = fs.inv_t * kLog2e, c2 = st_m * kLog2e;
+          float s4 = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (v0 + j < V) s4 += __builtin_amdgcn_exp2f(fmaf(sum[j], c1, -c2));
+          st_s += (double)s4;
         } else if (EPI == 2) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)

@@ -207,7 +207,8 @@ __device__ __forceinline__ void panel_stats(const f32x4 (&acc)[R][NT], uint16_t*
   int* li = (int*)((char*)xs + 12 * NW * kTok);               // [NW][kTok] argmax indices
   const int g1 = (int)fs.gamma + 1;
   __syncthreads();  // every wave is done with the X buffers
-  // Pass 1: per-token maxima (with the lowest index at T == 0) over the wave's rows.
+  // Pass 1: per-token maxima (with the lowest index at T == 0) over the wave's
+  // rows; at T > 0 the max of a = z * fl32(1/T) is fl32(max z * fl32(1/T)).
   float pm[NT];
   int pi[NT];
 #pragma unroll
@@ -219,7 +220,7 @@ __device__ __forceinline__ void panel_stats(const f32x4 (&acc)[R][NT], uint16_t*
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int v = (vt0 + r) * 16 + 4 * g + j;
-        const float a = EPI == 1 ? acc[r][t][j] * fs.inv_t : acc[r][t][j];
+        const float a = acc[r][t][j];
         if (v < V && (a > pm[t] || (EPI == 2 && a == pm[t] && v < pi[t]))) {
           pm[t] = a;
           pi[t] = v;
@@ -235,7 +236,7 @@ __device__ __forceinline__ void panel_stats(const f32x4 (&acc)[R][NT], uint16_t*
       }
     }
     if (g == 0) {
-      lm[wv * kTok + t * 16 + m] = pm[t];
+      lm[wv * kTok + t * 16 + m] = EPI == 1 ? pm[t] * fs.inv_t : pm[t];
       if (EPI == 2) li[wv * kTok + t * 16 + m] = pi[t];
     }
     if (EPI == 1 && t * 16 + m < ncols) {  // the drafted token's logit, from the lane that holds it
@@ -279,7 +280,11 @@ __device__ __forceinline__ void panel_stats(const f32x4 (&acc)[R][NT], uint16_t*
     }
     return;
   }
-  // Pass 2: fp32 exp(a - M) summed in fp64 against the workgroup maximum M of each token.
+  // Pass 2: exp(a - M) against the workgroup maximum M of each token, each term
+  // 2^(z * c1 - c2) with c1 = fl32(1/T) * log2(e), c2 = M * log2(e) (one FMA
+  // into the hardware base-2 exponential); the four terms of a vocabulary tile
+  // are added in fp32, the tiles in fp64.
+  const float c1 = fs.inv_t * 1.4426950408889634f;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     float M = lm[t * 16 + m];
@@ -287,11 +292,16 @@ __device__ __forceinline__ void panel_stats(const f32x4 (&acc)[R][NT], uint16_t*
     for (int w = 1; w < NW; ++w) M = fmaxf(M, lm[w * kTok + t * 16 + m]);
     double ps = 0.0;
     if (M > -INFINITY) {
+      const float c2 = M * 1.4426950408889634f;
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+      for (int r = 0; r < R; ++r) {
+        const int v = (vt0 + r) * 16 + 4 * g;
+        float s4 = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if ((vt0 + r) * 16 + 4 * g + j < V) ps += (double)expf(acc[r][t][j] * fs.inv_t - M);
+          if (v + j < V) s4 += __builtin_amdgcn_exp2f(fmaf(acc[r][t][j], c1, -c2));
+        ps += (double)s4;
+      }
     }
     ps += __shfl_xor(ps, 16);
     ps += __shfl_xor(ps, 32);
