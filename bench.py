@@ -30,8 +30,8 @@ GEMM_SOURCES = [os.path.join(HERE, "speculative_decoding_verification_09_amd", "
 # FETCH_SIZE, 1.0 for WRITE_SIZE).  Keyed by workload, weight layout and the SHA-256 of the GEMM source the
 # counters were taken on: once that source changes, the record no longer describes the kernel and traffic is null.
 MEASURED_TRAFFIC = {
-    ("lmhead_b1_g4", "packed"): {"fetch_bytes": 1051182267, "write_bytes": 2565120,
-                                 "source_sha256": "7f33c36b9ee2543568b65653ae97f3ad16a00ecbbbe554e03ee671892580fdb6"},
+    ("lmhead_b1_g4", "packed"): {"fetch_bytes": 1051163766, "write_bytes": 2565120,
+                                 "source_sha256": "1f93f1b336852fd7aba81f1353f16b27a9aafc496cbaa0eb7316699445a86ea7"},
 }
 
 
