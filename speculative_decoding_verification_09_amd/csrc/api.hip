@@ -13,6 +13,10 @@ constexpr int kVersion = 10200;  // 1.2.0
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Where a step's scoring scratch starts in its workspace: after the sampling
+// arrays, rounded up to 256 bytes.
+size_t stats_scratch_offset(size_t sampling_bytes) { return (sampling_bytes + 255) & ~(size_t)255; }
+
 // Largest sizes the kernels index with 32-bit arithmetic in places.
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 constexpr int64_t kMaxRows = (int64_t)1 << 26;
@@ -146,8 +150,12 @@ size_t specdec_step_workspace_bytes(int64_t B, int64_t gamma, int64_t d, int64_t
   if (B < 1 || B > kMaxRows || gamma < 0 || gamma > SPECDEC_MAX_GAMMA || V < 1 || V > kMaxDim) return 0;
   const int64_t N = B * (gamma + 1);
   if (check_logits_shape(N, d, V, weight_layout) != SPECDEC_OK) return 0;
-  const size_t r = specdec::reject_workspace_bytes(B, gamma, V);
-  const size_t g = specdec::gemm_workspace_bytes(N, d, V, weight_layout == SPECDEC_WEIGHTS_PACKED);
+  const bool packed = weight_layout == SPECDEC_WEIGHTS_PACKED;
+  // The fused path keeps the scoring kernel's scratch after the sampling
+  // arrays; the unfused one runs the two passes one after the other.
+  const size_t r = stats_scratch_offset(specdec::reject_workspace_bytes(B, gamma, V)) +
+                   (packed ? specdec::gemm_stats_scratch_bytes(N, d, V) : 0);
+  const size_t g = specdec::gemm_workspace_bytes(N, d, V, packed);
   return r > g ? r : g;
 }
 
@@ -251,8 +259,9 @@ int specdec_verify_step(const void* X, const void* W, int weight_layout, const f
   if (weight_layout == SPECDEC_WEIGHTS_PACKED && specdec::reject_fused_stats(a, &fs) &&
       specdec::gemm_stats_parts(N, d, V, fs.pstride) > 0) {
     int64_t nparts = 0, nparts_draft = 0;
+    void* scratch = (char*)workspace + stats_scratch_offset(specdec::reject_workspace_bytes(B, gamma, V));
     if (specdec::launch_gemm_with_stats((const uint16_t*)X, (const uint16_t*)W, logits, N, d, V, fs, &nparts,
-                                        &nparts_draft, s) != hipSuccess)
+                                        &nparts_draft, scratch, s) != hipSuccess)
       return SPECDEC_ERR_LAUNCH;
     return specdec::launch_reject_after_fused(a, nparts, nparts_draft, s) == hipSuccess ? SPECDEC_OK
                                                                                          : SPECDEC_ERR_LAUNCH;
@@ -329,8 +338,10 @@ int specdec_tree_verify_greedy(const float* target_logits, const int32_t* parent
 size_t specdec_tree_step_workspace_bytes(int64_t B, int64_t M, int64_t d, int64_t V, int weight_layout) {
   if (B < 1 || B > kMaxRows || M < 1 || M > SPECDEC_MAX_TREE_NODES || V < 1 || V > kMaxDim) return 0;
   if (check_logits_shape(B * M, d, V, weight_layout) != SPECDEC_OK) return 0;
-  const size_t r = specdec::tree_workspace_bytes(B, M, V);
-  const size_t g = specdec::gemm_workspace_bytes(B * M, d, V, weight_layout == SPECDEC_WEIGHTS_PACKED);
+  const bool packed = weight_layout == SPECDEC_WEIGHTS_PACKED;
+  const size_t r = stats_scratch_offset(specdec::tree_workspace_bytes(B, M, V)) +
+                   (packed ? specdec::gemm_stats_scratch_bytes(B * M, d, V) : 0);
+  const size_t g = specdec::gemm_workspace_bytes(B * M, d, V, packed);
   return r > g ? r : g;
 }
 
@@ -353,8 +364,9 @@ int specdec_tree_verify_step(const void* X, const void* W, int weight_layout, co
   if (weight_layout == SPECDEC_WEIGHTS_PACKED && specdec::tree_fused_stats(t, &fs) &&
       specdec::gemm_stats_parts(N, d, V, fs.pstride) > 0) {
     int64_t nparts = 0, nparts_draft = 0;
+    void* scratch = (char*)workspace + stats_scratch_offset(specdec::tree_workspace_bytes(B, M, V));
     if (specdec::launch_gemm_with_stats((const uint16_t*)X, (const uint16_t*)W, logits, N, d, V, fs, &nparts,
-                                        &nparts_draft, s) != hipSuccess)
+                                        &nparts_draft, scratch, s) != hipSuccess)
       return SPECDEC_ERR_LAUNCH;
     return specdec::launch_tree_greedy(t, nparts, s) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
   }

@@ -480,6 +480,164 @@ __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restri
   }
 }
 
+// Deep panel kernel, for many positions, where the work is bound by the matrix
+// cores rather than by HBM.  One wave per SIMD: the four waves of a block share
+// a token pass of NT*16 positions staged through LDS, each wave owns R
+// vocabulary tiles, and its R x NT accumulator tiles live in the matrix-core
+// registers.  Each step is one MFMA k-step (32 k) and one barrier; the W
+// fragments of the next D-1 steps and the X rows of the next F steps are in
+// flight in registers meanwhile, so that a load has D-1 (W) or F (X) steps of
+// matrix work to arrive in.  Work items and their order on the XCDs are those
+// of the panel kernel, with k-groups of cpk steps; W loads are nontemporal
+// only when a single token pass reads W (NTL), since with several passes the
+// passes of one vocabulary block share W through the XCD's L2.
+template <int NT, int R, int D, int F, bool NTL, bool OUT_BF16, int EPI, bool PX = false>
+__global__ __launch_bounds__(256) void deep_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp,
+                                                   void* __restrict__ Y, int N, int d, int V, int npass, int cpk,
+                                                   FusedStats fs) {
+  constexpr int NW = 4, kThreads = NW * 64;
+  constexpr int kXPT = NT / 4;  // 16-byte X units per thread per step
+  static_assert(NT % 4 == 0 && D == 4 && F == D, "deep kernel ring shapes");
+  constexpr int kBufElems = NT * 512;  // bf16 per LDS buffer: NT fragments of 16 x 32
+  extern __shared__ __align__(16) uint16_t xs[];
+
+  const int nsteps = d >> 5;
+  const int ntiles = (V + 15) >> 4;
+  const int nvb = (ntiles + NW * R - 1) / (NW * R);
+  const int ngroups = (nsteps + cpk - 1) / cpk;
+  const int id = (int)blockIdx.x;
+  if (EPI == 1 && fs.done != nullptr) {  // the draw kernel's counters, for the step that follows
+    const int64_t gid = (int64_t)id * kThreads + threadIdx.x;
+    if (gid < fs.B) fs.done[gid] = 0u;
+  }
+  const int slot = id >> 3;
+  const int gi = (id & 7) + 8 * (slot / npass);
+  if (gi >= nvb * ngroups) return;
+  const int vb = gi % nvb, group = gi / nvb;
+  const int s0 = group * cpk, s1 = min(s0 + cpk, nsteps);
+  const int n0 = (slot % npass) * NT * 16;
+  const int ncols = min(N - n0, NT * 16);
+
+  const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, g = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int vt0 = vb * NW * R + wv * R;
+
+  // Loads are issued without conditions, steps past the group's end clamped
+  // to its last step (such values are never used), so that the compiler
+  // counts outstanding loads exactly.  X unit u = tid + 256 j: token tile
+  // u / 64, lane position u % 64; rows past N read row N-1.
+  const uint16_t* xrow[kXPT];
+#pragma unroll
+  for (int j = 0; j < kXPT; ++j) {
+    const int u = tid + j * kThreads, l = u & 63;
+    if (PX) {
+      const int tile = min((n0 >> 4) + (u >> 6), ((N + 15) >> 4) - 1);
+      xrow[j] = X + (size_t)tile * nsteps * 512 + l * 8;
+    } else {
+      const int n = min(n0 + (u >> 6) * 16 + (l & 15), N - 1);
+      xrow[j] = X + (size_t)n * d + 8 * (l >> 4);
+    }
+  }
+  auto load_x = [&](u32x4(&dst)[kXPT], int s) {
+    const int sc = min(s, s1 - 1) * (PX ? 512 : 32);
+#pragma unroll
+    for (int j = 0; j < kXPT; ++j) dst[j] = *(const u32x4*)(xrow[j] + sc);
+  };
+  auto store_x = [&](const u32x4(&src)[kXPT], int buf) {
+#pragma unroll
+    for (int j = 0; j < kXPT; ++j) *(u32x4*)(xs + buf * kBufElems + (tid + j * kThreads) * 8) = src[j];
+  };
+  const uint16_t* wrow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) wrow[r] = Wp + (size_t)min(vt0 + r, ntiles - 1) * nsteps * 512;
+  auto load_w = [&](u32x4(&dst)[R], int s) {
+    const int off = min(s, s1 - 1) * 512 + lane * 8;
+#pragma unroll
+    for (int r = 0; r < R; ++r) dst[r] = load_w16<NTL>(wrow[r] + off);
+  };
+
+  f32x4 acc[R][NT];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Step i (from s0) uses W ring slot i % D; X of step j is staged in
+  // register slot j % F.
+  u32x4 wr[D][R], xr[F][kXPT], bf[2][NT];
+  auto read_b = [&](u32x4(&dst)[NT], int buf) {
+    const uint16_t* xb = xs + buf * kBufElems + lane * 8;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) dst[t] = *(const u32x4*)(xb + t * 512);
+  };
+  auto mfmas = [&](const u32x4(&wa)[R], const u32x4(&b)[NT]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r][t] = mfma(wa[r], b[t], acc[r][t]);
+  };
+  // X of step j goes to LDS buffer j % 4 three steps ahead (at step j - 3) and
+  // its B fragments are read into registers one step ahead (at step j - 1);
+  // the workgroup meets at a barrier after every odd step only, which is
+  // enough: a store and its reads are always separated by one, and so are the
+  // reads of a buffer and its next store, four steps on.
+  //
+  // Prologue: X of steps 0 to 2 into LDS, then the loads in flight at the top
+  // of every trip, in the order the trips issue them (W of step j, then X of
+  // step j + 3), so that the compiler's wait counts at the loop head are those
+  // of the steady state.
+#pragma unroll
+  for (int j = 0; j < 3; ++j) load_x(xr[j], s0 + j);
+#pragma unroll
+  for (int j = 0; j < 3; ++j) store_x(xr[j], j);
+  __syncthreads();
+  read_b(bf[0], 0);
+  __syncthreads();  // buffer 0 is stored again at step 1
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    load_w(wr[j], s0 + j);
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(xr[(j + 3) % F], s0 + j + 3);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // One step; I = i % D is a compile-time index.  Steps past the group's end
+  // (in its last trip) skip their MFMAs only.
+  auto step = [&](auto I_, int s) {
+    constexpr int I = decltype(I_)::value;
+    read_b(bf[(I + 1) & 1], (I + 1) & 3);  // X of step s + 1
+    __builtin_amdgcn_sched_barrier(0);     // issue those reads before the MFMAs
+    if (s < s1) mfmas(wr[I], bf[I & 1]);
+    load_w(wr[I], s + D);
+    store_x(xr[(I + 3) % F], (I + 3) & 3);  // X of step s + 3
+    load_x(xr[(I + 3) % F], s + 3 + F);
+    if (I & 1) __syncthreads();
+  };
+  for (int s = s0; s < s1; s += D) {
+    step(std::integral_constant<int, 0>{}, s);
+    step(std::integral_constant<int, 1>{}, s + 1);
+    step(std::integral_constant<int, 2>{}, s + 2);
+    step(std::integral_constant<int, 3>{}, s + 3);
+  }
+
+  if (EPI != 0) panel_stats<NT, R, NW, EPI>(acc, xs, fs, N, V, n0, ncols, vt0, vb, wv, lane);
+
+  const bool split = ngroups > 1;
+  float* part = (float*)Y + (size_t)group * N * V;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t v0 = (int64_t)(vt0 + r) * 16 + 4 * g;
+    if (v0 >= V) continue;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int n = t * 16 + m;
+      if (n >= ncols) continue;
+      if (split)
+        store4<false>(part, (size_t)(n0 + n) * V + v0, v0, V, acc[r][t]);
+      else
+        store4<OUT_BF16>(Y, (size_t)(n0 + n) * V + v0, v0, V, acc[r][t]);
+    }
+  }
+}
+
 // Sums the k-group partials P [groups][N][V] in group order into Y.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, void* __restrict__ Y,
@@ -568,9 +726,32 @@ hipError_t launch_panel(const PanelPlan& p, const uint16_t* X, const uint16_t* W
   return hipGetLastError();
 }
 
+// The deep kernel takes a plan from plan_panel with NW = 4 and KS = 1 (its
+// chunks are single k-steps).
+template <int NT, int R, int D, bool PX = false>
+hipError_t launch_deep(const PanelPlan& p, const uint16_t* X, const uint16_t* Wp, void* Y, int64_t N, int64_t d,
+                       int64_t V, bool out_bf16, hipStream_t stream, const FusedStats* fs = nullptr) {
+  constexpr size_t kLds = 4ull * NT * 1024;
+  static_assert((size_t)4 * NT * 16 * 16 <= kLds, "deep statistics LDS");
+  auto pick = [&](auto ntl) {
+    constexpr bool L = decltype(ntl)::value;
+    auto k = out_bf16 ? deep_kernel<NT, R, D, D, L, true, 0, PX> : deep_kernel<NT, R, D, D, L, false, 0, PX>;
+    if (fs) k = fs->greedy ? deep_kernel<NT, R, D, D, L, false, 2, PX> : deep_kernel<NT, R, D, D, L, false, 1, PX>;
+    return k;
+  };
+  auto k = p.npass == 1 ? pick(std::true_type{}) : pick(std::false_type{});
+  hipError_t e = allow_lds(k, kLds);
+  if (e != hipSuccess) return e;
+  const FusedStats none{};
+  hipLaunchKernelGGL(k, dim3((unsigned)p.grid), dim3(256), kLds, stream, X, Wp, Y, (int)N, (int)d, (int)V,
+                     (int)p.npass, (int)p.cpk, fs ? *fs : none);
+  return hipGetLastError();
+}
+
 // The panel configurations the dispatcher uses, by N (chosen by measurement).
 struct PanelShape {
   int NT, R, NW, KS;
+  bool deep = false;  // deep kernel (NW = 4, KS = 1) over packed X
 };
 // Shapes (token tiles x vocabulary tiles per wave, waves, k-steps per chunk)
 // chosen from timings of every candidate on the LM heads (V = 128256 and
@@ -582,6 +763,9 @@ struct PanelShape {
 // still the fastest there), so the statistics epilogue never uses it.
 PanelShape panel_shape(int64_t N, int64_t d, int64_t V, bool with_stats) {
   const bool big_v = V >= 65536;
+  // Past 64 positions, with d a multiple of 128 (whole trips of four k-steps),
+  // the deep kernel: 128 x 64 tiles per wave, one wave per SIMD.
+  if (N > 64 && d % 128 == 0) return PanelShape{8, 4, 4, 1, true};
   if (N <= 64) {
     if (!big_v) return N <= 32 ? PanelShape{4, 1, 8, 4} : PanelShape{4, 2, 8, 2};
     return d <= 4096 ? PanelShape{4, 2, 8, 2} : PanelShape{4, 4, 8, 2};
@@ -593,6 +777,7 @@ PanelShape panel_shape(int64_t N, int64_t d, int64_t V, bool with_stats) {
 hipError_t launch_panel_shape(const PanelShape& s, const PanelPlan& p, const uint16_t* X, const uint16_t* Wp, void* Y,
                               int64_t N, int64_t d, int64_t V, bool out_bf16, hipStream_t stream,
                               const FusedStats* fs = nullptr) {
+  if (s.deep) return launch_deep<8, 4, 4, true>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);
   if (s.NT == 4 && s.R == 1) return launch_panel<4, 1, 8, 4>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);
   if (s.NT == 4 && s.R == 2) return launch_panel<4, 2, 8, 2>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);
   if (s.NT == 4) return launch_panel<4, 4, 8, 2>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);
@@ -601,12 +786,21 @@ hipError_t launch_panel_shape(const PanelShape& s, const PanelPlan& p, const uin
   return launch_panel<8, 4, 8, 2>(p, X, Wp, Y, N, d, V, out_bf16, stream, nullptr);
 }
 
-// What the dispatcher will run for a shape, and the workspace it needs.
+// The deep kernel's copy of X: ceil(N / 16) 16-row tiles in the packed
+// weight layout (one 1 KB block per tile and k-step), so that its X loads are
+// whole 1 KB blocks like its W loads.
+size_t xpack_bytes(int64_t N, int64_t d) {
+  return ((size_t)((N + 15) / 16) * 16 * d * sizeof(uint16_t) + 255) & ~(size_t)255;
+}
+
+// What the dispatcher will run for a shape, and the workspace it needs: the
+// packed X (deep kernel), then the k-group partials.
 struct GemmPlan {
   enum Kind { kSweep, kPanel, kTiled } kind;
   SweepPlan sweep;
   PanelShape shape;
   PanelPlan panel;
+  size_t xpack;  // bytes of packed X at the start of the workspace
   size_t workspace;
 };
 
@@ -625,7 +819,16 @@ GemmPlan plan_gemm(int64_t N, int64_t d, int64_t V, bool packed, bool with_stats
   g.kind = GemmPlan::kPanel;
   g.shape = panel_shape(N, d, V, with_stats);
   g.panel = plan_panel(N, d, V, g.shape.NT, g.shape.R, g.shape.NW, g.shape.KS, cus);
-  if (g.panel.groups > 1) g.workspace = (size_t)g.panel.groups * N * V * sizeof(float);
+  if (g.shape.deep) {
+    // k-groups of whole trips of four k-steps.
+    const int64_t nsteps = d / 32, ntiles = (V + 15) / 16, nvb = (ntiles + 15) / 16;
+    g.panel.cpk = (g.panel.cpk + 3) / 4 * 4;
+    g.panel.groups = (nsteps + g.panel.cpk - 1) / g.panel.cpk;
+    g.panel.grid = 8 * ((nvb * g.panel.groups + 7) / 8) * g.panel.npass;
+    g.xpack = xpack_bytes(N, d);
+  }
+  g.workspace = g.xpack;
+  if (g.panel.groups > 1) g.workspace += (size_t)g.panel.groups * N * V * sizeof(float);
   return g;
 }
 
@@ -646,12 +849,23 @@ int64_t gemm_stats_parts(int64_t N, int64_t d, int64_t V, int64_t pstride) {
   return parts > 0 && parts <= kFusedStatsMaxParts && parts <= pstride ? parts : 0;
 }
 
+size_t gemm_stats_scratch_bytes(int64_t N, int64_t d, int64_t V) {
+  return gemm::plan_gemm(N, d, V, true, true).xpack;
+}
+
 hipError_t launch_gemm_with_stats(const uint16_t* X, const uint16_t* Wp, float* Y, int64_t N, int64_t d, int64_t V,
-                                  const FusedStats& fs, int64_t* nparts, int64_t* nparts_draft, hipStream_t stream) {
+                                  const FusedStats& fs, int64_t* nparts, int64_t* nparts_draft, void* scratch,
+                                  hipStream_t stream) {
   using namespace gemm;
   const int64_t parts = gemm_stats_parts(N, d, V, fs.pstride);
   if (parts == 0) return hipErrorNotSupported;
   const GemmPlan g = plan_gemm(N, d, V, true, true);
+  if (g.xpack > 0) {
+    if (scratch == nullptr) return hipErrorInvalidValue;
+    const hipError_t e = launch_pack_weights(X, (uint16_t*)scratch, N, d, stream);
+    if (e != hipSuccess) return e;
+    X = (const uint16_t*)scratch;
+  }
   if (g.kind == GemmPlan::kSweep) {
     // The sweep kernel also summarises the (at most 7) draft rows itself, in
     // the same slots as the target rows.
@@ -690,9 +904,15 @@ hipError_t launch_skinny_gemm(const uint16_t* X, const uint16_t* W, void* Y, int
       return launch_sweep(g.sweep, X, W, Y, N, d, V, out_bf16, stream);
     }
     case GemmPlan::kPanel: {
+      if (g.xpack > 0) {
+        const hipError_t e = launch_pack_weights(X, (uint16_t*)workspace, N, d, stream);
+        if (e != hipSuccess) return e;
+        X = (const uint16_t*)workspace;
+      }
+      float* part = (float*)((char*)workspace + g.xpack);
       if (g.panel.groups == 1) return launch_panel_shape(g.shape, g.panel, X, W, Y, N, d, V, out_bf16, stream);
-      hipError_t e = launch_panel_shape(g.shape, g.panel, X, W, workspace, N, d, V, false, stream);
-      return e != hipSuccess ? e : launch_reduce((const float*)workspace, Y, N, V, g.panel.groups, out_bf16, stream);
+      hipError_t e = launch_panel_shape(g.shape, g.panel, X, W, part, N, d, V, false, stream);
+      return e != hipSuccess ? e : launch_reduce(part, Y, N, V, g.panel.groups, out_bf16, stream);
     }
     default:
       break;

@@ -86,7 +86,7 @@ hipError_t launch_warp_cuts(const float* target, const float* draft, int64_t n_t
 // epilogue: for every row, one partial per workgroup of that kernel, in the
 // reject workspace's partial slots.  Target rows are [0, B*(gamma+1)), draft
 // rows B*(gamma+1) + b*gamma + i.
-constexpr int64_t kFusedStatsMaxParts = 512;  // workgroups (partials per row)
+constexpr int64_t kFusedStatsMaxParts = 1024;  // workgroups (partials per row)
 constexpr int64_t kFusedStatsMaxRows = 512;   // B*(gamma+1)
 struct FusedStats {
   float* cmax;            // [row][pstride]: max of z/T (greedy: max of z)
@@ -112,13 +112,18 @@ hipError_t launch_draft_stats(const FusedStats& fs, int64_t n_target, int64_t V,
 // Partials per row that launch_gemm_with_stats will produce for this shape
 // (0: the shape does not take the statistics epilogue).
 int64_t gemm_stats_parts(int64_t N, int64_t d, int64_t V, int64_t pstride);
-// The scoring GEMM with the statistics epilogue (packed W, sweep or panel
-// kernel without k-groups, at most kFusedStatsMaxParts partials per row); the
-// same launch summarises the draft rows.  Returns the partial counts of target
-// and draft rows, or hipErrorNotSupported, launching nothing, for shapes it
-// does not take.
+// Device scratch that launch_gemm_with_stats needs for this shape (the packed
+// copy of X of the deep kernel; 0 for the other kernels), 256-byte multiple.
+size_t gemm_stats_scratch_bytes(int64_t N, int64_t d, int64_t V);
+// The scoring GEMM with the statistics epilogue (packed W, sweep, panel or
+// deep kernel without k-groups, at most kFusedStatsMaxParts partials per row);
+// the same launch summarises the draft rows.  scratch: at least
+// gemm_stats_scratch_bytes, disjoint from the statistics arrays.  Returns the
+// partial counts of target and draft rows, or hipErrorNotSupported, launching
+// nothing, for shapes it does not take.
 hipError_t launch_gemm_with_stats(const uint16_t* X, const uint16_t* Wp, float* Y, int64_t N, int64_t d, int64_t V,
-                                  const FusedStats& fs, int64_t* nparts, int64_t* nparts_draft, hipStream_t stream);
+                                  const FusedStats& fs, int64_t* nparts, int64_t* nparts_draft, void* scratch,
+                                  hipStream_t stream);
 
 // Tree verification (greedy), M <= 64 nodes per tree.
 struct TreeArgs {

@@ -186,9 +186,9 @@ def test_python_binding_rejects_host_tensors():
 
 
 def test_workspace_size_queries():
-    """The scoring GEMM needs no workspace at the LM-head shapes; shapes with few output rows and a long k range
-    (the projection that maps 28672 inputs to 8192 outputs) split k and keep fp32 partials; the step's workspace
-    covers both stages."""
+    """The scoring GEMM needs no workspace at the LM-head shapes up to 64 positions; shapes with few output rows
+    and a long k range (the projection that maps 28672 inputs to 8192 outputs) split k and keep fp32 partials;
+    the deep kernel keeps a packed copy of X; the step's workspace covers both stages."""
     PK, RM = sd.SPECDEC_WEIGHTS_PACKED, sd.SPECDEC_WEIGHTS_ROW_MAJOR
     assert sd.logits_workspace_bytes(5, 4096, 128256, PK) == 0
     assert sd.logits_workspace_bytes(64, 8192, 128256, PK) == 0
@@ -198,9 +198,15 @@ def test_workspace_size_queries():
         assert need > 0 and need % (N * 8192 * 4) == 0
     assert sd.logits_workspace_bytes(0, 4096, 100, PK) == 0
     assert sd.logits_workspace_bytes(5, 4100, 100, PK) == 0  # packed needs d % 32 == 0
-    assert sd.step_workspace_bytes(1, 4, 4096, 128256, PK) == sd.workspace_bytes(1, 4, 128256)
+    up = lambda n: (n + 255) // 256 * 256
+    assert sd.step_workspace_bytes(1, 4, 4096, 128256, PK) == up(sd.workspace_bytes(1, 4, 128256))
     big = sd.logits_workspace_bytes(56, 28672, 8192, PK)
-    assert sd.step_workspace_bytes(7, 7, 28672, 8192, PK) == max(big, sd.workspace_bytes(7, 7, 8192))
+    assert sd.step_workspace_bytes(7, 7, 28672, 8192, PK) == max(big, up(sd.workspace_bytes(7, 7, 8192)))
+    # Past 64 positions (d % 128 == 0) the deep kernel reads a packed copy of X: N x d bf16 of scratch,
+    # after the sampling arrays when the step fuses the statistics.
+    assert sd.logits_workspace_bytes(128, 4096, 128256, PK) == 128 * 4096 * 2
+    assert sd.logits_workspace_bytes(130, 4096, 128256, PK) == 144 * 4096 * 2
+    assert sd.step_workspace_bytes(16, 7, 4096, 128256, PK) == up(sd.workspace_bytes(16, 7, 128256)) + 128 * 4096 * 2
     assert sd.step_workspace_bytes(0, 4, 4096, 100, PK) == 0
 
 
@@ -234,4 +240,4 @@ def test_tree_argument_checks():
     assert tv(logits=A + 4) == 3
     assert tv(wb=ws - 1) == 5
     assert sd.tree_step_workspace_bytes(1, 16, 4096, 128256, sd.SPECDEC_WEIGHTS_PACKED) == \
-        sd.tree_workspace_bytes(1, 16, 128256)
+        (sd.tree_workspace_bytes(1, 16, 128256) + 255) // 256 * 256

@@ -26,15 +26,17 @@ SHAPES = [
     (100, 1024, 2053), (200, 320, 515), (320, 136, 300), (513, 96, 129), (1, 4104, 4099),
 ]
 # Packed weights (d % 32 == 0).  Covers the sweep kernel (long vocabularies,
-# N <= 16, X whole in LDS: up to 16 positions, vocabulary tails), and every
-# panel shape (4x1, 4x2, 4x4, 8x2, 8x4 token x vocabulary tiles per wave) with
-# and without k-groups, k-step counts that leave waves idle or partly filled
-# (d = 96, 5120), vocabulary tails.
+# N <= 16, X whole in LDS: up to 16 positions, vocabulary tails), every panel
+# shape (4x1, 4x2, 4x4, 8x2, 8x4 token x vocabulary tiles per wave) and the
+# deep kernel, with and without k-groups, k-step counts that leave waves idle
+# or partly filled (d = 96, 5120), vocabulary tails.
 PACKED_SHAPES = [
     (1, 64, 17), (5, 4096, 1000), (5, 8192, 515), (3, 5120, 513), (7, 96, 50), (16, 4096, 300),
     (16, 32, 16), (8, 28672, 40), (17, 256, 1000), (33, 512, 777), (64, 1024, 1030), (100, 512, 2053),
     (200, 320, 515), (513, 96, 129), (16, 256, 65541), (9, 4096, 65536), (12, 1024, 70001),
     (40, 1024, 66000), (8, 4128, 65536), (120, 256, 65541), (130, 128, 65536),
+    # the deep kernel (N > 64, d % 128 == 0): several trips, k-groups, token passes, tails
+    (96, 4096, 3000), (300, 1024, 4100), (65, 384, 1029), (512, 256, 2000),
 ]
 
 

@@ -149,6 +149,10 @@ FUSED = [
     # long vocabularies, up to 16 positions: the sweep kernel's epilogue (draft rows in its spare workgroups)
     ("sweep_logits", 1, 4, 256, 65600, 1.0), ("sweep_16", 2, 7, 128, 66001, 0.9), ("sweep_greedy", 3, 4, 64, 65536, 0.0),
     ("sweep_probs", 2, 3, 128, 65541, 1.0), ("sweep_onehot", 2, 5, 128, 65600, 1.0),
+    # past 64 positions with d % 128 == 0: the deep kernel's epilogue (packed X in the scratch)
+    ("deep_greedy", 20, 4, 128, 3001, 0.0), ("deep_logits", 24, 5, 256, 5000, 1.0),
+    ("deep_probs", 16, 7, 384, 4099, 0.8), ("deep_onehot", 33, 3, 128, 2050, 1.2),
+    ("deep_passes_greedy", 64, 4, 128, 1500, 0.0),
 ]
 
 
