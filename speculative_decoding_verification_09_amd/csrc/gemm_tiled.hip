@@ -763,9 +763,11 @@ struct PanelShape {
 // still the fastest there), so the statistics epilogue never uses it.
 PanelShape panel_shape(int64_t N, int64_t d, int64_t V, bool with_stats) {
   const bool big_v = V >= 65536;
-  // Past 64 positions, with d a multiple of 128 (whole trips of four k-steps),
-  // the deep kernel: 128 x 64 tiles per wave, one wave per SIMD.
-  if (N > 64 && d % 128 == 0) return PanelShape{8, 4, 4, 1, true};
+  // With d a multiple of 128 (whole trips of four k-steps), the deep kernel
+  // (128 x 64 tiles per wave, one wave per SIMD) past 128 positions, and past
+  // 64 with the statistics epilogue; at 65 to 128 positions without it the
+  // 8x4 and 8x2 panels measured as fast or faster.
+  if (d % 128 == 0 && (N > 128 || (N > 64 && with_stats))) return PanelShape{8, 4, 4, 1, true};
   if (N <= 64) {
     if (!big_v) return N <= 32 ? PanelShape{4, 1, 8, 4} : PanelShape{4, 2, 8, 2};
     return d <= 4096 ? PanelShape{4, 2, 8, 2} : PanelShape{4, 4, 8, 2};

@@ -202,9 +202,10 @@ def test_workspace_size_queries():
     assert sd.step_workspace_bytes(1, 4, 4096, 128256, PK) == up(sd.workspace_bytes(1, 4, 128256))
     big = sd.logits_workspace_bytes(56, 28672, 8192, PK)
     assert sd.step_workspace_bytes(7, 7, 28672, 8192, PK) == max(big, up(sd.workspace_bytes(7, 7, 8192)))
-    # Past 64 positions (d % 128 == 0) the deep kernel reads a packed copy of X: N x d bf16 of scratch,
-    # after the sampling arrays when the step fuses the statistics.
-    assert sd.logits_workspace_bytes(128, 4096, 128256, PK) == 128 * 4096 * 2
+    # The deep kernel (d % 128 == 0; past 128 positions, or past 64 with the step's statistics) reads a packed
+    # copy of X: N x d bf16 (N rounded up to 16) of scratch, after the sampling arrays when the step fuses the
+    # statistics.
+    assert sd.logits_workspace_bytes(128, 4096, 128256, PK) == 0
     assert sd.logits_workspace_bytes(130, 4096, 128256, PK) == 144 * 4096 * 2
     assert sd.step_workspace_bytes(16, 7, 4096, 128256, PK) == up(sd.workspace_bytes(16, 7, 128256)) + 128 * 4096 * 2
     assert sd.step_workspace_bytes(0, 4, 4096, 100, PK) == 0

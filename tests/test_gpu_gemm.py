@@ -35,8 +35,8 @@ PACKED_SHAPES = [
     (16, 32, 16), (8, 28672, 40), (17, 256, 1000), (33, 512, 777), (64, 1024, 1030), (100, 512, 2053),
     (200, 320, 515), (513, 96, 129), (16, 256, 65541), (9, 4096, 65536), (12, 1024, 70001),
     (40, 1024, 66000), (8, 4128, 65536), (120, 256, 65541), (130, 128, 65536),
-    # the deep kernel (N > 64, d % 128 == 0): several trips, k-groups, token passes, tails
-    (96, 4096, 3000), (300, 1024, 4100), (65, 384, 1029), (512, 256, 2000),
+    # the deep kernel (N > 128, d % 128 == 0): several trips, k-groups, token passes, tails
+    (96, 4096, 3000), (300, 1024, 4100), (65, 384, 1029), (512, 256, 2000), (129, 4096, 1000), (160, 8192, 700),
 ]
 
 
