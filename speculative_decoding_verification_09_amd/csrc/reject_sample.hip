@@ -44,7 +44,7 @@ namespace {
 
 constexpr int kStatChunk = 2048;   // vocabulary entries per statistics work item (one wave)
 constexpr int kDrawChunk = 1024;   // vocabulary entries per draw work item (one wave)
-constexpr int kMergeBatch = 16;    // rows whose argmax partials one wave loads together
+constexpr int kGreedyWaves = 8;    // waves of the greedy rule's workgroup (one per sequence)
 constexpr int kWavesPerBlock = 4;
 constexpr float kQFloor = 1e-12f;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -614,47 +614,51 @@ __global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
   }
 }
 
-// 2'. Greedy decide (T == 0): one wave per sequence; lanes run over the chunk
-//     partials of each row in turn (all loads of a batch issued first), then
-//     lane i holds row i's argmax.
-__global__ __launch_bounds__(kWavesPerBlock * 64) void greedy_kernel(const int32_t* __restrict__ tokens, int64_t B,
-                                                                      int64_t gamma, int64_t V,
-                                                                      int32_t* __restrict__ out_tokens,
-                                                                      int32_t* __restrict__ out_num, Ws ws) {
-  const int lane = threadIdx.x & 63;
-  const int64_t b = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (b >= B) return;
+// 2'. Greedy decide (T == 0): one workgroup per sequence.  Wave w merges the
+//     chunk partials of rows w, w + kGreedyWaves, ... (each lane issuing four
+//     loads at a time), leaving row i's argmax in LDS; wave 0 then compares
+//     the drafted tokens with them, lane i <-> row i.
+__global__ __launch_bounds__(kGreedyWaves * 64) void greedy_kernel(const int32_t* __restrict__ tokens, int64_t B,
+                                                                    int64_t gamma, int64_t V,
+                                                                    int32_t* __restrict__ out_tokens,
+                                                                    int32_t* __restrict__ out_num, Ws ws) {
+  __shared__ int sh_best[64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t b = blockIdx.x;
   const int64_t g1 = gamma + 1;
   const int64_t nch = ws.nparts;
-  const bool drafted = lane < gamma;
-  const int xi = drafted ? clamp_token(tokens[b * gamma + lane], V) : 0;
-  int mine = 0;
-  for (int r0 = 0; r0 < g1; r0 += kMergeBatch) {
-    float cv[kMergeBatch];
-    int ci[kMergeBatch];
+  for (int64_t r = w; r < g1; r += kGreedyWaves) {
+    const size_t base = (size_t)(b * g1 + r) * ws.pstride;
+    float cv = -INFINITY;
+    int ci = 0x7fffffff;
+    for (int64_t c0 = 0; c0 < nch; c0 += 4 * 64) {
+      float v[4];
+      int ix[4];
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      cv[j] = -INFINITY;
-      ci[j] = 0x7fffffff;
-      if (r0 + j < g1) {
-        const size_t base = (size_t)(b * g1 + r0 + j) * ws.pstride;
-        for (int64_t c = lane; c < nch; c += 64) {
-          const float v = ws.cmax[base + c];
-          const int ix = ws.cidx[base + c];
-          if (v > cv[j] || (v == cv[j] && ix < ci[j])) {
-            cv[j] = v;
-            ci[j] = ix;
-          }
+      for (int u = 0; u < 4; ++u) {
+        const int64_t c = c0 + u * 64 + lane;
+        v[u] = -INFINITY;
+        ix[u] = 0x7fffffff;
+        if (c < nch) {
+          v[u] = ws.cmax[base + c];
+          ix[u] = ws.cidx[base + c];
         }
       }
-    }
 #pragma unroll
-    for (int j = 0; j < kMergeBatch; ++j) {
-      if (r0 + j >= g1) break;
-      wave_argmax(cv[j], ci[j]);
-      if (lane == r0 + j) mine = (ci[j] >= 0 && ci[j] < V) ? ci[j] : 0;  // all-NaN row: any in-range id
+      for (int u = 0; u < 4; ++u)
+        if (v[u] > cv || (v[u] == cv && ix[u] < ci)) {
+          cv = v[u];
+          ci = ix[u];
+        }
     }
+    wave_argmax(cv, ci);
+    if (lane == 0) sh_best[r] = (ci >= 0 && ci < V) ? ci : 0;  // all-NaN row: any in-range id
   }
+  __syncthreads();
+  if (w != 0) return;
+  const bool drafted = lane < gamma;
+  const int xi = drafted ? clamp_token(tokens[b * gamma + lane], V) : 0;
+  const int mine = lane < g1 ? sh_best[lane] : 0;
   const uint64_t miss = ballot(drafted && xi != mine);
   const int k = miss ? (int)__builtin_ctzll(miss) : (int)gamma;
   const int gk = __shfl(mine, k);
@@ -832,8 +836,8 @@ hipError_t launch_decide(const RejectArgs& a, const Ws& ws, hipStream_t stream) 
   const float inv_t = greedy ? 1.0f : (float)(1.0 / (double)a.temperature);
   const dim3 blk(kWavesPerBlock * 64);
   if (greedy) {
-    hipLaunchKernelGGL(greedy_kernel, dim3(blocks_for(a.B, kWavesPerBlock)), blk, 0, stream, a.tokens, a.B, a.gamma,
-                       a.V, a.out_tokens, a.out_num, ws);
+    hipLaunchKernelGGL(greedy_kernel, dim3((unsigned)a.B), dim3(kGreedyWaves * 64), 0, stream, a.tokens, a.B,
+                       a.gamma, a.V, a.out_tokens, a.out_num, ws);
     return hipGetLastError();
   }
   const int64_t ndc = draw_chunks(a.V);
