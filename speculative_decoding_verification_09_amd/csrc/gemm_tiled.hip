@@ -322,6 +322,87 @@ __device__ __forceinline__ void panel_stats(const f32x4 (&acc)[R][NT], uint16_t*
 }
 
 // ---------------------------------------------------------------------------
+// Draft-row statistics on the workgroups of a panel grid that have no work
+// item (the grid is a multiple of 8).  Idle workgroup e of E takes
+// vocabulary slice e of every draft row (a multiple of 4 entries); wave w takes
+// the rows w, w + NW, ...  One pass per row: each lane keeps the running max
+// of its z and its sum of exp(a - fl32(max z * fl32(1/T))), the terms formed as
+// in the statistics epilogue and the sum rescaled when the max grows, with
+// four 16-byte loads in flight; the lanes then meet in the same (max a, sum)
+// form.  Writes slot e of each draft row, and the drafted token's logit from
+// the slice that holds it.
+template <int NW>
+__device__ void idle_draft_stats(const FusedStats& fs, int N, int V, int e, int E, int wv, int lane) {
+  constexpr float kL2e = 1.4426950408889634f;
+  const int L = (((V + E - 1) / E) + 3) & ~3;
+  const int s0 = min(e * L, V), s1 = min(s0 + L, V);
+  const int nd = (int)(fs.B * fs.gamma);
+  const float c1 = fs.inv_t * kL2e;
+  const bool vec = (V & 3) == 0;
+  for (int j = wv; j < nd; j += NW) {
+    const float* row = fs.draft + (size_t)j * V;
+    float zm = -INFINITY;
+    double s = 0.0;
+    for (int v0 = s0 + 4 * lane; v0 < s1; v0 += 1024) {
+      float z[16];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int v = v0 + 256 * u;
+        if (vec && v + 3 < s1) {
+          const f32x4 t = *(const f32x4*)(row + v);
+          z[4 * u + 0] = t[0];
+          z[4 * u + 1] = t[1];
+          z[4 * u + 2] = t[2];
+          z[4 * u + 3] = t[3];
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) z[4 * u + q] = v + q < s1 ? row[v + q] : -INFINITY;
+        }
+      }
+      float bm = z[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) bm = fmaxf(bm, z[i]);
+      if (bm > zm) {
+        if (s > 0.0) s *= (double)__builtin_amdgcn_exp2f((zm * fs.inv_t - bm * fs.inv_t) * kL2e);
+        zm = bm;
+      }
+      if (zm > -INFINITY) {
+        const float c2 = zm * fs.inv_t * kL2e;
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s4[i >> 2] += __builtin_amdgcn_exp2f(fmaf(z[i], c1, -c2));
+        s += (double)s4[0] + (double)s4[1] + (double)s4[2] + (double)s4[3];
+      }
+    }
+    float M = zm;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    if (M > -INFINITY && s > 0.0) s *= (double)__builtin_amdgcn_exp2f((zm * fs.inv_t - M * fs.inv_t) * kL2e);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    if (lane == 0) {
+      const size_t slot = (size_t)(N + j) * fs.pstride + e;
+      fs.cmax[slot] = M * fs.inv_t;
+      fs.csum[slot] = M > -INFINITY ? s : 0.0;
+      const int32_t x = fs.tokens[j];
+      const int xc = x < 0 ? 0 : (x >= V ? V - 1 : x);
+      if (xc >= s0 && xc < s1) fs.zx[N + j] = row[xc];
+    }
+  }
+}
+
+// Index e and count E of the idle workgroups of a grid laid out as the panel
+// kernel's (8 * ceil(items / 8) slots per token pass, items = vocabulary
+// blocks x k-groups); -1 for a workgroup with a work item.
+__device__ __forceinline__ int idle_index(int id, int items, int npass, int& E) {
+  const int rem = items & 7;
+  E = rem ? (8 - rem) * npass : 0;
+  const int slot = id >> 3;
+  const int gi = (id & 7) + 8 * (slot / npass);
+  return gi >= items ? (slot % npass) * (8 - rem) + ((id & 7) - rem) : -1;
+}
+
+// ---------------------------------------------------------------------------
 // Panel kernel.  Work items are (vocabulary block, k-group, token pass): a
 // vocabulary block is NW*R 16-row tiles, a token pass NT*16 tokens, and a
 // k-group cpk chunks of KS MFMA k-steps (32 k each).  Block id i runs on XCD
@@ -357,7 +438,14 @@ __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restri
   }
   const int slot = id >> 3;
   const int gi = (id & 7) + 8 * (slot / npass);
-  if (gi >= nvb * ngroups) return;
+  if (gi >= nvb * ngroups) {
+    if (EPI == 1 && fs.draft != nullptr) {  // the launcher hands the draft rows to the idle workgroups
+      int E;
+      const int e = idle_index(id, nvb * ngroups, npass, E);
+      idle_draft_stats<NW>(fs, N, V, e, E, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), threadIdx.x & 63);
+    }
+    return;
+  }
   const int vb = gi % nvb, group = gi / nvb;
   const int c0 = group * cpk, c1 = min(c0 + cpk, nch_all);
   const int n0 = (slot % npass) * NT * 16;
@@ -834,6 +922,25 @@ GemmPlan plan_gemm(int64_t N, int64_t d, int64_t V, bool packed, bool with_stats
   return g;
 }
 
+// Workgroups of a panel grid without a work item: the items
+// (vocabulary blocks x k-groups) are rounded up to a multiple of 8 per token
+// pass.
+int64_t idle_workgroups(const GemmPlan& g, int64_t V) {
+  const int64_t ntiles = (V + 15) / 16, rows = (int64_t)g.shape.NW * g.shape.R;
+  const int64_t items = (ntiles + rows - 1) / rows * g.panel.groups, rem = items % 8;
+  return rem ? (8 - rem) * g.panel.npass : 0;
+}
+
+// Whether `idle` workgroups can summarise nd draft rows well within the GEMM:
+// each reads its share at about 5 GB/s per wave (measured on the 8-wave
+// panel), against W streamed at about 6.5 TB/s; the share must take at most
+// 60% of the GEMM's time.
+bool idle_drafts_fit(const GemmPlan& g, int64_t nd, int64_t d, int64_t V, int64_t idle) {
+  const double share = 4.0 * (double)nd * (double)V / (double)idle;
+  const double t_idle = share / (5e9 * g.shape.NW), t_gemm = 2.0 * (double)V * (double)d / 6.5e12;
+  return t_idle <= 0.6 * t_gemm;
+}
+
 }  // namespace
 }  // namespace gemm
 
@@ -875,16 +982,23 @@ hipError_t launch_gemm_with_stats(const uint16_t* X, const uint16_t* Wp, float* 
     if (e == hipSuccess) *nparts = *nparts_draft = parts;
     return e;
   }
-  // Many draft rows: the statistics kernel summarises them first, one
-  // partial per 2048-entry chunk; the panel kernel forms the target rows'.
+  // Many draft rows: the workgroups of the grid that have no vocabulary block
+  // summarise them during the GEMM when they can finish well within it;
+  // otherwise the statistics kernel does first, one partial per 2048-entry
+  // chunk.  Either way the panel (or deep) kernel forms the target rows'.
   int64_t dparts = parts;
+  FusedStats run = fs;
   if (fs.draft != nullptr) {
-    const hipError_t e = launch_draft_stats(fs, N, V, &dparts, stream);
-    if (e != hipSuccess) return e;
+    const int64_t idle = g.shape.deep ? 0 : idle_workgroups(g, V);  // the deep kernel's grid is busy for longer
+    if (idle > 0 && idle_drafts_fit(g, fs.B * fs.gamma, d, V, idle)) {
+      dparts = idle;
+    } else {
+      const hipError_t e = launch_draft_stats(fs, N, V, &dparts, stream);
+      if (e != hipSuccess) return e;
+      run.draft = nullptr;
+    }
   }
-  FusedStats target_only = fs;
-  target_only.draft = nullptr;
-  const hipError_t e = launch_panel_shape(g.shape, g.panel, X, Wp, Y, N, d, V, false, stream, &target_only);
+  const hipError_t e = launch_panel_shape(g.shape, g.panel, X, Wp, Y, N, d, V, false, stream, &run);
   if (e == hipSuccess) {
     *nparts = parts;
     *nparts_draft = dparts;

@@ -153,6 +153,8 @@ FUSED = [
     ("deep_greedy", 20, 4, 128, 3001, 0.0), ("deep_logits", 24, 5, 256, 5000, 1.0),
     ("deep_probs", 16, 7, 384, 4099, 0.8), ("deep_onehot", 33, 3, 128, 2050, 1.2),
     ("deep_passes_greedy", 64, 4, 128, 1500, 0.0),
+    # draft logits summarised by the panel grid's idle workgroups during the GEMM (long k, many draft rows)
+    ("panel_idle_drafts", 4, 4, 4096, 65600, 0.9), ("panel_idle_drafts_tail", 3, 7, 4096, 65541, 1.3),
 ]
 
 
