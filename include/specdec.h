@@ -336,7 +336,9 @@ int specdec_kv_rollback_after_verify(int32_t* block_tables, int32_t* seq_lens, i
                                      void* stream);
 
 /* Contiguous keys and values: k_out, v_out device [R][heads][max_len][head_dim];
- * entries t < min(seq_lens[r], max_len) are written, the rest left as they are. */
+ * entries t < min(seq_lens[r], max_len) are written, the rest left as they are.
+ * max_len <= 2^24 and max_len * head_dim * elem_bytes <= 2^34 (SPECDEC_ERR_SHAPE
+ * otherwise). */
 int specdec_kv_gather(const void* k_pool, const void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
                       int64_t R, int64_t num_blocks, int64_t heads, int64_t block_size, int64_t head_dim,
                       int64_t elem_bytes, int64_t max_blocks, int64_t max_len, void* k_out, void* v_out,

@@ -495,6 +495,7 @@ int specdec_kv_gather(const void* k_pool, const void* v_pool, const int32_t* blo
   if (st != SPECDEC_OK) return st;
   if (!k_out || !v_out) return SPECDEC_ERR_NULL;
   if (max_len < 1 || max_len > ((int64_t)1 << 24)) return SPECDEC_ERR_SHAPE;
+  if (max_len * (head_dim * elem_bytes / 16) > ((int64_t)1 << 30)) return SPECDEC_ERR_SHAPE;  // 32-bit unit index
   if (!aligned16(k_out) || !aligned16(v_out)) return SPECDEC_ERR_ALIGN;
   const specdec::KvArgs a = kv_args((void*)k_pool, (void*)v_pool, (int32_t*)block_tables, (int32_t*)seq_lens, nullptr,
                                     nullptr, nullptr, R, num_blocks, heads, block_size, head_dim, elem_bytes,

@@ -181,23 +181,60 @@ __global__ __launch_bounds__(kBookThreads) void kv_rollback_kernel(const int32_t
 }
 
 // Contiguous keys and values: out[r][h][t][:] for t < min(lens[r], max_len).
+// Grid y runs over (request, head) pairs, grid x over the 16-byte units of
+// one pair's max_len rows, so a unit's token and offset come from 32-bit
+// arithmetic (shifts when the row and block sizes are powers of two); each
+// thread moves two units of K and two of V per trip, with streaming
+// (nontemporal) loads and stores: the copy is touched once.
 __global__ __launch_bounds__(256) void kv_gather_kernel(const uint8_t* __restrict__ kpool,
                                                         const uint8_t* __restrict__ vpool,
                                                         const int32_t* __restrict__ tables,
                                                         const int32_t* __restrict__ lens, int64_t R, int64_t heads,
                                                         int64_t bs, int64_t row_units, int64_t max_blocks,
-                                                        int64_t num_blocks, int64_t max_len, uint8_t* __restrict__ kout,
-                                                        uint8_t* __restrict__ vout) {
-  const int64_t total = R * heads * max_len * row_units;
-  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * 256) {
-    const int64_t u = idx % row_units, rest = idx / row_units;
-    const int64_t t = rest % max_len, rh = rest / max_len, h = rh % heads, r = rh / heads;
-    if (t >= lens[r] || t / bs >= max_blocks) continue;
-    const int64_t phys = tables[r * max_blocks + t / bs];
-    if (phys < 0 || phys >= num_blocks) continue;
-    const int64_t src = ((phys * heads + h) * bs + t % bs) * row_units + u;
-    ((u32x4*)kout)[idx] = ((const u32x4*)kpool)[src];
-    ((u32x4*)vout)[idx] = ((const u32x4*)vpool)[src];
+                                                        int64_t num_blocks, int64_t max_len, int ru_shift, int bs_shift,
+                                                        uint8_t* __restrict__ kout, uint8_t* __restrict__ vout) {
+  const int ru = (int)row_units, bsi = (int)bs;
+  const int per = (int)(max_len * row_units);  // units of one (request, head) pair
+  const int stride = (int)gridDim.x * 256;
+  for (int64_t rh = blockIdx.y; rh < R * heads; rh += gridDim.y) {
+    const int64_t r = rh / heads, h = rh - r * heads;
+    const int len = (int)min((int64_t)lens[r], max_len);
+    const int32_t* tab = tables + r * max_blocks;
+    const int64_t out0 = rh * (int64_t)per;
+    auto src_of = [&](int i, int64_t& src) {  // false where the unit is not written
+      const int t = ru_shift >= 0 ? i >> ru_shift : i / ru;
+      const int u = i - t * ru;
+      if (t >= len) return false;
+      const int lb = bs_shift >= 0 ? t >> bs_shift : t / bsi;
+      if (lb >= max_blocks) return false;
+      const int64_t phys = tab[lb];
+      if (phys < 0 || phys >= num_blocks) return false;
+      src = ((phys * heads + h) * bs + (t - lb * bsi)) * row_units + u;
+      return true;
+    };
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < per; i += 2 * stride) {
+      const int i2 = i + stride;
+      int64_t s0 = 0, s1 = 0;
+      const bool w0 = src_of(i, s0);
+      const bool w1 = i2 < per && src_of(i2, s1);
+      u32x4 k0, v0, k1, v1;
+      if (w0) {
+        k0 = __builtin_nontemporal_load((const u32x4*)kpool + s0);
+        v0 = __builtin_nontemporal_load((const u32x4*)vpool + s0);
+      }
+      if (w1) {
+        k1 = __builtin_nontemporal_load((const u32x4*)kpool + s1);
+        v1 = __builtin_nontemporal_load((const u32x4*)vpool + s1);
+      }
+      if (w0) {
+        __builtin_nontemporal_store(k0, (u32x4*)kout + out0 + i);
+        __builtin_nontemporal_store(v0, (u32x4*)vout + out0 + i);
+      }
+      if (w1) {
+        __builtin_nontemporal_store(k1, (u32x4*)kout + out0 + i2);
+        __builtin_nontemporal_store(v1, (u32x4*)vout + out0 + i2);
+      }
+    }
   }
 }
 
@@ -237,9 +274,15 @@ hipError_t launch_kv_rollback(const KvArgs& a, const int32_t* keep_lens, const i
 
 hipError_t launch_kv_gather(const KvArgs& a, int64_t max_len, void* kout, void* vout, hipStream_t stream) {
   const int64_t units = a.head_dim * a.elem / 16;
-  hipLaunchKernelGGL(kv_gather_kernel, dim3(grid_for(a.R * a.heads * max_len * units)), dim3(256), 0, stream,
-                     (const uint8_t*)a.kpool, (const uint8_t*)a.vpool, a.tables, a.lens, a.R, a.heads, a.block_size,
-                     units, a.max_blocks, a.num_blocks, max_len, (uint8_t*)kout, (uint8_t*)vout);
+  // One pair's units are indexed in 32 bits.
+  if (max_len * units > INT32_MAX / 2) return hipErrorInvalidValue;
+  auto log2_or_neg = [](int64_t x) { return x > 0 && (x & (x - 1)) == 0 ? __builtin_ctzll((uint64_t)x) : -1; };
+  const int64_t pairs = a.R * a.heads, per = max_len * units;
+  const int64_t gx = (per + 511) / 512;  // two units per thread
+  const dim3 grid((unsigned)(gx < 1 ? 1 : (gx > 4096 ? 4096 : gx)), (unsigned)(pairs < 65535 ? pairs : 65535));
+  hipLaunchKernelGGL(kv_gather_kernel, grid, dim3(256), 0, stream, (const uint8_t*)a.kpool, (const uint8_t*)a.vpool,
+                     a.tables, a.lens, a.R, a.heads, a.block_size, units, a.max_blocks, a.num_blocks, max_len,
+                     log2_or_neg(units), log2_or_neg(a.block_size), (uint8_t*)kout, (uint8_t*)vout);
   return hipGetLastError();
 }
 

@@ -242,3 +242,22 @@ def test_tree_argument_checks():
     assert tv(wb=ws - 1) == 5
     assert sd.tree_step_workspace_bytes(1, 16, 4096, 128256, sd.SPECDEC_WEIGHTS_PACKED) == \
         (sd.tree_workspace_bytes(1, 16, 128256) + 255) // 256 * 256
+
+
+@needs_no_gpu
+def test_kv_gather_argument_checks():
+    """The gather indexes one (request, head) pair's 16-byte units in 32 bits: max_len * head_dim * elem_bytes
+    may not pass 2^34."""
+    lib = sd.library()
+
+    def gather(max_len=16, head_dim=128, elem=2, out=A):
+        return lib.specdec_kv_gather(P(A), P(A), P(A), P(A), 4, 64, 8, 16, head_dim, elem, 8, max_len, P(out), P(A),
+                                     None)
+
+    assert gather(out=0) == 1
+    assert gather(max_len=0) == 2
+    assert gather(max_len=(1 << 24) + 1) == 2
+    assert gather(max_len=1 << 24, head_dim=65536, elem=4) == 2  # 2^24 * 2^14 units
+    assert gather(max_len=1 << 21, head_dim=8192, elem=4) == 2    # 2^21 * 2^11 = 2^32 units
+    assert gather(out=A + 8) == 3
+

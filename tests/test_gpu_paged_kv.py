@@ -68,8 +68,11 @@ def test_page_script(orc):
     assert int(host(kv.status)[0]) == 0
 
 
+# Row sizes and block sizes include non-powers of two (the gather's division path): D=24 fp32 is 6 units of
+# 16 bytes per row, blocks of 6 tokens.
 @pytest.mark.parametrize("R,nb,bs,H,D,dtype", [(5, 64, 4, 2, 8, np.float32), (37, 512, 16, 4, 64, np.uint16),
-                                               (2000, 9000, 8, 1, 8, np.uint16)])
+                                               (2000, 9000, 8, 1, 8, np.uint16), (7, 100, 6, 3, 24, np.float32),
+                                               (9, 200, 5, 2, 40, np.uint16)])
 def test_random_batches(orc, R, nb, bs, H, D, dtype):
     tdt = torch.float32 if dtype == np.float32 else torch.bfloat16
     mb = 12
