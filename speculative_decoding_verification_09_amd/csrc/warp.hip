@@ -20,8 +20,11 @@
 //   * a second pass copies the candidates into LDS: for top-k every entry at
 //     or above that bucket when they are at most kCap (top-p then runs on the
 //     same candidates, with no further pass), else that bucket alone;
-//   * in LDS the cut is the crossing of the running weight in composite order:
-//     a single wave ranks up to 64 candidates directly, more take radix levels
+//   * in LDS the candidates of the top-k case are sorted by composite (a
+//     bitonic network), so the top-k cut is the k-th of them and the top-p cut
+//     the first rank where the prefix mass reaches the target; elsewhere the
+//     cut is the crossing of the running weight in composite order, found by
+//     a single wave ranking up to 64 candidates directly, or by radix levels
 //     of 12 bits over the composite;
 //   * a bucket with more than kCap entries is split by a second global level
 //     on the next 12 key bits, and one still too full (runs of equal logits)
@@ -389,6 +392,72 @@ __device__ Cut select_cut(const float* __restrict__ row, int V, int R, u64 need,
   return Cut{(uint32_t)(c >> kIdxBits), (int32_t)(kIdxMask - (uint32_t)(c & kIdxMask))};
 }
 
+// Sorts sh.comp[0, n) into descending order (n <= kCap): a bitonic network
+// over the next power of two, the padding zeros (below every composite of a
+// real entry but a possible 0, which then sorts among them) last.
+__device__ void sort_desc(int n, Shared& sh) {
+  int P = 1;
+  while (P < n) P <<= 1;
+  for (int i = n + threadIdx.x; i < P; i += kThreads) sh.comp[i] = 0ull;
+  __syncthreads();
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = threadIdx.x; t < (P >> 1); t += kThreads) {
+        const int i = 2 * stride * (t / stride) + (t % stride), j = i + stride;
+        const bool desc = (i & size) == 0;  // the final merge (size == P) is descending
+        const u64 a = sh.comp[i], b = sh.comp[j];
+        if ((a < b) == desc) {
+          sh.comp[i] = b;
+          sh.comp[j] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Both cuts from n candidates in LDS that include every entry of the row's
+// top k (top_k <= n): sorted, the top-k cut is the top_k-th; top-p then runs
+// over those top_k entries in rank order (masses exact in fixed point).
+__device__ void cuts_from_candidates(int n, int64_t top_k, bool tp, float top_p, float inv_t, float zmax, Shared& sh,
+                                     Cut& cut) {
+  sort_desc(n, sh);
+  const int kk = (int)top_k;  // top_k < V <= 2^23 and top_k <= n <= kCap
+  const u64 ck = sh.comp[kk - 1];
+  cut = Cut{(uint32_t)(ck >> kIdxBits), (int32_t)(kIdxMask - (uint32_t)(ck & kIdxMask))};
+  if (!tp) return;
+  // Thread t holds ranks 2t and 2t + 1.
+  u64 m[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int i = 2 * (int)threadIdx.x + e;
+    m[e] = i < kk ? mass_fixed(key_value((uint32_t)(sh.comp[i] >> kIdxBits)), inv_t, zmax) : 0ull;
+  }
+  const u64 before = block_exclusive(m[0] + m[1], sh.red);
+  const u64 total = block_sum(m[0] + m[1], sh.red);
+  const double t = ceil((double)top_p * (double)total);
+  u64 need = t < 1.0 ? 1ull : (u64)t;
+  if (need > total) need = total;
+  if (threadIdx.x == 0) sh.found = -1;
+  __syncthreads();
+  if (need > 0) {
+    u64 run = before;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = 2 * (int)threadIdx.x + e;
+      if (m[e] > 0 && run < need && run + m[e] >= need) sh.found = i;
+      run += m[e];
+    }
+  }
+  __syncthreads();
+  const int f = sh.found;
+  if (f >= 0) {
+    const u64 cp = sh.comp[f];
+    cut = Cut{(uint32_t)(cp >> kIdxBits), (int32_t)(kIdxMask - (uint32_t)(cp & kIdxMask))};
+  }
+  __syncthreads();
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void warp_cut_kernel(const float* __restrict__ target,
                                                             const float* __restrict__ draft, int64_t n_target,
@@ -420,24 +489,8 @@ __global__ __launch_bounds__(kThreads) void warp_cut_kernel(const float* __restr
     if (held <= (u64)kCap) {
       // Every entry at or above the cut's bucket fits in LDS: both cuts from there.
       const int n = compact<false, VEC>(row, V, R, 0xfff00000u, b << 20, true, cut, inv_t, zmax, sh);
-      const u64 ck = lds_select<false>(n, (u64)top_k, 0ull, sh);
-      cut = Cut{(uint32_t)(ck >> kIdxBits), (int32_t)(kIdxMask - (uint32_t)(ck & kIdxMask))};
-      if (tp) {
-        u64 part = 0;
-        for (int i = threadIdx.x; i < n; i += kThreads) {
-          const u64 c = sh.comp[i];
-          const u64 m = c >= ck ? mass_fixed(key_value((uint32_t)(c >> kIdxBits)), inv_t, zmax) : 0ull;
-          sh.cw[i] = m;
-          part += m;
-        }
-        const u64 total = block_sum(part, sh.red);
-        const double t = ceil((double)top_p * (double)total);
-        u64 need = t < 1.0 ? 1ull : (u64)t;
-        if (need > total) need = total;
-        const u64 cp = need > 0 ? lds_select<true>(n, need, ck, sh) : 0ull;
-        if (cp != 0ull) cut = Cut{(uint32_t)(cp >> kIdxBits), (int32_t)(kIdxMask - (uint32_t)(cp & kIdxMask))};
-        done_p = true;
-      }
+      cuts_from_candidates(n, top_k, tp, top_p, inv_t, zmax, sh, cut);
+      done_p = tp;
     } else {
       cut = select_cut<false, VEC>(row, V, R, (u64)top_k, cut, inv_t, zmax, sh);
     }
