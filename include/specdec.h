@@ -94,13 +94,19 @@ size_t specdec_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  * device.  0 means none (the workspace argument may then be NULL).  When the
  * output rows are too few to occupy every compute unit, or X is too large to
  * stage whole, the k range is split into groups whose fp32 partial sums are
- * kept here and then added in group order.  Returns 0 for invalid sizes. */
+ * kept here and then added in group order.  For many positions with packed
+ * weights (past 128 positions, d % 128 == 0) it also holds a copy of X in the
+ * packed layout (ceil(N/16)*16*d bf16), which the kernel for that regime
+ * reads.  Returns 0 for invalid sizes. */
 size_t specdec_logits_workspace_bytes(int64_t N, int64_t d, int64_t V, int weight_layout);
 
 /* Bytes of device workspace that specdec_verify_step needs: the larger of
- * specdec_workspace_bytes(B, gamma, V) and
- * specdec_logits_workspace_bytes(B*(gamma+1), d, V, weight_layout), since the
- * two stages use it one after the other.  Returns 0 for invalid sizes. */
+ * specdec_logits_workspace_bytes(B*(gamma+1), d, V, weight_layout) and
+ * specdec_workspace_bytes(B, gamma, V) rounded up to 256 bytes plus, with
+ * packed weights past 64 positions (d % 128 == 0), the packed copy of X that
+ * the scoring kernel reads while it also forms the softmax statistics.  The
+ * unfused path runs the two stages one after the other in the same bytes.
+ * Returns 0 for invalid sizes. */
 size_t specdec_step_workspace_bytes(int64_t B, int64_t gamma, int64_t d, int64_t V, int weight_layout);
 
 /* Bytes of the packed weight layout of a [V, d] bf16 matrix (d % 32 == 0):
@@ -265,7 +271,9 @@ int specdec_tree_verify_greedy(const float* target_logits, const int32_t* parent
                                int64_t B, int64_t M, int64_t V, int32_t* out_tokens, int32_t* out_num_emitted,
                                int32_t* out_nodes, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace for specdec_tree_verify_step (0 for invalid sizes). */
+/* Bytes of workspace for specdec_tree_verify_step, composed as for
+ * specdec_step_workspace_bytes with specdec_tree_workspace_bytes(B, M, V) as
+ * the sampling part (0 for invalid sizes). */
 size_t specdec_tree_step_workspace_bytes(int64_t B, int64_t M, int64_t d, int64_t V, int weight_layout);
 
 /* The whole tree step: scores of all B*M nodes (X [B*M, d] bf16, row b*M + i
