@@ -657,11 +657,16 @@ __global__ __launch_bounds__(256) void deep_kernel(const uint16_t* __restrict__ 
 #pragma unroll
     for (int t = 0; t < NT; ++t) dst[t] = *(const u32x4*)(xb + t * 512);
   };
+  // Token tiles past N (in the last token pass) skip their MFMAs; the test is
+  // uniform over the workgroup.
+  const int ntv = min(NT, (ncols + 15) >> 4);
   auto mfmas = [&](const u32x4(&wa)[R], const u32x4(&b)[NT]) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
+      if (t < ntv) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[r][t] = mfma(wa[r], b[t], acc[r][t]);
+        for (int r = 0; r < R; ++r) acc[r][t] = mfma(wa[r], b[t], acc[r][t]);
+      }
   };
   // X of step j goes to LDS buffer j % 4 three steps ahead (at step j - 3) and
   // its B fragments are read into registers one step ahead (at step j - 1);
