@@ -198,8 +198,8 @@ hipError_t launch_tiled(const uint16_t* X, const uint16_t* W, void* Y, int64_t N
 // Statistics epilogue of the panel kernel (see below).  xs: the kernel's LDS,
 // free once the main loop has ended.
 template <int NT, int R, int NW, int EPI>
-__device__ __forceinline__ void panel_stats(const f32x4 (&acc)[R][NT], uint16_t* xs, const FusedStats& fs, int N,
-                                            int V, int n0, int ncols, int vt0, int vb, int wv, int lane) {
+__device__ __forceinline__ void panel_stats(const f32x4 (&acc)[R][NT], uint16_t* xs, const FusedStats& fs, int V,
+                                            int n0, int ncols, int vt0, int vb, int wv, int lane) {
   constexpr int kTok = NT * 16;
   const int m = lane & 15, g = lane >> 4;
   float* lm = (float*)xs;                                     // [NW][kTok] wave maxima
@@ -547,7 +547,7 @@ __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restri
     compute(wa, 0, c);
   }
 
-  if (EPI != 0) panel_stats<NT, R, NW, EPI>(acc, xs, fs, N, V, n0, ncols, vt0, vb, wv, lane);
+  if (EPI != 0) panel_stats<NT, R, NW, EPI>(acc, xs, fs, V, n0, ncols, vt0, vb, wv, lane);
 
   // Lane holds tokens n0 + 16t + m, vocabulary rows 16*(vt0 + r) + 4g .. +3.
   const bool split = ngroups > 1;
@@ -711,7 +711,7 @@ __global__ __launch_bounds__(256) void deep_kernel(const uint16_t* __restrict__ 
     step(std::integral_constant<int, 3>{}, s + 3);
   }
 
-  if (EPI != 0) panel_stats<NT, R, NW, EPI>(acc, xs, fs, N, V, n0, ncols, vt0, vb, wv, lane);
+  if (EPI != 0) panel_stats<NT, R, NW, EPI>(acc, xs, fs, V, n0, ncols, vt0, vb, wv, lane);
 
   const bool split = ngroups > 1;
   float* part = (float*)Y + (size_t)group * N * V;

@@ -618,8 +618,8 @@ __global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
 //     chunk partials of rows w, w + kGreedyWaves, ... (each lane issuing four
 //     loads at a time), leaving row i's argmax in LDS; wave 0 then compares
 //     the drafted tokens with them, lane i <-> row i.
-__global__ __launch_bounds__(kGreedyWaves * 64) void greedy_kernel(const int32_t* __restrict__ tokens, int64_t B,
-                                                                    int64_t gamma, int64_t V,
+__global__ __launch_bounds__(kGreedyWaves * 64) void greedy_kernel(const int32_t* __restrict__ tokens, int64_t gamma,
+                                                                    int64_t V,
                                                                     int32_t* __restrict__ out_tokens,
                                                                     int32_t* __restrict__ out_num, Ws ws) {
   __shared__ int sh_best[64];
@@ -727,7 +727,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void tree_mask_kernel(const in
 // four partials per lane in flight), then wave 0 applies the rule.
 constexpr int kTreeWaves = 16;
 __global__ __launch_bounds__(kTreeWaves * 64) void tree_greedy_kernel(
-    const int32_t* __restrict__ parents, const int32_t* __restrict__ node_tokens, int64_t B, int M, int64_t V,
+    const int32_t* __restrict__ parents, const int32_t* __restrict__ node_tokens, int M, int64_t V,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_num, int32_t* __restrict__ out_nodes, Ws ws) {
   __shared__ int sh_best[64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -834,10 +834,9 @@ hipError_t launch_decide(const RejectArgs& a, const Ws& ws, hipStream_t stream) 
   const bool greedy = a.temperature == 0.0f;
   const bool vec = (a.V & 3) == 0;
   const float inv_t = greedy ? 1.0f : (float)(1.0 / (double)a.temperature);
-  const dim3 blk(kWavesPerBlock * 64);
   if (greedy) {
-    hipLaunchKernelGGL(greedy_kernel, dim3((unsigned)a.B), dim3(kGreedyWaves * 64), 0, stream, a.tokens, a.B,
-                       a.gamma, a.V, a.out_tokens, a.out_num, ws);
+    hipLaunchKernelGGL(greedy_kernel, dim3((unsigned)a.B), dim3(kGreedyWaves * 64), 0, stream, a.tokens, a.gamma,
+                       a.V, a.out_tokens, a.out_num, ws);
     return hipGetLastError();
   }
   const int64_t ndc = draw_chunks(a.V);
@@ -938,7 +937,7 @@ hipError_t launch_tree_greedy(const TreeArgs& t, int64_t nparts, hipStream_t str
     ws = bind(t.workspace, L, nparts);
   }
   hipLaunchKernelGGL(tree_greedy_kernel, dim3((unsigned)t.B), dim3(kTreeWaves * 64), 0, stream, t.parents,
-                     t.node_tokens, t.B, (int)t.M, t.V, t.out_tokens, t.out_num, t.out_nodes, ws);
+                     t.node_tokens, (int)t.M, t.V, t.out_tokens, t.out_num, t.out_nodes, ws);
   return hipGetLastError();
 }
 

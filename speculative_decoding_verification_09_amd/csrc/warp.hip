@@ -474,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void warp_cut_kernel(const float* __restr
   // Pass 1: the row maximum, and the top-k level-1 histogram.
   if (tk) clear_bins(sh, false);
   float zm = -INFINITY;
-  for_row<VEC>(row, V, R, [&](int v, float z) {
+  for_row<VEC>(row, V, R, [&](int /*v*/, float z) {
     zm = fmaxf(zm, z);
     if (tk) atomicAdd(&sh.cnt[order_key(z) >> 20], 1u);
   });
