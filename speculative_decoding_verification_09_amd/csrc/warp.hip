@@ -164,10 +164,10 @@ __device__ __forceinline__ void clear_bins(Shared& sh, bool mass) {
 
 // Calls f(v, z) for every entry of the row; wave w takes the contiguous range
 // [w*R, (w+1)*R) (R a multiple of 256) in steps of 256 entries, lane l the 4
-// entries at 4l, two steps' loads issued together.
+// entries at 4l, four steps' loads issued together.
 template <bool VEC, class F>
 __device__ __forceinline__ void for_row(const float* __restrict__ row, int V, int R, F&& f) {
-  constexpr int U = 2;
+  constexpr int U = 4;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int b0 = w * R, b1 = min(b0 + R, V);
   for (int base = b0; base < b1; base += U * 256) {
