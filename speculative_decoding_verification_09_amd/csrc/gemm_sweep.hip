@@ -247,7 +247,9 @@ __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restri
 
   // Draft rows: workgroups with the smaller tile count take consecutive
   // vocabulary slices (a multiple of 4 entries each); the others leave empty
-  // partials.  Wave w takes draft rows w, w + NW, ...
+  // partials.  Wave w takes draft rows w, w + NW, ...  A lane loads sixteen
+  // entries at a time, all before any use; the fp64 sum is rescaled when the
+  // running maximum grows (only for slices past 1024 entries).
   const int G = (int)gridDim.x;
   const int rem = ntiles % G;
   const int ndraft = rem == 0 ? G : G - rem;
@@ -257,13 +259,28 @@ __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restri
   const int nd = (int)(fs.B * fs.gamma);
   for (int j = wv; j < nd; j += NW) {
     const float* row = fs.draft + (size_t)j * V;
+    constexpr int kPer = 16;
     float mx = -INFINITY;
-    for (int v = s0 + lane; v < s1; v += 64) mx = fmaxf(mx, row[v] * fs.inv_t);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
     double sm = 0.0;
-    if (mx > -INFINITY)
-      for (int v = s0 + lane; v < s1; v += 64) sm += (double)expf(row[v] * fs.inv_t - mx);
+    for (int c0 = s0; c0 < s1; c0 += 64 * kPer) {
+      float a[kPer];
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        const int v = c0 + 64 * e + lane;
+        a[e] = v < s1 ? row[v] * fs.inv_t : -INFINITY;
+      }
+      float bm = a[0];
+#pragma unroll
+      for (int e = 1; e < kPer; ++e) bm = fmaxf(bm, a[e]);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) bm = fmaxf(bm, __shfl_xor(bm, o));
+      const float mn = fmaxf(mx, bm);  // wave-uniform
+      if (mn == -INFINITY) continue;
+      if (sm > 0.0) sm *= exp((double)mx - (double)mn);
+      mx = mn;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) sm += (double)expf(a[e] - mx);
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) sm += __shfl_xor(sm, o);
     if (lane == 0) {
