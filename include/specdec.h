@@ -91,7 +91,10 @@ size_t specdec_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
 
 /* Bytes of device workspace that specdec_verify_logits needs for N positions,
  * hidden size d, V outputs and the given weight layout, on the current
- * device.  0 means none (the workspace argument may then be NULL).  When the
+ * device.  0 means none (the workspace argument may then be NULL).  With
+ * packed weights, at most 16 positions, V >= 65536 and d <= 4096 it is 256
+ * bytes: the counter of the queue from which the workgroups take vocabulary
+ * tiles (reset by the call itself before use).  When the
  * output rows are too few to occupy every compute unit, or X is too large to
  * stage whole, the k range is split into groups whose fp32 partial sums are
  * kept here and then added in group order.  For many positions with packed
@@ -104,7 +107,8 @@ size_t specdec_logits_workspace_bytes(int64_t N, int64_t d, int64_t V, int weigh
  * specdec_logits_workspace_bytes(B*(gamma+1), d, V, weight_layout) and
  * specdec_workspace_bytes(B, gamma, V) rounded up to 256 bytes plus, with
  * packed weights past 64 positions (d % 128 == 0), the packed copy of X that
- * the scoring kernel reads while it also forms the softmax statistics.  The
+ * the scoring kernel reads while it also forms the softmax statistics (or,
+ * where specdec_logits_workspace_bytes names the tile queue, its 256 bytes).  The
  * unfused path runs the two stages one after the other in the same bytes.
  * Returns 0 for invalid sizes. */
 size_t specdec_step_workspace_bytes(int64_t B, int64_t gamma, int64_t d, int64_t V, int weight_layout);

@@ -47,36 +47,51 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Sweep kernel (packed W, small N).  The kernel can split the k range into
-// groups of spk k-steps (KG = ceil(nsteps / spk) groups): block b takes group
-// b % KG of the tiles t = b / KG + j * (gridDim.x / KG), holds only that slice
-// of X in LDS, and writes its partial sums to slice b % KG of Y (fp32
-// [KG][N][V]).  The planner runs it with one group (spk = nsteps), where Y is
-// the output.
-// Inside a block, wave w owns k-steps [w*spw, (w+1)*spw) of the group, taken
-// SPW at a time; a work unit u is (tile u / ngroups, register group
-// u % ngroups).
+// Sweep kernel (packed W, small N).  Persistent, one workgroup per CU.  A
+// workgroup takes one 16-row tile at a time; its 8 waves split the tile's k
+// range (wave w owns k-steps [w*spw, (w+1)*spw), spw <= SPW: d up to
+// NW*SPW*32), each loading its slice straight into A-operand registers, and
+// the partial sums meet in LDS in a fixed order.
 //
-// Inside the main loop every global load is issued unconditionally, with its
-// address clamped into the wave's k range where a register group runs past it
-// (those values are never used): the compiler can then count outstanding loads
-// exactly and keeps the next unit's loads in flight while the current unit
-// computes, instead of draining all of them at each branch join.
+// Tiles come in two phases.  First a fixed share: workgroup b takes tiles b,
+// b + G, ..., b + (S-1)*G (G = grid size, S*G about 85% of the tiles), the
+// next tile's loads in flight while the current one computes.  Then a queue:
+// a ticket counter (zeroed by a one-thread kernel before each launch) hands
+// out the remaining tiles in the order asked for.  HBM does not serve every
+// CU equally fast (measured on the LM-head sweep: with fixed shares only, the
+// workgroups on four of the eight XCDs finished 11-15% later than those on
+// the other four, whatever tiles they were given), so fixed shares alone
+// leave half the chip idle at the end; with the queue every workgroup
+// finishes within about one tile of the others.  The queue is kept to the
+// last 15% because each ticket is a device-scope atomic on one address, and
+// handing out every tile that way measurably slowed the whole stream.
+// In the queue phase thread 0 asks for the next ticket right after the
+// current tile's loads go out, and reads the answer once they have been
+// used.
+//
+// Every global load is issued unconditionally, with its address clamped into
+// the wave's k range (those values are never used): the compiler can then
+// count outstanding loads exactly and keeps the next tile's loads in flight
+// while the current tile computes, instead of draining all of them at each
+// branch join.
 //
 // Statistics epilogue (EPI 1: softmax at temperature T, EPI 2: argmax), used
-// by the whole verification step with one k-group: wave 0 folds every tile's
-// finished logits into a running per-lane state (max of a = z * fl32(1/T) and
-// an fp64 sum of fp32 exp(a - max), rescaled when the max grows; or the
-// largest z with its lowest index), records the logit of each row's drafted
-// token from the tile that holds it, and at the end leaves one partial per
-// (row, workgroup).  With draft logits, the workgroups that have one tile
-// fewer (they finish first) also summarise a slice of every draft row, one
-// wave per row (few rows here: B*(gamma+1) <= 16).
+// by the verification step: wave 0 folds every tile's finished logits into a
+// running per-lane state (max of a = z * fl32(1/T) and an fp64 sum of fp32
+// exp(a - max), rescaled when the max grows; or the largest z with its lowest
+// index), records the logit of each row's drafted token from the tile that
+// holds it, and at the end leaves one partial per (row, workgroup).  With
+// draft logits, workgroup b first summarises the 2048-entry slices b, b + G,
+// ... of every draft row (few rows here: B*gamma <= 15), before its first
+// tile; the queue evens out the difference.
+constexpr int kDraftSlice = 2048;
+
 template <int NW, int SPW, bool NTL, bool OUT_BF16, int EPI>
 __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp,
-                                                        void* __restrict__ Y, int N, int d, int V, int spk,
-                                                        FusedStats fs) {
+                                                        void* __restrict__ Y, int N, int d, int V, int S,
+                                                        unsigned* __restrict__ tickets, FusedStats fs) {
   extern __shared__ __align__(16) uint16_t lds[];
+  __shared__ int sh_tile;  // the next queue tile, passed from thread 0 to the workgroup
   const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, g = lane >> 4;
   if (EPI == 1 && fs.done != nullptr) {  // the draw kernel's counters, for the step that follows
     const int64_t gid = (int64_t)blockIdx.x * (NW * 64) + tid;
@@ -85,29 +100,71 @@ __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restri
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int nsteps = d >> 5;
   const int ntiles = (V + 15) >> 4;
-  const int kgs = (nsteps + spk - 1) / spk;
-  const int kg = (int)blockIdx.x % kgs;
-  const int stream = (int)blockIdx.x / kgs, nstream = (int)gridDim.x / kgs;
-  const int ks0 = kg * spk;                       // first k-step of the group
-  const int kw = min(spk, nsteps - ks0);          // k-steps in the group (>= 1)
-  const int pitch = spk * 32 + kPad;
-  const int spw = (kw + NW - 1) / NW;             // k-steps per wave and tile
-  const int ngroups = (spw + SPW - 1) / SPW;      // register groups per wave and tile
+  const int G = (int)gridDim.x;
+  const int qbase = S * G;  // the first tile of the queue (S * G <= ntiles)
+  // Ticket k names tile qbase + k; past the last tile, ntiles (no tile).
+  auto tile_of = [&](unsigned k) { return k < (unsigned)(ntiles - qbase) ? qbase + (int)k : ntiles; };
+  auto ask = [&]() { return __hip_atomic_fetch_add(tickets, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  if (S == 0 && tid == 0) sh_tile = tile_of(ask());  // no fixed share: the first tile comes from the queue
+  const int pitch = nsteps * 32 + kPad;
+  const int spw = (nsteps + NW - 1) / NW;         // k-steps per wave and tile (<= SPW)
   uint16_t* xs = lds;
   f32x4* red = (f32x4*)(lds + (((size_t)N * pitch + 7) & ~(size_t)7));
-  const int units_per_row = kw * 4;               // 16-byte units of one X row slice
+  const int units_per_row = nsteps * 4;           // 16-byte units of one X row
   for (int i = tid; i < N * units_per_row; i += NW * 64) {
     const int n = i / units_per_row, u = i - n * units_per_row;
-    *(u32x4*)(xs + n * pitch + u * 8) = *(const u32x4*)(X + (size_t)n * d + (size_t)ks0 * 32 + u * 8);
+    *(u32x4*)(xs + n * pitch + u * 8) = *(const u32x4*)(X + (size_t)n * d + u * 8);
+  }
+
+  if (EPI == 1 && fs.draft != nullptr) {
+    // Draft rows: wave w takes rows w and w + NW; a lane loads its 32 entries
+    // of a slice before any use, and the fp64 sum is rescaled when the running
+    // maximum grows.  Workgroups without a slice leave empty partials.
+    const int nd = (int)(fs.B * fs.gamma);
+    const int nsl = (V + kDraftSlice - 1) / kDraftSlice;
+    for (int j = wv; j < nd; j += NW) {
+      const float* row = fs.draft + (size_t)j * V;
+      constexpr int kPer = kDraftSlice / 64;
+      float mx = -INFINITY;
+      double sm = 0.0;
+      for (int c = (int)blockIdx.x; c < nsl; c += G) {
+        float a[kPer];
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+          const int v = c * kDraftSlice + 64 * e + lane;
+          a[e] = v < V ? row[v] * fs.inv_t : -INFINITY;
+        }
+        float bm = a[0];
+#pragma unroll
+        for (int e = 1; e < kPer; ++e) bm = fmaxf(bm, a[e]);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) bm = fmaxf(bm, __shfl_xor(bm, o));
+        const float mn = fmaxf(mx, bm);  // wave-uniform
+        if (mn == -INFINITY) continue;
+        if (sm > 0.0) sm *= exp((double)mx - (double)mn);
+        mx = mn;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) sm += (double)expf(a[e] - mx);
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) sm += __shfl_xor(sm, o);
+      if (lane == 0) {
+        const size_t slot = (size_t)(N + j) * fs.pstride + blockIdx.x;
+        fs.cmax[slot] = mx;
+        fs.csum[slot] = sm;
+        const int32_t x = fs.tokens[j];
+        const int xc = x < 0 ? 0 : (x >= V ? V - 1 : x);
+        if ((xc / kDraftSlice) % G == (int)blockIdx.x) fs.zx[N + j] = row[xc];
+      }
+    }
   }
   __syncthreads();
+
   const bool live = m < N;
   const int mx = live ? m : N - 1;                // lanes past N read a valid row; their column is not stored
-  const int my0 = wv * spw;                       // first k-step of this wave, relative to ks0
-  const int my1 = min(my0 + spw, kw);             // one past the last
-  const int last = max(0, min(my1, kw) - 1);      // a k-step of the group this wave may address
-  const int64_t units = stream < ntiles ? (int64_t)((ntiles - stream + nstream - 1) / nstream) * ngroups : 0;
-  float* part = (float*)Y + (size_t)kg * N * V;   // this group's slice when the k range is split
+  const int my0 = wv * spw;                       // first k-step of this wave
+  const int my1 = min(my0 + spw, nsteps);         // one past the last
+  const int last = max(0, my1 - 1);               // a k-step this wave may address
 
   // Statistics state of lane (token m, rows 4g .. 4g+3 of each tile).
   float st_m = -INFINITY;
@@ -123,30 +180,28 @@ __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restri
     }
   }
 
-  auto load = [&](u32x4(&dst)[SPW], int64_t u) {
-    const int t = stream + (int)(u / ngroups) * nstream;
-    const int s0 = my0 + (int)(u % ngroups) * SPW;
-    const uint16_t* p = Wp + ((size_t)t * nsteps + ks0) * 512 + lane * 8;
+  auto load = [&](u32x4(&dst)[SPW], int t) {
+    const uint16_t* p = Wp + (size_t)t * nsteps * 512 + lane * 8;
 #pragma unroll
-    for (int s = 0; s < SPW; ++s) dst[s] = load_w16<NTL>(p + (size_t)min(s0 + s, last) * 512);
+    for (int s = 0; s < SPW; ++s) dst[s] = load_w16<NTL>(p + (size_t)min(my0 + s, last) * 512);
   };
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  auto consume = [&](const u32x4(&a)[SPW], int64_t u) {
-    const int grp = (int)(u % ngroups);
-    const int s0 = my0 + grp * SPW;
+  unsigned ticket = 0u;  // thread 0: the ticket asked for during the current tile
+  // Tile t from registers a.  With pass_on, thread 0 turns its ticket into
+  // the next queue tile for the workgroup, between the two barriers.
+  auto consume = [&](const u32x4(&a)[SPW], int t, bool pass_on) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
-      if (s0 + s < my1) {
-        const u32x4 bf = *(const u32x4*)(xs + mx * pitch + (s0 + s) * 32 + 8 * g);
+      if (my0 + s < my1) {
+        const u32x4 bf = *(const u32x4*)(xs + mx * pitch + (my0 + s) * 32 + 8 * g);
         acc = mfma(a[s], bf, acc);
       }
     }
-    if (grp != ngroups - 1) return;
-    // Last group of the tile: sum the waves' partials in a fixed order.
+    // Sum the waves' partials in a fixed order.
     red[wv * 64 + lane] = acc;
-    acc = f32x4{0.f, 0.f, 0.f, 0.f};
     __syncthreads();
     if (wv == 0) {
+      if (pass_on && lane == 0) sh_tile = tile_of(ticket);
       f32x4 sum = red[lane];
 #pragma unroll
       for (int w = 1; w < NW; ++w) {
@@ -156,19 +211,15 @@ __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restri
         sum[2] += o[2];
         sum[3] += o[3];
       }
-      const int t = stream + (int)(u / ngroups) * nstream;
       const int64_t v0 = (int64_t)t * 16 + 4 * g;
       if (live && v0 < V) {
-        if (kgs == 1)
-          store4<OUT_BF16>(Y, (size_t)m * V + v0, v0, V, sum);
-        else
-          store4<false>(part, (size_t)m * V + v0, v0, V, sum);
+        store4<OUT_BF16>(Y, (size_t)m * V + v0, v0, V, sum);
         if (EPI == 1) {  // terms 2^(z * c1 - max * log2(e)), c1 = fl32(1/T) * log2(e)
           constexpr float kLog2e = 1.4426950408889634f;
           float zt = -INFINITY;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (v0 + j < V) zt = fmaxf(zt, sum[j]);
+          for (int q = 0; q < 4; ++q)
+            if (v0 + q < V) zt = fmaxf(zt, sum[q]);
           const float mt = zt * fs.inv_t;  // = max of fl32(z * fl32(1/T)) over the four
           if (mt > st_m) {
             if (st_s > 0.0) st_s *= (double)__builtin_amdgcn_exp2f((st_m - mt) * kLog2e);
@@ -177,15 +228,15 @@ __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restri
           const float c1 = fs.inv_t * kLog2e, c2 = st_m * kLog2e;
           float s4 = 0.0f;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (v0 + j < V) s4 += __builtin_amdgcn_exp2f(fmaf(sum[j], c1, -c2));
+          for (int q = 0; q < 4; ++q)
+            if (v0 + q < V) s4 += __builtin_amdgcn_exp2f(fmaf(sum[q], c1, -c2));
           st_s += (double)s4;
         } else if (EPI == 2) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (v0 + j < V && (sum[j] > st_m || (sum[j] == st_m && (int)v0 + j < st_i))) {
-              st_m = sum[j];
-              st_i = (int)v0 + j;
+          for (int q = 0; q < 4; ++q)
+            if (v0 + q < V && (sum[q] > st_m || (sum[q] == st_m && (int)v0 + q < st_i))) {
+              st_m = sum[q];
+              st_i = (int)v0 + q;
             }
         }
         if (EPI == 1 && st_x >= v0 && st_x < v0 + 4) fs.zx[m] = sum[st_x - (int)v0];
@@ -193,25 +244,45 @@ __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restri
     }
     __syncthreads();
   };
-  if (units <= 0) return;
-  // Two units per trip so the prefetch registers swap roles without copies;
-  // the loop body loads only units that exist, and the last one or two units
-  // are peeled off so that no load is issued past the end.
-  u32x4 a0[SPW], a1[SPW];
-  load(a0, 0);
-  int64_t u = 0;
-  for (; u + 2 < units; u += 2) {
-    load(a1, u + 1);
-    consume(a0, u);
-    load(a0, u + 2);
-    consume(a1, u + 1);
+
+  // Fixed share: two tiles per trip so the prefetch registers swap roles
+  // without copies; the last one or two tiles are peeled off so that no load
+  // is issued past the share, and the last one also passes on the first
+  // queue tile.
+  if (S > 0) {
+    const int b = (int)blockIdx.x;
+    u32x4 a0[SPW], a1[SPW];
+    load(a0, b);
+    int j = 0;
+    for (; j + 2 < S; j += 2) {
+      load(a1, b + (j + 1) * G);
+      consume(a0, b + j * G, false);
+      load(a0, b + (j + 2) * G);
+      consume(a1, b + (j + 1) * G, false);
+    }
+    if (j + 1 < S) {
+      load(a1, b + (j + 1) * G);
+      consume(a0, b + j * G, false);
+      if (tid == 0) ticket = ask();
+      consume(a1, b + (j + 1) * G, true);
+    } else {
+      if (tid == 0) ticket = ask();
+      consume(a0, b + j * G, true);
+    }
   }
-  if (u + 1 < units) {
-    load(a1, u + 1);
-    consume(a0, u);
-    consume(a1, u + 1);
-  } else {
-    consume(a0, u);
+  // Queue: one tile at a time (a second register set for prefetching
+  // measured no faster here).  Thread 0 asks for the next ticket right after
+  // the tile's loads go out and passes it on while the tile is reduced.
+  // Every wave reads the tile index after the barrier that follows its
+  // publication, so all waves take the same tiles and meet at the same
+  // barriers.
+  for (;;) {
+    const int t = __builtin_amdgcn_readfirstlane(sh_tile);
+    if (t >= ntiles) break;
+    u32x4 a[SPW];
+    load(a, t);
+    if (tid == 0) ticket = ask();
+    consume(a, t, true);
   }
   if (EPI == 0) return;
 
@@ -243,64 +314,38 @@ __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restri
         fs.cidx[slot] = st_i;
     }
   }
-  if (EPI != 1 || fs.draft == nullptr) return;
+}
 
-  // Draft rows: workgroups with the smaller tile count take consecutive
-  // vocabulary slices (a multiple of 4 entries each); the others leave empty
-  // partials.  Wave w takes draft rows w, w + NW, ...  A lane loads sixteen
-  // entries at a time, all before any use; the fp64 sum is rescaled when the
-  // running maximum grows (only for slices past 1024 entries).
-  const int G = (int)gridDim.x;
-  const int rem = ntiles % G;
-  const int ndraft = rem == 0 ? G : G - rem;
-  const int rank = rem == 0 ? (int)blockIdx.x : (int)blockIdx.x - rem;
-  const int L = (((V + ndraft - 1) / ndraft) + 3) & ~3;
-  const int s0 = rank >= 0 ? min(rank * L, V) : V, s1 = rank >= 0 ? min(s0 + L, V) : V;
-  const int nd = (int)(fs.B * fs.gamma);
-  for (int j = wv; j < nd; j += NW) {
-    const float* row = fs.draft + (size_t)j * V;
-    constexpr int kPer = 16;
-    float mx = -INFINITY;
-    double sm = 0.0;
-    for (int c0 = s0; c0 < s1; c0 += 64 * kPer) {
-      float a[kPer];
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) {
-        const int v = c0 + 64 * e + lane;
-        a[e] = v < s1 ? row[v] * fs.inv_t : -INFINITY;
-      }
-      float bm = a[0];
-#pragma unroll
-      for (int e = 1; e < kPer; ++e) bm = fmaxf(bm, a[e]);
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) bm = fmaxf(bm, __shfl_xor(bm, o));
-      const float mn = fmaxf(mx, bm);  // wave-uniform
-      if (mn == -INFINITY) continue;
-      if (sm > 0.0) sm *= exp((double)mx - (double)mn);
-      mx = mn;
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) sm += (double)expf(a[e] - mx);
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) sm += __shfl_xor(sm, o);
-    if (lane == 0) {
-      const size_t slot = (size_t)(N + j) * fs.pstride + blockIdx.x;
-      fs.cmax[slot] = mx;
-      fs.csum[slot] = sm;
-      const int32_t x = fs.tokens[j];
-      const int xc = x < 0 ? 0 : (x >= V ? V - 1 : x);
-      if (xc >= s0 && xc < s1) fs.zx[N + j] = row[xc];
-    }
-  }
+__global__ __launch_bounds__(64) void reset_tickets_kernel(unsigned* __restrict__ tickets) {
+  if (threadIdx.x == 0) tickets[0] = 0u;
 }
 
 constexpr int kSweepWaves = 8;
 constexpr int kSweepGroup = 16;
 constexpr size_t kSweepLdsLimit = 150 * 1024;
 
-size_t sweep_lds_bytes(int64_t N, int64_t spk) {
-  return (((size_t)N * (size_t)(spk * 32 + kPad) + 7) & ~(size_t)7) * sizeof(uint16_t) +
-         (size_t)kSweepWaves * 64 * 16;
+size_t sweep_lds_bytes(int64_t N, int64_t d) {
+  return (((size_t)N * (size_t)(d + kPad) + 7) & ~(size_t)7) * sizeof(uint16_t) + (size_t)kSweepWaves * 64 * 16;
+}
+
+template <bool OUT_BF16, int EPI>
+hipError_t launch_sweep_kernel(const SweepPlan& p, const uint16_t* X, const uint16_t* Wp, void* Y, int64_t N,
+                               int64_t d, int64_t V, void* tickets, const FusedStats& fs, hipStream_t stream) {
+  if (tickets == nullptr) return hipErrorInvalidValue;
+  const size_t lds = sweep_lds_bytes(N, d);
+  auto k = sweep_kernel<kSweepWaves, kSweepGroup, true, OUT_BF16, EPI>;
+  hipError_t e = allow_lds(k, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(reset_tickets_kernel, dim3(1), dim3(64), 0, stream, (unsigned*)tickets);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // The fixed share: about 85% of the tiles (measured on the LM-head sweep:
+  // 80-90% equally fast, 70% and 95% slower).
+  const int64_t ntiles = (V + 15) / 16;
+  const int S = (int)(ntiles * 17 / (20 * p.grid));
+  hipLaunchKernelGGL(k, dim3((unsigned)p.grid), dim3(kSweepWaves * 64), lds, stream, X, Wp, Y, (int)N, (int)d, (int)V, S,
+                     (unsigned*)tickets, fs);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -308,42 +353,26 @@ size_t sweep_lds_bytes(int64_t N, int64_t spk) {
 SweepPlan plan_sweep(int64_t N, int64_t d, int64_t V, int cus) {
   SweepPlan p{};
   const int64_t nsteps = d / 32, ntiles = (V + 15) / 16;
-  // One k-group: X whole in LDS (the dispatcher takes the panel kernel otherwise).
-  if (N > 16 || nsteps < 1 || sweep_lds_bytes(N, nsteps) > kSweepLdsLimit) return p;
+  // X whole in LDS and one register group per wave and tile (the dispatcher
+  // takes the panel kernel otherwise).
+  if (N > 16 || nsteps < 1 || nsteps > kSweepWaves * kSweepGroup || sweep_lds_bytes(N, d) > kSweepLdsLimit) return p;
   p.ok = true;
-  p.spk = nsteps;
-  p.kgroups = 1;
   p.grid = ntiles < cus ? ntiles : cus;
   return p;
 }
 
 hipError_t launch_sweep(const SweepPlan& p, const uint16_t* X, const uint16_t* Wp, void* Y, int64_t N, int64_t d,
-                        int64_t V, bool out_bf16, hipStream_t stream) {
-  const size_t lds = sweep_lds_bytes(N, p.spk);
-  auto k = out_bf16 ? sweep_kernel<kSweepWaves, kSweepGroup, true, true, 0>
-                    : sweep_kernel<kSweepWaves, kSweepGroup, true, false, 0>;
-  hipError_t e = allow_lds(k, lds);
-  if (e != hipSuccess) return e;
+                        int64_t V, bool out_bf16, void* tickets, hipStream_t stream) {
   const FusedStats none{};
-  hipLaunchKernelGGL(k, dim3((unsigned)p.grid), dim3(kSweepWaves * 64), lds, stream, X, Wp, Y, (int)N, (int)d, (int)V,
-                     (int)p.spk, none);
-  return hipGetLastError();
+  return out_bf16 ? launch_sweep_kernel<true, 0>(p, X, Wp, Y, N, d, V, tickets, none, stream)
+                  : launch_sweep_kernel<false, 0>(p, X, Wp, Y, N, d, V, tickets, none, stream);
 }
 
-}  // namespace gemm
-
-namespace gemm {
-
 hipError_t launch_sweep_with_stats(const SweepPlan& p, const uint16_t* X, const uint16_t* Wp, float* Y, int64_t N,
-                                   int64_t d, int64_t V, const FusedStats& fs, int64_t* nparts, hipStream_t stream) {
-  const size_t lds = sweep_lds_bytes(N, p.spk);
-  auto k = fs.greedy ? sweep_kernel<kSweepWaves, kSweepGroup, true, false, 2>
-                     : sweep_kernel<kSweepWaves, kSweepGroup, true, false, 1>;
-  hipError_t e = allow_lds(k, lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3((unsigned)p.grid), dim3(kSweepWaves * 64), lds, stream, X, Wp, (void*)Y, (int)N, (int)d,
-                     (int)V, (int)p.spk, fs);
-  e = hipGetLastError();
+                                   int64_t d, int64_t V, const FusedStats& fs, void* tickets, int64_t* nparts,
+                                   hipStream_t stream) {
+  const hipError_t e = fs.greedy ? launch_sweep_kernel<false, 2>(p, X, Wp, Y, N, d, V, tickets, fs, stream)
+                                 : launch_sweep_kernel<false, 1>(p, X, Wp, Y, N, d, V, tickets, fs, stream);
   if (e == hipSuccess) *nparts = p.grid;
   return e;
 }

@@ -889,7 +889,8 @@ size_t xpack_bytes(int64_t N, int64_t d) {
 }
 
 // What the dispatcher will run for a shape, and the workspace it needs: the
-// packed X (deep kernel), then the k-group partials.
+// sweep kernel's tile queue; or the packed X (deep kernel), then the k-group
+// partials.
 struct GemmPlan {
   enum Kind { kSweep, kPanel, kTiled } kind;
   SweepPlan sweep;
@@ -909,6 +910,7 @@ GemmPlan plan_gemm(int64_t N, int64_t d, int64_t V, bool packed, bool with_stats
   g.sweep = plan_sweep(N, d, V, cus);
   if (g.sweep.ok && V >= 65536 && d <= 4096) {
     g.kind = GemmPlan::kSweep;
+    g.workspace = kSweepTicketBytes;
     return g;
   }
   g.kind = GemmPlan::kPanel;
@@ -964,7 +966,8 @@ int64_t gemm_stats_parts(int64_t N, int64_t d, int64_t V, int64_t pstride) {
 }
 
 size_t gemm_stats_scratch_bytes(int64_t N, int64_t d, int64_t V) {
-  return gemm::plan_gemm(N, d, V, true, true).xpack;
+  const gemm::GemmPlan g = gemm::plan_gemm(N, d, V, true, true);
+  return g.kind == gemm::GemmPlan::kSweep ? g.workspace : g.xpack;
 }
 
 hipError_t launch_gemm_with_stats(const uint16_t* X, const uint16_t* Wp, float* Y, int64_t N, int64_t d, int64_t V,
@@ -981,9 +984,9 @@ hipError_t launch_gemm_with_stats(const uint16_t* X, const uint16_t* Wp, float* 
     X = (const uint16_t*)scratch;
   }
   if (g.kind == GemmPlan::kSweep) {
-    // The sweep kernel also summarises the (at most 7) draft rows itself, in
+    // The sweep kernel also summarises the (at most 15) draft rows itself, in
     // the same slots as the target rows.
-    const hipError_t e = launch_sweep_with_stats(g.sweep, X, Wp, Y, N, d, V, fs, nparts, stream);
+    const hipError_t e = launch_sweep_with_stats(g.sweep, X, Wp, Y, N, d, V, fs, scratch, nparts, stream);
     if (e == hipSuccess) *nparts = *nparts_draft = parts;
     return e;
   }
@@ -1022,7 +1025,7 @@ hipError_t launch_skinny_gemm(const uint16_t* X, const uint16_t* W, void* Y, int
   if (g.workspace > 0 && !workspace) return hipErrorInvalidValue;
   switch (g.kind) {
     case GemmPlan::kSweep: {
-      return launch_sweep(g.sweep, X, W, Y, N, d, V, out_bf16, stream);
+      return launch_sweep(g.sweep, X, W, Y, N, d, V, out_bf16, workspace, stream);
     }
     case GemmPlan::kPanel: {
       if (g.xpack > 0) {

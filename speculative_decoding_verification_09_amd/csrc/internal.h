@@ -15,21 +15,24 @@ hipError_t launch_skinny_gemm(const uint16_t* X, const uint16_t* W, void* Y, int
                               bool out_bf16, bool packed, void* workspace, hipStream_t stream);
 
 namespace gemm {
-// The sweep kernel (packed W, at most 16 positions, X whole in LDS: one
-// k-group of spk = d/32 k-steps; ok is false when X does not fit).
+// The sweep kernel (packed W, at most 16 positions, X whole in LDS; ok is
+// false when X does not fit).  tickets: 4 bytes of device memory for its tile
+// queue, reset by the launch itself.
 struct SweepPlan {
   bool ok;
-  int64_t spk, kgroups, grid;
+  int64_t grid;
 };
+constexpr size_t kSweepTicketBytes = 256;
 SweepPlan plan_sweep(int64_t N, int64_t d, int64_t V, int cus);
 hipError_t launch_sweep(const SweepPlan& p, const uint16_t* X, const uint16_t* Wp, void* Y, int64_t N, int64_t d,
-                        int64_t V, bool out_bf16, hipStream_t stream);
+                        int64_t V, bool out_bf16, void* tickets, hipStream_t stream);
 }  // namespace gemm
 struct FusedStats;
 namespace gemm {
-// The sweep kernel with the statistics epilogue (one k-group, fp32 logits).
+// The sweep kernel with the statistics epilogue (fp32 logits).
 hipError_t launch_sweep_with_stats(const SweepPlan& p, const uint16_t* X, const uint16_t* Wp, float* Y, int64_t N,
-                                   int64_t d, int64_t V, const FusedStats& fs, int64_t* nparts, hipStream_t stream);
+                                   int64_t d, int64_t V, const FusedStats& fs, void* tickets, int64_t* nparts,
+                                   hipStream_t stream);
 }  // namespace gemm
 
 // Bytes of device workspace the scoring GEMM needs for this shape (0: none).
@@ -113,7 +116,8 @@ hipError_t launch_draft_stats(const FusedStats& fs, int64_t n_target, int64_t V,
 // (0: the shape does not take the statistics epilogue).
 int64_t gemm_stats_parts(int64_t N, int64_t d, int64_t V, int64_t pstride);
 // Device scratch that launch_gemm_with_stats needs for this shape (the packed
-// copy of X of the deep kernel; 0 for the other kernels), 256-byte multiple.
+// copy of X of the deep kernel, the sweep kernel's tile queue; 0 for the
+// panel kernel), 256-byte multiple.
 size_t gemm_stats_scratch_bytes(int64_t N, int64_t d, int64_t V);
 // The scoring GEMM with the statistics epilogue (packed W, sweep, panel or
 // deep kernel without k-groups, at most kFusedStatsMaxParts partials per row);

@@ -186,11 +186,14 @@ def test_python_binding_rejects_host_tensors():
 
 
 def test_workspace_size_queries():
-    """The scoring GEMM needs no workspace at the LM-head shapes up to 64 positions; shapes with few output rows
+    """The scoring GEMM needs 256 bytes (the sweep kernel's tile queue) at the long-vocabulary shapes up to 16
+    positions and no workspace at the other LM-head shapes up to 64 positions; shapes with few output rows
     and a long k range (the projection that maps 28672 inputs to 8192 outputs) split k and keep fp32 partials;
     the deep kernel keeps a packed copy of X; the step's workspace covers both stages."""
     PK, RM = sd.SPECDEC_WEIGHTS_PACKED, sd.SPECDEC_WEIGHTS_ROW_MAJOR
-    assert sd.logits_workspace_bytes(5, 4096, 128256, PK) == 0
+    assert sd.logits_workspace_bytes(5, 4096, 128256, PK) == 256
+    assert sd.logits_workspace_bytes(16, 4096, 65536, PK) == 256
+    assert sd.logits_workspace_bytes(5, 4096, 65535, PK) == 0
     assert sd.logits_workspace_bytes(64, 8192, 128256, PK) == 0
     assert sd.logits_workspace_bytes(5, 4096, 128256, RM) == 0
     for N in (5, 8, 64):
@@ -199,7 +202,8 @@ def test_workspace_size_queries():
     assert sd.logits_workspace_bytes(0, 4096, 100, PK) == 0
     assert sd.logits_workspace_bytes(5, 4100, 100, PK) == 0  # packed needs d % 32 == 0
     up = lambda n: (n + 255) // 256 * 256
-    assert sd.step_workspace_bytes(1, 4, 4096, 128256, PK) == up(sd.workspace_bytes(1, 4, 128256))
+    assert sd.step_workspace_bytes(1, 4, 4096, 128256, PK) == up(sd.workspace_bytes(1, 4, 128256)) + 256
+    assert sd.step_workspace_bytes(1, 4, 4096, 128256, RM) == up(sd.workspace_bytes(1, 4, 128256))
     big = sd.logits_workspace_bytes(56, 28672, 8192, PK)
     assert sd.step_workspace_bytes(7, 7, 28672, 8192, PK) == max(big, up(sd.workspace_bytes(7, 7, 8192)))
     # The deep kernel (d % 128 == 0; past 128 positions, or past 64 with the step's statistics) reads a packed
@@ -240,8 +244,9 @@ def test_tree_argument_checks():
     assert tv(M=65) == 2
     assert tv(logits=A + 4) == 3
     assert tv(wb=ws - 1) == 5
+    # One tree of 16 nodes scores with the sweep kernel: its tile queue follows the tree arrays.
     assert sd.tree_step_workspace_bytes(1, 16, 4096, 128256, sd.SPECDEC_WEIGHTS_PACKED) == \
-        (sd.tree_workspace_bytes(1, 16, 128256) + 255) // 256 * 256
+        (sd.tree_workspace_bytes(1, 16, 128256) + 255) // 256 * 256 + 256
 
 
 @needs_no_gpu
