@@ -197,15 +197,37 @@ hipError_t launch_tiled(const uint16_t* X, const uint16_t* W, void* Y, int64_t N
 // ---------------------------------------------------------------------------
 // Statistics epilogue of the panel kernel (see below).  xs: the kernel's LDS,
 // free once the main loop has ended.
+// The drafted token of each of a lane's NT tokens (n0 + 16t + lane % 16),
+// clamped into [0, V), or -1 for a token without one: loaded before the main
+// loop (EPI 1 only), so that no global load round trip waits at its end.
+template <int NT, int EPI>
+__device__ __forceinline__ void drafted_tokens(const FusedStats& fs, int V, int n0, int ncols, int lane,
+                                               int (&xd)[NT]) {
+  const int m = lane & 15;
+  const int g1 = (int)fs.gamma + 1;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    xd[t] = -1;
+    if (EPI == 1 && t * 16 + m < ncols) {
+      const int n = n0 + t * 16 + m;
+      const int bq = n / g1, iq = n - bq * g1;
+      if (iq < fs.gamma) {
+        const int32_t x = fs.tokens[bq * fs.gamma + iq];
+        xd[t] = x < 0 ? 0 : (x >= V ? V - 1 : x);
+      }
+    }
+  }
+}
+
 template <int NT, int R, int NW, int EPI>
 __device__ __forceinline__ void panel_stats(const f32x4 (&acc)[R][NT], uint16_t* xs, const FusedStats& fs, int V,
-                                            int n0, int ncols, int vt0, int vb, int wv, int lane) {
+                                            int n0, int ncols, int vt0, int vb, int wv, int lane,
+                                            const int (&xd)[NT]) {
   constexpr int kTok = NT * 16;
   const int m = lane & 15, g = lane >> 4;
   float* lm = (float*)xs;                                     // [NW][kTok] wave maxima
   double* ls = (double*)((char*)xs + 4 * NW * kTok);          // [NW][kTok] wave sums (8-byte aligned)
   int* li = (int*)((char*)xs + 12 * NW * kTok);               // [NW][kTok] argmax indices
-  const int g1 = (int)fs.gamma + 1;
   __syncthreads();  // every wave is done with the X buffers
   // Pass 1: per-token maxima (with the lowest index at T == 0) over the wave's
   // rows; at T > 0 the max of a = z * fl32(1/T) is fl32(max z * fl32(1/T)).
@@ -239,25 +261,19 @@ __device__ __forceinline__ void panel_stats(const f32x4 (&acc)[R][NT], uint16_t*
       lm[wv * kTok + t * 16 + m] = EPI == 1 ? pm[t] * fs.inv_t : pm[t];
       if (EPI == 2) li[wv * kTok + t * 16 + m] = pi[t];
     }
-    if (EPI == 1 && t * 16 + m < ncols) {  // the drafted token's logit, from the lane that holds it
-      const int n = n0 + t * 16 + m;
-      const int bq = n / g1, iq = n - bq * g1;
-      if (iq < fs.gamma) {
-        const int32_t x = fs.tokens[bq * fs.gamma + iq];
-        const int xc = x < 0 ? 0 : (x >= V ? V - 1 : x);
-        const int rel = xc - vt0 * 16 - 4 * g;  // = 16r + j when this lane holds it
-        bool hit = false;
-        float zv = 0.0f;
+    if (EPI == 1 && xd[t] >= 0) {  // the drafted token's logit, from the lane that holds it
+      const int rel = xd[t] - vt0 * 16 - 4 * g;  // = 16r + j when this lane holds it
+      bool hit = false;
+      float zv = 0.0f;
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+      for (int r = 0; r < R; ++r)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (rel == 16 * r + j) {  // static indices only: acc stays in registers
-              hit = true;
-              zv = acc[r][t][j];
-            }
-        if (hit) fs.zx[n] = zv;
-      }
+        for (int j = 0; j < 4; ++j)
+          if (rel == 16 * r + j) {  // static indices only: acc stays in registers
+            hit = true;
+            zv = acc[r][t][j];
+          }
+      if (hit) fs.zx[n0 + t * 16 + m] = zv;
     }
   }
   __syncthreads();
@@ -452,6 +468,8 @@ __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restri
   const int ncols = min(N - n0, NT * 16);
 
   const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, g = lane >> 4;
+  int xd[NT];
+  drafted_tokens<NT, EPI>(fs, V, n0, ncols, lane, xd);
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int vt0 = vb * NW * R + wv * R;              // this wave's first 16-row tile
 
@@ -547,7 +565,7 @@ __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restri
     compute(wa, 0, c);
   }
 
-  if (EPI != 0) panel_stats<NT, R, NW, EPI>(acc, xs, fs, V, n0, ncols, vt0, vb, wv, lane);
+  if (EPI != 0) panel_stats<NT, R, NW, EPI>(acc, xs, fs, V, n0, ncols, vt0, vb, wv, lane, xd);
 
   // Lane holds tokens n0 + 16t + m, vocabulary rows 16*(vt0 + r) + 4g .. +3.
   const bool split = ngroups > 1;
@@ -607,6 +625,8 @@ __global__ __launch_bounds__(256) void deep_kernel(const uint16_t* __restrict__ 
   const int ncols = min(N - n0, NT * 16);
 
   const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, g = lane >> 4;
+  int xd[NT];
+  drafted_tokens<NT, EPI>(fs, V, n0, ncols, lane, xd);
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int vt0 = vb * NW * R + wv * R;
 
@@ -711,7 +731,7 @@ __global__ __launch_bounds__(256) void deep_kernel(const uint16_t* __restrict__ 
     step(std::integral_constant<int, 3>{}, s + 3);
   }
 
-  if (EPI != 0) panel_stats<NT, R, NW, EPI>(acc, xs, fs, V, n0, ncols, vt0, vb, wv, lane);
+  if (EPI != 0) panel_stats<NT, R, NW, EPI>(acc, xs, fs, V, n0, ncols, vt0, vb, wv, lane, xd);
 
   const bool split = ngroups > 1;
   float* part = (float*)Y + (size_t)group * N * V;
