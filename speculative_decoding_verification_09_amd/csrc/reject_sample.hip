@@ -407,31 +407,48 @@ __device__ void select_seq(const float* __restrict__ target, const float* __rest
                            int32_t* __restrict__ out_tokens, const Ws& ws, const DrawDesc& D, int lane) {
   const int64_t ndc = draw_chunks(V);
   const int64_t g1 = gamma + 1;
-  // The first 64 chunk totals in one round of loads.
+  // The first 64*K chunk totals of both weights (all of them up to V = 262144)
+  // in one round of loads, kept in registers for the search below.
+  constexpr int K = 4;
   const double* pr = ws.sres + b * ndc;
   const double* pp = ws.sp + b * ndc;
-  const double pj_r = lane < ndc ? pr[lane] : 0.0;
-  const double pj_p = lane < ndc ? pp[lane] : 0.0;
+  double cr[K], cp[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int64_t c = 64 * k + lane;
+    cr[k] = c < ndc ? pr[c] : 0.0;
+    cp[k] = c < ndc ? pp[c] : 0.0;
+  }
   const DrawRow R = make_row<WARP>(target, draft, draft_kind, B, b, gamma, V, D, inv_t, ws);
-  double tot = 0.0;
-  if (R.has_q) {
-    tot = wave_sum(pj_r);
-    for (int64_t j0 = 64; j0 < ndc; j0 += 64) tot += wave_sum(j0 + lane < ndc ? pr[j0 + lane] : 0.0);
+  double lr = 0.0, lp = 0.0;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    lr += cr[k];
+    lp += cp[k];
   }
+  for (int64_t j0 = 64 * K; j0 < ndc; j0 += 64) {  // longer vocabularies
+    lr += j0 + lane < ndc ? pr[j0 + lane] : 0.0;
+    lp += j0 + lane < ndc ? pp[j0 + lane] : 0.0;
+  }
+  double tot = R.has_q ? wave_sum(lr) : 0.0;
   const bool use_p = !(tot > 0.0);
+  if (use_p) tot = wave_sum(lp);
   const double* part = use_p ? pp : pr;
-  double pj = use_p ? pj_p : pj_r;
-  if (use_p) {
-    tot = wave_sum(pj_p);
-    for (int64_t j0 = 64; j0 < ndc; j0 += 64) tot += wave_sum(j0 + lane < ndc ? pp[j0 + lane] : 0.0);
-  }
   const double t = (double)D.u * tot;
   // First chunk whose running total passes t (or, if rounding leaves none,
-  // the last chunk with mass).
+  // the last chunk with mass), 64 chunks at a time in vocabulary order.
   int64_t cs = -1, clast = 0;
   double before = 0.0, run = 0.0;
   for (int64_t j0 = 0; j0 < ndc && cs < 0; j0 += 64) {
-    if (j0 > 0) pj = j0 + lane < ndc ? part[j0 + lane] : 0.0;
+    double pj = 0.0;
+    if (j0 < 64 * K) {  // from registers, by static indices only
+      const int k = (int)(j0 >> 6);
+#pragma unroll
+      for (int q = 0; q < K; ++q)
+        if (q == k) pj = use_p ? cp[q] : cr[q];
+    } else {
+      pj = j0 + lane < ndc ? part[j0 + lane] : 0.0;
+    }
     const double incl = run + wave_inclusive_scan(pj, lane);
     const uint64_t hit = ballot(j0 + lane < ndc && t < incl);
     const uint64_t pos = ballot(j0 + lane < ndc && pj > 0.0);
