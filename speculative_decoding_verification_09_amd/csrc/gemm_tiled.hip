@@ -568,20 +568,41 @@ __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restri
   if (EPI != 0) panel_stats<NT, R, NW, EPI>(acc, xs, fs, V, n0, ncols, vt0, vb, wv, lane, xd);
 
   // Lane holds tokens n0 + 16t + m, vocabulary rows 16*(vt0 + r) + 4g .. +3.
-  const bool split = ngroups > 1;
-  float* part = (float*)Y + (size_t)group * N * V;
+  if (ngroups > 1) {  // fp32 partials of this k-group
+    float* part = (float*)Y + (size_t)group * N * V;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int64_t v0 = (int64_t)(vt0 + r) * 16 + 4 * g;
-    if (v0 >= V) continue;
+    for (int r = 0; r < R; ++r) {
+      const int64_t v0 = (int64_t)(vt0 + r) * 16 + 4 * g;
+      if (v0 >= V) continue;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int n = t * 16 + m;
-      if (n >= ncols) continue;
-      if (split)
-        store4<false>(part, (size_t)(n0 + n) * V + v0, v0, V, acc[r][t]);
-      else
-        store4<OUT_BF16>(Y, (size_t)(n0 + n) * V + v0, v0, V, acc[r][t]);
+      for (int t = 0; t < NT; ++t) {
+        const int n = t * 16 + m;
+        if (n < ncols) store4<false>(part, (size_t)(n0 + n) * V + v0, v0, V, acc[r][t]);
+      }
+    }
+    return;
+  }
+  // Y goes out through LDS, one token tile at a time, so that consecutive
+  // lanes write consecutive 16 bytes of one row of Y (the block's rows of a
+  // token are contiguous) instead of 64-byte pieces of 16 rows.  The token
+  // rows in LDS are padded by 16 bytes, which spreads a wave's writes over
+  // the banks.
+  constexpr int kRows = NW * R * 16;  // vocabulary rows of the block
+  constexpr int kPitch = kRows + 4;   // floats per token row in LDS
+  float* st = (float*)xs;
+  const int64_t vbase = (int64_t)vb * kRows;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    __syncthreads();  // the previous users of the LDS are done
+#pragma unroll
+    for (int r = 0; r < R; ++r) *(f32x4*)(st + m * kPitch + (wv * R + r) * 16 + 4 * g) = acc[r][t];
+    __syncthreads();
+    for (int i = tid; i < 16 * (kRows / 4); i += kThreads) {
+      const int tok = i / (kRows / 4), q = i - tok * (kRows / 4);
+      const int n = t * 16 + tok;
+      const int64_t v0 = vbase + 4 * q;
+      if (n < ncols && v0 < V)
+        store4<OUT_BF16>(Y, (size_t)(n0 + n) * V + v0, v0, V, *(const f32x4*)(st + tok * kPitch + 4 * q));
     }
   }
 }
@@ -817,9 +838,12 @@ PanelPlan plan_panel(int64_t N, int64_t d, int64_t V, int NT, int R, int NW, int
   return p;
 }
 
+// Two X buffers for the main loop; the output staging afterwards takes one
+// token tile of the block (16 padded rows of NW*R*16 floats).
 template <int NT, int R, int NW, int KS>
 constexpr size_t panel_lds_bytes() {
-  return 2ull * NT * KS * 1024;
+  constexpr size_t x = 2ull * NT * KS * 1024, y = 16ull * (NW * R * 16 + 4) * sizeof(float);
+  return x > y ? x : y;
 }
 
 template <int NT, int R, int NW, int KS>
