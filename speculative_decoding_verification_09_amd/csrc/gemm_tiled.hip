@@ -418,6 +418,37 @@ __device__ __forceinline__ int idle_index(int id, int items, int npass, int& E) 
   return gi >= items ? (slot % npass) * (8 - rem) + ((id & 7) - rem) : -1;
 }
 
+// Writes a block's outputs Y[n0 + n][vb*NW*R*16 + v] (lane: tokens n0 + 16t +
+// lane % 16, rows 16*(vb*NW*R + wv*R + r) + 4*(lane / 16) .. +3) through LDS,
+// one token tile at a time, so that consecutive lanes write consecutive 16
+// bytes of one row of Y (a token's rows of the block are contiguous) instead
+// of 64-byte pieces of 16 rows.  The token rows in LDS are padded by 16 bytes,
+// which spreads a wave's writes over the banks.  st: 16 * (NW*R*16 + 4) floats
+// of LDS whose previous users are done at the first barrier.
+template <int NT, int R, int NW, bool OUT_BF16>
+__device__ __forceinline__ void store_block(const f32x4 (&acc)[R][NT], float* st, void* Y, int V, int n0, int ncols,
+                                            int vb, int wv, int lane) {
+  constexpr int kThreads = NW * 64;
+  constexpr int kRows = NW * R * 16;  // vocabulary rows of the block
+  constexpr int kPitch = kRows + 4;   // floats per token row in LDS
+  const int m = lane & 15, g = lane >> 4, tid = wv * 64 + lane;
+  const int64_t vbase = (int64_t)vb * kRows;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    __syncthreads();  // the previous users of the LDS are done
+#pragma unroll
+    for (int r = 0; r < R; ++r) *(f32x4*)(st + m * kPitch + (wv * R + r) * 16 + 4 * g) = acc[r][t];
+    __syncthreads();
+    for (int i = tid; i < 16 * (kRows / 4); i += kThreads) {
+      const int tok = i / (kRows / 4), q = i - tok * (kRows / 4);
+      const int n = t * 16 + tok;
+      const int64_t v0 = vbase + 4 * q;
+      if (n < ncols && v0 < V)
+        store4<OUT_BF16>(Y, (size_t)(n0 + n) * V + v0, v0, V, *(const f32x4*)(st + tok * kPitch + 4 * q));
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Panel kernel.  Work items are (vocabulary block, k-group, token pass): a
 // vocabulary block is NW*R 16-row tiles, a token pass NT*16 tokens, and a
@@ -582,29 +613,7 @@ __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restri
     }
     return;
   }
-  // Y goes out through LDS, one token tile at a time, so that consecutive
-  // lanes write consecutive 16 bytes of one row of Y (the block's rows of a
-  // token are contiguous) instead of 64-byte pieces of 16 rows.  The token
-  // rows in LDS are padded by 16 bytes, which spreads a wave's writes over
-  // the banks.
-  constexpr int kRows = NW * R * 16;  // vocabulary rows of the block
-  constexpr int kPitch = kRows + 4;   // floats per token row in LDS
-  float* st = (float*)xs;
-  const int64_t vbase = (int64_t)vb * kRows;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    __syncthreads();  // the previous users of the LDS are done
-#pragma unroll
-    for (int r = 0; r < R; ++r) *(f32x4*)(st + m * kPitch + (wv * R + r) * 16 + 4 * g) = acc[r][t];
-    __syncthreads();
-    for (int i = tid; i < 16 * (kRows / 4); i += kThreads) {
-      const int tok = i / (kRows / 4), q = i - tok * (kRows / 4);
-      const int n = t * 16 + tok;
-      const int64_t v0 = vbase + 4 * q;
-      if (n < ncols && v0 < V)
-        store4<OUT_BF16>(Y, (size_t)(n0 + n) * V + v0, v0, V, *(const f32x4*)(st + tok * kPitch + 4 * q));
-    }
-  }
+  store_block<NT, R, NW, OUT_BF16>(acc, (float*)xs, Y, V, n0, ncols, vb, wv, lane);
 }
 
 // Deep panel kernel, for many positions, where the work is bound by the matrix
@@ -754,6 +763,9 @@ __global__ __launch_bounds__(256) void deep_kernel(const uint16_t* __restrict__ 
 
   if (EPI != 0) panel_stats<NT, R, NW, EPI>(acc, xs, fs, V, n0, ncols, vt0, vb, wv, lane, xd);
 
+  // Stored straight from the accumulators (staging them through LDS as the
+  // panel kernel does measured slower here: this kernel is bound by the
+  // matrix cores, and the staging adds two barriers per token tile).
   const bool split = ngroups > 1;
   float* part = (float*)Y + (size_t)group * N * V;
 #pragma unroll
