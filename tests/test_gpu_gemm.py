@@ -185,6 +185,27 @@ def test_pack_layout(V, d):
     assert np.array_equal(got, expect)
 
 
+@pytest.mark.parametrize("N,d,V", [(5, 4096, 65541), (16, 256, 70001)])
+def test_sweep_tile_queue_workspace(orc, N, d, V):
+    """The sweep kernel takes its last tiles from a queue whose counter sits in the workspace and is reset by
+    the call itself: a workspace full of 0xFF bytes, then the same workspace again (left at the previous call's
+    final count), then again with other inputs, all give the exact result (integer inputs)."""
+    need = sd.logits_workspace_bytes(N, d, V, sd.SPECDEC_WEIGHTS_PACKED)
+    assert need == 256
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    for call, seed in enumerate((61, 61, 62)):
+        X_bits = synth.integer_bf16((N, d), 8, seed, N)
+        W_bits = synth.integer_bf16((V, d), 8, seed + 100, V)
+        X = dev_bf16(X_bits)
+        W = weights(W_bits, True)
+        Y = torch.full((N, V), float("nan"), device="cuda", dtype=torch.float32)
+        announce(f"sweep queue call {call} N={N} d={d} V={V}")
+        sd.specdec_verify_logits(X, W, Y, sd.SPECDEC_OUT_F32, workspace=ws)
+        torch.cuda.synchronize()
+        ref = orc.linear(X_bits, W_bits)
+        assert np.array_equal(host(Y).astype(np.float64), ref), (call, np.nanmax(np.abs(host(Y) - ref)))
+
+
 def test_nan_poisoned_output_fully_written(orc):
     """Every output entry is written (the buffer starts as NaN)."""
     X = synth.normal_bf16((37, 72), 1.0, 47, 0)
