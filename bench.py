@@ -148,6 +148,31 @@ def main():
     torch.cuda.synchronize()
     gemm_ms = ev0.elapsed_time(ev1) / K
 
+    # ---- the reject stage alone on the step's logits (specdec_reject_sample: statistics pass, then the rule),
+    # warm (the logits just written, K back-to-back calls) and flushed (a 512 MiB write between calls, each call
+    # between its own two events)
+    rule = {}
+    if T > 0:
+        rws = sd.new_workspace(B, g, V)
+        tl = logits.view(B, g + 1, V)
+        rule["warm_ms"] = _time_launches(lambda: sd.specdec_reject_sample(tl, draft, tokens, T, uni, out_tok, out_num,
+                                                                          rws, stream=stream), K, args.warmup, stream)
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        times = []
+        for _ in range(10):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            sd.specdec_reject_sample(tl, draft, tokens, T, uni, out_tok, out_num, rws, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        rule["flushed_ms"] = float(np.median(times))
+        del flush, rws
+        # the step's own tokens again (the rule above wrote the same outputs from the same inputs)
+        step()
+        torch.cuda.synchronize()
+
     gemm_bytes, step_bytes = algorithmic_bytes(w)
     gemm_gbps = gemm_bytes / (gemm_ms * 1e-3) / 1e9
     step_gbps = step_bytes / (ms_step * 1e-3) / 1e9
@@ -164,18 +189,34 @@ def main():
         uh = synth.step_uniforms(w)
         toks = tokens.cpu().numpy()
         dr = draft.cpu().numpy() if draft is not None else None
-        reps = 0
+        # One host core: the oracle is single-threaded C; the process is pinned to the core it runs on for the
+        # duration, so that the scheduler does not move it.
+        pinned = None
+        if hasattr(os, "sched_setaffinity"):
+            old_mask = os.sched_getaffinity(0)
+            core = min(old_mask)
+            os.sched_setaffinity(0, {core})
+            pinned = core
+        reps, t_lin, t_rule = 0, 0.0, 0.0
         t0 = time.perf_counter()
         while reps == 0 or time.perf_counter() - t0 < args.cpu_seconds:
             b = reps % B
+            ta = time.perf_counter()
             zb = orc.linear(Xh[b * rows_per_seq:(b + 1) * rows_per_seq], Wh).astype(np.float32)
+            tb = time.perf_counter()
             orc.verify(zb[None], dr[b:b + 1] if dr is not None else None, toks[b:b + 1], uh[b:b + 1], T)
+            t_lin += tb - ta
+            t_rule += time.perf_counter() - tb
             reps += 1
         cpu_s = time.perf_counter() - t0
+        if pinned is not None:
+            os.sched_setaffinity(0, old_mask)
         cpu = {"value": reps * rows_per_seq / cpu_s, "unit": "positions/s", "cores": 1, "kind": "oracle",
                "sample": f"{reps} sequence(s) of {rows_per_seq} positions (B={B}: "
                          f"{'whole steps' if B == 1 else 'sequences of one step'}): fp64 scoring over the full "
-                         f"{V}x{d} weights plus the rule, single-threaded C, {cpu_s:.1f} s"}
+                         f"{V}x{d} weights plus the rule, single-threaded C, {cpu_s:.1f} s",
+               "scoring_s_per_sequence": t_lin / reps, "rule_s_per_sequence": t_rule / reps,
+               "pinned_core": pinned, "host_cpus": os.cpu_count(), "cpu_model": _cpu_model()}
 
     out = {
         "metric": METRIC,
@@ -196,6 +237,7 @@ def main():
         "step_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
         "step_bytes": step_bytes,
         "emitted_tokens_per_s": emitted / (ms_step * 1e-3),
+        "reject_stage": rule or None,
         "roofline": {"kernel": "scoring GEMM (specdec_verify_logits)", "bound": "hbm", "achieved": gemm_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gemm_gbps / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(w.name, args.layout), "bytes_per_launch": gemm_bytes,
@@ -260,6 +302,17 @@ def step_inputs(w, layout_name: str):
     torch.cuda.synchronize()
 
     return X, W, logits, out_tok, out_num, ws, gemm_ws, uni, draft, tokens
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _time_launches(fn, K: int, warmup: int, stream) -> float:
