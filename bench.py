@@ -99,8 +99,8 @@ def main():
         return
     w = synth.WORKLOADS[args.workload]
     if w.d == 0:
-        print(f"workload {w.name} has no scoring GEMM; pick an LM-head workload", file=sys.stderr)
-        sys.exit(2)
+        toy_reject(args, w)
+        return
     B, g, V, d, T = w.B, w.gamma, w.V, w.d, w.temperature
     N = B * (g + 1)
     dev = torch.device("cuda")
@@ -302,6 +302,62 @@ def step_inputs(w, layout_name: str):
     torch.cuda.synchronize()
 
     return X, W, logits, out_tok, out_num, ws, gemm_ws, uni, draft, tokens
+
+
+def toy_reject(args, w):
+    """The reject-only toy workload (no scoring GEMM): one target row z ~ N(0, target_std) over V tokens and its
+    draft z + N(0, noise_std), replicated over B trials of gamma drafts; drafted tokens x ~ q drawn with the
+    library itself (gamma = 0 calls), per-position uniforms from the seeded generator.  Times
+    specdec_reject_sample (K back-to-back calls between two events, inputs resident) and reports, from the
+    outputs, the first emitted token's total-variation distance to p and the mean emitted count against the
+    closed form (1 - alpha^(gamma+1)) / (1 - alpha), alpha = sum min(p, q)."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_verification_09_amd as sd
+    import synth
+
+    B, g, V, T = w.B, w.gamma, w.V, w.temperature
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    z = synth.normal_f32((1, V), w.target_std, w.seed, synth.STREAM_TARGET)
+    dz = z + synth.normal_f32((1, V), w.noise_std, w.seed, synth.STREAM_DRAFT_NOISE)
+    zt = torch.from_numpy(z).to(dev).expand(B, g + 1, V).contiguous()
+    zd = torch.from_numpy(dz).to(dev).expand(B, g, V).contiguous()
+    du = torch.zeros((B * g, 1, 2), dtype=torch.float32, device=dev)
+    du[:, 0, 1] = torch.from_numpy(synth.draft_sample_uniforms(w).reshape(-1)).to(dev)
+    dt = torch.empty((B * g, 1), dtype=torch.int32, device=dev)
+    dn = torch.empty((B * g,), dtype=torch.int32, device=dev)
+    sd.specdec_reject_sample(zd.view(B * g, 1, V), None, torch.empty((B * g, 0), dtype=torch.int32, device=dev), T,
+                             du, dt, dn, sd.new_workspace(B * g, 0, V))
+    tokens = dt.view(B, g).contiguous()
+    uni = torch.from_numpy(synth.step_uniforms(w)).to(dev)
+    out_tok = torch.empty((B, g + 1), dtype=torch.int32, device=dev)
+    out_num = torch.empty((B,), dtype=torch.int32, device=dev)
+    ws = sd.new_workspace(B, g, V)
+    torch.cuda.synchronize()
+    ms = _time_launches(lambda: sd.specdec_reject_sample(zt, zd, tokens, T, uni, out_tok, out_num, ws, stream=stream),
+                        args.steps, args.warmup, stream)
+    first = out_tok[:, 0].cpu().numpy()
+    num = out_num.cpu().numpy().astype(np.float64)
+
+    def softmax(a):
+        e = np.exp((a.astype(np.float64) / T) - (a.astype(np.float64) / T).max())
+        return e / e.sum()
+
+    p, q = softmax(z[0]), softmax(dz[0])
+    tv = 0.5 * np.abs(np.bincount(first, minlength=V) / B - p).sum()
+    alpha = float(np.minimum(p, q).sum())
+    expected = (1 - alpha ** (g + 1)) / (1 - alpha)
+    print(json.dumps({
+        "metric": "verified positions/sec (reject stage alone)", "value": B * (g + 1) / (ms * 1e-3),
+        "unit": "positions/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "gamma": g, "V": V, "temperature": T},
+        "input_bytes": (B * (g + 1) * V + B * g * V) * 4,
+        "tv_first_token": tv, "mean_emitted": float(num.mean()), "closed_form_emitted": expected,
+        "emitted_se": float(num.std() / np.sqrt(B)),
+    }))
 
 
 def _cpu_model() -> str:

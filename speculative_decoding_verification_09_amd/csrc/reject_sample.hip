@@ -631,6 +631,188 @@ __global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
   }
 }
 
+// 2''. Small vocabularies (V <= kSmallV, T > 0, no warping): the whole rule
+//     for one sequence in one wave, for batches of many short rows (such as
+//     many trials over a few tokens), where a workgroup per sequence and
+//     per-chunk partials in the workspace would leave the GPU mostly idle.
+//     The arithmetic is that of kernels 1-3 with one statistics chunk and one
+//     draw chunk per row, so both paths give the same bits: lane l holds
+//     entries 4l .. 4l+3 of a row (row max and sum of the four fp32 terms, as
+//     in the statistics kernel; weights and their totals, as in the draw
+//     kernel), and the final rescan takes 16 consecutive entries per lane, as
+//     in the select.  Rows are loaded four at a time.
+constexpr int kSmallV = 256;
+template <bool VEC>
+__device__ __forceinline__ void load4(const float* __restrict__ row, int64_t V, int lane, float fill, float (&x)[4]) {
+  const int64_t v = 4 * (int64_t)lane;
+  if (VEC && v + 3 < V) {
+    const f32x4 t = *(const f32x4*)(row + v);
+    x[0] = t[0];
+    x[1] = t[1];
+    x[2] = t[2];
+    x[3] = t[3];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = v + e < V ? row[v + e] : fill;
+  }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kWavesPerBlock * 64) void small_rule_kernel(
+    const float* __restrict__ target, const float* __restrict__ draft, int draft_kind,
+    const int32_t* __restrict__ tokens, const float* __restrict__ uniforms, int64_t B, int64_t gamma, int64_t V,
+    float inv_t, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_num, float* __restrict__ out_probs) {
+  const int lane = threadIdx.x & 63;
+  const int64_t b = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (b >= B) return;  // whole waves; no barriers below
+  const int64_t g1 = gamma + 1;
+  const bool q_logits = draft_kind == 0;
+  const bool has_row = lane < g1, drafted = lane < gamma;
+  const float u_acc = drafted ? uniforms[(b * g1 + lane) * 2 + 0] : 0.0f;
+  const float u_smp = has_row ? uniforms[(b * g1 + lane) * 2 + 1] : 0.0f;
+  const int xi = drafted ? clamp_token(tokens[b * gamma + lane], V) : 0;
+  const float q_given = drafted && draft_kind == 1 ? draft[(size_t)(b * gamma + lane) * V + xi]
+                                                  : (draft_kind == 2 ? 1.0f : 0.0f);
+  // Row j < g1: target row j; g1 <= j < g1 + gamma: draft row j - g1 (draft logits).  Lane i keeps the
+  // statistics of target row i (and draft row i): the max of a, Z and the drafted token's probability.
+  const int nrows = (int)(q_logits ? g1 + gamma : g1);
+  float mt = 0.0f, mq = 0.0f, px = 0.0f, qx = q_given;
+  double zt = 1.0, zq = 1.0;
+  const float c1 = inv_t * kLog2e;
+  for (int j0 = 0; j0 < nrows; j0 += 4) {
+    float x[4][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // rows past the last read the last one again (never used)
+      const int j = min(j0 + q, nrows - 1);
+      const float* row = j < g1 ? target + (size_t)(b * g1 + j) * V : draft + (size_t)(b * gamma + (j - g1)) * V;
+      load4<VEC>(row, V, lane, -INFINITY, x[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = j0 + q;
+      if (j >= nrows) break;
+      const int i = j < g1 ? j : j - (int)g1;  // position of the row
+      const float mx = wave_max(fmaxf(fmaxf(x[q][0], x[q][1]), fmaxf(x[q][2], x[q][3]))) * inv_t;
+      double s = 0.0;
+      if (mx > -INFINITY) {
+        const float c2 = mx * kLog2e;
+        const float s4 = (__builtin_amdgcn_exp2f(fmaf(x[q][0], c1, -c2)) + __builtin_amdgcn_exp2f(fmaf(x[q][1], c1, -c2))) +
+                         (__builtin_amdgcn_exp2f(fmaf(x[q][2], c1, -c2)) + __builtin_amdgcn_exp2f(fmaf(x[q][3], c1, -c2)));
+        s = (double)s4;
+      }
+      const double Z = wave_sum(s);
+      // The drafted token's logit, from the lane that holds it.
+      const int xr = i < gamma ? __shfl(xi, i) : 0;
+      float zx = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) zx = (xr & 3) == e ? x[q][e] : zx;
+      zx = __shfl(zx, xr >> 2);
+      const float pr = i < gamma ? (float)(exp((double)(zx * inv_t) - (double)mx) / Z) : 0.0f;
+      if (lane == i) {
+        if (j < g1) {
+          mt = mx;
+          zt = Z;
+          px = pr;
+        } else {
+          mq = mx;
+          zq = Z;
+          qx = pr;
+        }
+      }
+    }
+  }
+  bool reject = false;
+  if (drafted) {
+    const float ratio = px / (qx > kQFloor ? qx : kQFloor);
+    const float thr = ratio < 1.0f ? ratio : 1.0f;
+    reject = !(u_acc < thr);
+  }
+  const uint64_t rej = ballot(reject);
+  const int k = rej ? (int)__builtin_ctzll(rej) : (int)gamma;
+  if (has_row && lane != k) out_tokens[b * g1 + lane] = lane < k ? xi : -1;
+  if (drafted && out_probs) {
+    out_probs[(b * gamma + lane) * 2 + 0] = px;
+    out_probs[(b * gamma + lane) * 2 + 1] = qx;
+  }
+  if (lane == 0) out_num[b] = k + 1;
+  // The draw at row k, with the draw kernel's weights.
+  DrawDesc D;
+  D.k = k;
+  D.mp = __shfl(mt, k);
+  D.ip = (float)(1.0 / __shfl(zt, k));
+  const int kq = k < gamma ? k : 0;
+  D.mq = __shfl(mq, kq);
+  D.iq = (float)(1.0 / __shfl(zq, kq));
+  D.u = __shfl(u_smp, k);
+  D.xk = k < gamma ? __shfl(xi, k) : -1;
+  D.pad = 0.0f;
+  DrawRow R;
+  R.zp = target + (size_t)(b * g1 + k) * V;
+  R.has_q = k < gamma;
+  R.zq = R.has_q && draft_kind != 2 ? draft + (size_t)(b * gamma + k) * V : nullptr;
+  R.mp = D.mp;
+  R.ip = D.ip;
+  R.mq = D.mq;
+  R.iq = D.iq;
+  R.inv_t = inv_t;
+  R.kind = draft_kind;
+  R.xk = D.xk;
+  R.pk = R.qk = 0u;
+  R.pi = R.qi = 0x7fffffff;
+  float zp4[4], zq4[4];
+  load4<VEC>(R.zp, V, lane, -INFINITY, zp4);
+  if (R.zq) load4<VEC>(R.zq, V, lane, draft_kind == 1 ? 0.0f : -INFINITY, zq4);
+  double sr = 0.0, sp = 0.0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float p, r;
+    weights<false>(R, 4 * lane + e, zp4[e], R.zq ? zq4[e] : 0.0f, p, r);
+    sr += (double)r;
+    sp += (double)p;
+  }
+  double tot = R.has_q ? wave_sum(sr) : 0.0;
+  const bool use_p = !(tot > 0.0);
+  if (use_p) tot = wave_sum(sp);
+  const double t = (double)D.u * tot;
+  // Rescan: lane l takes the 16 consecutive entries starting at 16l (one chunk, nothing before it).
+  const int64_t s0 = 16 * (int64_t)lane;
+  float w[16];
+  double lsum = 0.0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t v = s0 + 4 * j;
+    float ap[4], aq[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ap[e] = v + e < V ? R.zp[v + e] : -INFINITY;
+      if (R.zq) aq[e] = v + e < V ? R.zq[v + e] : (R.kind == 1 ? 0.0f : -INFINITY);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float p, r;
+      weights<false>(R, v + e, ap[e], R.zq ? aq[e] : 0.0f, p, r);
+      w[4 * j + e] = use_p ? p : r;
+      lsum += (double)w[4 * j + e];
+    }
+  }
+  const double incl = wave_inclusive_scan(lsum, lane);
+  double C = incl - lsum;
+  int hit = -1, lastpos = -1;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    C += (double)w[e];
+    if (w[e] > 0.0f) {
+      lastpos = (int)(s0 + e);
+      if (hit < 0 && t < C) hit = (int)(s0 + e);
+    }
+  }
+  const uint64_t hits = ballot(hit >= 0);
+  lastpos = wave_max_i(lastpos);
+  int tok = hits ? __shfl(hit, __builtin_ctzll(hits)) : lastpos;
+  if (tok < 0 || tok >= V) tok = 0;  // no positive weight anywhere (non-finite inputs)
+  if (lane == 0) out_tokens[b * g1 + k] = tok;
+}
+
 // 2'. Greedy decide (T == 0): one workgroup per sequence.  Wave w merges the
 //     chunk partials of rows w, w + kGreedyWaves, ... (each lane issuing four
 //     loads at a time), leaving row i's argmax in LDS; wave 0 then compares
@@ -969,6 +1151,16 @@ hipError_t launch_reject_sample(const RejectArgs& a, hipStream_t stream) {
   const dim3 blk(kWavesPerBlock * 64);
   const dim3 g1(blocks_for(n_rows * stat_chunks(a.V), kWavesPerBlock));
   const bool warp = warp_active(a);
+  if (!greedy && !warp && a.V <= kSmallV) {  // one wave per sequence does the whole rule
+    const dim3 gs(blocks_for(a.B, kWavesPerBlock));
+    if (vec)
+      hipLaunchKernelGGL(small_rule_kernel<true>, gs, blk, 0, stream, a.target, a.draft, a.draft_kind, a.tokens,
+                         a.uniforms, a.B, a.gamma, a.V, inv_t, a.out_tokens, a.out_num, a.out_probs);
+    else
+      hipLaunchKernelGGL(small_rule_kernel<false>, gs, blk, 0, stream, a.target, a.draft, a.draft_kind, a.tokens,
+                         a.uniforms, a.B, a.gamma, a.V, inv_t, a.out_tokens, a.out_num, a.out_probs);
+    return hipGetLastError();
+  }
   if (warp) {  // the per-row cuts, read by every later kernel
     const hipError_t ew = launch_warp_cuts(a.target, a.draft, n_target, n_rows, a.V, inv_t, a.top_k, a.top_p,
                                            ws.wkey, ws.widx, stream);
