@@ -150,7 +150,7 @@ def test_greedy_ties_lowest_index(orc):
 # ---------------------------------------------------------------------------
 # Edge cases.
 
-@pytest.mark.parametrize("V", [1, 2, 3, 5, 31, 1023, 1024, 1025, 2049, 4099])
+@pytest.mark.parametrize("V", [1, 2, 3, 5, 31, 64, 255, 256, 257, 1023, 1024, 1025, 2049, 4099])
 def test_vocab_sizes(orc, V):
     B, g = 300, 3
     zt, zd, x, u = _sampled_inputs(orc, B, g, V, 2.0, 1.0, 1.0, seed=100 + V)
@@ -159,11 +159,12 @@ def test_vocab_sizes(orc, V):
     _check(tok, num, orc.verify(zt, zd, x, u, 1.0), max_excused_frac=0.01)
 
 
-@pytest.mark.parametrize("g", [0, 1, 63])
-def test_gamma_extremes(orc, g):
-    B, V = 200 if g < 63 else 8, 777
-    zt, zd, x, u = _sampled_inputs(orc, B, g, V, 1.5, 0.7, 0.9, seed=200 + g)
-    announce(f"reject gamma={g}")
+# V = 777 takes the general path; V = 200 the one-wave-per-sequence kernel for small vocabularies.
+@pytest.mark.parametrize("g,V", [(0, 777), (1, 777), (63, 777), (0, 200), (63, 200), (62, 37)])
+def test_gamma_extremes(orc, g, V):
+    B = 200 if g < 62 else 8
+    zt, zd, x, u = _sampled_inputs(orc, B, g, V, 1.5, 0.7, 0.9, seed=200 + g if V == 777 else 300 + g + V)
+    announce(f"reject gamma={g} V={V}")
     tok, num, _ = reject(zt, zd if g else None, x, u, 0.9)
     _check(tok, num, orc.verify(zt, zd, x, u, 0.9), max_excused_frac=0.01)
     if g == 0:
