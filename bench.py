@@ -31,7 +31,7 @@ GEMM_SOURCES = [os.path.join(HERE, "speculative_decoding_verification_09_amd", "
 # counters were taken on: once that source changes, the record no longer describes the kernel and traffic is null.
 MEASURED_TRAFFIC = {
     ("lmhead_b1_g4", "packed"): {"fetch_bytes": 1051154653, "write_bytes": 2616848,
-                                 "source_sha256": "f508233baa6b8fe5e51d91ca4d96b32d9ca488d6fb9348d0868028bf0c2ffc8e"},
+                                 "source_sha256": "35f675362734d11c2eddaf9aedd8e3b18b35e6273c3fed0475eb69aedfa4d403"},
 }
 
 

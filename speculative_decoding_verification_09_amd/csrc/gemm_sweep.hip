@@ -21,10 +21,11 @@
 //
 // Sweep kernel: persistent, one workgroup per CU.  A workgroup takes one
 // 16-row tile at a time; its 8 waves split the tile's k range and each streams
-// a contiguous slice, the next work unit prefetched into a second register
-// buffer; partial sums meet in LDS in a fixed order.  At any moment the whole
-// GPU reads within a window of about (#CUs x tile size), which keeps HBM
-// streaming close to a plain sequential read.
+// a contiguous slice, the next tile prefetched into a second register buffer;
+// partial sums meet in LDS in a fixed order.  At any moment the whole GPU
+// reads within a window of about (#CUs x tile size), which keeps HBM
+// streaming close to a plain sequential read; the last tiles come from a
+// queue, so that every workgroup finishes at about the same time.
 #include "gemm_common.h"
 
 namespace specdec {
