@@ -257,7 +257,7 @@ int specdec_verify_step(const void* X, const void* W, int weight_layout, const f
   // logits again.
   specdec::FusedStats fs;
   if (weight_layout == SPECDEC_WEIGHTS_PACKED && specdec::reject_fused_stats(a, &fs) &&
-      specdec::gemm_stats_parts(N, d, V, fs.pstride, fs.greedy) > 0) {
+      specdec::gemm_stats_parts(N, d, V, fs.pstride) > 0) {
     int64_t nparts = 0, nparts_draft = 0;
     void* scratch = (char*)workspace + stats_scratch_offset(specdec::reject_workspace_bytes(B, gamma, V));
     if (specdec::launch_gemm_with_stats((const uint16_t*)X, (const uint16_t*)W, logits, N, d, V, fs, &nparts,
@@ -362,7 +362,7 @@ int specdec_tree_verify_step(const void* X, const void* W, int weight_layout, co
   const hipStream_t s = (hipStream_t)stream;
   specdec::FusedStats fs;
   if (weight_layout == SPECDEC_WEIGHTS_PACKED && specdec::tree_fused_stats(t, &fs) &&
-      specdec::gemm_stats_parts(N, d, V, fs.pstride, fs.greedy) > 0) {
+      specdec::gemm_stats_parts(N, d, V, fs.pstride) > 0) {
     int64_t nparts = 0, nparts_draft = 0;
     void* scratch = (char*)workspace + stats_scratch_offset(specdec::tree_workspace_bytes(B, M, V));
     if (specdec::launch_gemm_with_stats((const uint16_t*)X, (const uint16_t*)W, logits, N, d, V, fs, &nparts,

@@ -1007,15 +1007,17 @@ bool idle_drafts_fit(const GemmPlan& g, int64_t nd, int64_t d, int64_t V, int64_
 }  // namespace
 }  // namespace gemm
 
-int64_t gemm_stats_parts(int64_t N, int64_t d, int64_t V, int64_t pstride, bool greedy) {
+int64_t gemm_stats_parts(int64_t N, int64_t d, int64_t V, int64_t pstride) {
   using namespace gemm;
   if (N > kFusedStatsMaxRows) return 0;
   const GemmPlan g = plan_gemm(N, d, V, true, true);
-  // The argmax epilogue on the deep kernel at 65-128 positions is slower than
-  // the plain 8x4 panel followed by the argmax statistics kernel (measured on
-  // 8 trees of 16 nodes, d = 4096, V = 128256: 248.6 us against 235-241 us for
-  // the tree step).
-  if (greedy && g.kind == GemmPlan::kPanel && g.shape.deep && N <= 128) return 0;
+  // At 65-128 positions with d <= 4096 the deep kernel with an epilogue is
+  // slower than the plain 8x4 panel followed by the statistics kernel
+  // (measured, V = 128256, d = 4096: 8 trees of 16 nodes 248.6 us against
+  // 235-241 us for the tree step; a softmax step at N = 128, 264-268 us
+  // against 240-253 us).  With d = 8192 the epilogue pays for itself
+  // (N = 96: 402-403 us fused against 416-419 us).
+  if (g.kind == GemmPlan::kPanel && g.shape.deep && N <= 128 && d <= 4096) return 0;
   int64_t parts = 0;
   if (g.kind == GemmPlan::kSweep) {
     parts = g.sweep.grid;
@@ -1035,7 +1037,7 @@ hipError_t launch_gemm_with_stats(const uint16_t* X, const uint16_t* Wp, float* 
                                   const FusedStats& fs, int64_t* nparts, int64_t* nparts_draft, void* scratch,
                                   hipStream_t stream) {
   using namespace gemm;
-  const int64_t parts = gemm_stats_parts(N, d, V, fs.pstride, fs.greedy);
+  const int64_t parts = gemm_stats_parts(N, d, V, fs.pstride);
   if (parts == 0) return hipErrorNotSupported;
   const GemmPlan g = plan_gemm(N, d, V, true, true);
   if (g.xpack > 0) {

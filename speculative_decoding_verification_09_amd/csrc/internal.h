@@ -113,9 +113,9 @@ hipError_t launch_reject_after_fused(const RejectArgs& a, int64_t nparts, int64_
 // (their count in *nparts); independent of the scoring kernel.
 hipError_t launch_draft_stats(const FusedStats& fs, int64_t n_target, int64_t V, int64_t* nparts, hipStream_t stream);
 // Partials per row that launch_gemm_with_stats will produce for this shape
-// and epilogue (greedy: argmax; 0: the shape does not take the statistics
-// epilogue, or is faster without it).
-int64_t gemm_stats_parts(int64_t N, int64_t d, int64_t V, int64_t pstride, bool greedy);
+// (0: the shape does not take the statistics epilogue, or is faster without
+// it).
+int64_t gemm_stats_parts(int64_t N, int64_t d, int64_t V, int64_t pstride);
 // Device scratch that launch_gemm_with_stats needs for this shape (the packed
 // copy of X of the deep kernel, the sweep kernel's tile queue; 0 for the
 // panel kernel), 256-byte multiple.

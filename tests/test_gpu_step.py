@@ -149,9 +149,12 @@ FUSED = [
     # long vocabularies, up to 16 positions: the sweep kernel's epilogue (draft rows in its spare workgroups)
     ("sweep_logits", 1, 4, 256, 65600, 1.0), ("sweep_16", 2, 7, 128, 66001, 0.9), ("sweep_greedy", 3, 4, 64, 65536, 0.0),
     ("sweep_probs", 2, 3, 128, 65541, 1.0), ("sweep_onehot", 2, 5, 128, 65600, 1.0),
-    # past 64 positions with d % 128 == 0: the deep kernel's epilogue (packed X in the scratch)
-    ("deep_greedy", 20, 4, 128, 3001, 0.0), ("deep_logits", 24, 5, 256, 5000, 1.0),
-    ("deep_probs", 16, 7, 384, 4099, 0.8), ("deep_onehot", 33, 3, 128, 2050, 1.2),
+    # past 128 positions (past 64 when d > 4096) with d % 128 == 0: the deep kernel's epilogue (packed X in the
+    # scratch)
+    ("deep_greedy", 26, 4, 128, 3001, 0.0), ("deep_logits", 24, 5, 256, 5000, 1.0),
+    ("deep_probs", 17, 7, 384, 4099, 0.8), ("deep_onehot", 33, 3, 128, 2050, 1.2),
+    # 65-128 positions with d <= 4096: the plain GEMM, then the statistics kernel
+    ("unfused_greedy_n100", 20, 4, 128, 3001, 0.0), ("unfused_probs_n128", 16, 7, 384, 4099, 0.8),
     ("deep_passes_greedy", 64, 4, 128, 1500, 0.0),
     # draft logits summarised by the panel grid's idle workgroups during the GEMM (long k, many draft rows)
     ("panel_idle_drafts", 4, 4, 4096, 65600, 0.9), ("panel_idle_drafts_tail", 3, 7, 4096, 65541, 1.3),
