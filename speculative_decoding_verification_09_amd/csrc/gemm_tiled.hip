@@ -241,12 +241,15 @@ __device__ __forceinline__ void panel_stats(const f32x4 (&acc)[R][NT], uint16_t*
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        // Bitwise tests and selects: short-circuit tests compile to a branch
+        // per element, which at one wave per SIMD costs microseconds here.
         const int v = (vt0 + r) * 16 + 4 * g + j;
         const float a = acc[r][t][j];
-        if (v < V && (a > pm[t] || (EPI == 2 && a == pm[t] && v < pi[t]))) {
-          pm[t] = a;
-          pi[t] = v;
-        }
+        bool take = a > pm[t];
+        if (EPI == 2) take = take | ((a == pm[t]) & (v < pi[t]));
+        take = take & (v < V);
+        pm[t] = take ? a : pm[t];
+        pi[t] = take ? v : pi[t];
       }
 #pragma unroll
     for (int o = 16; o <= 32; o <<= 1) {
