@@ -231,6 +231,10 @@ __device__ __forceinline__ void panel_stats(const f32x4 (&acc)[R][NT], uint16_t*
   __syncthreads();  // every wave is done with the X buffers
   // Pass 1: per-token maxima (with the lowest index at T == 0) over the wave's
   // rows; at T > 0 the max of a = z * fl32(1/T) is fl32(max z * fl32(1/T)).
+  // Bitwise tests and selects throughout, and each shuffle round issued for
+  // all NT tokens before any of them is merged: with short-circuit tests every
+  // element and every merge became a branch, and each token's two shuffles
+  // waited in turn, which at one wave per SIMD cost microseconds here.
   float pm[NT];
   int pi[NT];
 #pragma unroll
@@ -241,8 +245,6 @@ __device__ __forceinline__ void panel_stats(const f32x4 (&acc)[R][NT], uint16_t*
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        // Bitwise tests and selects: short-circuit tests compile to a branch
-        // per element, which at one wave per SIMD costs microseconds here.
         const int v = (vt0 + r) * 16 + 4 * g + j;
         const float a = acc[r][t][j];
         bool take = a > pm[t];
@@ -251,15 +253,29 @@ __device__ __forceinline__ void panel_stats(const f32x4 (&acc)[R][NT], uint16_t*
         pm[t] = take ? a : pm[t];
         pi[t] = take ? v : pi[t];
       }
+  }
 #pragma unroll
-    for (int o = 16; o <= 32; o <<= 1) {
-      const float om = __shfl_xor(pm[t], o);
-      const int oi = __shfl_xor(pi[t], o);
-      if (om > pm[t] || (om == pm[t] && oi < pi[t])) {
-        pm[t] = om;
-        pi[t] = oi;
+  for (int o = 16; o <= 32; o <<= 1) {
+    float om[NT];
+    int oi[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      om[t] = __shfl_xor(pm[t], o);
+      if (EPI == 2) oi[t] = __shfl_xor(pi[t], o);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (EPI == 2) {
+        const bool take = (om[t] > pm[t]) | ((om[t] == pm[t]) & (oi[t] < pi[t]));
+        pm[t] = take ? om[t] : pm[t];
+        pi[t] = take ? oi[t] : pi[t];
+      } else {
+        pm[t] = om[t] > pm[t] ? om[t] : pm[t];
       }
     }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
     if (g == 0) {
       lm[wv * kTok + t * 16 + m] = EPI == 1 ? pm[t] * fs.inv_t : pm[t];
       if (EPI == 2) li[wv * kTok + t * 16 + m] = pi[t];
