@@ -935,7 +935,15 @@ PanelShape panel_shape(int64_t N, int64_t d, int64_t V, bool with_stats) {
   // (128 x 64 tiles per wave, one wave per SIMD) past 128 positions, and past
   // 64 with the statistics epilogue; at 65 to 128 positions without it the
   // 8x4 and 8x2 panels measured as fast or faster.
-  if (d % 128 == 0 && (N > 128 || (N > 64 && with_stats))) return PanelShape{8, 4, 4, 1, true};
+  // Its token pass is 128 positions, or on long vocabularies 192 where that
+  // takes fewer passes (N = 129-192, 257-384, ...): each pass streams all of
+  // W from L2 into the CUs, the kernel's limit, so at N = 320, V = 152064
+  // two passes of 192 ran the step ~22 us (3.5%) faster than passes of 128,
+  // 128 and 64.  On the 28672-row projection at N = 512 three passes of 192
+  // took 329 us against 257 us for four of 128: with 112 vocabulary blocks
+  // the work items fill the CUs in fewer, more uneven rounds.
+  if (d % 128 == 0 && (N > 128 || (N > 64 && with_stats)))
+    return PanelShape{big_v && (N + 191) / 192 < (N + 127) / 128 ? 12 : 8, 4, 4, 1, true};
   if (N <= 64) {
     if (!big_v) return N <= 32 ? PanelShape{4, 1, 8, 4} : PanelShape{4, 2, 8, 2};
     return d <= 4096 ? PanelShape{4, 2, 8, 2} : PanelShape{4, 4, 8, 2};
@@ -947,6 +955,7 @@ PanelShape panel_shape(int64_t N, int64_t d, int64_t V, bool with_stats) {
 hipError_t launch_panel_shape(const PanelShape& s, const PanelPlan& p, const uint16_t* X, const uint16_t* Wp, void* Y,
                               int64_t N, int64_t d, int64_t V, bool out_bf16, hipStream_t stream,
                               const FusedStats* fs = nullptr) {
+  if (s.deep && s.NT == 12) return launch_deep<12, 4, 4, true>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);
   if (s.deep) return launch_deep<8, 4, 4, true>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);
   if (s.NT == 4 && s.R == 1) return launch_panel<4, 1, 8, 4>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);
   if (s.NT == 4 && s.R == 2) return launch_panel<4, 2, 8, 2>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);

@@ -37,6 +37,8 @@ PACKED_SHAPES = [
     (40, 1024, 66000), (8, 4128, 65536), (120, 256, 65541), (130, 128, 65536),
     # the deep kernel (N > 128, d % 128 == 0): several trips, k-groups, token passes, tails
     (96, 4096, 3000), (300, 1024, 4100), (65, 384, 1029), (512, 256, 2000), (129, 4096, 1000), (160, 8192, 700),
+    # its 192-position passes (long vocabularies, fewer passes than 128): a ragged last pass and vocabulary tail
+    (260, 128, 65541),
 ]
 
 

@@ -156,6 +156,8 @@ FUSED = [
     # 65-128 positions with d <= 4096: the plain GEMM, then the statistics kernel
     ("unfused_greedy_n100", 20, 4, 128, 3001, 0.0), ("unfused_probs_n128", 16, 7, 384, 4099, 0.8),
     ("deep_passes_greedy", 64, 4, 128, 1500, 0.0),
+    # long vocabularies: the deep kernel's 192-position passes (one pass at N = 180, a ragged second at 260)
+    ("deep192_logits", 30, 5, 128, 65600, 1.0), ("deep192_greedy", 52, 4, 128, 65541, 0.0),
     # draft logits summarised by the panel grid's idle workgroups during the GEMM (long k, many draft rows)
     ("panel_idle_drafts", 4, 4, 4096, 65600, 0.9), ("panel_idle_drafts_tail", 3, 7, 4096, 65541, 1.3),
 ]
