@@ -113,6 +113,26 @@ size_t specdec_logits_workspace_bytes(int64_t N, int64_t d, int64_t V, int weigh
  * Returns 0 for invalid sizes. */
 size_t specdec_step_workspace_bytes(int64_t B, int64_t gamma, int64_t d, int64_t V, int weight_layout);
 
+/* How specdec_verify_step runs for a shape on the current device, as a set of
+ * flags (0 for invalid sizes):
+ *   SPECDEC_STEP_FUSED_STATISTICS    the scoring kernel forms the softmax
+ *       (or argmax) partials of every target row as it writes the logits, so
+ *       the sampling stage does not read the logits back (packed weights)
+ *   SPECDEC_STEP_GREEDY_WITHOUT_LOGITS  at T == 0 the step may be given
+ *       logits == NULL: the scoring kernel takes every row's argmax itself and
+ *       stores no scores ([LLMI] section 4, failure mode 1: greedy decoding
+ *       needs only the argmax; [MATH] "Greedy Decoding Equivalence")
+ * The same flags hold for specdec_tree_verify_step with B trees of M nodes
+ * (pass gamma = M - 1). */
+#define SPECDEC_STEP_FUSED_STATISTICS 1
+#define SPECDEC_STEP_GREEDY_WITHOUT_LOGITS 2
+int specdec_step_options(int64_t B, int64_t gamma, int64_t d, int64_t V, int weight_layout);
+
+/* Name of the kernel that computes the scores of this shape on the current
+ * device ("sweep_kernel", "panel_kernel", "deep_kernel" or "tiled_kernel"),
+ * for matching profiler records; "" for invalid sizes.  Never NULL. */
+const char* specdec_scoring_kernel(int64_t N, int64_t d, int64_t V, int weight_layout);
+
 /* Bytes of the packed weight layout of a [V, d] bf16 matrix (d % 32 == 0):
  * ceil(V/16)*16*d*2.  Returns 0 for invalid sizes. */
 size_t specdec_packed_weight_bytes(int64_t V, int64_t d);
@@ -191,7 +211,11 @@ int specdec_reject_sample(const float* target_logits, const float* draft, int dr
  *   X [B*(gamma+1), d] and W [V, d] bf16 in weight_layout, as in
  *            specdec_verify_logits
  *   logits   device fp32 [B*(gamma+1), V]: caller scratch that receives the
- *            target logits
+ *            target logits.  May be NULL at temperature == 0 when
+ *            specdec_step_options reports SPECDEC_STEP_GREEDY_WITHOUT_LOGITS
+ *            for the shape: the scoring kernel then takes every row's argmax
+ *            and no scores are written or read back (SPECDEC_ERR_NULL
+ *            otherwise)
  *   workspace at least specdec_step_workspace_bytes(B, gamma, d, V,
  *            weight_layout) bytes, shared by the two stages
  * Other arguments as in specdec_reject_sample. */
@@ -283,7 +307,10 @@ size_t specdec_tree_step_workspace_bytes(int64_t B, int64_t M, int64_t d, int64_
 /* The whole tree step: scores of all B*M nodes (X [B*M, d] bf16, row b*M + i
  * the hidden state of node i of tree b; W as in specdec_verify_logits) into
  * `logits` fp32 [B*M, V], then specdec_tree_verify_greedy on them.  With
- * packed weights the scoring kernel forms the rows' argmax partials itself. */
+ * packed weights the scoring kernel forms the rows' argmax partials itself;
+ * then `logits` may be NULL where specdec_step_options(B, M - 1, d, V,
+ * weight_layout) reports SPECDEC_STEP_GREEDY_WITHOUT_LOGITS (no scores are
+ * written; SPECDEC_ERR_NULL otherwise). */
 int specdec_tree_verify_step(const void* X, const void* W, int weight_layout, const int32_t* parents,
                              const int32_t* node_tokens, int64_t B, int64_t M, int64_t d, int64_t V, float* logits,
                              int32_t* out_tokens, int32_t* out_num_emitted, int32_t* out_nodes, void* workspace,

@@ -25,6 +25,8 @@ SPECDEC_OUT_F32 = 0
 SPECDEC_OUT_BF16 = 1
 SPECDEC_WEIGHTS_ROW_MAJOR = 0
 SPECDEC_WEIGHTS_PACKED = 1
+SPECDEC_STEP_FUSED_STATISTICS = 1
+SPECDEC_STEP_GREEDY_WITHOUT_LOGITS = 2
 SPECDEC_MAX_GAMMA = 63
 SPECDEC_MAX_TREE_NODES = 64
 
@@ -34,6 +36,8 @@ EXPORTED = [
     "specdec_workspace_bytes",
     "specdec_logits_workspace_bytes",
     "specdec_step_workspace_bytes",
+    "specdec_step_options",
+    "specdec_scoring_kernel",
     "specdec_packed_weight_bytes",
     "specdec_pack_weights",
     "specdec_verify_logits",
@@ -75,6 +79,10 @@ def _load() -> ctypes.CDLL:
     lib.specdec_logits_workspace_bytes.restype = ctypes.c_size_t
     lib.specdec_step_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
     lib.specdec_step_workspace_bytes.restype = ctypes.c_size_t
+    lib.specdec_step_options.argtypes = [I64, I64, I64, I64, I]
+    lib.specdec_step_options.restype = I
+    lib.specdec_scoring_kernel.argtypes = [I64, I64, I64, I]
+    lib.specdec_scoring_kernel.restype = ctypes.c_char_p
     lib.specdec_packed_weight_bytes.argtypes = [I64, I64]
     lib.specdec_packed_weight_bytes.restype = ctypes.c_size_t
     lib.specdec_pack_weights.argtypes = [P, P, I64, I64, P]
@@ -146,6 +154,24 @@ def logits_workspace_bytes(N: int, d: int, V: int, weight_layout: int) -> int:
 def step_workspace_bytes(B: int, gamma: int, d: int, V: int, weight_layout: int) -> int:
     """Workspace of specdec_verify_step."""
     return int(_lib.specdec_step_workspace_bytes(int(B), int(gamma), int(d), int(V), int(weight_layout)))
+
+
+def step_options(B: int, gamma: int, d: int, V: int, weight_layout: int) -> int:
+    """Flags of specdec_step_options (SPECDEC_STEP_FUSED_STATISTICS, SPECDEC_STEP_GREEDY_WITHOUT_LOGITS)."""
+    return int(_lib.specdec_step_options(int(B), int(gamma), int(d), int(V), int(weight_layout)))
+
+
+def step_fuses_statistics(B: int, gamma: int, d: int, V: int, weight_layout: int) -> bool:
+    return bool(step_options(B, gamma, d, V, weight_layout) & SPECDEC_STEP_FUSED_STATISTICS)
+
+
+def step_accepts_null_logits(B: int, gamma: int, d: int, V: int, weight_layout: int) -> bool:
+    """Whether a greedy (T == 0) step of this shape may be called with logits=None."""
+    return bool(step_options(B, gamma, d, V, weight_layout) & SPECDEC_STEP_GREEDY_WITHOUT_LOGITS)
+
+
+def scoring_kernel_name(N: int, d: int, V: int, weight_layout: int) -> str:
+    return _lib.specdec_scoring_kernel(int(N), int(d), int(V), int(weight_layout)).decode()
 
 
 def _ptr(t):
@@ -283,7 +309,8 @@ def _step_shapes(X, W, draft, draft_tokens, uniforms, logits, out_tokens, out_nu
     if N != B * (g + 1):
         raise ValueError(f"X has {N} rows, expected B*(gamma+1) = {B * (g + 1)}")
     _expect(X, torch.bfloat16, (N, d), "X")
-    _expect(logits, torch.float32, (N, V), "logits")
+    if logits is not None:
+        _expect(logits, torch.float32, (N, V), "logits")
     if draft is not None:
         _expect(draft, torch.float32, (B, g, V), "draft")
     _expect(draft_tokens, torch.int32, (B, g), "draft_tokens")
@@ -300,7 +327,8 @@ def specdec_verify_step(X, W, draft, draft_tokens, temperature: float, uniforms,
                         out_num_emitted, workspace, out_probs=None, draft_kind: int = SPECDEC_DRAFT_LOGITS,
                         stream=None):
     """specdec_verify_logits into `logits` [B*(g+1), V] fp32, then specdec_reject_sample on it.
-    W is a bf16 [V, d] tensor or a PackedWeights handle."""
+    W is a bf16 [V, d] tensor or a PackedWeights handle.  logits may be None for a greedy step (T == 0) of a shape
+    for which step_accepts_null_logits() holds."""
     B, g, d, V, wp, layout = _step_shapes(X, W, draft, draft_tokens, uniforms, logits, out_tokens, out_num_emitted,
                                           out_probs)
     _check(_lib.specdec_verify_step(_ptr(X), wp, layout, _ptr(draft), int(draft_kind), _ptr(draft_tokens),
@@ -384,7 +412,8 @@ def specdec_tree_verify_step(X, W, parents, node_tokens, logits, out_tokens, out
     if dw != d or N != B * M:
         raise ValueError("X must be [B*M, d] with the weights' d")
     _expect(X, torch.bfloat16, (N, d), "X")
-    _expect(logits, torch.float32, (N, V), "logits")
+    if logits is not None:
+        _expect(logits, torch.float32, (N, V), "logits")
     for t, n in ((parents, "parents"), (node_tokens, "node_tokens"), (out_tokens, "out_tokens"),
                  (out_nodes, "out_nodes")):
         _expect(t, torch.int32, (B, M), n)

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kVersion = 10200;  // 1.2.0
+constexpr int kVersion = 10300;  // 1.3.0
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -29,9 +29,11 @@ int check_logits_shape(int64_t N, int64_t d, int64_t V, int weight_layout) {
   return SPECDEC_OK;
 }
 
+// y_optional: Y may be NULL (a greedy step whose scoring kernel takes the
+// argmax itself and stores no scores).
 int check_logits_args(const void* X, const void* W, const void* Y, int64_t N, int64_t d, int64_t V, int out_dtype,
-                      int weight_layout) {
-  if (!X || !W || !Y) return SPECDEC_ERR_NULL;
+                      int weight_layout, bool y_optional = false) {
+  if (!X || !W || (!Y && !y_optional)) return SPECDEC_ERR_NULL;
   const int st = check_logits_shape(N, d, V, weight_layout);
   if (st != SPECDEC_OK) return st;
   if (out_dtype != SPECDEC_OUT_F32 && out_dtype != SPECDEC_OUT_BF16) return SPECDEC_ERR_ARG;
@@ -47,7 +49,8 @@ int check_logits_args(const void* X, const void* W, const void* Y, int64_t N, in
 
 int check_reject_args(const float* target, const float* draft, int draft_kind, const int32_t* tokens, float T,
                       const float* uniforms, int64_t B, int64_t gamma, int64_t V, const int32_t* out_tokens,
-                      const int32_t* out_num, const float* out_probs, const void* ws, size_t ws_bytes) {
+                      const int32_t* out_num, const float* out_probs, const void* ws, size_t ws_bytes,
+                      bool target_optional = false) {
   if (B < 1 || B > kMaxRows || gamma < 0 || gamma > SPECDEC_MAX_GAMMA || V < 1 || V > kMaxDim)
     return SPECDEC_ERR_SHAPE;
   if ((size_t)B * (size_t)(gamma + 1) * (size_t)V > ((size_t)1 << 40)) return SPECDEC_ERR_SHAPE;
@@ -55,7 +58,7 @@ int check_reject_args(const float* target, const float* draft, int draft_kind, c
     return SPECDEC_ERR_ARG;
   if (isnan(T) || T < 0.0f || isinf(T)) return SPECDEC_ERR_TEMPERATURE;
   const bool greedy = T == 0.0f;
-  if (!target || !out_tokens || !out_num) return SPECDEC_ERR_NULL;
+  if ((!target && !target_optional) || !out_tokens || !out_num) return SPECDEC_ERR_NULL;
   if (gamma > 0 && !tokens) return SPECDEC_ERR_NULL;
   if (!greedy && !uniforms) return SPECDEC_ERR_NULL;
   if (!greedy && gamma > 0 && draft_kind != SPECDEC_DRAFT_ONEHOT && !draft) return SPECDEC_ERR_NULL;
@@ -99,6 +102,15 @@ int check_warp_args(int64_t top_k, float top_p, int64_t V) {
   if (top_k < 0 || !(top_p > 0.0f && top_p <= 1.0f)) return SPECDEC_ERR_ARG;
   if (((top_k > 0 && top_k < V) || top_p < 1.0f) && V > ((int64_t)1 << 23)) return SPECDEC_ERR_SHAPE;
   return SPECDEC_OK;
+}
+
+// Partials per row that the scoring kernel of a step of this shape forms
+// itself (0: a separate statistics pass reads the logits back).  required: the
+// step keeps no logits, so the epilogue is taken wherever it can be formed.
+int64_t step_fused_parts(int64_t B, int64_t gamma, int64_t d, int64_t V, int weight_layout, bool required) {
+  if (weight_layout != SPECDEC_WEIGHTS_PACKED) return 0;
+  const int64_t pstride = specdec::reject_fusable_stride(B, gamma, V);
+  return pstride > 0 ? specdec::gemm_stats_parts(B * (gamma + 1), d, V, pstride, required) : 0;
 }
 
 }  // namespace
@@ -157,6 +169,20 @@ size_t specdec_step_workspace_bytes(int64_t B, int64_t gamma, int64_t d, int64_t
                    (packed ? specdec::gemm_stats_scratch_bytes(N, d, V) : 0);
   const size_t g = specdec::gemm_workspace_bytes(N, d, V, packed);
   return r > g ? r : g;
+}
+
+int specdec_step_options(int64_t B, int64_t gamma, int64_t d, int64_t V, int weight_layout) {
+  if (B < 1 || B > kMaxRows || gamma < 0 || gamma > SPECDEC_MAX_GAMMA || V < 1 || V > kMaxDim) return 0;
+  if (check_logits_shape(B * (gamma + 1), d, V, weight_layout) != SPECDEC_OK) return 0;
+  int flags = 0;
+  if (step_fused_parts(B, gamma, d, V, weight_layout, false) > 0) flags |= SPECDEC_STEP_FUSED_STATISTICS;
+  if (step_fused_parts(B, gamma, d, V, weight_layout, true) > 0) flags |= SPECDEC_STEP_GREEDY_WITHOUT_LOGITS;
+  return flags;
+}
+
+const char* specdec_scoring_kernel(int64_t N, int64_t d, int64_t V, int weight_layout) {
+  if (check_logits_shape(N, d, V, weight_layout) != SPECDEC_OK) return "";
+  return specdec::scoring_kernel_name(N, d, V, weight_layout == SPECDEC_WEIGHTS_PACKED);
 }
 
 int specdec_verify_logits(const void* X, const void* W, void* Y, int64_t N, int64_t d, int64_t V, int out_dtype,
@@ -243,11 +269,16 @@ int specdec_verify_step(const void* X, const void* W, int weight_layout, const f
                         void* stream) {
   if (B < 1 || B > kMaxRows || gamma < 0 || gamma > SPECDEC_MAX_GAMMA) return SPECDEC_ERR_SHAPE;
   const int64_t N = B * (gamma + 1);
-  int st = check_logits_args(X, W, logits, N, d, V, SPECDEC_OUT_F32, weight_layout);
+  // No logits: allowed for a greedy step whose scoring kernel takes the argmax
+  // itself (checked once the sizes are known to be valid).
+  const bool no_logits = logits == nullptr;
+  int st = check_logits_args(X, W, logits, N, d, V, SPECDEC_OUT_F32, weight_layout, no_logits);
   if (st != SPECDEC_OK) return st;
   st = check_reject_args(logits, draft, draft_kind, draft_tokens, temperature, uniforms, B, gamma, V, out_tokens,
-                         out_num_emitted, out_probs, workspace, workspace_bytes);
+                         out_num_emitted, out_probs, workspace, workspace_bytes, no_logits);
   if (st != SPECDEC_OK) return st;
+  if (no_logits && (temperature != 0.0f || step_fused_parts(B, gamma, d, V, weight_layout, true) == 0))
+    return SPECDEC_ERR_NULL;
   if (workspace_bytes < specdec_step_workspace_bytes(B, gamma, d, V, weight_layout)) return SPECDEC_ERR_WORKSPACE;
   const specdec::RejectArgs a = reject_args(logits, draft, draft_kind, draft_tokens, temperature, uniforms, B, gamma,
                                             V, out_tokens, out_num_emitted, out_probs, workspace, workspace_bytes);
@@ -257,11 +288,11 @@ int specdec_verify_step(const void* X, const void* W, int weight_layout, const f
   // logits again.
   specdec::FusedStats fs;
   if (weight_layout == SPECDEC_WEIGHTS_PACKED && specdec::reject_fused_stats(a, &fs) &&
-      specdec::gemm_stats_parts(N, d, V, fs.pstride) > 0) {
+      specdec::gemm_stats_parts(N, d, V, fs.pstride, no_logits) > 0) {
     int64_t nparts = 0, nparts_draft = 0;
     void* scratch = (char*)workspace + stats_scratch_offset(specdec::reject_workspace_bytes(B, gamma, V));
     if (specdec::launch_gemm_with_stats((const uint16_t*)X, (const uint16_t*)W, logits, N, d, V, fs, &nparts,
-                                        &nparts_draft, scratch, s) != hipSuccess)
+                                        &nparts_draft, scratch, s, no_logits) != hipSuccess)
       return SPECDEC_ERR_LAUNCH;
     return specdec::launch_reject_after_fused(a, nparts, nparts_draft, s) == hipSuccess ? SPECDEC_OK
                                                                                          : SPECDEC_ERR_LAUNCH;
@@ -351,22 +382,26 @@ int specdec_tree_verify_step(const void* X, const void* W, int weight_layout, co
                              size_t workspace_bytes, void* stream) {
   if (B < 1 || B > kMaxRows || M < 1 || M > SPECDEC_MAX_TREE_NODES) return SPECDEC_ERR_SHAPE;
   const int64_t N = B * M;
-  int st = check_logits_args(X, W, logits, N, d, V, SPECDEC_OUT_F32, weight_layout);
+  const bool no_logits = logits == nullptr;  // allowed where the scoring kernel takes the argmax itself
+  int st = check_logits_args(X, W, logits, N, d, V, SPECDEC_OUT_F32, weight_layout, no_logits);
   if (st != SPECDEC_OK) return st;
-  st = check_tree_args(logits, parents, node_tokens, B, M, V, out_tokens, out_num_emitted, out_nodes, workspace,
-                       workspace_bytes);
+  // The tree checks want a logits pointer; without logits, X stands in for it (it is not read there).
+  st = check_tree_args(no_logits ? X : logits, parents, node_tokens, B, M, V, out_tokens, out_num_emitted, out_nodes,
+                       workspace, workspace_bytes);
   if (st != SPECDEC_OK) return st;
   if (workspace_bytes < specdec_tree_step_workspace_bytes(B, M, d, V, weight_layout)) return SPECDEC_ERR_WORKSPACE;
   const specdec::TreeArgs t =
       tree_args(logits, parents, node_tokens, B, M, V, out_tokens, out_num_emitted, out_nodes, workspace);
   const hipStream_t s = (hipStream_t)stream;
   specdec::FusedStats fs;
-  if (weight_layout == SPECDEC_WEIGHTS_PACKED && specdec::tree_fused_stats(t, &fs) &&
-      specdec::gemm_stats_parts(N, d, V, fs.pstride) > 0) {
+  const bool fused = weight_layout == SPECDEC_WEIGHTS_PACKED && specdec::tree_fused_stats(t, &fs) &&
+                     specdec::gemm_stats_parts(N, d, V, fs.pstride, no_logits) > 0;
+  if (no_logits && !fused) return SPECDEC_ERR_NULL;
+  if (fused) {
     int64_t nparts = 0, nparts_draft = 0;
     void* scratch = (char*)workspace + stats_scratch_offset(specdec::tree_workspace_bytes(B, M, V));
     if (specdec::launch_gemm_with_stats((const uint16_t*)X, (const uint16_t*)W, logits, N, d, V, fs, &nparts,
-                                        &nparts_draft, scratch, s) != hipSuccess)
+                                        &nparts_draft, scratch, s, no_logits) != hipSuccess)
       return SPECDEC_ERR_LAUNCH;
     return specdec::launch_tree_greedy(t, nparts, s) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
   }

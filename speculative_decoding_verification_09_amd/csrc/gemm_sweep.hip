@@ -76,8 +76,9 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
 // while the current tile computes, instead of draining all of them at each
 // branch join.
 //
-// Statistics epilogue (EPI 1: softmax at temperature T, EPI 2: argmax), used
-// by the verification step: wave 0 folds every tile's finished logits into a
+// Statistics epilogue (EPI 1: softmax at temperature T, EPI 2: argmax; with
+// the argmax, Y may be null and the scores are then not stored), used by the
+// verification step: wave 0 folds every tile's finished logits into a
 // running per-lane state (max of a = z * fl32(1/T) and an fp64 sum of fp32
 // exp(a - max), rescaled when the max grows; or the largest z with its lowest
 // index), records the logit of each row's drafted token from the tile that
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restri
       }
       const int64_t v0 = (int64_t)t * 16 + 4 * g;
       if (live && v0 < V) {
-        store4<OUT_BF16>(Y, (size_t)m * V + v0, v0, V, sum);
+        if (EPI != 2 || Y != nullptr) store4<OUT_BF16>(Y, (size_t)m * V + v0, v0, V, sum);
         if (EPI == 1) {  // terms 2^(z * c1 - max * log2(e)), c1 = fl32(1/T) * log2(e)
           constexpr float kLog2e = 1.4426950408889634f;
           float zt = -INFINITY;

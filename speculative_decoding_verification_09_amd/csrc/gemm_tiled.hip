@@ -481,7 +481,8 @@ __device__ __forceinline__ void store_block(const f32x4 (&acc)[R][NT], float* st
 // k-group only), for the whole verification step: every wave reduces its
 // 16*R vocabulary rows per token, the NW wave partials meet in LDS, and the
 // workgroup leaves one partial per (row, vocabulary block), plus the logit of
-// each drafted token from the lane that holds it.
+// each drafted token from the lane that holds it.  With the argmax, Y may be
+// null: the scores are then not stored.
 template <int NT, int R, int NW, int KS, bool OUT_BF16, int EPI>
 __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp,
                                                         void* __restrict__ Y, int N, int d, int V, int npass, int cpk,
@@ -632,6 +633,7 @@ __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restri
     }
     return;
   }
+  if (EPI == 2 && Y == nullptr) return;  // a greedy step that keeps no logits
   store_block<NT, R, NW, OUT_BF16>(acc, (float*)xs, Y, V, n0, ncols, vb, wv, lane);
 }
 
@@ -646,10 +648,17 @@ __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restri
 // of the panel kernel, with k-groups of cpk steps; W loads are nontemporal
 // only when a single token pass reads W (NTL), since with several passes the
 // passes of one vocabulary block share W through the XCD's L2.
+//
+// The token passes of a vocabulary block split N evenly (ptok positions each, a
+// multiple of 16, at most NT*16), so that they take equally long: the passes
+// that read the same W rows then stay level with each other, and the later
+// ones find those rows in the XCD's L2 instead of fetching them from HBM again
+// (measured at N = 320: passes of 192 and 128 positions fetched 1.59x the
+// bytes of W from HBM).
 template <int NT, int R, int D, int F, bool NTL, bool OUT_BF16, int EPI, bool PX = false>
 __global__ __launch_bounds__(256) void deep_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp,
                                                    void* __restrict__ Y, int N, int d, int V, int npass, int cpk,
-                                                   FusedStats fs) {
+                                                   int ptok, FusedStats fs) {
   constexpr int NW = 4, kThreads = NW * 64;
   constexpr int kXPT = NT / 4;  // 16-byte X units per thread per step
   static_assert(NT % 4 == 0 && D == 4 && F == D, "deep kernel ring shapes");
@@ -670,8 +679,8 @@ __global__ __launch_bounds__(256) void deep_kernel(const uint16_t* __restrict__ 
   if (gi >= nvb * ngroups) return;
   const int vb = gi % nvb, group = gi / nvb;
   const int s0 = group * cpk, s1 = min(s0 + cpk, nsteps);
-  const int n0 = (slot % npass) * NT * 16;
-  const int ncols = min(N - n0, NT * 16);
+  const int n0 = (slot % npass) * ptok;
+  const int ncols = min(N - n0, ptok);
 
   const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, g = lane >> 4;
   int xd[NT];
@@ -784,7 +793,9 @@ __global__ __launch_bounds__(256) void deep_kernel(const uint16_t* __restrict__ 
 
   // Stored straight from the accumulators (staging them through LDS as the
   // panel kernel does measured slower here: this kernel is bound by the
-  // matrix cores, and the staging adds two barriers per token tile).
+  // matrix cores, and the staging adds two barriers per token tile).  A
+  // greedy step that keeps no logits passes a null Y.
+  if (EPI == 2 && Y == nullptr) return;
   const bool split = ngroups > 1;
   float* part = (float*)Y + (size_t)group * N * V;
 #pragma unroll
@@ -843,9 +854,10 @@ hipError_t launch_reduce(const float* P, void* Y, int64_t N, int64_t V, int64_t 
   return hipGetLastError();
 }
 
-// Launch geometry of one panel configuration for a shape.
+// Launch geometry of one panel configuration for a shape (ptok: positions
+// per token pass of the deep kernel).
 struct PanelPlan {
-  int64_t npass, cpk, groups, grid;
+  int64_t npass, cpk, groups, grid, ptok;
 };
 
 // Splits the k range into groups only when the (vocabulary block, token pass)
@@ -912,7 +924,7 @@ hipError_t launch_deep(const PanelPlan& p, const uint16_t* X, const uint16_t* Wp
   if (e != hipSuccess) return e;
   const FusedStats none{};
   hipLaunchKernelGGL(k, dim3((unsigned)p.grid), dim3(256), kLds, stream, X, Wp, Y, (int)N, (int)d, (int)V,
-                     (int)p.npass, (int)p.cpk, fs ? *fs : none);
+                     (int)p.npass, (int)p.cpk, (int)p.ptok, fs ? *fs : none);
   return hipGetLastError();
 }
 
@@ -1005,6 +1017,9 @@ GemmPlan plan_gemm(int64_t N, int64_t d, int64_t V, bool packed, bool with_stats
     const int64_t nsteps = d / 32, ntiles = (V + 15) / 16, nvb = (ntiles + 15) / 16;
     g.panel.cpk = (g.panel.cpk + 3) / 4 * 4;
     g.panel.groups = (nsteps + g.panel.cpk - 1) / g.panel.cpk;
+    // Equal token passes: the 16-row token tiles spread evenly over the passes.
+    const int64_t ntok_tiles = (N + 15) / 16;
+    g.panel.ptok = 16 * ((ntok_tiles + g.panel.npass - 1) / g.panel.npass);
     g.panel.grid = 8 * ((nvb * g.panel.groups + 7) / 8) * g.panel.npass;
     g.xpack = xpack_bytes(N, d);
   }
@@ -1035,7 +1050,7 @@ bool idle_drafts_fit(const GemmPlan& g, int64_t nd, int64_t d, int64_t V, int64_
 }  // namespace
 }  // namespace gemm
 
-int64_t gemm_stats_parts(int64_t N, int64_t d, int64_t V, int64_t pstride) {
+int64_t gemm_stats_parts(int64_t N, int64_t d, int64_t V, int64_t pstride, bool required) {
   using namespace gemm;
   if (N > kFusedStatsMaxRows) return 0;
   const GemmPlan g = plan_gemm(N, d, V, true, true);
@@ -1044,8 +1059,9 @@ int64_t gemm_stats_parts(int64_t N, int64_t d, int64_t V, int64_t pstride) {
   // (measured, V = 128256, d = 4096: 8 trees of 16 nodes 248.6 us against
   // 235-241 us for the tree step; a softmax step at N = 128, 264-268 us
   // against 240-253 us).  With d = 8192 the epilogue pays for itself
-  // (N = 96: 402-403 us fused against 416-419 us).
-  if (g.kind == GemmPlan::kPanel && g.shape.deep && N <= 128 && d <= 4096) return 0;
+  // (N = 96: 402-403 us fused against 416-419 us).  A step without logits
+  // takes the epilogue all the same.
+  if (!required && g.kind == GemmPlan::kPanel && g.shape.deep && N <= 128 && d <= 4096) return 0;
   int64_t parts = 0;
   if (g.kind == GemmPlan::kSweep) {
     parts = g.sweep.grid;
@@ -1063,9 +1079,10 @@ size_t gemm_stats_scratch_bytes(int64_t N, int64_t d, int64_t V) {
 
 hipError_t launch_gemm_with_stats(const uint16_t* X, const uint16_t* Wp, float* Y, int64_t N, int64_t d, int64_t V,
                                   const FusedStats& fs, int64_t* nparts, int64_t* nparts_draft, void* scratch,
-                                  hipStream_t stream) {
+                                  hipStream_t stream, bool required) {
   using namespace gemm;
-  const int64_t parts = gemm_stats_parts(N, d, V, fs.pstride);
+  if (Y == nullptr && !fs.greedy) return hipErrorInvalidValue;
+  const int64_t parts = gemm_stats_parts(N, d, V, fs.pstride, required);
   if (parts == 0) return hipErrorNotSupported;
   const GemmPlan g = plan_gemm(N, d, V, true, true);
   if (g.xpack > 0) {
@@ -1107,6 +1124,15 @@ hipError_t launch_gemm_with_stats(const uint16_t* X, const uint16_t* Wp, float* 
 
 size_t gemm_workspace_bytes(int64_t N, int64_t d, int64_t V, bool packed) {
   return gemm::plan_gemm(N, d, V, packed).workspace;
+}
+
+const char* scoring_kernel_name(int64_t N, int64_t d, int64_t V, bool packed) {
+  const gemm::GemmPlan g = gemm::plan_gemm(N, d, V, packed);
+  switch (g.kind) {
+    case gemm::GemmPlan::kSweep: return "sweep_kernel";
+    case gemm::GemmPlan::kPanel: return g.shape.deep ? "deep_kernel" : "panel_kernel";
+    default: return "tiled_kernel";
+  }
 }
 
 hipError_t launch_skinny_gemm(const uint16_t* X, const uint16_t* W, void* Y, int64_t N, int64_t d, int64_t V,

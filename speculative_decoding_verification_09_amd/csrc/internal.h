@@ -113,9 +113,14 @@ hipError_t launch_reject_after_fused(const RejectArgs& a, int64_t nparts, int64_
 // (their count in *nparts); independent of the scoring kernel.
 hipError_t launch_draft_stats(const FusedStats& fs, int64_t n_target, int64_t V, int64_t* nparts, hipStream_t stream);
 // Partials per row that launch_gemm_with_stats will produce for this shape
-// (0: the shape does not take the statistics epilogue, or is faster without
-// it).
-int64_t gemm_stats_parts(int64_t N, int64_t d, int64_t V, int64_t pstride);
+// (0: the shape does not take the statistics epilogue, or, unless required,
+// is faster without it).  required: the caller keeps no logits, so the
+// epilogue is taken wherever the kernels can form it.
+int64_t gemm_stats_parts(int64_t N, int64_t d, int64_t V, int64_t pstride, bool required = false);
+// Slots per row of the reject workspace's partials, when its shape can take
+// partials from the scoring kernel (B*(gamma+1) rows within the limit); 0
+// otherwise.
+int64_t reject_fusable_stride(int64_t B, int64_t gamma, int64_t V);
 // Device scratch that launch_gemm_with_stats needs for this shape (the packed
 // copy of X of the deep kernel, the sweep kernel's tile queue; 0 for the
 // panel kernel), 256-byte multiple.
@@ -123,12 +128,16 @@ size_t gemm_stats_scratch_bytes(int64_t N, int64_t d, int64_t V);
 // The scoring GEMM with the statistics epilogue (packed W, sweep, panel or
 // deep kernel without k-groups, at most kFusedStatsMaxParts partials per row);
 // the same launch summarises the draft rows.  scratch: at least
-// gemm_stats_scratch_bytes, disjoint from the statistics arrays.  Returns the
-// partial counts of target and draft rows, or hipErrorNotSupported, launching
-// nothing, for shapes it does not take.
+// gemm_stats_scratch_bytes, disjoint from the statistics arrays.  Y may be
+// null with the argmax epilogue (fs.greedy): the logits are then not stored.
+// Returns the partial counts of target and draft rows, or
+// hipErrorNotSupported, launching nothing, for shapes it does not take.
 hipError_t launch_gemm_with_stats(const uint16_t* X, const uint16_t* Wp, float* Y, int64_t N, int64_t d, int64_t V,
                                   const FusedStats& fs, int64_t* nparts, int64_t* nparts_draft, void* scratch,
-                                  hipStream_t stream);
+                                  hipStream_t stream, bool required = false);
+// Name of the kernel that computes the scores of this shape (the one that
+// dominates a step's time).
+const char* scoring_kernel_name(int64_t N, int64_t d, int64_t V, bool packed);
 
 // Tree verification (greedy), M <= 64 nodes per tree.
 struct TreeArgs {

@@ -1006,6 +1006,11 @@ inline unsigned blocks_for(int64_t items, int per) { return (unsigned)((items + 
 
 size_t reject_workspace_bytes(int64_t B, int64_t gamma, int64_t V) { return make_layout(B, gamma, V).total; }
 
+int64_t reject_fusable_stride(int64_t B, int64_t gamma, int64_t V) {
+  const Layout L = make_layout(B, gamma, V);
+  return B * (gamma + 1) > kMaxFusedRows || L.pstride < kMaxFusedParts ? 0 : L.pstride;
+}
+
 bool reject_fused_stats(const RejectArgs& a, FusedStats* fs) {
   const Layout L = make_layout(a.B, a.gamma, a.V);
   if (a.B * (a.gamma + 1) > kMaxFusedRows || L.pstride < kMaxFusedParts || warp_active(a)) return false;

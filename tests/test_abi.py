@@ -36,7 +36,7 @@ def test_status_strings_and_version():
     for s in range(1, 8):
         assert sd.status_string(s) and sd.status_string(s) != "unknown status"
     assert sd.status_string(99) == "unknown status"
-    assert sd.version() == 10200
+    assert sd.version() == 10300
 
 
 def test_workspace_bytes():
@@ -169,6 +169,10 @@ def test_step_argument_checks():
 
     assert step(X=0) == 1
     assert step(logits=0) == 1
+    # Without logits only a greedy step whose scoring kernel takes the argmax itself (packed weights)
+    assert step(logits=0, T=0.0) == 1
+    assert step(logits=0, T=0.5, lay=1) == 1
+    assert step(logits=0, T=0.0, lay=1, B=1, g=4, d=4096, V=128256, wsb=16) == 5  # the null is accepted
     assert step(B=0) == 2
     assert step(g=64) == 2
     assert step(d=7) == 2
@@ -266,3 +270,49 @@ def test_kv_gather_argument_checks():
     assert gather(max_len=1 << 21, head_dim=8192, elem=4) == 2    # 2^21 * 2^11 = 2^32 units
     assert gather(out=A + 8) == 3
 
+
+
+def test_step_options():
+    """Which steps fuse the statistics into the scoring kernel, and which greedy steps may omit the logits: every
+    packed shape whose kernel can form the partials (up to 512 positions without a k split); at 65-128 positions
+    with d <= 4096 the fused kernel is slower, so the step fuses only when it keeps no logits."""
+    PK, RM = sd.SPECDEC_WEIGHTS_PACKED, sd.SPECDEC_WEIGHTS_ROW_MAJOR
+    F, G = sd.SPECDEC_STEP_FUSED_STATISTICS, sd.SPECDEC_STEP_GREEDY_WITHOUT_LOGITS
+    assert sd.step_options(1, 4, 4096, 128256, PK) == F | G
+    assert sd.step_options(8, 7, 8192, 128256, PK) == F | G
+    assert sd.step_options(64, 4, 5120, 152064, PK) == F | G
+    assert sd.step_options(20, 4, 4096, 128256, PK) == G
+    assert sd.step_options(1, 4, 4096, 128256, RM) == 0
+    assert sd.step_options(8, 63, 4096, 128256, PK) == F | G  # 512 positions, the limit of the fused partials
+    assert sd.step_options(9, 63, 4096, 128256, PK) == 0
+    assert sd.step_options(0, 4, 4096, 128256, PK) == 0
+    assert sd.step_options(1, 4, 4100, 128256, PK) == 0
+
+
+def test_scoring_kernel_names():
+    PK, RM = sd.SPECDEC_WEIGHTS_PACKED, sd.SPECDEC_WEIGHTS_ROW_MAJOR
+    assert sd.scoring_kernel_name(5, 4096, 128256, PK) == "sweep_kernel"
+    assert sd.scoring_kernel_name(64, 8192, 128256, PK) == "panel_kernel"
+    assert sd.scoring_kernel_name(320, 5120, 152064, PK) == "deep_kernel"
+    assert sd.scoring_kernel_name(5, 4096, 128256, RM) == "tiled_kernel"
+    assert sd.scoring_kernel_name(0, 4096, 128256, PK) == ""
+
+
+def test_size_queries_from_many_threads():
+    """The library may be called from several host threads at once: the size and plan queries (which read the
+    per-device compute-unit cache) give the same answers concurrently as alone."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    PK = sd.SPECDEC_WEIGHTS_PACKED
+    shapes = [(1, 4, 4096, 128256), (8, 7, 8192, 128256), (64, 4, 5120, 152064), (7, 7, 28672, 8192),
+              (20, 4, 4096, 128256), (3, 0, 256, 5000)]
+
+    def answers(_):
+        return [(sd.step_workspace_bytes(*s, PK), sd.logits_workspace_bytes(s[0] * (s[1] + 1), s[2], s[3], PK),
+                 sd.step_options(*s, PK), sd.scoring_kernel_name(s[0] * (s[1] + 1), s[2], s[3], PK))
+                for s in shapes]
+
+    alone = answers(0)
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        for got in ex.map(answers, range(64)):
+            assert got == alone

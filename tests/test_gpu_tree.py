@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle_pins
+import parity_tally
 import speculative_decoding_verification_09_amd as sd
 import synth
 from gpu_util import abs_dot_bound, announce, dev, dev_bf16, host, reject, weights
@@ -148,3 +149,13 @@ def test_tree_step(orc, B, M, d, V, packed):
         assert min(gaps) < band, (b, ot[b], t)
         excused += 1
     assert excused <= max(1, B // 10)
+    parity_tally.record("greedy", B - excused, excused, max_dz=band / 4)
+    if packed and sd.step_accepts_null_logits(B, M - 1, d, V, layout):
+        # the same tree step without a logits buffer: the outputs must be the same bits
+        announce(f"tree step B={B} M={M} d={d} V={V} without logits")
+        ot2 = torch.full((B, M), -7, dtype=torch.int32, device="cuda")
+        on2 = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+        nd2 = torch.full((B, M), -7, dtype=torch.int32, device="cuda")
+        sd.specdec_tree_verify_step(Xd, Wd, dev(par), dev(tok), None, ot2, on2, nd2, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(ot2), ot) and np.array_equal(host(on2), on) and np.array_equal(host(nd2), nd)
