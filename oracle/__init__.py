@@ -50,10 +50,11 @@ PLANTS = {
 }
 
 
-def build_library(out_path: str = LIBRARY, plant: int = 0) -> str:
-    """Compile the oracle with gcc -O2 (no OpenMP, no SIMD intrinsics)."""
+def build_library(out_path: str = LIBRARY, plant: int = 0, extra_flags=()) -> str:
+    """Compile the oracle with gcc -O2 (no OpenMP, no SIMD intrinsics); extra_flags are appended (a sanitizer
+    build, for instance)."""
     cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-Wall", "-Wextra",
-           f"-DORACLE_PLANT={int(plant)}", SOURCE, "-o", out_path + ".tmp", "-lm"]
+           f"-DORACLE_PLANT={int(plant)}", *extra_flags, SOURCE, "-o", out_path + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(out_path + ".tmp", out_path)
     return out_path
