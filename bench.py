@@ -5,9 +5,14 @@ gamma+1 positions of every sequence (one pass over the LM-head weights) and
 the rejection-sampling kernels.  Inputs are synthetic, seeded, and resident in
 HBM before timing starts.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+The headline is the larger Llama-8B-shaped step (B=8, gamma=7, d=8192,
+V=128256, 64 positions); the one-sequence step (B=1, gamma=4, d=4096) is timed
+in the same run and reported beside it.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-b1]
     python bench.py --projection-sweep     (the decoder-projection GEMM sweep over N; one JSON line)
     python bench.py --extensions           (warping, one-hot drafts, tree verification, paged KV; one JSON line)
+    python bench.py --pmc-summary FETCH_CSV WRITE_CSV   (per-kernel HBM bytes from two rocprofv3 --pmc runs)
 """
 from __future__ import annotations
 
@@ -19,46 +24,52 @@ import sys
 import time
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 METRIC = "verified positions/sec and achieved HBM GB/s (% of peak) per verify step"
 HERE = os.path.dirname(os.path.abspath(__file__))
-# The sources of the dominant kernel (the sweep scoring GEMM) that the traffic record below was measured on.
-GEMM_SOURCES = [os.path.join(HERE, "speculative_decoding_verification_09_amd", "csrc", f)
-                for f in ("gemm_common.h", "gemm_sweep.hip")]
+CSRC = os.path.join(HERE, "speculative_decoding_verification_09_amd", "csrc")
 
-# HBM bytes per scoring launch, from hardware counters (FETCH_SIZE and WRITE_SIZE, each in its own rocprofv3
-# --pmc run of this script, scaled by what the same counter reads for a plain device copy of known size: 2.0 for
-# FETCH_SIZE, 1.0 for WRITE_SIZE).  Keyed by workload, weight layout and the SHA-256 of the GEMM source the
-# counters were taken on: once that source changes, the record no longer describes the kernel and traffic is null.
+# HBM bytes per launch of the dominant kernel, from hardware counters: FETCH_SIZE and WRITE_SIZE, each in its own
+# rocprofv3 --pmc run of this script with --copy-calibration, scaled by what the same counter reads for a plain
+# device copy of known size (2.0 for FETCH_SIZE, 1.0 for WRITE_SIZE); `python bench.py --pmc-summary` prints them.
+# Keyed by workload and weight layout, with the SHA-256 of the kernel's sources at the time of measurement: once a
+# source changes, the record no longer describes the kernel and traffic is reported as null.
 MEASURED_TRAFFIC = {
-    ("lmhead_b1_g4", "packed"): {"fetch_bytes": 1051154653, "write_bytes": 2616848,
+    ("lmhead_b1_g4", "packed"): {"kernel": "sweep_kernel", "sources": ["gemm_common.h", "gemm_sweep.hip"],
+                                 "fetch_bytes": 1051154653, "write_bytes": 2616848,
                                  "source_sha256": "35f675362734d11c2eddaf9aedd8e3b18b35e6273c3fed0475eb69aedfa4d403"},
 }
 
 
+def sources_sha256(names) -> str:
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def measured_traffic(workload: str, layout: str):
     rec = MEASURED_TRAFFIC.get((workload, layout))
-    if rec is None:
-        return None
-    h = hashlib.sha256()
-    for path in GEMM_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
-    if h.hexdigest() != rec["source_sha256"]:
+    if rec is None or sources_sha256(rec["sources"]) != rec["source_sha256"]:
         return None
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
-def algorithmic_bytes(w):
-    """Bytes the step must move at minimum: W and X read once, fp32 logits written once and read once by the
-    statistics pass, draft logits read once, and the one (target, draft) row pair where each sequence ends
-    read again by the draw."""
+def algorithmic_bytes(w, fused: bool, with_logits: bool):
+    """Bytes the step must move at minimum, and those of its scoring GEMM.  The GEMM reads W and X once and writes
+    the fp32 logits once (not at all when a greedy step keeps no logits).  The sampling stage reads the target
+    logits once more unless the GEMM forms their statistics itself (fused), reads the draft logits once, and reads
+    the one (target, draft) row pair where each sequence ends a second time (T > 0)."""
     N = w.B * (w.gamma + 1)
-    gemm = w.V * w.d * 2 + N * w.d * 2 + N * w.V * 4
-    if w.temperature == 0.0:
-        reject = N * w.V * 4
-    else:
-        reject = N * w.V * 4 + w.B * w.gamma * w.V * 4 + w.B * w.V * 8
-    return gemm, gemm + reject
+    y = N * w.V * 4
+    gemm = w.V * w.d * 2 + N * w.d * 2 + y
+    step = w.V * w.d * 2 + N * w.d * 2 + (y if with_logits else 0)
+    if not fused:
+        step += y
+    if w.temperature > 0.0:
+        step += w.B * w.gamma * w.V * 4 + w.B * w.V * 8
+    return gemm, step
 
 
 def main():
@@ -66,8 +77,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="lmhead_b1_g4")
+    ap.add_argument("--workload", default="lmhead_b8_g7")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-b1", action="store_true", help="do not also time the one-sequence step (lmhead_b1_g4)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="the CPU baseline times whole oracle sequences until this much time has passed")
     ap.add_argument("--projection-sweep", action="store_true",
@@ -77,15 +89,19 @@ def main():
                     help="also run one plain 256 MiB device copy (a known byte count for hardware counters)")
     ap.add_argument("--extensions", action="store_true",
                     help="time the extensions (warping, one-hot drafts, tree verification, paged KV) instead")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE)")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    import speculative_decoding_verification_09_amd as sd
+    import speculative_decoding_verification_09_amd as sd  # noqa: F401  (fails loudly without the HIP library)
     import synth
 
     if not torch.cuda.is_available():
@@ -101,33 +117,93 @@ def main():
     if w.d == 0:
         toy_reject(args, w)
         return
-    B, g, V, d, T = w.B, w.gamma, w.V, w.d, w.temperature
-    N = B * (g + 1)
-    dev = torch.device("cuda")
-    X, W, logits, out_tok, out_num, ws, gemm_ws, uni, draft, tokens = step_inputs(w, args.layout)
-    layout = sd.SPECDEC_WEIGHTS_PACKED if args.layout == "packed" else sd.SPECDEC_WEIGHTS_ROW_MAJOR
-    stream = torch.cuda.current_stream()
-    probs = None
     if args.copy_calibration:
-        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
 
+    m = measure_step(w, args)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, m, args.cpu_seconds)
+    state = m.pop("_state")
+    del state
+    b1 = None
+    if not args.no_b1 and w.name != "lmhead_b1_g4":
+        torch.cuda.empty_cache()
+        m1 = measure_step(synth.WORKLOADS["lmhead_b1_g4"], args)
+        m1.pop("_state")
+        b1 = {k: m1[k] for k in ("ms_per_step", "positions_per_s", "step_hbm_gbps", "step_frac_of_peak",
+                                 "step_bytes", "step_times_us", "roofline", "reject_stage")}
+        b1["config"] = m1["config"]
+
+    out = {
+        "metric": METRIC,
+        "value": m["positions_per_s"],
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": m["config"],
+        "step_hbm_gbps": m["step_hbm_gbps"],
+        "step_frac_of_peak": m["step_frac_of_peak"],
+        "step_bytes": m["step_bytes"],
+        "step_times_us": m["step_times_us"],
+        "emitted_tokens_per_s": m["emitted_tokens_per_s"],
+        "reject_stage": m["reject_stage"],
+        "roofline": m["roofline"],
+        "cpu_baseline": cpu,
+        "b1_step": b1,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _percentiles(times_ms):
+    import numpy as np
+
+    t = np.asarray(times_ms, dtype=np.float64) * 1e3
+    return {"median": float(np.median(t)), "p10": float(np.percentile(t, 10)), "p90": float(np.percentile(t, 90)),
+            "mean": float(t.mean()), "n": int(t.size)}
+
+
+def measure_step(w, args):
+    """Times one workload's verify step (inputs resident in HBM) and its dominant kernel.
+
+    Timed region 1 (the headline): K whole steps back to back between two events on the launch stream; the mean.
+    Timed region 2: K steps with an event between consecutive steps, for the median and p10/p90 of single steps
+    (each interval also holds one event's own cost).  Timed region 3 (the roofline of the dominant kernel): K
+    scoring launches back to back between two events."""
+    import torch
+
+    import speculative_decoding_verification_09_amd as sd
+
+    B, g, V, d, T = w.B, w.gamma, w.V, w.d, w.temperature
+    N = B * (g + 1)
+    X, W, logits, out_tok, out_num, ws, gemm_ws, uni, draft, tokens = step_inputs(w, args.layout)
+    layout = sd.SPECDEC_WEIGHTS_PACKED if args.layout == "packed" else sd.SPECDEC_WEIGHTS_ROW_MAJOR
+    stream = torch.cuda.current_stream()
+    fused = sd.step_fuses_statistics(B, g, d, V, layout)
+    # A greedy step whose scoring kernel takes the argmax itself needs no logits buffer.
+    step_logits = None if (T == 0.0 and sd.step_accepts_null_logits(B, g, d, V, layout)) else logits
+
     def step():
-        sd.specdec_verify_step(X, W, draft, tokens, T, uni if T > 0 else None, logits, out_tok, out_num, ws,
-                               out_probs=probs, stream=stream)
+        sd.specdec_verify_step(X, W, draft, tokens, T, uni if T > 0 else None, step_logits, out_tok, out_num, ws,
+                               stream=stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
-    # ---- timed region 1 (the headline): K whole steps back to back, events on the launch stream
     K = args.steps
     evs = torch.cuda.Event(enable_timing=True)
     eve = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     evs.record(stream)
     for _ in range(K):
         step()
@@ -136,8 +212,15 @@ def main():
     ms_step = evs.elapsed_time(eve) / K
     emitted = int(out_num.sum().item())
 
-    # ---- timed region 2 (the roofline of the dominant kernel): K scoring launches back to back on the same
-    # stream between two events.  (An event between every launch would add its own release to each interval.)
+    evl = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    evl[0].record(stream)
+    for i in range(K):
+        step()
+        evl[i + 1].record(stream)
+    torch.cuda.synchronize()
+    singles = [evl[i].elapsed_time(evl[i + 1]) for i in range(K)]
+
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -148,16 +231,17 @@ def main():
     torch.cuda.synchronize()
     gemm_ms = ev0.elapsed_time(ev1) / K
 
-    # ---- the reject stage alone on the step's logits (specdec_reject_sample: statistics pass, then the rule),
-    # warm (the logits just written, K back-to-back calls) and flushed (a 512 MiB write between calls, each call
-    # between its own two events)
-    rule = {}
+    # The reject stage alone on the step's logits (specdec_reject_sample: its own statistics pass, then the rule),
+    # warm (K back-to-back calls right after the logits were written) and flushed (a 512 MiB write before each
+    # call, each call between its own two events; median of 10).
+    rule = None
     if T > 0:
         rws = sd.new_workspace(B, g, V)
         tl = logits.view(B, g + 1, V)
-        rule["warm_ms"] = _time_launches(lambda: sd.specdec_reject_sample(tl, draft, tokens, T, uni, out_tok, out_num,
-                                                                          rws, stream=stream), K, args.warmup, stream)
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        rule = {"warm_ms": _time_launches(lambda: sd.specdec_reject_sample(tl, draft, tokens, T, uni, out_tok, out_num,
+                                                                           rws, stream=stream), K, args.warmup,
+                                          stream)}
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         times = []
         for _ in range(10):
             flush.fill_(1)
@@ -167,84 +251,137 @@ def main():
             e1.record(stream)
             torch.cuda.synchronize()
             times.append(e0.elapsed_time(e1))
-        rule["flushed_ms"] = float(np.median(times))
+        rule["flushed_ms"] = _percentiles(times)["median"] * 1e-3
         del flush, rws
-        # the step's own tokens again (the rule above wrote the same outputs from the same inputs)
-        step()
-        torch.cuda.synchronize()
+    # The step's outputs once more, with the logits kept, for the parity check of the CPU baseline (the outputs
+    # are the same with or without a logits buffer).
+    sd.specdec_verify_step(X, W, draft, tokens, T, uni if T > 0 else None, logits, out_tok, out_num, ws,
+                           stream=stream)
+    torch.cuda.synchronize()
 
-    gemm_bytes, step_bytes = algorithmic_bytes(w)
+    gemm_bytes, step_bytes = algorithmic_bytes(w, fused, step_logits is not None)
     gemm_gbps = gemm_bytes / (gemm_ms * 1e-3) / 1e9
     step_gbps = step_bytes / (ms_step * 1e-3) / 1e9
-    positions_per_s = N / (ms_step * 1e-3)
-
-    # ---- CPU baseline: the oracle as it stands, single-threaded, on a bounded sample of the same workload
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-
-        orc = oracle.load()
-        Xh, Wh = synth.lm_head_inputs(w)
-        rows_per_seq = g + 1
-        uh = synth.step_uniforms(w)
-        toks = tokens.cpu().numpy()
-        dr = draft.cpu().numpy() if draft is not None else None
-        # One host core: the oracle is single-threaded C; the process is pinned to the core it runs on for the
-        # duration, so that the scheduler does not move it.
-        pinned = None
-        if hasattr(os, "sched_setaffinity"):
-            old_mask = os.sched_getaffinity(0)
-            core = min(old_mask)
-            os.sched_setaffinity(0, {core})
-            pinned = core
-        reps, t_lin, t_rule = 0, 0.0, 0.0
-        t0 = time.perf_counter()
-        while reps == 0 or time.perf_counter() - t0 < args.cpu_seconds:
-            b = reps % B
-            ta = time.perf_counter()
-            zb = orc.linear(Xh[b * rows_per_seq:(b + 1) * rows_per_seq], Wh).astype(np.float32)
-            tb = time.perf_counter()
-            orc.verify(zb[None], dr[b:b + 1] if dr is not None else None, toks[b:b + 1], uh[b:b + 1], T)
-            t_lin += tb - ta
-            t_rule += time.perf_counter() - tb
-            reps += 1
-        cpu_s = time.perf_counter() - t0
-        if pinned is not None:
-            os.sched_setaffinity(0, old_mask)
-        cpu = {"value": reps * rows_per_seq / cpu_s, "unit": "positions/s", "cores": 1, "kind": "oracle",
-               "sample": f"{reps} sequence(s) of {rows_per_seq} positions (B={B}: "
-                         f"{'whole steps' if B == 1 else 'sequences of one step'}): fp64 scoring over the full "
-                         f"{V}x{d} weights plus the rule, single-threaded C, {cpu_s:.1f} s",
-               "scoring_s_per_sequence": t_lin / reps, "rule_s_per_sequence": t_rule / reps,
-               "pinned_core": pinned, "host_cpus": os.cpu_count(), "cpu_model": _cpu_model()}
-
-    out = {
-        "metric": METRIC,
-        "value": positions_per_s,
-        "unit": "positions/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
+    flops = 2.0 * N * d * V
+    roof = {"kernel": sd.scoring_kernel_name(N, d, V, layout), "bound": "hbm", "achieved": gemm_gbps,
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gemm_gbps / HBM_PEAK_GBPS,
+            "traffic": measured_traffic(w.name, args.layout), "bytes_per_launch": gemm_bytes,
+            "avg_launch_ms": gemm_ms,
+            "mfma_tflops": flops / (gemm_ms * 1e-3) / 1e12,
+            "mfma_frac": flops / (gemm_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+    return {
         "config": {"workload": w.name, "B": B, "gamma": g, "d": d, "V": V, "N": N, "temperature": T,
-                   "draft_noise_std": w.noise_std, "weight_layout": args.layout},
+                   "draft_noise_std": w.noise_std, "weight_layout": args.layout,
+                   "statistics_fused": bool(fused), "logits_written": step_logits is not None},
+        "ms_per_step": ms_step,
+        "positions_per_s": N / (ms_step * 1e-3),
         "step_hbm_gbps": step_gbps,
         "step_frac_of_peak": step_gbps / HBM_PEAK_GBPS,
         "step_bytes": step_bytes,
+        "step_times_us": _percentiles(singles),
         "emitted_tokens_per_s": emitted / (ms_step * 1e-3),
-        "reject_stage": rule or None,
-        "roofline": {"kernel": "scoring GEMM (specdec_verify_logits)", "bound": "hbm", "achieved": gemm_gbps,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gemm_gbps / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(w.name, args.layout), "bytes_per_launch": gemm_bytes,
-                     "avg_launch_ms": gemm_ms},
-        "cpu_baseline": cpu,
+        "reject_stage": rule,
+        "roofline": roof,
+        "_state": {"logits": logits, "out_tok": out_tok, "out_num": out_num, "draft": draft, "tokens": tokens},
     }
-    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, m, seconds: float):
+    """The oracle as it stands (single-threaded C, fp64), pinned to one host core, on whole sequences of the same
+    workload until `seconds` have passed: scoring over the full weights, then the rule.  Each sequence it finishes
+    is also compared with the GPU step's outputs on the same inputs: the logits (max |dz| against the oracle's fp64
+    scores) and the emitted tokens and counts, element by element, near ties counted."""
+    import numpy as np
+
+    import oracle
+    from oracle.parity import compare_steps, end_to_end_bands
+    import synth
+
+    orc = oracle.load()
+    B, g, V, d, T = w.B, w.gamma, w.V, w.d, w.temperature
+    st = m["_state"]
+    Xh, Wh = synth.lm_head_inputs(w)
+    g1 = g + 1
+    uh = synth.step_uniforms(w) if T > 0 else None
+    toks = st["tokens"].cpu().numpy()
+    dr = st["draft"].cpu().numpy() if st["draft"] is not None else None
+    gpu_logits = st["logits"].cpu().numpy()
+    gpu_tok = st["out_tok"].cpu().numpy()
+    gpu_num = st["out_num"].cpu().numpy()
+    pinned = None
+    if hasattr(os, "sched_setaffinity"):
+        old_mask = os.sched_getaffinity(0)
+        pinned = min(old_mask)
+        os.sched_setaffinity(0, {pinned})
+    reps, t_lin, t_rule = 0, 0.0, 0.0
+    seqs, outs, dzs = [], [], []
+    t0 = time.perf_counter()
+    while reps == 0 or time.perf_counter() - t0 < seconds:
+        b = reps % B
+        ta = time.perf_counter()
+        z64 = orc.linear(Xh[b * g1:(b + 1) * g1], Wh)
+        tb = time.perf_counter()
+        ora = orc.verify(z64.astype(np.float32)[None], dr[b:b + 1] if dr is not None else None, toks[b:b + 1],
+                         uh[b:b + 1] if uh is not None else None, T)
+        t_lin += tb - ta
+        t_rule += time.perf_counter() - tb
+        reps += 1
+        if b not in seqs:
+            seqs.append(b)
+            outs.append(ora)
+            dzs.append(float(np.abs(gpu_logits[b * g1:(b + 1) * g1].astype(np.float64) - z64).max()))
+    cpu_s = time.perf_counter() - t0
+    if pinned is not None:
+        os.sched_setaffinity(0, old_mask)
+    # Parity of the sequences the oracle finished.
+    max_dz = max(dzs)
+    exact = excused = 0
+    failures = []
+    for b, ora in zip(seqs, outs):
+        acc_band, draw_band = end_to_end_bands(max_dz, T, ora["draw_mass"])
+        r = compare_steps(gpu_tok[b:b + 1], gpu_num[b:b + 1], ora, acc_band, draw_band)
+        exact += r["exact"]
+        excused += r["excused"]
+        failures += [b] if r["failures"] else []
+    return {"value": reps * g1 / cpu_s, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} sequence(s) of {g1} positions ({'whole steps' if B == 1 else f'of the {B} in a step'}):"
+                      f" fp64 scoring over the full {V}x{d} weights plus the rule, single-threaded C, {cpu_s:.1f} s",
+            "scoring_s_per_sequence": t_lin / reps, "rule_s_per_sequence": t_rule / reps,
+            "pinned_core": pinned, "host_cpus": os.cpu_count(), "cpu_model": _cpu_model(),
+            "parity": {"sequences": seqs, "exact": exact, "excused": excused, "failures": failures,
+                       "max_dz": max_dz}}
+
+
+def pmc_summary(fetch_csv: str, write_csv: str):
+    """Per-kernel HBM bytes per dispatch from the counter_collection.csv files of two rocprofv3 runs (one with
+    --pmc FETCH_SIZE, one with --pmc WRITE_SIZE, both of `bench.py ... --copy-calibration`).  Each counter is
+    scaled by what it reads for the plain device copy (__amd_rocclr_copyBuffer, 256 MiB read and written)."""
+    import csv
+    from collections import defaultdict
+
+    def load(path, counter):
+        d = defaultdict(list)
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] == counter:
+                    d[row["Kernel_Name"]].append(float(row["Counter_Value"]))
+        return d
+
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    copy_kib = 256 * 1024.0
+    cf = copy_kib / sum(fetch.get("__amd_rocclr_copyBuffer", [copy_kib]))
+    cw = copy_kib / sum(write.get("__amd_rocclr_copyBuffer", [copy_kib]))
+    print(f"copy calibration: FETCH_SIZE x{cf:.4f}, WRITE_SIZE x{cw:.4f}")
+    print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM bytes per dispatch |")
+    print("|---|---|---|---|---|")
+    for k in sorted(fetch, key=lambda k: -sum(fetch[k])):
+        if k == "__amd_rocclr_copyBuffer" or k not in write:
+            continue
+        f = sum(fetch[k]) / len(fetch[k])
+        wr = sum(write[k]) / len(write[k])
+        name = k.replace("(anonymous namespace)::", "").replace("specdec::", "").replace("void ", "").split("(")[0]
+        print(f"| {name} | {len(fetch[k])} | {f:.1f} | {wr:.1f} | {(f * cf + wr * cw) * 1024:.4e} |")
+        print(f"    fetch_bytes={int(f * cf * 1024)} write_bytes={int(wr * cw * 1024)}")
 
 
 def step_inputs(w, layout_name: str):
@@ -512,7 +649,6 @@ def extensions(args):
     print(json.dumps(out), flush=True)
 
 
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 
 
 def projection_sweep(args):

@@ -5,6 +5,8 @@
 // receives D[rows 4*(l/16) .. +3][col l%16].
 #pragma once
 
+#include <atomic>
+
 #include "internal.h"
 
 namespace specdec {
@@ -68,17 +70,19 @@ inline hipError_t allow_lds(K kernel, size_t bytes) {
   return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device, cached per device.  Host threads may
+// call this at once: each slot is an atomic, and two threads that both miss
+// store the same value.
 inline int device_cus() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];  // zero-initialised (static storage)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 }  // namespace gemm

@@ -14,7 +14,7 @@ import torch
 
 import speculative_decoding_verification_09_amd as sd
 import synth
-from gpu_util import announce, dev_bf16, gemm, host, weights
+from gpu_util import announce, dev_bf16, gemm, host, oracle_linear, weights
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +39,8 @@ PACKED_SHAPES = [
     (96, 4096, 3000), (300, 1024, 4100), (65, 384, 1029), (512, 256, 2000), (129, 4096, 1000), (160, 8192, 700),
     # its 192-position passes (long vocabularies, fewer passes than 128): a ragged last pass and vocabulary tail
     (260, 128, 65541),
+    # ... over several trips of its prefetch ring, one pass and two (the second ragged)
+    (200, 1024, 65600), (330, 2048, 66000),
 ]
 
 
@@ -92,7 +94,7 @@ def test_packed_integer_bit_exact(orc, N, d, V):
     W = synth.integer_bf16((V, d), 8, 72, V)
     announce(f"gemm packed integer N={N} d={d} V={V}")
     Y = host(gemm(X, W, packed=True))
-    assert np.array_equal(Y.astype(np.float64), orc.linear(X, W))
+    assert np.array_equal(Y.astype(np.float64), oracle_linear(orc, X, W))
 
 
 @pytest.mark.parametrize("N,d,V", PACKED_SHAPES)
@@ -101,7 +103,7 @@ def test_packed_normal_within_fp32_bound(orc, N, d, V):
     W = synth.normal_bf16((V, d), 0.02, 82, V)
     announce(f"gemm packed normal N={N} d={d} V={V}")
     Y = host(gemm(X, W, packed=True)).astype(np.float64)
-    ref = orc.linear(X, W)
+    ref = oracle_linear(orc, X, W)
     bound = _bound(synth.bf16_to_f32(X), synth.bf16_to_f32(W), d)
     assert np.all(np.abs(Y - ref) <= bound + 1e-30)
 

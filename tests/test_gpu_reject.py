@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 import oracle_pins
+import parity_tally
 import speculative_decoding_verification_09_amd as sd
 import synth
 from gpu_util import announce, compare_steps, first_token_tv, reject
@@ -128,6 +129,7 @@ def test_greedy_b64_bit_exact(orc):
     ora = orc.verify(zt, None, x, None, 0.0)
     assert np.array_equal(num, ora["num_emitted"])
     assert np.array_equal(tok, ora["tokens"])
+    parity_tally.record("greedy", B)
 
 
 def test_greedy_ties_lowest_index(orc):
@@ -145,6 +147,7 @@ def test_greedy_ties_lowest_index(orc):
     tok, num, _ = reject(zt, None, x, None, 0.0, probs=False)
     ora = orc.verify(zt, None, x, None, 0.0)
     assert np.array_equal(tok, ora["tokens"]) and np.array_equal(num, ora["num_emitted"])
+    parity_tally.record("greedy", B)
 
 
 # ---------------------------------------------------------------------------

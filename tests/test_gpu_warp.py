@@ -20,7 +20,9 @@ import torch
 
 import speculative_decoding_verification_09_amd as sd
 import synth
-from gpu_util import (abs_dot_bound, announce, compare_steps, dev, dev_bf16, first_token_tv, host, reject,
+import parity_tally
+from oracle.parity import compare_steps
+from gpu_util import (abs_dot_bound, announce, dev, dev_bf16, first_token_tv, host, reject,
                       reject_warped, weights)
 
 pytestmark = pytest.mark.gpu
@@ -75,6 +77,8 @@ def _check(tok, num, ora, acc_band=ACC_BAND, draw_band=DRAW_BAND, warp_band=WARP
     res = compare_steps(tok, num, ora, acc_band, draw_band)
     fails = [b for b in res["failures"] if not ora["warp_margin"][b] < warp_band]
     excused = res["excused"] + len(res["failures"]) - len(fails)
+    parity_tally.record("sampled", res["exact"], res["excused_accept"], res["excused_draw"],
+                        len(res["failures"]) - len(fails), len(fails))
     print(f"  exact={res['exact']} excused={excused} failures={fails[:10]}", flush=True)
     assert not fails, f"sequences differ without a near tie: {fails[:10]}"
     assert excused <= max(1, max_frac * len(num))
@@ -217,6 +221,8 @@ def test_warped_step(orc, packed):
         gap = min(_topk_gap(zt[b, i], k) for i in range(g + 1))
         if not (ora["warp_margin"][b] < max(WARP_BAND, 4 * max_dz / T) or gap < 4 * max_dz):
             fails.append(b)
+    parity_tally.record("sampled", res["exact"], res["excused_accept"], res["excused_draw"],
+                        len(res["failures"]) - len(fails), len(fails), max_dz=max_dz)
     print(f"  max|dz|={max_dz:.3e} exact={res['exact']} failures={fails}", flush=True)
     assert not fails
     assert res["exact"] >= B - max(1, B // 3)
