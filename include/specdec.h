@@ -52,7 +52,9 @@ typedef enum {
   SPECDEC_ERR_TEMPERATURE = 4, /* temperature < 0 or NaN                            */
   SPECDEC_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required           */
   SPECDEC_ERR_LAUNCH = 6,      /* the HIP runtime refused a launch                  */
-  SPECDEC_ERR_ARG = 7          /* an enumerated argument has an unknown value       */
+  SPECDEC_ERR_ARG = 7,         /* an enumerated argument has an unknown value       */
+  SPECDEC_ERR_SCRATCH = 8,     /* the shape's workspace exceeds the static buffer   */
+  SPECDEC_ERR_DEVICE = 9       /* the runtime gave no current device or buffer      */
 } specdec_status;
 
 /* How the draft distribution is given. */
@@ -224,6 +226,32 @@ int specdec_verify_step(const void* X, const void* W, int weight_layout, const f
                         int64_t gamma, int64_t d, int64_t V, float* logits, int32_t* out_tokens,
                         int32_t* out_num_emitted, float* out_probs, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * specdec_verify_step with the library's own static workspace instead of a
+ * caller-provided one.  The workspace is a file-scope device array of
+ * SPECDEC_NOALLOC_MAX_WORKSPACE bytes, one copy on every GPU the library runs
+ * on, held until the process ends; its device address is looked up once per
+ * device, on the first call made with that device current.  The call itself
+ * allocates nothing and frees nothing.
+ *   Arguments as in specdec_verify_step, without the workspace; the caller
+ *   still provides every input and output (logits as in specdec_verify_step).
+ *   SPECDEC_ERR_SCRATCH (before any device call) when
+ *   specdec_step_workspace_bytes(B, gamma, d, V, weight_layout) exceeds
+ *   SPECDEC_NOALLOC_MAX_WORKSPACE (32 MiB: up to about 512 positions of a
+ *   Llama-sized head); SPECDEC_ERR_DEVICE when the runtime cannot report the
+ *   current device or the buffer's address.
+ * Every call on one GPU uses that GPU's one buffer, which keeps the last
+ * call's contents (nothing in it needs to start at zero: each call
+ * initialises what it reads).  Calls that overlap in time on one GPU (from
+ * several host threads, or on several streams) race on it: order them on one
+ * stream, or give each its own workspace through specdec_verify_step. */
+#define SPECDEC_NOALLOC_MAX_WORKSPACE ((size_t)32 << 20)
+int specdec_verify_step_noalloc(const void* X, const void* W, int weight_layout, const float* draft, int draft_kind,
+                                const int32_t* draft_tokens, float temperature, const float* uniforms, int64_t B,
+                                int64_t gamma, int64_t d, int64_t V, float* logits, int32_t* out_tokens,
+                                int32_t* out_num_emitted, float* out_probs, void* stream);
 
 /* Top-k / top-p warping before the rule ([LESS] "Why the output is exactly p":
  * the sampling settings reshape p, and q before drafting, and the rule then

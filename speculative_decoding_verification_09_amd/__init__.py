@@ -43,6 +43,7 @@ EXPORTED = [
     "specdec_verify_logits",
     "specdec_reject_sample",
     "specdec_verify_step",
+    "specdec_verify_step_noalloc",
     "specdec_reject_sample_warped",
     "specdec_verify_step_warped",
     "specdec_tree_mask",
@@ -94,6 +95,9 @@ def _load() -> ctypes.CDLL:
     lib.specdec_verify_step.argtypes = [P, P, I, P, I, P, ctypes.c_float, P, I64, I64, I64, I64, P, P, P, P, P,
                                         ctypes.c_size_t, P]
     lib.specdec_verify_step.restype = I
+    lib.specdec_verify_step_noalloc.argtypes = [P, P, I, P, I, P, ctypes.c_float, P, I64, I64, I64, I64, P, P, P, P,
+                                                P]
+    lib.specdec_verify_step_noalloc.restype = I
     lib.specdec_reject_sample_warped.argtypes = [P, P, I, P, ctypes.c_float, I64, ctypes.c_float, P, I64, I64, I64, P,
                                                  P, P, P, ctypes.c_size_t, P]
     lib.specdec_reject_sample_warped.restype = I
@@ -336,6 +340,23 @@ def specdec_verify_step(X, W, draft, draft_tokens, temperature: float, uniforms,
                                     _ptr(out_num_emitted), _ptr(out_probs), _ptr(workspace), workspace.numel(),
                                     _stream(stream)), "specdec_verify_step")
     return out_tokens, out_num_emitted
+
+
+def specdec_verify_step_noalloc(X, W, draft, draft_tokens, temperature: float, uniforms, logits, out_tokens,
+                                out_num_emitted, out_probs=None, draft_kind: int = SPECDEC_DRAFT_LOGITS, stream=None):
+    """specdec_verify_step with the library's static device workspace (no workspace argument; the call allocates
+    nothing); see include/specdec.h."""
+    B, g, d, V, wp, layout = _step_shapes(X, W, draft, draft_tokens, uniforms, logits, out_tokens, out_num_emitted,
+                                          out_probs)
+    _check(_lib.specdec_verify_step_noalloc(_ptr(X), wp, layout, _ptr(draft), int(draft_kind), _ptr(draft_tokens),
+                                            float(temperature), _ptr(uniforms), B, g, d, V, _ptr(logits),
+                                            _ptr(out_tokens), _ptr(out_num_emitted), _ptr(out_probs),
+                                            _stream(stream)), "specdec_verify_step_noalloc")
+    return out_tokens, out_num_emitted
+
+
+NOALLOC_MAX_WORKSPACE = 32 << 20
+SPECDEC_ERR_SCRATCH = 8
 
 
 def specdec_verify_step_warped(X, W, draft, draft_tokens, temperature: float, top_k: int, top_p: float, uniforms,

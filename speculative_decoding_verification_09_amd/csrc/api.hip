@@ -4,6 +4,8 @@
 // layout of every argument, are in include/specdec.h.
 #include <math.h>
 
+#include <atomic>
+
 #include "../../include/specdec.h"
 #include "internal.h"
 
@@ -127,6 +129,10 @@ const char* specdec_status_string(int status) {
     case SPECDEC_ERR_WORKSPACE: return "workspace is NULL or too small";
     case SPECDEC_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
     case SPECDEC_ERR_ARG: return "an enumerated argument has an unknown value";
+    case SPECDEC_ERR_SCRATCH:
+      return "the shape needs more workspace than the library's static device buffer holds (use the entry point "
+             "that takes a workspace)";
+    case SPECDEC_ERR_DEVICE: return "the HIP runtime could not report the current device or its buffer";
     default: return "unknown status";
   }
 }
@@ -302,6 +308,59 @@ int specdec_verify_step(const void* X, const void* W, int weight_layout, const f
                             stream) != SPECDEC_OK)
     return SPECDEC_ERR_LAUNCH;
   return specdec::launch_reject_sample(a, s) == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_LAUNCH;
+}
+
+}  // extern "C"
+
+namespace {
+
+// The static device buffer of specdec_verify_step_noalloc: file-scope device
+// memory, one copy on every GPU the library runs on, zero when the code object
+// is loaded and held until the process ends.  In host code `scratch` names a
+// host-side stand-in; its device address on the current device comes from
+// hipGetSymbolAddress, once per device, and only that address is handed to
+// the kernels.
+constexpr size_t kStaticScratchBytes = SPECDEC_NOALLOC_MAX_WORKSPACE;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];  // per device, null until looked up
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device), or null when the runtime cannot give it.
+void* static_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // Two host threads may both look it up: they get the same address.
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int specdec_verify_step_noalloc(const void* X, const void* W, int weight_layout, const float* draft, int draft_kind,
+                                const int32_t* draft_tokens, float temperature, const float* uniforms, int64_t B,
+                                int64_t gamma, int64_t d, int64_t V, float* logits, int32_t* out_tokens,
+                                int32_t* out_num_emitted, float* out_probs, void* stream) {
+  // Sizes first, without touching the device: a shape whose workspace does
+  // not fit the static buffer is refused before anything else.
+  if (B < 1 || B > kMaxRows || gamma < 0 || gamma > SPECDEC_MAX_GAMMA) return SPECDEC_ERR_SHAPE;
+  const size_t need = specdec_step_workspace_bytes(B, gamma, d, V, weight_layout);
+  if (need == 0) {
+    const int st = check_logits_shape(B * (gamma + 1), d, V, weight_layout);
+    return st != SPECDEC_OK ? st : SPECDEC_ERR_SHAPE;
+  }
+  if (need > kStaticScratchBytes) return SPECDEC_ERR_SCRATCH;
+  void* ws = static_scratch();
+  if (ws == nullptr) return SPECDEC_ERR_DEVICE;
+  return specdec_verify_step(X, W, weight_layout, draft, draft_kind, draft_tokens, temperature, uniforms, B, gamma, d,
+                             V, logits, out_tokens, out_num_emitted, out_probs, ws, kStaticScratchBytes, stream);
 }
 
 size_t specdec_tree_workspace_bytes(int64_t B, int64_t M, int64_t V) {

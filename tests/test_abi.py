@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     assert sd.status_string(0) == "ok"
-    for s in range(1, 8):
+    for s in range(1, 10):
         assert sd.status_string(s) and sd.status_string(s) != "unknown status"
     assert sd.status_string(99) == "unknown status"
     assert sd.version() == 10300
@@ -316,3 +316,20 @@ def test_size_queries_from_many_threads():
     with ThreadPoolExecutor(max_workers=8) as ex:
         for got in ex.map(answers, range(64)):
             assert got == alone
+
+
+def test_noalloc_size_checks_come_first():
+    """The allocation-free step refuses a shape whose workspace exceeds its static buffer before any device call
+    (so this runs without a GPU), and invalid sizes as the workspace step does."""
+    lib = sd.library()
+
+    def call(B=1024, g=31, d=256, V=128256, lay=1):
+        return lib.specdec_verify_step_noalloc(P(A), P(A), lay, None, 0, P(A), 0.0, None, B, g, d, V, None, P(A),
+                                               P(A), None, None)
+
+    assert sd.step_workspace_bytes(1024, 31, 256, 128256, 1) > sd.NOALLOC_MAX_WORKSPACE
+    assert call() == sd.SPECDEC_ERR_SCRATCH
+    assert call(B=0) == 2
+    assert call(g=64) == 2
+    assert call(d=100) == 2
+    assert call(lay=5) == 7
