@@ -96,7 +96,7 @@ size_t specdec_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
  * device.  0 means none (the workspace argument may then be NULL).  With
  * packed weights, at most 16 positions, V >= 65536 and d <= 4096 it is 256
  * bytes: the counter of the queue from which the workgroups take vocabulary
- * tiles (reset by the call itself before use).  When the
+ * tiles (initialised by the call itself).  When the
  * output rows are too few to occupy every compute unit, or X is too large to
  * stage whole, the k range is split into groups whose fp32 partial sums are
  * kept here and then added in group order.  For many positions with packed

@@ -26,6 +26,8 @@
 // reads within a window of about (#CUs x tile size), which keeps HBM
 // streaming close to a plain sequential read; the last tiles come from a
 // queue, so that every workgroup finishes at about the same time.
+#include <chrono>
+
 #include "gemm_common.h"
 
 namespace specdec {
@@ -57,8 +59,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
 // Tiles come in two phases.  First a fixed share: workgroup b takes tiles b,
 // b + G, ..., b + (S-1)*G (G = grid size, S*G about 85% of the tiles), the
 // next tile's loads in flight while the current one computes.  Then a queue:
-// a ticket counter (zeroed by a one-thread kernel before each launch) hands
-// out the remaining tiles in the order asked for.  HBM does not serve every
+// a ticket counter hands out the remaining tiles in the order asked for.  HBM does not serve every
 // CU equally fast (measured on the LM-head sweep: with fixed shares only, the
 // workgroups on four of the eight XCDs finished 11-15% later than those on
 // the other four, whatever tiles they were given), so fixed shares alone
@@ -69,6 +70,18 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
 // In the queue phase thread 0 asks for the next ticket right after the
 // current tile's loads go out, and reads the answer once they have been
 // used.
+//
+// The counter lives in the caller's workspace, which holds anything on entry.
+// Workgroup 0 zeroes it as its first act and then publishes a tag unique to
+// this launch (from the host, 64 bits) next to it, with release order; every
+// workgroup reads that word one tile before its first ticket and asks only
+// once it holds this launch's tag.  A launch thus never needs a separate
+// reset (measured: a one-thread reset kernel before the sweep cost 1.5 us of
+// the 166 us one-sequence step).  Waiting for the tag ends: workgroup 0 runs
+// its first instructions without waiting on anything, and the grid (at most
+// one workgroup per CU) is resident as a whole.  The wait is bounded all the
+// same; past the bound a workgroup takes no queue tile (the bound, about a
+// second, is never reached while the grid is resident).
 //
 // Every global load is issued unconditionally, with its address clamped into
 // the wave's k range (those values are never used): the compiler can then
@@ -88,13 +101,20 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
 // tile; the queue evens out the difference.
 constexpr int kDraftSlice = 2048;
 
+constexpr int kTagSpinLimit = 1 << 22;  // polls of the launch tag, each after a short sleep
+
 template <int NW, int SPW, bool NTL, bool OUT_BF16, int EPI>
 __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp,
                                                         void* __restrict__ Y, int N, int d, int V, int S,
-                                                        unsigned* __restrict__ tickets, FusedStats fs) {
+                                                        unsigned* __restrict__ tickets, uint64_t tag, FusedStats fs) {
   extern __shared__ __align__(16) uint16_t lds[];
   __shared__ int sh_tile;  // the next queue tile, passed from thread 0 to the workgroup
   const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, g = lane >> 4;
+  uint64_t* const ready = (uint64_t*)(tickets + 2);  // the launch tag, 8 bytes after the counter
+  if (blockIdx.x == 0 && tid == 0) {
+    __hip_atomic_store(tickets, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(ready, tag, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
   if (EPI == 1 && fs.done != nullptr) {  // the draw kernel's counters, for the step that follows
     const int64_t gid = (int64_t)blockIdx.x * (NW * 64) + tid;
     if (gid < fs.B) fs.done[gid] = 0u;
@@ -107,7 +127,21 @@ __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restri
   // Ticket k names tile qbase + k; past the last tile, ntiles (no tile).
   auto tile_of = [&](unsigned k) { return k < (unsigned)(ntiles - qbase) ? qbase + (int)k : ntiles; };
   auto ask = [&]() { return __hip_atomic_fetch_add(tickets, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-  if (S == 0 && tid == 0) sh_tile = tile_of(ask());  // no fixed share: the first tile comes from the queue
+  // Thread 0: the tag word as last read (read early, one tile ahead of the
+  // first ticket), and the first ticket once it shows this launch's tag.
+  uint64_t seen = 0;
+  auto read_tag = [&]() { seen = __hip_atomic_load(ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  auto first_ask = [&]() {
+    for (int i = 0; seen != tag && i < kTagSpinLimit; ++i) {
+      __builtin_amdgcn_s_sleep(2);
+      read_tag();
+    }
+    return seen == tag ? ask() : 0xffffffffu;  // past the bound: no queue tile
+  };
+  if (S == 0 && tid == 0) {  // no fixed share: the first tile comes from the queue
+    read_tag();
+    sh_tile = tile_of(first_ask());
+  }
   const int pitch = nsteps * 32 + kPad;
   const int spw = (nsteps + NW - 1) / NW;         // k-steps per wave and tile (<= SPW)
   uint16_t* xs = lds;
@@ -254,21 +288,24 @@ __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restri
   if (S > 0) {
     const int b = (int)blockIdx.x;
     u32x4 a0[SPW], a1[SPW];
+    if (S == 1 && tid == 0) read_tag();
     load(a0, b);
     int j = 0;
     for (; j + 2 < S; j += 2) {
+      if (j + 4 >= S && tid == 0) read_tag();  // the last trip: a tile or two ahead of the first ticket
       load(a1, b + (j + 1) * G);
       consume(a0, b + j * G, false);
       load(a0, b + (j + 2) * G);
       consume(a1, b + (j + 1) * G, false);
     }
     if (j + 1 < S) {
+      if (j == 0 && tid == 0) read_tag();
       load(a1, b + (j + 1) * G);
       consume(a0, b + j * G, false);
-      if (tid == 0) ticket = ask();
+      if (tid == 0) ticket = first_ask();
       consume(a1, b + (j + 1) * G, true);
     } else {
-      if (tid == 0) ticket = ask();
+      if (tid == 0) ticket = first_ask();
       consume(a0, b + j * G, true);
     }
   }
@@ -318,8 +355,16 @@ __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restri
   }
 }
 
-__global__ __launch_bounds__(64) void reset_tickets_kernel(unsigned* __restrict__ tickets) {
-  if (threadIdx.x == 0) tickets[0] = 0u;
+// A tag unique to each launch in this process (a bijective mix of a counter
+// that starts at a value drawn from the clock and an address), never 0.
+uint64_t next_launch_tag() {
+  static std::atomic<uint64_t> counter{(uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() ^
+                                       ((uint64_t)(uintptr_t)&counter << 17)};
+  uint64_t z = counter.fetch_add(0x9e3779b97f4a7c15ull, std::memory_order_relaxed) + 0x9e3779b97f4a7c15ull;
+  z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+  z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+  z ^= z >> 31;
+  return z ? z : 1;
 }
 
 constexpr int kSweepWaves = 8;
@@ -338,15 +383,12 @@ hipError_t launch_sweep_kernel(const SweepPlan& p, const uint16_t* X, const uint
   auto k = sweep_kernel<kSweepWaves, kSweepGroup, true, OUT_BF16, EPI>;
   hipError_t e = allow_lds(k, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(reset_tickets_kernel, dim3(1), dim3(64), 0, stream, (unsigned*)tickets);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   // The fixed share: about 85% of the tiles (measured on the LM-head sweep:
   // 80-90% equally fast, 70% and 95% slower).
   const int64_t ntiles = (V + 15) / 16;
   const int S = (int)(ntiles * 17 / (20 * p.grid));
   hipLaunchKernelGGL(k, dim3((unsigned)p.grid), dim3(kSweepWaves * 64), lds, stream, X, Wp, Y, (int)N, (int)d, (int)V, S,
-                     (unsigned*)tickets, fs);
+                     (unsigned*)tickets, next_launch_tag(), fs);
   return hipGetLastError();
 }
 

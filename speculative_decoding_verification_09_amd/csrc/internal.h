@@ -16,8 +16,8 @@ hipError_t launch_skinny_gemm(const uint16_t* X, const uint16_t* W, void* Y, int
 
 namespace gemm {
 // The sweep kernel (packed W, at most 16 positions, X whole in LDS; ok is
-// false when X does not fit).  tickets: 4 bytes of device memory for its tile
-// queue, reset by the launch itself.
+// false when X does not fit).  tickets: 16 bytes of device memory for its tile
+// queue (a counter and a launch tag), initialised by the launch itself.
 struct SweepPlan {
   bool ok;
   int64_t grid;
