@@ -164,12 +164,13 @@ __global__ __launch_bounds__(NW * 64) void sweep_kernel(const uint16_t* __restri
       float mx = -INFINITY;
       double sm = 0.0;
       for (int c = (int)blockIdx.x; c < nsl; c += G) {
+        // Loads from clamped indices first, all in flight together (guarded
+        // loads compiled to one round trip per entry), then the mask.
         float a[kPer];
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) {
-          const int v = c * kDraftSlice + 64 * e + lane;
-          a[e] = v < V ? row[v] * fs.inv_t : -INFINITY;
-        }
+        for (int e = 0; e < kPer; ++e) a[e] = row[min(c * kDraftSlice + 64 * e + lane, V - 1)];
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) a[e] = c * kDraftSlice + 64 * e + lane < V ? a[e] * fs.inv_t : -INFINITY;
         float bm = a[0];
 #pragma unroll
         for (int e = 1; e < kPer; ++e) bm = fmaxf(bm, a[e]);
