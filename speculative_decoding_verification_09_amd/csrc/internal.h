@@ -80,10 +80,24 @@ __device__ __forceinline__ uint32_t order_key(float z) {
 __device__ __forceinline__ bool warp_kept(uint32_t key, int64_t v, uint32_t cut_key, int32_t cut_idx) {
   return key > cut_key || (key == cut_key && v <= (int64_t)cut_idx);
 }
+// Where the warp cut kernel leaves each warped row's statistics, in the
+// layout of the statistics pass: per row, pstride slots of (max of z/T, sum of
+// exp(z/T - max)), of which nch are read; the drafted token's logit; and the
+// draw kernel's per-sequence counters, zeroed.
+struct WarpStats {
+  float* cmax;
+  double* csum;
+  float* zx;
+  int64_t pstride, nch;
+  const int32_t* tokens;  // [B, gamma]
+  int64_t gamma, B;
+  uint32_t* done;         // [B]
+};
 // One workgroup per row: rows [0, n_target) of target, then rows of draft.
+// Writes each row's cut and its statistics after warping.
 hipError_t launch_warp_cuts(const float* target, const float* draft, int64_t n_target, int64_t n_rows, int64_t V,
                             float inv_t, int64_t top_k, float top_p, uint32_t* cut_key, int32_t* cut_idx,
-                            hipStream_t stream);
+                            const WarpStats& so, hipStream_t stream);
 
 // Softmax (or argmax) statistics formed by the scoring kernel itself, as an
 // epilogue: for every row, one partial per workgroup of that kernel, in the

@@ -177,10 +177,10 @@ __device__ __forceinline__ int clamp_token(int32_t t, int64_t V) { return t < 0 
 //    draft rows [B*(gamma+1), B*(2*gamma+1)) (row B*(gamma+1) + b*gamma + i).
 //    Lane l of a wave takes the 32 entries 256*j + 4*l + e (j < 8, e < 4) of
 //    its 2048-entry chunk (1 KB per load instruction).  Rows [row0, n_rows)
-//    are summarised.  WARP: entries the row's warp cut drops count as -inf (so
-//    does a dropped drafted token).  The first n_done threads also zero the
-//    draw kernel's per-sequence counters.
-template <bool VEC, bool GREEDY, bool WARP>
+//    are summarised.  The first n_done threads also zero the draw kernel's
+//    per-sequence counters.  (Warped rows are summarised by the warp cut
+//    kernel itself.)
+template <bool VEC, bool GREEDY>
 __global__ __launch_bounds__(kWavesPerBlock * 64) void stats_kernel(const float* __restrict__ target,
                                                                      const float* __restrict__ draft,
                                                                      const int32_t* __restrict__ tokens,
@@ -231,15 +231,6 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void stats_kernel(const float*
     }
     return;
   }
-  uint32_t wk = 0;
-  int32_t wi = 0x7fffffff;
-  if (WARP) {
-    wk = ws.wkey[r];
-    wi = ws.widx[r];
-#pragma unroll
-    for (int e = 0; e < PL; ++e)
-      if (!warp_kept(order_key(x[e]), c0 + 256 * (e >> 2) + 4 * lane + (e & 3), wk, wi)) x[e] = -INFINITY;
-  }
   // The drafted token of this row, if it falls in this chunk.
   const int64_t g1 = gamma + 1;
   const int64_t b = is_target ? r / g1 : (r - n_target_rows) / gamma;
@@ -247,8 +238,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void stats_kernel(const float*
   if (i < gamma && lane == 0) {
     const int xt = clamp_token(tokens[b * gamma + i], V);
     if (xt >= c0 && xt < c0 + kStatChunk) {
-      const float zx = row[xt];
-      ws.zx[r] = (!WARP || warp_kept(order_key(zx), xt, wk, wi)) ? zx : -INFINITY;
+      ws.zx[r] = row[xt];
     }
   }
   // The chunk max of a = z * fl32(1/T) is fl32(max z * fl32(1/T)) (the product
@@ -261,7 +251,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void stats_kernel(const float*
   for (int e = 0; e < PL; ++e) zm = fmaxf(zm, x[e]);
   const float mx = wave_max(zm) * inv_t;
   double sum = 0.0;
-  if (mx > -INFINITY) {  // a chunk the warp cut drops whole has no mass
+  if (mx > -INFINITY) {
     const float c1 = inv_t * kLog2e, c2 = mx * kLog2e;
 #pragma unroll
     for (int e = 0; e < PL; e += 4) {
@@ -1080,10 +1070,10 @@ hipError_t launch_draft_stats(const FusedStats& fs, int64_t n_target, int64_t V,
   ws.nparts = ws.nparts_d = nch;
   const dim3 grid(blocks_for(nd * nch, kWavesPerBlock)), blk(kWavesPerBlock * 64);
   if ((V & 3) == 0)
-    hipLaunchKernelGGL((stats_kernel<true, false, false>), grid, blk, 0, stream, nullptr, fs.draft, fs.tokens,
+    hipLaunchKernelGGL((stats_kernel<true, false>), grid, blk, 0, stream, nullptr, fs.draft, fs.tokens,
                        n_target, n_target, n_target + nd, fs.gamma, V, fs.inv_t, ws, (int64_t)0);
   else
-    hipLaunchKernelGGL((stats_kernel<false, false, false>), grid, blk, 0, stream, nullptr, fs.draft, fs.tokens,
+    hipLaunchKernelGGL((stats_kernel<false, false>), grid, blk, 0, stream, nullptr, fs.draft, fs.tokens,
                        n_target, n_target, n_target + nd, fs.gamma, V, fs.inv_t, ws, (int64_t)0);
   return hipGetLastError();
 }
@@ -1130,10 +1120,10 @@ hipError_t launch_tree_greedy(const TreeArgs& t, int64_t nparts, hipStream_t str
     const int64_t rows = t.B * t.M;
     const dim3 g1(blocks_for(rows * stat_chunks(t.V), kWavesPerBlock));
     if ((t.V & 3) == 0)
-      hipLaunchKernelGGL((stats_kernel<true, true, false>), g1, blk, 0, stream, t.logits, nullptr, nullptr, rows, 0, rows,
+      hipLaunchKernelGGL((stats_kernel<true, true>), g1, blk, 0, stream, t.logits, nullptr, nullptr, rows, 0, rows,
                          (int64_t)0, t.V, 1.0f, ws, (int64_t)0);
     else
-      hipLaunchKernelGGL((stats_kernel<false, true, false>), g1, blk, 0, stream, t.logits, nullptr, nullptr, rows, 0, rows,
+      hipLaunchKernelGGL((stats_kernel<false, true>), g1, blk, 0, stream, t.logits, nullptr, nullptr, rows, 0, rows,
                          (int64_t)0, t.V, 1.0f, ws, (int64_t)0);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1166,20 +1156,20 @@ hipError_t launch_reject_sample(const RejectArgs& a, hipStream_t stream) {
                          a.uniforms, a.B, a.gamma, a.V, inv_t, a.out_tokens, a.out_num, a.out_probs);
     return hipGetLastError();
   }
-  if (warp) {  // the per-row cuts, read by every later kernel
+  if (warp) {  // the per-row cuts and the warped rows' statistics (no statistics pass)
+    const WarpStats so{ws.cmax, ws.csum, ws.zx, ws.pstride, stat_chunks(a.V), a.tokens, a.gamma, a.B, ws.done};
     const hipError_t ew = launch_warp_cuts(a.target, a.draft, n_target, n_rows, a.V, inv_t, a.top_k, a.top_p,
-                                           ws.wkey, ws.widx, stream);
+                                           ws.wkey, ws.widx, so, stream);
     if (ew != hipSuccess) return ew;
+    return launch_decide(a, ws, stream);
   }
-#define SPECDEC_STATS(V4, GR, WP)                                                                                        \
-  hipLaunchKernelGGL((stats_kernel<V4, GR, WP>), g1, blk, 0, stream, a.target, a.draft, a.tokens, n_target, 0, n_rows, \
+#define SPECDEC_STATS(V4, GR)                                                                                        \
+  hipLaunchKernelGGL((stats_kernel<V4, GR>), g1, blk, 0, stream, a.target, a.draft, a.tokens, n_target, 0, n_rows, \
                      a.gamma, a.V, inv_t, ws, greedy ? (int64_t)0 : a.B)
   if (greedy) {
-    if (vec) SPECDEC_STATS(true, true, false); else SPECDEC_STATS(false, true, false);
-  } else if (warp) {
-    if (vec) SPECDEC_STATS(true, false, true); else SPECDEC_STATS(false, false, true);
+    if (vec) SPECDEC_STATS(true, true); else SPECDEC_STATS(false, true);
   } else {
-    if (vec) SPECDEC_STATS(true, false, false); else SPECDEC_STATS(false, false, false);
+    if (vec) SPECDEC_STATS(true, false); else SPECDEC_STATS(false, false);
   }
 #undef SPECDEC_STATS
   const hipError_t e = hipGetLastError();

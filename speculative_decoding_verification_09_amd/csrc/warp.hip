@@ -165,9 +165,8 @@ __device__ __forceinline__ void clear_bins(Shared& sh, bool mass) {
 // Calls f(v, z) for every entry of the row; wave w takes the contiguous range
 // [w*R, (w+1)*R) (R a multiple of 256) in steps of 256 entries, lane l the 4
 // entries at 4l, four steps' loads issued together.
-template <bool VEC, class F>
+template <bool VEC, class F, int U = 4>
 __device__ __forceinline__ void for_row(const float* __restrict__ row, int V, int R, F&& f) {
-  constexpr int U = 4;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int b0 = w * R, b1 = min(b0 + R, V);
   for (int base = b0; base < b1; base += U * 256) {
@@ -392,10 +391,65 @@ __device__ Cut select_cut(const float* __restrict__ row, int V, int R, u64 need,
   return Cut{(uint32_t)(c >> kIdxBits), (int32_t)(kIdxMask - (uint32_t)(c & kIdxMask))};
 }
 
+// Sorts sh.comp[0, S) into descending order with wave 0 alone (n <= S real
+// entries, the rest zeros; S = 256 or 512): a bitonic network over S values
+// held S/64 to a lane (value e in lane e % 64, register e / 64), partners in
+// other lanes reached by shuffles, in the same lane by register swaps.  No
+// barrier inside: measured against the workgroup-wide network, whose barrier
+// per stage cost about 15 us per batch of warped rows at a few hundred
+// candidates.
+template <int S>
+__device__ void sort_desc_wave(int n, Shared& sh) {
+  constexpr int J = S / 64;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    u64 x[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) x[j] = lane + 64 * j < n ? sh.comp[lane + 64 * j] : 0ull;
+#pragma unroll
+    for (int size = 2; size <= S; size <<= 1) {
+#pragma unroll
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          const int e = lane + 64 * j;
+          const bool desc = (e & size) == 0;  // the final merge (size == S) is descending
+          if (stride >= 64) {
+            const int jp = j ^ (stride >> 6);
+            if (jp > j) {  // each pair once, from its lower register
+              const u64 a = x[j], b = x[jp];
+              const bool swap = (a < b) == desc;
+              x[j] = swap ? b : a;
+              x[jp] = swap ? a : b;
+            }
+          } else {
+            const u64 o = (u64)__shfl_xor((long long)x[j], stride);
+            const bool lower = (e & stride) == 0;  // e below its partner
+            // the lower one keeps the larger value when the merge is descending
+            const bool take_max = lower == desc;
+            x[j] = take_max ? (o > x[j] ? o : x[j]) : (o < x[j] ? o : x[j]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < J; ++j) sh.comp[lane + 64 * j] = x[j];
+  }
+  __syncthreads();
+}
+
 // Sorts sh.comp[0, n) into descending order (n <= kCap): a bitonic network
 // over the next power of two, the padding zeros (below every composite of a
 // real entry but a possible 0, which then sorts among them) last.
 __device__ void sort_desc(int n, Shared& sh) {
+  if (n <= 256) {
+    sort_desc_wave<256>(n, sh);
+    return;
+  }
+  if (n <= 512) {
+    sort_desc_wave<512>(n, sh);
+    return;
+  }
   int P = 1;
   while (P < n) P <<= 1;
   for (int i = n + threadIdx.x; i < P; i += kThreads) sh.comp[i] = 0ull;
@@ -419,13 +473,14 @@ __device__ void sort_desc(int n, Shared& sh) {
 // Both cuts from n candidates in LDS that include every entry of the row's
 // top k (top_k <= n): sorted, the top-k cut is the top_k-th; top-p then runs
 // over those top_k entries in rank order (masses exact in fixed point).
-__device__ void cuts_from_candidates(int n, int64_t top_k, bool tp, float top_p, float inv_t, float zmax, Shared& sh,
-                                     Cut& cut) {
+// Returns how many entries the cut keeps: ranks [0, that) of sh.comp.
+__device__ int cuts_from_candidates(int n, int64_t top_k, bool tp, float top_p, float inv_t, float zmax, Shared& sh,
+                                    Cut& cut) {
   sort_desc(n, sh);
   const int kk = (int)top_k;  // top_k < V <= 2^23 and top_k <= n <= kCap
   const u64 ck = sh.comp[kk - 1];
   cut = Cut{(uint32_t)(ck >> kIdxBits), (int32_t)(kIdxMask - (uint32_t)(ck & kIdxMask))};
-  if (!tp) return;
+  if (!tp) return kk;
   // Thread t holds ranks 2t and 2t + 1.
   u64 m[2];
 #pragma unroll
@@ -456,6 +511,19 @@ __device__ void cuts_from_candidates(int n, int64_t top_k, bool tp, float top_p,
     cut = Cut{(uint32_t)(cp >> kIdxBits), (int32_t)(kIdxMask - (uint32_t)(cp & kIdxMask))};
   }
   __syncthreads();
+  return f >= 0 ? f + 1 : kk;
+}
+
+__device__ __forceinline__ double block_sum_f64(double v, u64* lds) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if (lane == 0) lds[wv] = __double_as_longlong(v);
+  __syncthreads();
+  double r = 0.0;
+  for (int w = 0; w < kWaves; ++w) r += __longlong_as_double(lds[w]);  // fixed order
+  __syncthreads();
+  return r;
 }
 
 template <bool VEC>
@@ -463,24 +531,113 @@ __global__ __launch_bounds__(kThreads) void warp_cut_kernel(const float* __restr
                                                             const float* __restrict__ draft, int64_t n_target,
                                                             int64_t V64, float inv_t, int64_t top_k, float top_p,
                                                             uint32_t* __restrict__ cut_key,
-                                                            int32_t* __restrict__ cut_idx) {
+                                                            int32_t* __restrict__ cut_idx, WarpStats so) {
   __shared__ Shared sh;
   const int V = (int)V64;
   const int64_t r = blockIdx.x;
   const float* row = r < n_target ? target + (size_t)r * V : draft + (size_t)(r - n_target) * V;
   const int R = ((V + kWaves * 256 - 1) / (kWaves * 256)) * 256;
   const bool tk = top_k > 0 && top_k < V, tp = top_p < 1.0f;
+  // Thread 0: the row's drafted token and its logit, loaded now for the end.
+  int xt = -1;
+  float zx = 0.0f;
+  if (threadIdx.x == 0) {
+    const int64_t g1 = so.gamma + 1;
+    const bool is_target = r < n_target;
+    const int64_t b = is_target ? r / g1 : (r - n_target) / (so.gamma > 0 ? so.gamma : 1);  // draft rows: gamma > 0
+    const int64_t i = is_target ? r - b * g1 : (r - n_target) - b * so.gamma;
+    if (i < so.gamma) {
+      const int32_t x = so.tokens[b * so.gamma + i];
+      xt = x < 0 ? 0 : (x >= V ? V - 1 : x);
+      zx = row[xt];
+    }
+  }
   Cut cut{0u, 0x7fffffff};  // keeps every entry
-  // Pass 1: the row maximum, and the top-k level-1 histogram.
-  if (tk) clear_bins(sh, false);
-  float zm = -INFINITY;
-  for_row<VEC>(row, V, R, [&](int /*v*/, float z) {
-    zm = fmaxf(zm, z);
-    if (tk) atomicAdd(&sh.cnt[order_key(z) >> 20], 1u);
-  });
-  const float zmax = block_max(zm, sh.redf);
   bool done_p = false;
-  if (tk) {
+  int nk = -1;  // when the kept entries are ranks [0, nk) of the sorted candidates in LDS
+  float zmax;
+  // A small top-k of a long row, in one pass: a strided sample of 16 entries
+  // per thread, histogrammed by key (12 bits, then the next 12 within the
+  // bucket), gives a threshold t0 at the sample entry whose count from the top
+  // stands for about 3*top_k row entries; the pass then takes the row maximum and
+  // collects every entry at or above t0 into LDS.  At least top_k of them,
+  // none lost to overflow: they hold the whole top k (the k-th largest key is
+  // at or above t0), and both cuts come from them.  Otherwise the passes
+  // below run as if nothing had been collected.  (Histogramming every entry
+  // of the row by bucket serialised on the LDS atomics of the crowded
+  // buckets: the one-pass path measured much faster.)
+  const bool collect = tk && top_k <= kCap / 4 && V >= 16 * kThreads;
+  if (collect) {
+    clear_bins(sh, false);
+    // Sample entries 4*(q*(4t + u)) + e of thread t (u, e < 4; q >= 1): 16384 in all.
+    const int q = V / (16 * kThreads);
+    uint32_t ks[16];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v0 = 4 * q * (4 * (int)threadIdx.x + u);  // v0 + 3 < V
+      if (VEC) {
+        const float4 t = *(const float4*)(row + v0);
+        ks[4 * u + 0] = order_key(t.x);
+        ks[4 * u + 1] = order_key(t.y);
+        ks[4 * u + 2] = order_key(t.z);
+        ks[4 * u + 3] = order_key(t.w);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ks[4 * u + e] = order_key(row[v0 + e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) atomicAdd(&sh.cnt[ks[e] >> 20], 1u);
+    __syncthreads();
+    // The s0-th largest sample stands for about 3*top_k row entries (mean);
+    // fewer than top_k row entries at or above it would need s0 of the row's
+    // top top_k - 1 in the sample, far out in the tail.
+    const u64 s0 = (u64)((3 * top_k * 16 * kThreads + V - 1) / V);  // >= 1
+    uint32_t b0, b1;
+    u64 above0, above1;
+    scan_bins<false>(kBins, s0, sh, b0, above0);
+    // ... refined by the sample's next 12 key bits within that bucket
+    clear_bins(sh, false);
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if ((ks[e] >> 20) == b0) atomicAdd(&sh.cnt[(ks[e] >> 8) & 0xfffu], 1u);
+    __syncthreads();
+    scan_bins<false>(kBins, s0 - above0, sh, b1, above1);
+    const uint32_t t0 = (b0 << 20) | (b1 << 8);
+    if (threadIdx.x == 0) sh.ncand = 0;
+    __syncthreads();
+    float zm = -INFINITY;
+    auto take = [&](int v, float z) {
+      zm = fmaxf(zm, z);
+      const uint32_t k = order_key(z);
+      if (k >= t0) {
+        const uint32_t s = atomicAdd(&sh.ncand, 1u);
+        if (s < (uint32_t)kCap) sh.comp[s] = composite(k, v);
+      }
+    };
+    for_row<VEC, decltype(take)&, 8>(row, V, R, take);  // eight 16-byte loads in flight per lane
+    zmax = block_max(zm, sh.redf);  // its barriers order the appends
+    const uint32_t napp = sh.ncand;
+    __syncthreads();
+    if (napp >= (uint32_t)top_k && napp <= (uint32_t)kCap) {
+      nk = cuts_from_candidates((int)napp, top_k, tp, top_p, inv_t, zmax, sh, cut);
+      done_p = tp;
+    } else {  // the level-1 histogram in a pass of its own
+      clear_bins(sh, false);
+      for_row<VEC>(row, V, R, [&](int, float z) { atomicAdd(&sh.cnt[order_key(z) >> 20], 1u); });
+      __syncthreads();
+    }
+  } else {
+    // Pass 1: the row maximum, and the top-k level-1 histogram.
+    if (tk) clear_bins(sh, false);
+    float zm = -INFINITY;
+    for_row<VEC>(row, V, R, [&](int /*v*/, float z) {
+      zm = fmaxf(zm, z);
+      if (tk) atomicAdd(&sh.cnt[order_key(z) >> 20], 1u);
+    });
+    zmax = block_max(zm, sh.redf);
+  }
+  if (tk && nk < 0) {
     uint32_t b;
     u64 above;
     scan_bins<false>(kBins, (u64)top_k, sh, b, above);
@@ -489,13 +646,14 @@ __global__ __launch_bounds__(kThreads) void warp_cut_kernel(const float* __restr
     if (held <= (u64)kCap) {
       // Every entry at or above the cut's bucket fits in LDS: both cuts from there.
       const int n = compact<false, VEC>(row, V, R, 0xfff00000u, b << 20, true, cut, inv_t, zmax, sh);
-      cuts_from_candidates(n, top_k, tp, top_p, inv_t, zmax, sh, cut);
+      nk = cuts_from_candidates(n, top_k, tp, top_p, inv_t, zmax, sh, cut);
       done_p = tp;
     } else {
       cut = select_cut<false, VEC>(row, V, R, (u64)top_k, cut, inv_t, zmax, sh);
     }
   }
   if (tp && !done_p) {
+    nk = -1;
     clear_bins(sh, true);
     u64 part = 0;
     for_row<VEC>(row, V, R, [&](int v, float z) {
@@ -519,20 +677,50 @@ __global__ __launch_bounds__(kThreads) void warp_cut_kernel(const float* __restr
     cut_key[r] = cut.key;
     cut_idx[r] = cut.idx;
   }
+  // The warped row's statistics, as the statistics pass would leave them (one
+  // partial in slot 0, the row's other slots empty): the max of a = z *
+  // fl32(1/T) over the kept entries (the row maximum: the first entry in rank
+  // order is always kept) and Z = sum over them of exp(a - max), each term
+  // 2^(z * c1 - c2) with c1 = fl32(1/T) * log2(e), c2 = max * log2(e), fp32
+  // terms summed in fp64; and the drafted token's logit (-inf when the cut
+  // drops it).  The kept entries are the candidates' ranks [0, nk) when the
+  // cut came from them; otherwise one more pass over the row.
+  const float mx = zmax * inv_t;
+  double zsum = 0.0;
+  if (mx > -INFINITY) {
+    const float c1 = inv_t * 1.4426950408889634f, c2 = mx * 1.4426950408889634f;
+    if (nk >= 0) {
+      for (int i = threadIdx.x; i < nk; i += kThreads)
+        zsum += (double)__builtin_amdgcn_exp2f(fmaf(key_value((uint32_t)(sh.comp[i] >> kIdxBits)), c1, -c2));
+    } else {
+      for_row<VEC>(row, V, R, [&](int v, float z) {
+        if (warp_kept(order_key(z), v, cut.key, cut.idx)) zsum += (double)__builtin_amdgcn_exp2f(fmaf(z, c1, -c2));
+      });
+    }
+  }
+  zsum = block_sum_f64(zsum, sh.red);
+  const size_t base = (size_t)r * so.pstride;
+  for (int c = threadIdx.x; c < so.nch; c += kThreads) {
+    so.cmax[base + c] = c == 0 ? mx : -INFINITY;
+    so.csum[base + c] = c == 0 ? zsum : 0.0;
+  }
+  if (threadIdx.x == 0 && xt >= 0) so.zx[r] = warp_kept(order_key(zx), xt, cut.key, cut.idx) ? zx : -INFINITY;
+  if (r == 0)
+    for (int64_t t = threadIdx.x; t < so.B; t += kThreads) so.done[t] = 0u;
 }
 
 }  // namespace
 
 hipError_t launch_warp_cuts(const float* target, const float* draft, int64_t n_target, int64_t n_rows, int64_t V,
                             float inv_t, int64_t top_k, float top_p, uint32_t* cut_key, int32_t* cut_idx,
-                            hipStream_t stream) {
+                            const WarpStats& so, hipStream_t stream) {
   if (n_rows == 0) return hipSuccess;
   if ((V & 3) == 0)
     hipLaunchKernelGGL(warp_cut_kernel<true>, dim3((unsigned)n_rows), dim3(kThreads), 0, stream, target, draft,
-                       n_target, V, inv_t, top_k, top_p, cut_key, cut_idx);
+                       n_target, V, inv_t, top_k, top_p, cut_key, cut_idx, so);
   else
     hipLaunchKernelGGL(warp_cut_kernel<false>, dim3((unsigned)n_rows), dim3(kThreads), 0, stream, target, draft,
-                       n_target, V, inv_t, top_k, top_p, cut_key, cut_idx);
+                       n_target, V, inv_t, top_k, top_p, cut_key, cut_idx, so);
   return hipGetLastError();
 }
 
