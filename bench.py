@@ -35,9 +35,12 @@ CSRC = os.path.join(HERE, "speculative_decoding_verification_09_amd", "csrc")
 # Keyed by workload and weight layout, with the SHA-256 of the kernel's sources at the time of measurement: once a
 # source changes, the record no longer describes the kernel and traffic is reported as null.
 MEASURED_TRAFFIC = {
+    ("lmhead_b8_g7", "packed"): {"kernel": "panel_kernel", "sources": ["gemm_common.h", "gemm_tiled.hip"],
+                                 "fetch_bytes": 2109515839, "write_bytes": 32833426,
+                                 "source_sha256": "aed973ab3b31ea057703ab8edf84b86f780f186c919085c68efb5df7a103190f"},
     ("lmhead_b1_g4", "packed"): {"kernel": "sweep_kernel", "sources": ["gemm_common.h", "gemm_sweep.hip"],
-                                 "fetch_bytes": 1051154653, "write_bytes": 2616848,
-                                 "source_sha256": "35f675362734d11c2eddaf9aedd8e3b18b35e6273c3fed0475eb69aedfa4d403"},
+                                 "fetch_bytes": 1051032073, "write_bytes": 2616919,
+                                 "source_sha256": "71a5ef05d4525c34539ab421a9d4ec98c8a843dc7aadc5c111ec70439d1dfb6b"},
 }
 
 
