@@ -654,14 +654,24 @@ __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restri
 // that read the same W rows then stay level with each other, and the later
 // ones find those rows in the XCD's L2 instead of fetching them from HBM again
 // (measured at N = 320: passes of 192 and 128 positions fetched 1.59x the
-// bytes of W from HBM).
-template <int NT, int R, int D, int F, bool NTL, bool OUT_BF16, int EPI, bool PX = false>
+// bytes of W from HBM).  FULL: every pass holds NT whole tiles of positions,
+// so the matrix steps run without a per-tile test.
+//
+// Measured at N = 320, d = 5120, V = 152064 (two passes of 160): about 530 us
+// per launch, against about 420 us with the W loads left out and 470 us with
+// every W load an L2 hit.  The X ring bounds the W prefetch: the wait for the
+// X rows stored at a step (loaded F steps before) is a count of outstanding
+// loads, which also waits for every W load issued before them, so a W ring
+// deeper than F bought nothing (D = 8 ran 2-3% slower, its registers spilling
+// into copies) and F is held to 4 by the register file.
+template <int NT, int R, int D, int F, bool NTL, bool OUT_BF16, int EPI, bool PX = false, bool FULL = false>
 __global__ __launch_bounds__(256) void deep_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp,
                                                    void* __restrict__ Y, int N, int d, int V, int npass, int cpk,
                                                    int ptok, FusedStats fs) {
   constexpr int NW = 4, kThreads = NW * 64;
-  constexpr int kXPT = NT / 4;  // 16-byte X units per thread per step
-  static_assert(NT % 4 == 0 && D == 4 && F == D, "deep kernel ring shapes");
+  constexpr int kXU = NT * 64;                            // 16-byte X units per step
+  constexpr int kXPT = (kXU + kThreads - 1) / kThreads;  // per thread
+  static_assert(NT % 2 == 0 && D == 4 && F == D, "deep kernel ring shapes");
   constexpr int kBufElems = NT * 512;  // bf16 per LDS buffer: NT fragments of 16 x 32
   extern __shared__ __align__(16) uint16_t xs[];
 
@@ -704,14 +714,18 @@ __global__ __launch_bounds__(256) void deep_kernel(const uint16_t* __restrict__ 
       xrow[j] = X + (size_t)n * d + 8 * (l >> 4);
     }
   }
+  // Unit j of a thread exists when tid + 256 j < kXU (a wave-uniform test).
   auto load_x = [&](u32x4(&dst)[kXPT], int s) {
     const int sc = min(s, s1 - 1) * (PX ? 512 : 32);
 #pragma unroll
-    for (int j = 0; j < kXPT; ++j) dst[j] = *(const u32x4*)(xrow[j] + sc);
+    for (int j = 0; j < kXPT; ++j)
+      if (kXU % kThreads == 0 || tid + j * kThreads < kXU) dst[j] = *(const u32x4*)(xrow[j] + sc);
   };
   auto store_x = [&](const u32x4(&src)[kXPT], int buf) {
 #pragma unroll
-    for (int j = 0; j < kXPT; ++j) *(u32x4*)(xs + buf * kBufElems + (tid + j * kThreads) * 8) = src[j];
+    for (int j = 0; j < kXPT; ++j)
+      if (kXU % kThreads == 0 || tid + j * kThreads < kXU)
+        *(u32x4*)(xs + buf * kBufElems + (tid + j * kThreads) * 8) = src[j];
   };
   const uint16_t* wrow[R];
 #pragma unroll
@@ -741,7 +755,7 @@ __global__ __launch_bounds__(256) void deep_kernel(const uint16_t* __restrict__ 
   auto mfmas = [&](const u32x4(&wa)[R], const u32x4(&b)[NT]) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
-      if (t < ntv) {
+      if (FULL || t < ntv) {
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r][t] = mfma(wa[r], b[t], acc[r][t]);
       }
@@ -913,13 +927,16 @@ hipError_t launch_deep(const PanelPlan& p, const uint16_t* X, const uint16_t* Wp
                        int64_t V, bool out_bf16, hipStream_t stream, const FusedStats* fs = nullptr) {
   constexpr size_t kLds = 4ull * NT * 1024;
   static_assert((size_t)4 * NT * 16 * 16 <= kLds, "deep statistics LDS");
-  auto pick = [&](auto ntl) {
-    constexpr bool L = decltype(ntl)::value;
-    auto k = out_bf16 ? deep_kernel<NT, R, D, D, L, true, 0, PX> : deep_kernel<NT, R, D, D, L, false, 0, PX>;
-    if (fs) k = fs->greedy ? deep_kernel<NT, R, D, D, L, false, 2, PX> : deep_kernel<NT, R, D, D, L, false, 1, PX>;
+  auto pick = [&](auto ntl, auto full) {
+    constexpr bool L = decltype(ntl)::value, FU = decltype(full)::value;
+    auto k = out_bf16 ? deep_kernel<NT, R, D, D, L, true, 0, PX, FU> : deep_kernel<NT, R, D, D, L, false, 0, PX, FU>;
+    if (fs) k = fs->greedy ? deep_kernel<NT, R, D, D, L, false, 2, PX, FU> : deep_kernel<NT, R, D, D, L, false, 1, PX, FU>;
     return k;
   };
-  auto k = p.npass == 1 ? pick(std::true_type{}) : pick(std::false_type{});
+  // Every token pass full (NT tiles of live positions): no per-tile test.
+  const bool full = p.ptok == NT * 16 && N % p.ptok == 0;
+  auto k = p.npass == 1 ? (full ? pick(std::true_type{}, std::true_type{}) : pick(std::true_type{}, std::false_type{}))
+                        : (full ? pick(std::false_type{}, std::true_type{}) : pick(std::false_type{}, std::false_type{}));
   hipError_t e = allow_lds(k, kLds);
   if (e != hipSuccess) return e;
   const FusedStats none{};
@@ -951,11 +968,15 @@ PanelShape panel_shape(int64_t N, int64_t d, int64_t V, bool with_stats) {
   // takes fewer passes (N = 129-192, 257-384, ...): each pass streams all of
   // W from L2 into the CUs, the kernel's limit, so at N = 320, V = 152064
   // two passes of 192 ran the step ~22 us (3.5%) faster than passes of 128,
-  // 128 and 64.  On the 28672-row projection at N = 512 three passes of 192
+  // 128 and 64.  Where passes of 160 are as few, the kernel takes ten token
+  // tiles instead of twelve: at N = 320 both passes then fill every tile and
+  // skip the per-tile tests (the launch 1.4% faster).  On the 28672-row projection at N = 512 three passes of 192
   // took 329 us against 257 us for four of 128: with 112 vocabulary blocks
   // the work items fill the CUs in fewer, more uneven rounds.
-  if (d % 128 == 0 && (N > 128 || (N > 64 && with_stats)))
-    return PanelShape{big_v && (N + 191) / 192 < (N + 127) / 128 ? 12 : 8, 4, 4, 1, true};
+  if (d % 128 == 0 && (N > 128 || (N > 64 && with_stats))) {
+    if (!(big_v && (N + 191) / 192 < (N + 127) / 128)) return PanelShape{8, 4, 4, 1, true};
+    return PanelShape{(N + 159) / 160 == (N + 191) / 192 ? 10 : 12, 4, 4, 1, true};
+  }
   if (N <= 64) {
     if (!big_v) return N <= 32 ? PanelShape{4, 1, 8, 4} : PanelShape{4, 2, 8, 2};
     return d <= 4096 ? PanelShape{4, 2, 8, 2} : PanelShape{4, 4, 8, 2};
@@ -968,6 +989,7 @@ hipError_t launch_panel_shape(const PanelShape& s, const PanelPlan& p, const uin
                               int64_t N, int64_t d, int64_t V, bool out_bf16, hipStream_t stream,
                               const FusedStats* fs = nullptr) {
   if (s.deep && s.NT == 12) return launch_deep<12, 4, 4, true>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);
+  if (s.deep && s.NT == 10) return launch_deep<10, 4, 4, true>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);
   if (s.deep) return launch_deep<8, 4, 4, true>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);
   if (s.NT == 4 && s.R == 1) return launch_panel<4, 1, 8, 4>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);
   if (s.NT == 4 && s.R == 2) return launch_panel<4, 2, 8, 2>(p, X, Wp, Y, N, d, V, out_bf16, stream, fs);

@@ -41,6 +41,8 @@ PACKED_SHAPES = [
     (260, 128, 65541),
     # ... over several trips of its prefetch ring, one pass and two (the second ragged)
     (200, 1024, 65600), (330, 2048, 66000),
+    # its 160-position passes: every tile full (one pass, two), and a ragged second pass
+    (160, 1024, 65536), (320, 256, 65541), (300, 128, 65600),
 ]
 
 

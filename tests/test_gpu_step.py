@@ -207,10 +207,13 @@ FUSED = [
     # 65-128 positions with d <= 4096: the plain GEMM, then the statistics kernel
     ("unfused_greedy_n100", 20, 4, 128, 3001, 0.0), ("unfused_probs_n128", 16, 7, 384, 4099, 0.8),
     ("deep_passes_greedy", 64, 4, 128, 1500, 0.0),
-    # long vocabularies: the deep kernel's 192-position passes (one pass at N = 180, a ragged second at 260)
+    # long vocabularies: the deep kernel's 192-position passes (one pass at N = 180); at N = 260 two ten-tile
+    # passes of 144 positions, the second ragged
     ("deep192_logits", 30, 5, 128, 65600, 1.0), ("deep192_greedy", 52, 4, 128, 65541, 0.0),
     # ... over many k-steps (several trips of the prefetch ring; 330 positions: a ragged second pass)
     ("deep192_long_k", 30, 5, 1024, 65600, 0.9), ("deep192_long_k_greedy", 66, 4, 2048, 65541, 0.0),
+    # ten-tile passes of 160 positions, every tile full (N = 320)
+    ("deep160_full_logits", 32, 9, 256, 65600, 1.0), ("deep160_full_greedy", 64, 4, 128, 65541, 0.0),
     # draft logits summarised by the panel grid's idle workgroups during the GEMM (long k, many draft rows)
     ("panel_idle_drafts", 4, 4, 4096, 65600, 0.9), ("panel_idle_drafts_tail", 3, 7, 4096, 65541, 1.3),
 ]
