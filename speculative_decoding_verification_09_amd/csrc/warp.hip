@@ -30,6 +30,12 @@
 //     on the next 12 key bits, and one still too full (runs of equal logits)
 //     by the last 8 bits; equal keys are then cut in index order by an
 //     ordered scan over wave-contiguous ranges.
+// For a small top-k of a long row a sampled threshold replaces the histogram:
+// one pass collects every entry above it together with the row maximum, and
+// the histogram passes run only when that catch is too small or too large.
+// The kernel also leaves the warped row's statistics for the draw (the max
+// and sum of exponentials over the kept entries, the drafted token's logit),
+// so a warped step needs no separate statistics pass.
 // The mass of v is fp32 exp((z_v - max z) * fl32(1/T)) (the difference first,
 // so its error stays near (1 + |z_v - max z| / T) * 2^-23 relative however
 // large the logits are) as an integer with 40 fraction bits: every sum is
