@@ -87,6 +87,8 @@ def main():
                     help="the CPU baseline times whole oracle sequences until this much time has passed")
     ap.add_argument("--projection-sweep", action="store_true",
                     help="time the scoring GEMM on the decoder projection shapes over N instead of the step")
+    ap.add_argument("--projection-n", type=int, nargs="+", default=None, metavar="N",
+                    help="with --projection-sweep: only these N")
     ap.add_argument("--layout", choices=["packed", "rowmajor"], default="packed", help="weight layout")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (a known byte count for hardware counters)")
@@ -110,6 +112,12 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.projection_sweep:
         projection_sweep(args)
         return
@@ -120,12 +128,6 @@ def main():
     if w.d == 0:
         toy_reject(args, w)
         return
-    if args.copy_calibration:
-        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     m = measure_step(w, args)
     cpu = None
@@ -357,8 +359,9 @@ def cpu_baseline(w, m, seconds: float):
 
 def pmc_summary(fetch_csv: str, write_csv: str):
     """Per-kernel HBM bytes per dispatch from the counter_collection.csv files of two rocprofv3 runs (one with
-    --pmc FETCH_SIZE, one with --pmc WRITE_SIZE, both of `bench.py ... --copy-calibration`).  Each counter is
-    scaled by what it reads for the plain device copy (__amd_rocclr_copyBuffer, 256 MiB read and written)."""
+    --pmc FETCH_SIZE, one with --pmc WRITE_SIZE, both of `bench.py ... --copy-calibration`), one line per kernel and
+    grid size.  Each counter is scaled by what it reads for the plain device copy (__amd_rocclr_copyBuffer, 256 MiB
+    read and written)."""
     import csv
     from collections import defaultdict
 
@@ -367,23 +370,27 @@ def pmc_summary(fetch_csv: str, write_csv: str):
         with open(path) as f:
             for row in csv.DictReader(f):
                 if row["Counter_Name"] == counter:
-                    d[row["Kernel_Name"]].append(float(row["Counter_Value"]))
+                    d[(row["Kernel_Name"], int(row["Grid_Size"]))].append(float(row["Counter_Value"]))
         return d
 
     fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
     copy_kib = 256 * 1024.0
-    cf = copy_kib / sum(fetch.get("__amd_rocclr_copyBuffer", [copy_kib]))
-    cw = copy_kib / sum(write.get("__amd_rocclr_copyBuffer", [copy_kib]))
+
+    def copy_total(d):
+        return sum(sum(v) for (k, _), v in d.items() if k == "__amd_rocclr_copyBuffer") or copy_kib
+
+    cf, cw = copy_kib / copy_total(fetch), copy_kib / copy_total(write)
     print(f"copy calibration: FETCH_SIZE x{cf:.4f}, WRITE_SIZE x{cw:.4f}")
-    print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM bytes per dispatch |")
-    print("|---|---|---|---|---|")
-    for k in sorted(fetch, key=lambda k: -sum(fetch[k])):
-        if k == "__amd_rocclr_copyBuffer" or k not in write:
+    print("| kernel | grid (threads) | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM bytes per dispatch |")
+    print("|---|---|---|---|---|---|")
+    for key in sorted(fetch, key=lambda k: -sum(fetch[k])):
+        k, grid = key
+        if k == "__amd_rocclr_copyBuffer" or key not in write:
             continue
-        f = sum(fetch[k]) / len(fetch[k])
-        wr = sum(write[k]) / len(write[k])
+        f = sum(fetch[key]) / len(fetch[key])
+        wr = sum(write[key]) / len(write[key])
         name = k.replace("(anonymous namespace)::", "").replace("specdec::", "").replace("void ", "").split("(")[0]
-        print(f"| {name} | {len(fetch[k])} | {f:.1f} | {wr:.1f} | {(f * cf + wr * cw) * 1024:.4e} |")
+        print(f"| {name} | {grid} | {len(fetch[key])} | {f:.1f} | {wr:.1f} | {(f * cf + wr * cw) * 1024:.4e} |")
         print(f"    fetch_bytes={int(f * cf * 1024)} write_bytes={int(wr * cw * 1024)}")
 
 
@@ -669,6 +676,7 @@ def projection_sweep(args):
     dev = torch.device("cuda")
     stream = torch.cuda.current_stream()
     points = []
+    Ns = args.projection_n or cfg["N"]
     Nmax = max(cfg["N"])
     for d_in, d_out in cfg["shapes"]:
         seed = cfg["seed"] + d_in
@@ -688,10 +696,14 @@ def projection_sweep(args):
             sd.specdec_verify_logits(Xw, W, Yw, sd.SPECDEC_OUT_BF16, workspace=wsw, stream=stream)
         torch.cuda.synchronize()
         del Xw, Yw, wsw
-        for N in cfg["N"]:
+        for N in Ns:
             X = Xall[:N].contiguous()
             Y = torch.empty((N, d_out), dtype=torch.bfloat16, device=dev)
             need = sd.logits_workspace_bytes(N, d_in, d_out, sd.SPECDEC_WEIGHTS_PACKED)
+            kernel = sd.scoring_kernel_name(N, d_in, d_out, sd.SPECDEC_WEIGHTS_PACKED)
+            # The deep kernel's workspace starts with the packed copy of X (16-row tiles, 256-byte aligned); the
+            # rest, if any, holds the fp32 partials of the k-groups.
+            xpack = ((N + 15) // 16 * 16 * d_in * 2 + 255) // 256 * 256 if kernel == "deep_kernel" else 0
             ws = torch.empty(max(1, need), dtype=torch.uint8, device=dev)
             for _ in range(args.warmup):
                 sd.specdec_verify_logits(X, W, Y, sd.SPECDEC_OUT_BF16, workspace=ws, stream=stream)
@@ -710,14 +722,16 @@ def projection_sweep(args):
             tflops = flops / (ms * 1e-3) / 1e12
             points.append({"d_in": d_in, "d_out": d_out, "N": N, "us": ms * 1e3, "gbps": gbps,
                            "hbm_frac": gbps / HBM_PEAK_GBPS, "tflops": tflops,
-                           "mfma_util": tflops / MFMA_BF16_PEAK_TFLOPS, "k_groups": need // max(1, N * d_out * 4)})
+                           "mfma_util": tflops / MFMA_BF16_PEAK_TFLOPS, "kernel": kernel,
+                           "k_groups": (need - xpack) // max(1, N * d_out * 4)})
         del W, Xall
-    low = min(p["hbm_frac"] for p in points if p["N"] <= 64)
+    # The value: the lowest fraction of HBM peak over N <= 64 (over the points run, if --projection-n left none).
+    low = min((p["hbm_frac"] for p in points if p["N"] <= 64), default=min(p["hbm_frac"] for p in points))
     out = {
         "metric": "projection GEMM sweep: lowest fraction of HBM peak over N <= 64 (per-N GB/s and MFMA use listed)",
         "value": low, "unit": "fraction of 8 TB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "higher_is_better": True, "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "projection_sweep", "shapes": cfg["shapes"], "N": cfg["N"], "weight_layout": "packed",
+        "config": {"workload": "projection_sweep", "shapes": cfg["shapes"], "N": list(Ns), "weight_layout": "packed",
                    "out_dtype": "bf16"},
         "points": points,
     }
