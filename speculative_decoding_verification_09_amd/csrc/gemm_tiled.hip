@@ -714,18 +714,20 @@ __global__ __launch_bounds__(256) void deep_kernel(const uint16_t* __restrict__ 
       xrow[j] = X + (size_t)n * d + 8 * (l >> 4);
     }
   }
-  // Unit j of a thread exists when tid + 256 j < kXU (a wave-uniform test).
+  // Unit j of a thread exists when tid + 256 j < kXU, that is (kXU being a
+  // multiple of 64) when 64 wv + 256 j < kXU: a test on the wave index, which
+  // compiles to a scalar branch.
+  auto has_unit = [&](int j) { return kXU % kThreads == 0 || wv * 64 + j * kThreads < kXU; };
   auto load_x = [&](u32x4(&dst)[kXPT], int s) {
     const int sc = min(s, s1 - 1) * (PX ? 512 : 32);
 #pragma unroll
     for (int j = 0; j < kXPT; ++j)
-      if (kXU % kThreads == 0 || tid + j * kThreads < kXU) dst[j] = *(const u32x4*)(xrow[j] + sc);
+      if (has_unit(j)) dst[j] = *(const u32x4*)(xrow[j] + sc);
   };
   auto store_x = [&](const u32x4(&src)[kXPT], int buf) {
 #pragma unroll
     for (int j = 0; j < kXPT; ++j)
-      if (kXU % kThreads == 0 || tid + j * kThreads < kXU)
-        *(u32x4*)(xs + buf * kBufElems + (tid + j * kThreads) * 8) = src[j];
+      if (has_unit(j)) *(u32x4*)(xs + buf * kBufElems + (tid + j * kThreads) * 8) = src[j];
   };
   const uint16_t* wrow[R];
 #pragma unroll
