@@ -397,63 +397,38 @@ __device__ Cut select_cut(const float* __restrict__ row, int V, int R, u64 need,
   return Cut{(uint32_t)(c >> kIdxBits), (int32_t)(kIdxMask - (uint32_t)(c & kIdxMask))};
 }
 
-// Sorts sh.comp[0, S) into descending order with wave 0 alone (n <= S real
-// entries, the rest zeros; S = 256 or 512): a bitonic network over S values
-// held S/64 to a lane (value e in lane e % 64, register e / 64), partners in
-// other lanes reached by shuffles, in the same lane by register swaps.  No
-// barrier inside: measured against the workgroup-wide network, whose barrier
-// per stage cost about 15 us per batch of warped rows at a few hundred
-// candidates.
-template <int S>
-__device__ void sort_desc_wave(int n, Shared& sh) {
-  constexpr int J = S / 64;
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    u64 x[J];
-#pragma unroll
-    for (int j = 0; j < J; ++j) x[j] = lane + 64 * j < n ? sh.comp[lane + 64 * j] : 0ull;
-#pragma unroll
-    for (int size = 2; size <= S; size <<= 1) {
-#pragma unroll
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-          const int e = lane + 64 * j;
-          const bool desc = (e & size) == 0;  // the final merge (size == S) is descending
-          if (stride >= 64) {
-            const int jp = j ^ (stride >> 6);
-            if (jp > j) {  // each pair once, from its lower register
-              const u64 a = x[j], b = x[jp];
-              const bool swap = (a < b) == desc;
-              x[j] = swap ? b : a;
-              x[jp] = swap ? a : b;
-            }
-          } else {
-            const u64 o = (u64)__shfl_xor((long long)x[j], stride);
-            const bool lower = (e & stride) == 0;  // e below its partner
-            // the lower one keeps the larger value when the merge is descending
-            const bool take_max = lower == desc;
-            x[j] = take_max ? (o > x[j] ? o : x[j]) : (o < x[j] ? o : x[j]);
-          }
-        }
-      }
+// Sorts sh.comp[0, n) into descending order by rank (n <= 2 * kThreads): the
+// rank of a candidate is the number of candidates above it (composites are
+// distinct), counted by each thread for its two over the whole list (reads
+// that every lane of a wave makes at once), then each is written to its rank.
+// No stage or barrier per step of a network; waves past n skip the count.
+__device__ void sort_desc_rank(int n, Shared& sh) {
+  const int t = threadIdx.x;
+  const u64 a = t < n ? sh.comp[t] : 0ull;
+  const u64 b = t + kThreads < n ? sh.comp[t + kThreads] : 0ull;
+  int ra = 0, rb = 0;
+  if (__builtin_amdgcn_readfirstlane(t >> 6) * 64 < n) {  // the wave holds a candidate
+    for (int j = 0; j < n; ++j) {
+      const u64 c = sh.comp[j];
+      ra += c > a;
+      rb += c > b;
     }
-#pragma unroll
-    for (int j = 0; j < J; ++j) sh.comp[lane + 64 * j] = x[j];
   }
+  __syncthreads();  // every count is done before the list is overwritten
+  if (t < n) sh.comp[ra] = a;
+  if (t + kThreads < n) sh.comp[rb] = b;
   __syncthreads();
 }
 
-// Sorts sh.comp[0, n) into descending order (n <= kCap): a bitonic network
-// over the next power of two, the padding zeros (below every composite of a
-// real entry but a possible 0, which then sorts among them) last.
+// Sorts sh.comp[0, n) into descending order (n <= kCap): by rank up to 512
+// candidates (measured: the b8 warped step 3 us faster than a one-wave
+// bitonic network, whose stages wait on shuffles in turn), else a bitonic
+// network over the next power of two, the padding zeros (below every
+// composite of a real entry but a possible 0, which then sorts among them)
+// last.
 __device__ void sort_desc(int n, Shared& sh) {
-  if (n <= 256) {
-    sort_desc_wave<256>(n, sh);
-    return;
-  }
   if (n <= 512) {
-    sort_desc_wave<512>(n, sh);
+    sort_desc_rank(n, sh);
     return;
   }
   int P = 1;
@@ -487,6 +462,47 @@ __device__ int cuts_from_candidates(int n, int64_t top_k, bool tp, float top_p, 
   const u64 ck = sh.comp[kk - 1];
   cut = Cut{(uint32_t)(ck >> kIdxBits), (int32_t)(kIdxMask - (uint32_t)(ck & kIdxMask))};
   if (!tp) return kk;
+  if (kk <= 128) {  // one wave, no workgroup scans: lane l holds ranks 2l and 2l + 1
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      u64 m[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int i = 2 * lane + e;
+        m[e] = i < kk ? mass_fixed(key_value((uint32_t)(sh.comp[i] >> kIdxBits)), inv_t, zmax) : 0ull;
+      }
+      u64 incl = m[0] + m[1];
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const u64 y = (u64)__shfl_up((long long)incl, o);
+        if (lane >= o) incl += y;
+      }
+      const u64 total = (u64)__shfl((long long)incl, 63);
+      const double t = ceil((double)top_p * (double)total);
+      u64 need = t < 1.0 ? 1ull : (u64)t;
+      if (need > total) need = total;
+      int f = -1;
+      if (need > 0) {
+        u64 run = incl - (m[0] + m[1]);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          if (m[e] > 0 && run < need && run + m[e] >= need) f = 2 * lane + e;
+          run += m[e];
+        }
+      }
+      const uint64_t hit = __ballot(f >= 0);
+      const int fw = hit ? __shfl(f, __builtin_ctzll(hit)) : -1;
+      if (lane == 0) sh.found = fw;
+    }
+    __syncthreads();
+    const int f = sh.found;
+    if (f >= 0) {
+      const u64 cp = sh.comp[f];
+      cut = Cut{(uint32_t)(cp >> kIdxBits), (int32_t)(kIdxMask - (uint32_t)(cp & kIdxMask))};
+    }
+    __syncthreads();
+    return f >= 0 ? f + 1 : kk;
+  }
   // Thread t holds ranks 2t and 2t + 1.
   u64 m[2];
 #pragma unroll
