@@ -591,12 +591,15 @@ __global__ __launch_bounds__(kThreads) void warp_cut_kernel(const float* __restr
   const bool collect = tk && top_k <= kCap / 4 && V >= 16 * kThreads;
   if (collect) {
     clear_bins(sh, false);
-    // Sample entries 4*(q*(4t + u)) + e of thread t (u, e < 4; q >= 1): 16384 in all.
+    // Sample entries 16*q*t + 4u + e of thread t (u, e < 4; q >= 1): 16384 in
+    // all, sixteen consecutive ones (one 64-byte line) at each of 1024 evenly
+    // spaced places, so the sample touches a quarter of the lines that
+    // sixteen scattered entries per thread would.
     const int q = V / (16 * kThreads);
     uint32_t ks[16];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int v0 = 4 * q * (4 * (int)threadIdx.x + u);  // v0 + 3 < V
+      const int v0 = 16 * q * (int)threadIdx.x + 4 * u;  // v0 + 3 < 16 q kThreads <= V
       if (VEC) {
         const float4 t = *(const float4*)(row + v0);
         ks[4 * u + 0] = order_key(t.x);
