@@ -877,18 +877,19 @@ struct PanelPlan {
 };
 
 // Splits the k range into groups only when the (vocabulary block, token pass)
-// work items would leave more than 15% of the CUs idle: the fewest groups
-// (each at least 4 chunks) that reach 85% of the CUs in one round.  Measured
-// on the projection shapes, a CU streams well over its share of the HBM
-// bandwidth, so a partly idle round still saturates HBM, while every extra
-// group writes and reads back fp32 partials N x V and adds a reduction.
+// work items would leave more than 15% of the CUs idle: then into as many
+// groups (each at least 4 chunks) as fill the CUs in one round.  A streaming
+// CU reads about 27 GB/s, so an idle CU is bandwidth lost (28672 -> 8192 at
+// N = 64: 7 groups on 224 CUs took 81.3 us, 8 groups on 256 took 79.8 us),
+// while a second round of items, or every extra group's fp32 partials N x V
+// written and read back, costs more than it gains.
 PanelPlan plan_panel(int64_t N, int64_t d, int64_t V, int NT, int R, int NW, int KS, int cus) {
   PanelPlan p{};
   const int64_t ntiles = (V + 15) / 16, nvb = (ntiles + NW * R - 1) / (NW * R);
   const int64_t nch = (d / 32 + KS - 1) / KS;
   p.npass = (N + NT * 16 - 1) / (NT * 16);
   const int64_t items = nvb * p.npass, want = (cus * 85 + 99) / 100;
-  int64_t gq = items >= want ? 1 : (want + items - 1) / items;
+  int64_t gq = items >= want ? 1 : (cus / items > 1 ? cus / items : 1);
   const int64_t gmax = nch / 4 > 1 ? nch / 4 : 1;
   if (gq > gmax) gq = gmax;
   p.cpk = (nch + gq - 1) / gq;
