@@ -578,8 +578,8 @@ __global__ __launch_bounds__(kThreads) void warp_cut_kernel(const float* __restr
   bool done_p = false;
   int nk = -1;  // when the kept entries are ranks [0, nk) of the sorted candidates in LDS
   float zmax;
-  // A small top-k of a long row, in one pass: a strided sample of 16 entries
-  // per thread, histogrammed by key (12 bits, then the next 12 within the
+  // A small top-k of a long row, in one pass: a sample of 16 entries per
+  // thread spread over the row, histogrammed by key (12 bits, then the next 12 within the
   // bucket), gives a threshold t0 at the sample entry whose count from the top
   // stands for about 3*top_k row entries; the pass then takes the row maximum and
   // collects every entry at or above t0 into LDS.  At least top_k of them,
