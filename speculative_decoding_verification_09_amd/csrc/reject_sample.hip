@@ -48,6 +48,8 @@ constexpr int kGreedyWaves = 8;    // waves of the greedy rule's workgroup (one 
 constexpr int kWavesPerBlock = 4;
 constexpr float kQFloor = 1e-12f;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLog2eLo = 1.925963e-08f;  // log2(e) minus its float value
+constexpr float kLn2 = 0.6931472f;
 constexpr int64_t kMaxFusedParts = kFusedStatsMaxParts;
 constexpr int64_t kMaxFusedRows = kFusedStatsMaxRows;
 
@@ -322,13 +324,27 @@ struct DrawRow {
   int32_t pi, qi;
 };
 
+// e^x for x <= 0, for the weights of the draw. x log2(e) is carried as its
+// rounded product h plus a correction l (that product's rounding error and the
+// tail of log2(e)), and 2^(h + l) = 2^h (1 + l ln 2) up to a relative 2^-34,
+// as |l| < 2^-16 for |x| <= 128. The hardware base-2 exponential gives 2^h.
+// x is clamped at -128, where e^x lies below the smallest subnormal, so a -inf
+// logit weighs exactly 0.
+__device__ __forceinline__ float exp_nonpos(float x) {
+  x = fmaxf(x, -128.0f);
+  const float h = x * kLog2e;
+  const float l = fmaf(x, kLog2eLo, fmaf(x, kLog2e, -h));
+  const float e = __builtin_amdgcn_exp2f(h);
+  return fmaf(e, l * kLn2, e);
+}
+
 // WARP: p_v (and q_v of draft logits) is 0 where the row's warp cut drops v.
 template <bool WARP>
 __device__ __forceinline__ void weights(const DrawRow& R, int64_t v, float zp, float zq, float& p, float& r) {
-  p = expf(zp * R.inv_t - R.mp) * R.ip;
+  p = exp_nonpos(zp * R.inv_t - R.mp) * R.ip;
   if (WARP && !warp_kept(order_key(zp), v, R.pk, R.pi)) p = 0.0f;
   if (R.has_q) {
-    float q = R.kind == 2 ? (v == R.xk ? 1.0f : 0.0f) : (R.kind == 1 ? zq : expf(zq * R.inv_t - R.mq) * R.iq);
+    float q = R.kind == 2 ? (v == R.xk ? 1.0f : 0.0f) : (R.kind == 1 ? zq : exp_nonpos(zq * R.inv_t - R.mq) * R.iq);
     if (WARP && R.kind == 0 && !warp_kept(order_key(zq), v, R.qk, R.qi)) q = 0.0f;
     const float dlt = p - q;
     r = dlt > 0.0f ? dlt : 0.0f;
