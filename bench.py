@@ -79,7 +79,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps before each timed region (300: about 0.1 s of the eight-sequence step, "
+                    "enough for the clocks to settle after the setup; after 10 the step measured ~2%% slower)")
     ap.add_argument("--workload", default="lmhead_b8_g7")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-b1", action="store_true", help="do not also time the one-sequence step (lmhead_b1_g4)")
