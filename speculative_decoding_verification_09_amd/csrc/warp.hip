@@ -201,6 +201,59 @@ __device__ __forceinline__ void for_row(const float* __restrict__ row, int V, in
   }
 }
 
+// The collecting pass: the running max zm of the row's entries, and A(z, v)
+// for every entry with z >= zt, over the same ranges as for_row with eight
+// 16-byte loads in flight per lane.  Steps that lie wholly inside the wave's
+// range load without tests.
+template <bool VEC, class A>
+__device__ __forceinline__ void collect_row(const float* __restrict__ row, int V, int R, float zt, float& zm, A&& append) {
+  constexpr int U = 8;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int b0 = w * R, b1 = min(b0 + R, V);
+  for (int base = b0; base < b1; base += U * 256) {
+    float z[U][4];
+    const bool whole = VEC && base + U * 256 <= b1;  // wave-uniform
+    if (whole) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float4 t = *(const float4*)(row + base + 256 * u + 4 * lane);
+        z[u][0] = t.x;
+        z[u][1] = t.y;
+        z[u][2] = t.z;
+        z[u][3] = t.w;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float g = fmaxf(fmaxf(z[u][0], z[u][1]), fmaxf(z[u][2], z[u][3]));
+        zm = fmaxf(zm, g);
+        if (g >= zt) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (z[u][e] >= zt) append(z[u][e], base + 256 * u + 4 * lane + e);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = base + 256 * u + 4 * lane + e;
+          z[u][e] = v < b1 ? row[v] : -INFINITY;
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = base + 256 * u + 4 * lane + e;
+          if (v < b1) {
+            zm = fmaxf(zm, z[u][e]);
+            if (z[u][e] >= zt) append(z[u][e], v);
+          }
+        }
+    }
+  }
+}
+
 // The cut among the n candidates in LDS: the candidate (those with composite >=
 // floor only) at which the running weight in composite order first reaches
 // need.  Returns its composite, or 0 if the weights never reach need.
@@ -631,16 +684,18 @@ __global__ __launch_bounds__(kThreads) void warp_cut_kernel(const float* __restr
     const uint32_t t0 = (b0 << 20) | (b1 << 8);
     if (threadIdx.x == 0) sh.ncand = 0;
     __syncthreads();
+    // order_key(z) >= t0 holds exactly for the non-NaN z >= zt (the keys
+    // below that of -inf, and those above that of +inf, are no float's), so
+    // the pass tests values: per four entries their largest against zt, and
+    // the four one by one only when it passes (for about 3*top_k of the row's
+    // entries), which keeps the pass at a few vector instructions per entry.
+    const float zt = t0 <= 0x007fffffu ? -INFINITY : (t0 > 0xff800000u ? __uint_as_float(0x7fc00000u) : key_value(t0));
     float zm = -INFINITY;
-    auto take = [&](int v, float z) {
-      zm = fmaxf(zm, z);
-      const uint32_t k = order_key(z);
-      if (k >= t0) {
-        const uint32_t s = atomicAdd(&sh.ncand, 1u);
-        if (s < (uint32_t)kCap) sh.comp[s] = composite(k, v);
-      }
+    auto append = [&](float z, int v) {
+      const uint32_t s = atomicAdd(&sh.ncand, 1u);
+      if (s < (uint32_t)kCap) sh.comp[s] = composite(order_key(z), v);
     };
-    for_row<VEC, decltype(take)&, 8>(row, V, R, take);  // eight 16-byte loads in flight per lane
+    collect_row<VEC>(row, V, R, zt, zm, append);  // eight 16-byte loads in flight per lane
     zmax = block_max(zm, sh.redf);  // its barriers order the appends
     const uint32_t napp = sh.ncand;
     __syncthreads();
