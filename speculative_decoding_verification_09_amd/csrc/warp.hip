@@ -601,6 +601,90 @@ __device__ __forceinline__ double block_sum_f64(double v, u64* lds) {
   return r;
 }
 
+// A key t0 with at least `need` of the sample's keys at or above it, close
+// above the need-th largest, from two small histograms near the top of the
+// sample: counts of the 16 12-bit buckets at and below the bucket of the
+// largest key (LDS atomics only from the few samples that fall there), then of
+// the 256 next-8-bit sub-buckets of the bucket where the count from the top
+// reaches `need`; each is scanned by one wave.  Returns 0 (no threshold) when
+// those 16 buckets hold fewer than `need` samples.  Uses sh.cnt[0, 272).
+__device__ uint32_t sample_threshold_near_top(const uint32_t (&ks)[16], uint32_t need, Shared& sh) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint32_t km = ks[0];
+#pragma unroll
+  for (int e = 1; e < 16; ++e) km = max(km, ks[e]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) km = max(km, (uint32_t)__shfl_xor((int)km, o));
+  if (threadIdx.x < 16 + 256) sh.cnt[threadIdx.x] = 0u;
+  if (lane == 0) sh.redf[wv] = __uint_as_float(km);
+  __syncthreads();
+  uint32_t kmax = 0u;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) kmax = max(kmax, __float_as_uint(sh.redf[w]));
+  const uint32_t kb = kmax >> 20;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const uint32_t d = kb - (ks[e] >> 20);  // bucket distance below the top one
+    if (d < 16u) atomicAdd(&sh.cnt[d], 1u);
+  }
+  __syncthreads();
+  if (wv == 0) {  // buckets kb, kb - 1, ... in lanes 0..15: where the count from the top reaches need
+    const uint32_t c = lane < 16 ? sh.cnt[lane] : 0u;
+    uint32_t incl = c;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const uint32_t y = (uint32_t)__shfl_up((int)incl, o);
+      if (lane >= o) incl += y;
+    }
+    const uint64_t hit = __ballot(lane < 16 && incl >= need);
+    if (lane == 0) sh.bin = hit ? kb - (uint32_t)__builtin_ctzll(hit) : 0xffffffffu;
+    const int l = hit ? __builtin_ctzll(hit) : 0;
+    const uint32_t above = (uint32_t)__shfl((int)(incl - c), l);
+    if (lane == 0) sh.above = above;
+  }
+  __syncthreads();
+  const uint32_t b = sh.bin;
+  const uint32_t need2 = need - (uint32_t)sh.above;
+  if (b == 0xffffffffu) {
+    __syncthreads();  // every thread has read sh.bin before it is written again
+    return 0u;
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if ((ks[e] >> 20) == b) atomicAdd(&sh.cnt[16 + ((ks[e] >> 12) & 0xffu)], 1u);
+  __syncthreads();
+  if (wv == 0) {  // sub-buckets 255 .. 0, four per lane from the top
+    uint32_t h[4], local = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      h[j] = sh.cnt[16 + 255 - 4 * lane - j];
+      local += h[j];
+    }
+    uint32_t incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = (uint32_t)__shfl_up((int)incl, o);
+      if (lane >= o) incl += y;
+    }
+    const uint64_t hit = __ballot(incl >= need2);  // the total of bucket b is at least need2
+    const int l = hit ? __builtin_ctzll(hit) : 63;
+    if (lane == l) {
+      uint32_t run = incl - local;
+      int sel = 3;
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {  // static indices: h stays in registers
+        if (sel == 3 && run + h[j] >= need2) sel = j;
+        if (sel == 3) run += h[j];
+      }
+      sh.bin = (b << 20) | ((uint32_t)(255 - 4 * lane - sel) << 12);
+    }
+  }
+  __syncthreads();
+  const uint32_t t0 = sh.bin;
+  __syncthreads();
+  return t0 == 0u ? 1u : t0;  // 0 is kept for "no threshold"; key 0 is no float's
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void warp_cut_kernel(const float* __restrict__ target,
                                                             const float* __restrict__ draft, int64_t n_target,
@@ -643,7 +727,6 @@ __global__ __launch_bounds__(kThreads) void warp_cut_kernel(const float* __restr
   // buckets: the one-pass path measured much faster.)
   const bool collect = tk && top_k <= kCap / 4 && V >= 16 * kThreads;
   if (collect) {
-    clear_bins(sh, false);
     // Sample entries 16*q*t + 4u + e of thread t (u, e < 4; q >= 1): 16384 in
     // all, sixteen consecutive ones (one 64-byte line) at each of 1024 evenly
     // spaced places, so the sample touches a quarter of the lines that
@@ -664,24 +747,28 @@ __global__ __launch_bounds__(kThreads) void warp_cut_kernel(const float* __restr
         for (int e = 0; e < 4; ++e) ks[4 * u + e] = order_key(row[v0 + e]);
       }
     }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) atomicAdd(&sh.cnt[ks[e] >> 20], 1u);
-    __syncthreads();
     // The s0-th largest sample stands for about 3*top_k row entries (mean);
     // fewer than top_k row entries at or above it would need s0 of the row's
     // top top_k - 1 in the sample, far out in the tail.
     const u64 s0 = (u64)((3 * top_k * 16 * kThreads + V - 1) / V);  // >= 1
-    uint32_t b0, b1;
-    u64 above0, above1;
-    scan_bins<false>(kBins, s0, sh, b0, above0);
-    // ... refined by the sample's next 12 key bits within that bucket
-    clear_bins(sh, false);
+    uint32_t t0 = sample_threshold_near_top(ks, (uint32_t)s0, sh);
+    if (t0 == 0u) {  // the top 16 buckets hold fewer than s0 samples: full 12-bit histograms
+      clear_bins(sh, false);
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      if ((ks[e] >> 20) == b0) atomicAdd(&sh.cnt[(ks[e] >> 8) & 0xfffu], 1u);
-    __syncthreads();
-    scan_bins<false>(kBins, s0 - above0, sh, b1, above1);
-    const uint32_t t0 = (b0 << 20) | (b1 << 8);
+      for (int e = 0; e < 16; ++e) atomicAdd(&sh.cnt[ks[e] >> 20], 1u);
+      __syncthreads();
+      uint32_t b0, b1;
+      u64 above0, above1;
+      scan_bins<false>(kBins, s0, sh, b0, above0);
+      // ... refined by the sample's next 12 key bits within that bucket
+      clear_bins(sh, false);
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if ((ks[e] >> 20) == b0) atomicAdd(&sh.cnt[(ks[e] >> 8) & 0xfffu], 1u);
+      __syncthreads();
+      scan_bins<false>(kBins, s0 - above0, sh, b1, above1);
+      t0 = (b0 << 20) | (b1 << 8);
+    }
     if (threadIdx.x == 0) sh.ncand = 0;
     __syncthreads();
     // order_key(z) >= t0 holds exactly for the non-NaN z >= zt (the keys
