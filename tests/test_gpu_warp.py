@@ -44,12 +44,20 @@ def _sample_warped(orc, z, us, T, top_k, top_p):
 
 def _inputs(orc, B, g, V, std, T, top_k, top_p, kind, ties, seed):
     """Target logits ~ N(0, std), or integers in [0, 4) (ties="ties": long runs of equal logits), or uniform in
-    [1, 1.125) (ties="narrow": one octave-eighth, so distinct values crowd one 12-bit key bucket); draft = target
+    [1, 1.125) (ties="narrow": one octave-eighth, so distinct values crowd one 12-bit key bucket), or N(0, std)
+    with 16 entries per row near 60 (ties="spikes": the two octaves below the largest value hold too few of the
+    row's sampled entries for the top-k threshold, so the full sample histograms run); draft = target
     + N(0, 1), or a fresh row of the same kind; drafted tokens drawn from the draft's warped distribution (logits),
     its unwarped one (probabilities) or uniformly over the vocabulary (one-hot)."""
     if ties in (True, "ties"):
         zt = synth.integers((B, g + 1, V), 0, 4, seed, synth.STREAM_TARGET).astype(np.float32)
         zd = synth.integers((B, g, V), 0, 4, seed, synth.STREAM_DRAFT_NOISE).astype(np.float32)
+    elif ties == "spikes":
+        zt = synth.normal_f32((B, g + 1, V), std, seed, synth.STREAM_TARGET)
+        pos = synth.integers((B, g + 1, 16), 0, V, seed + 1, synth.STREAM_REPLACE)
+        amp = np.float32(60.0) + synth.normal_f32((B, g + 1, 16), 1.0, seed + 1, synth.STREAM_TARGET)
+        np.put_along_axis(zt, pos, amp, axis=2)
+        zd = zt[:, :g] + synth.normal_f32((B, g, V), 1.0, seed, synth.STREAM_DRAFT_NOISE)
     elif ties == "narrow":
         zt = 1.0 + np.float32(0.125) * synth.uniforms((B, g + 1, V), seed, synth.STREAM_TARGET)
         zd = 1.0 + np.float32(0.125) * synth.uniforms((B, g, V), seed, synth.STREAM_DRAFT_NOISE)
@@ -108,6 +116,7 @@ CASES = [
     (24, 3, 32000, 0.0, 1.0, 100, 1.0, 2, "ties", 0.02),   # runs of equal keys past capacity: index-order scan
     (24, 3, 32000, 0.0, 1.0, 0, 0.5, 2, "ties", 0.05),     # the same for top-p
     (24, 3, 32000, 0.0, 1.0, 3000, 0.9, 0, "ties", 0.05),  # both, over capacity
+    (24, 3, 32000, 2.0, 1.0, 50, 0.9, 0, "spikes", 0.02),  # a few far larger logits: the sample's full histograms
 ]
 
 
