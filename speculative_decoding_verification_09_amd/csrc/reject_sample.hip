@@ -66,6 +66,8 @@ struct DrawDesc {
   float mq, iq;    // draft row (draft logits only)
   float u;         // the uniform that drives the draw
   int32_t xk;      // drafted token of row k (one-hot drafts), -1 on the bonus row
+  float pz, qz;    // warp cuts of the target and draft rows k as values (see value_cut)
+  int32_t pi, qi;
   float pad;
 };
 
@@ -320,7 +322,7 @@ struct DrawRow {
   int kind;         // draft kind: 0 logits, 1 probabilities, 2 one-hot
   bool has_q;       // the step ends on a drafted row (a residual), not on the bonus row
   int xk;           // the drafted token of that row (one-hot drafts)
-  uint32_t pk, qk;  // warp cuts of the two rows (WARP only)
+  float pz, qz;     // warp cuts of the two rows as values (WARP only), see value_cut
   int32_t pi, qi;
 };
 
@@ -338,14 +340,35 @@ __device__ __forceinline__ float exp_nonpos(float x) {
   return fmaf(e, l * kLn2, e);
 }
 
+// A warp cut (key ck, index ci: entry v with key k kept iff k > ck, or k == ck
+// and v <= ci) as a test on values: a non-NaN z is kept iff z > cz, or
+// z == cz and v <= the returned index.  Keys order values (-0 and +0 share
+// one key and compare equal), so at the key of a float this is the key test;
+// keys below that of -inf keep every entry, keys above that of +inf none (a
+// NaN cz compares false), and the one key no float has (that -0 would have
+// without sharing) keeps exactly the z >= -0.
+struct ValueCut {
+  float z;
+  int32_t idx;
+};
+__device__ __forceinline__ ValueCut value_cut(uint32_t ck, int32_t ci) {
+  if (ck < 0x007fffffu) return {-INFINITY, 0x7fffffff};
+  if (ck > 0xff800000u) return {__uint_as_float(0x7fc00000u), -1};
+  if (ck == 0x7fffffffu) return {__uint_as_float(0x80000001u), -1};
+  return {__uint_as_float((ck & 0x80000000u) ? (ck & 0x7fffffffu) : ~ck), ci};
+}
+__device__ __forceinline__ bool value_kept(float z, int64_t v, float cz, int32_t ci) {
+  return z > cz || (z == cz && v <= (int64_t)ci);
+}
+
 // WARP: p_v (and q_v of draft logits) is 0 where the row's warp cut drops v.
 template <bool WARP>
 __device__ __forceinline__ void weights(const DrawRow& R, int64_t v, float zp, float zq, float& p, float& r) {
   p = exp_nonpos(zp * R.inv_t - R.mp) * R.ip;
-  if (WARP && !warp_kept(order_key(zp), v, R.pk, R.pi)) p = 0.0f;
+  if (WARP && !value_kept(zp, v, R.pz, R.pi)) p = 0.0f;
   if (R.has_q) {
     float q = R.kind == 2 ? (v == R.xk ? 1.0f : 0.0f) : (R.kind == 1 ? zq : exp_nonpos(zq * R.inv_t - R.mq) * R.iq);
-    if (WARP && R.kind == 0 && !warp_kept(order_key(zq), v, R.qk, R.qi)) q = 0.0f;
+    if (WARP && R.kind == 0 && !value_kept(zq, v, R.qz, R.qi)) q = 0.0f;
     const float dlt = p - q;
     r = dlt > 0.0f ? dlt : 0.0f;
   } else {
@@ -368,18 +391,10 @@ __device__ __forceinline__ DrawRow make_row(const float* __restrict__ target, co
   R.inv_t = inv_t;
   R.kind = draft_kind;
   R.xk = D.xk;
-  R.pk = R.qk = 0u;
-  R.pi = R.qi = 0x7fffffff;
-  if (WARP) {
-    const int64_t rt = b * (gamma + 1) + D.k;
-    R.pk = ws.wkey[rt];
-    R.pi = ws.widx[rt];
-    if (R.zq && draft_kind == 0) {
-      const int64_t rd = B * (gamma + 1) + b * gamma + D.k;
-      R.qk = ws.wkey[rd];
-      R.qi = ws.widx[rd];
-    }
-  }
+  R.pz = WARP ? D.pz : -INFINITY;
+  R.pi = WARP ? D.pi : 0x7fffffff;
+  R.qz = WARP ? D.qz : -INFINITY;
+  R.qi = WARP ? D.qi : 0x7fffffff;
   return R;
 }
 
@@ -551,6 +566,18 @@ __global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
   const float u_smp = has_row ? uniforms[(b * g1 + lane) * 2 + 1] : 0.0f;
   const int xi = drafted ? clamp_token(tokens[b * gamma + lane], V) : 0;
   const float q_given = drafted && q_probs ? draft[(size_t)(b * gamma + lane) * V + xi] : (q_onehot ? 1.0f : 0.0f);
+  // The warp cuts of the rows (lane i <-> target row i and draft row i), loaded now so that no load waits once
+  // the row where the step ends is known.
+  uint32_t ck_t = 0u, ck_d = 0u;
+  int32_t ci_t = 0x7fffffff, ci_d = 0x7fffffff;
+  if (WARP && has_row) {
+    ck_t = ws.wkey[b * g1 + lane];
+    ci_t = ws.widx[b * g1 + lane];
+  }
+  if (WARP && drafted && draft_kind == 0) {
+    ck_d = ws.wkey[B * g1 + b * gamma + lane];
+    ci_d = ws.widx[B * g1 + b * gamma + lane];
+  }
   // Rows of the sequence: j < g1 target row j, then draft row j - g1 (draft logits).
   const int nrows = (int)(draft_kind != 0 ? g1 : g1 + gamma);
   for (int j = wv; j < nrows; j += WB) {
@@ -591,6 +618,18 @@ __global__ __launch_bounds__(WB * 64) void draw_sum_kernel(
   D.iq = (float)(1.0 / __shfl(rzq, kq));
   D.u = __shfl(u_smp, k);
   D.xk = k < gamma ? __shfl(xi, k) : -1;
+  D.pz = D.qz = -INFINITY;
+  D.pi = D.qi = 0x7fffffff;
+  if (WARP) {
+    const ValueCut cp = value_cut((uint32_t)__shfl((int)ck_t, k), __shfl(ci_t, k));
+    D.pz = cp.z;
+    D.pi = cp.idx;
+    if (k < gamma && draft_kind == 0) {
+      const ValueCut cq = value_cut((uint32_t)__shfl((int)ck_d, k), __shfl(ci_d, k));
+      D.qz = cq.z;
+      D.qi = cq.idx;
+    }
+  }
   D.pad = 0.0f;
 
   if (c == 0) {
@@ -751,6 +790,8 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void small_rule_kernel(
   D.iq = (float)(1.0 / __shfl(zq, kq));
   D.u = __shfl(u_smp, k);
   D.xk = k < gamma ? __shfl(xi, k) : -1;
+  D.pz = D.qz = -INFINITY;
+  D.pi = D.qi = 0x7fffffff;
   D.pad = 0.0f;
   DrawRow R;
   R.zp = target + (size_t)(b * g1 + k) * V;
@@ -763,7 +804,7 @@ __global__ __launch_bounds__(kWavesPerBlock * 64) void small_rule_kernel(
   R.inv_t = inv_t;
   R.kind = draft_kind;
   R.xk = D.xk;
-  R.pk = R.qk = 0u;
+  R.pz = R.qz = -INFINITY;
   R.pi = R.qi = 0x7fffffff;
   float zp4[4], zq4[4];
   load4<VEC>(R.zp, V, lane, -INFINITY, zp4);
