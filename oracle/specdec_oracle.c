@@ -774,5 +774,5 @@ void oracle_kv_gather(const uint8_t* kpool, const uint8_t* vpool, const int32_t*
     }
 }
 
-/* Which mistake (if any) this build carries; 0 for the real oracle. */
+/* Which mistake (if any) this compiled copy of the oracle carries (ORACLE_PLANT); 0 for the real oracle. */
 int oracle_planted(void) { return ORACLE_PLANT; }
