@@ -33,6 +33,9 @@
 // For a small top-k of a long row a sampled threshold replaces the histogram:
 // one pass collects every entry above it together with the row maximum, and
 // the histogram passes run only when that catch is too small or too large.
+// The threshold comes from small histograms of the sample's top buckets, and
+// the pass compares values (the largest of each four first), forming keys
+// only for the entries it collects.
 // The kernel also leaves the warped row's statistics for the draw (the max
 // and sum of exponentials over the kept entries, the drafted token's logit),
 // so a warped step needs no separate statistics pass.
