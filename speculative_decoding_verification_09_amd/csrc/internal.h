@@ -69,6 +69,23 @@ size_t reject_workspace_bytes(int64_t B, int64_t gamma, int64_t V);
 // greedy rule; with warping, the per-row cuts are found first.
 hipError_t launch_reject_sample(const RejectArgs& a, hipStream_t stream);
 
+// e^x for x <= 0 (the weights of the draw, the masses of the top-p cut). x
+// log2(e) is carried as its rounded product h plus a correction l (that
+// product's rounding error and the tail of log2(e)), and 2^(h + l) =
+// 2^h (1 + l ln 2) up to a relative 2^-34, as |l| < 2^-16 for |x| <= 128. The
+// hardware base-2 exponential gives 2^h. x is clamped at -128, where e^x lies
+// below the smallest subnormal, so a -inf logit weighs exactly 0.
+__device__ __forceinline__ float exp_nonpos(float x) {
+  constexpr float kLog2eHi = 1.4426950408889634f;
+  constexpr float kLog2eLo = 1.925963e-08f;  // log2(e) minus its float value
+  constexpr float kLn2 = 0.6931472f;
+  x = fmaxf(x, -128.0f);
+  const float h = x * kLog2eHi;
+  const float l = fmaf(x, kLog2eLo, fmaf(x, kLog2eHi, -h));
+  const float e = __builtin_amdgcn_exp2f(h);
+  return fmaf(e, l * kLn2, e);
+}
+
 // Order-preserving integer image of an fp32 logit (larger value, larger key;
 // -0 and +0 map to one key).  A warped row keeps entry v iff
 // key(z_v) > cut_key, or key(z_v) == cut_key and v <= cut_idx: the entries
@@ -80,6 +97,27 @@ __device__ __forceinline__ uint32_t order_key(float z) {
 __device__ __forceinline__ bool warp_kept(uint32_t key, int64_t v, uint32_t cut_key, int32_t cut_idx) {
   return key > cut_key || (key == cut_key && v <= (int64_t)cut_idx);
 }
+// A warp cut (key ck, index ci: entry v with key k kept iff k > ck, or k == ck
+// and v <= ci) as a test on values: a non-NaN z is kept iff z > cz, or
+// z == cz and v <= the returned index.  Keys order values (-0 and +0 share
+// one key and compare equal), so at the key of a float this is the key test;
+// keys below that of -inf keep every entry, keys above that of +inf none (a
+// NaN cz compares false), and the one key no float has (that -0 would have
+// without sharing) keeps exactly the z >= -0.
+struct ValueCut {
+  float z;
+  int32_t idx;
+};
+__device__ __forceinline__ ValueCut value_cut(uint32_t ck, int32_t ci) {
+  if (ck < 0x007fffffu) return {-INFINITY, 0x7fffffff};
+  if (ck > 0xff800000u) return {__uint_as_float(0x7fc00000u), -1};
+  if (ck == 0x7fffffffu) return {__uint_as_float(0x80000001u), -1};
+  return {__uint_as_float((ck & 0x80000000u) ? (ck & 0x7fffffffu) : ~ck), ci};
+}
+__device__ __forceinline__ bool value_kept(float z, int64_t v, float cz, int32_t ci) {
+  return z > cz || (z == cz && v <= (int64_t)ci);
+}
+
 // Where the warp cut kernel leaves each warped row's statistics, in the
 // layout of the statistics pass: per row, pstride slots of (max of z/T, sum of
 // exp(z/T - max)), of which nch are read; the drafted token's logit; and the

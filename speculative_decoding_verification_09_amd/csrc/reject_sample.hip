@@ -48,8 +48,6 @@ constexpr int kGreedyWaves = 8;    // waves of the greedy rule's workgroup (one 
 constexpr int kWavesPerBlock = 4;
 constexpr float kQFloor = 1e-12f;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLog2eLo = 1.925963e-08f;  // log2(e) minus its float value
-constexpr float kLn2 = 0.6931472f;
 constexpr int64_t kMaxFusedParts = kFusedStatsMaxParts;
 constexpr int64_t kMaxFusedRows = kFusedStatsMaxRows;
 
@@ -325,41 +323,6 @@ struct DrawRow {
   float pz, qz;     // warp cuts of the two rows as values (WARP only), see value_cut
   int32_t pi, qi;
 };
-
-// e^x for x <= 0, for the weights of the draw. x log2(e) is carried as its
-// rounded product h plus a correction l (that product's rounding error and the
-// tail of log2(e)), and 2^(h + l) = 2^h (1 + l ln 2) up to a relative 2^-34,
-// as |l| < 2^-16 for |x| <= 128. The hardware base-2 exponential gives 2^h.
-// x is clamped at -128, where e^x lies below the smallest subnormal, so a -inf
-// logit weighs exactly 0.
-__device__ __forceinline__ float exp_nonpos(float x) {
-  x = fmaxf(x, -128.0f);
-  const float h = x * kLog2e;
-  const float l = fmaf(x, kLog2eLo, fmaf(x, kLog2e, -h));
-  const float e = __builtin_amdgcn_exp2f(h);
-  return fmaf(e, l * kLn2, e);
-}
-
-// A warp cut (key ck, index ci: entry v with key k kept iff k > ck, or k == ck
-// and v <= ci) as a test on values: a non-NaN z is kept iff z > cz, or
-// z == cz and v <= the returned index.  Keys order values (-0 and +0 share
-// one key and compare equal), so at the key of a float this is the key test;
-// keys below that of -inf keep every entry, keys above that of +inf none (a
-// NaN cz compares false), and the one key no float has (that -0 would have
-// without sharing) keeps exactly the z >= -0.
-struct ValueCut {
-  float z;
-  int32_t idx;
-};
-__device__ __forceinline__ ValueCut value_cut(uint32_t ck, int32_t ci) {
-  if (ck < 0x007fffffu) return {-INFINITY, 0x7fffffff};
-  if (ck > 0xff800000u) return {__uint_as_float(0x7fc00000u), -1};
-  if (ck == 0x7fffffffu) return {__uint_as_float(0x80000001u), -1};
-  return {__uint_as_float((ck & 0x80000000u) ? (ck & 0x7fffffffu) : ~ck), ci};
-}
-__device__ __forceinline__ bool value_kept(float z, int64_t v, float cz, int32_t ci) {
-  return z > cz || (z == cz && v <= (int64_t)ci);
-}
 
 // WARP: p_v (and q_v of draft logits) is 0 where the row's warp cut drops v.
 template <bool WARP>

@@ -56,7 +56,6 @@ constexpr int kBins = 4096;  // 12-bit digits
 constexpr int kCap = 2048;   // candidates held in LDS
 constexpr int kIdxBits = 23;
 constexpr uint32_t kIdxMask = (1u << kIdxBits) - 1;
-constexpr double kFix = 1099511627776.0;  // 2^40
 
 typedef unsigned long long u64;
 
@@ -78,9 +77,15 @@ struct Shared {
   int found;
 };
 
+// floor(e * 2^40) for e = 2^((z - zmax) * (fl32(1/T) * log2(e))) in [0, 1]
+// (the difference first, then one rounding more than z/T - max/T itself, then
+// the hardware base-2 exponential): 256 e is exact in fp32, its integer part
+// h counts units of 2^32, and (256 e - h) * 2^32, exact too, truncates to the
+// rest.  0 for -inf logits and wherever e underflows.
 __device__ __forceinline__ u64 mass_fixed(float z, float inv_t, float zmax) {
-  const float e = expf((z - zmax) * inv_t);
-  return e > 0.0f ? (u64)((double)e * kFix) : 0ull;  // 0 for -inf logits
+  const float s = __builtin_amdgcn_exp2f((z - zmax) * (inv_t * 1.4426950408889634f)) * 256.0f;
+  const float h = truncf(s);
+  return ((u64)(uint32_t)h << 32) | (u64)(uint32_t)((s - h) * 4294967296.0f);
 }
 __device__ __forceinline__ u64 composite(uint32_t key, int v) {
   return ((u64)key << kIdxBits) | (u64)(kIdxMask - (uint32_t)v);
@@ -304,6 +309,157 @@ __device__ u64 lds_select(int n, u64 need, u64 floor, Shared& sh) {
     hi = lo;
   }
   return prefix;
+}
+
+// Calls f(v, z) for every entry of the row over the same ranges as for_row,
+// U 16-byte loads in flight per lane; steps that lie wholly inside the wave's
+// range load and call without per-entry tests.
+template <bool VEC, int U = 8, class F>
+__device__ __forceinline__ void for_row_lean(const float* __restrict__ row, int V, int R, F&& f) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int b0 = w * R, b1 = min(b0 + R, V);
+  for (int base = b0; base < b1; base += U * 256) {
+    float z[U][4];
+    if (VEC && base + U * 256 <= b1) {  // wave-uniform
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float4 t = *(const float4*)(row + base + 256 * u + 4 * lane);
+        z[u][0] = t.x;
+        z[u][1] = t.y;
+        z[u][2] = t.z;
+        z[u][3] = t.w;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f(base + 256 * u + 4 * lane + e, z[u][e]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = base + 256 * u + 4 * lane + e;
+          z[u][e] = v < b1 ? row[v] : 0.0f;
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = base + 256 * u + 4 * lane + e;
+          if (v < b1) f(v, z[u][e]);
+        }
+    }
+  }
+}
+
+// The value zt with order_key(z) >= t exactly for the non-NaN z >= zt (the
+// keys below that of -inf, and those above that of +inf, are no float's; a
+// NaN zt compares false).
+__device__ __forceinline__ float key_floor_value(uint32_t t) {
+  return t <= 0x007fffffu ? -INFINITY : (t > 0xff800000u ? __uint_as_float(0x7fc00000u) : key_value(t));
+}
+
+// Top-p alone over a long row, from a window of keys around the cut.  The
+// sample of the collecting path (16 entries per thread), weighed by its
+// masses, puts the cut in a 12-bit key bucket bc.  One pass over the row then
+// takes every entry's mass (the row's total), the masses above the window of
+// buckets bc - 4 .. bc + 3 (per thread, no atomics), and the window's
+// histogram at 11-bit resolution (4096 bins of 2^11 keys).  The bin where the
+// running mass from the top reaches the target is compacted into LDS and the
+// cut found among its entries, as select_cut's last step does.  Returns false
+// (LDS changed, nothing else) when the cut lies outside the window or its bin
+// holds more than kCap entries; the full passes then run.
+template <bool VEC>
+__device__ __noinline__ bool top_p_window(const float* __restrict__ row, int V, int R, float top_p, float inv_t, float zmax,
+                             Shared& sh, Cut& cut) {
+  const int q = V / (16 * kThreads);
+  u64 stot = 0;
+  clear_bins(sh, true);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int v0 = 16 * q * (int)threadIdx.x + 4 * u;  // v0 + 3 < 16 q kThreads <= V
+    float z[4];
+    if (VEC) {
+      const float4 t = *(const float4*)(row + v0);
+      z[0] = t.x;
+      z[1] = t.y;
+      z[2] = t.z;
+      z[3] = t.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[e] = row[v0 + e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const u64 m = mass_fixed(z[e], inv_t, zmax);
+      if (m > 0) atomicAdd(&sh.mass[order_key(z[e]) >> 20], m);
+      stot += m;
+    }
+  }
+  const u64 S = block_sum(stot, sh.red);  // its barriers also order the atomics before the scan
+  if (S == 0) return false;
+  const double ts = ceil((double)top_p * (double)S);
+  const u64 sneed = ts < 1.0 ? 1ull : (ts > (double)S ? S : (u64)ts);
+  uint32_t bc;
+  u64 sabove;
+  scan_bins<true>(kBins, sneed, sh, bc, sabove);
+  const uint32_t blo = bc >= 4 ? bc - 4 : 0u;
+  const u64 whi = (u64)min(bc + 4u, (uint32_t)kBins) << 20;  // window: keys [blo << 20, whi)
+  const uint32_t wlo = blo << 20;
+  const float zwlo = key_floor_value(wlo);
+  const float zwhi = whi > 0xffffffffull ? __uint_as_float(0x7fc00000u) : key_floor_value((uint32_t)whi);
+
+  clear_bins(sh, true);
+  u64 tot = 0, hi = 0;
+  for_row_lean<VEC, 4>(row, V, R, [&](int v, float z) {
+    const u64 m = mass_fixed(z, inv_t, zmax);
+    tot += m;
+    if (z >= zwhi) {
+      hi += m;
+    } else if (z >= zwlo && m > 0) {
+      const uint32_t f = (order_key(z) - wlo) >> 11;
+      atomicAdd(&sh.cnt[f], 1u);
+      atomicAdd(&sh.mass[f], m);
+    }
+  });
+  tot = block_sum(tot, sh.red);
+  hi = block_sum(hi, sh.red);  // also orders the atomics before the scan
+  const double t = ceil((double)top_p * (double)tot);
+  u64 need = t < 1.0 ? 1ull : (t > (double)tot ? tot : (u64)t);
+  if (tot == 0 || hi >= need) return false;
+  need -= hi;
+  uint32_t f;
+  u64 above;
+  scan_bins<true>(kBins, need, sh, f, above);
+  const bool found = above + sh.mass[f] >= need;  // else the window holds less than need
+  const int nf = (int)sh.cnt[f];
+  __syncthreads();
+  if (!found || nf > kCap) return false;
+  need -= above;
+  const uint32_t flo = wlo + (f << 11);
+  const u64 fhi = (u64)flo + 2048;
+  const float zflo = key_floor_value(flo);
+  const float zfhi = fhi > 0xffffffffull ? __uint_as_float(0x7fc00000u) : key_floor_value((uint32_t)fhi);
+  if (threadIdx.x == 0) sh.ncand = 0;
+  __syncthreads();
+  for_row_lean<VEC, 4>(row, V, R, [&](int v, float z) {
+    if (z >= zflo && !(z >= zfhi)) {
+      const u64 m = mass_fixed(z, inv_t, zmax);
+      if (m > 0) {
+        const uint32_t sl = atomicAdd(&sh.ncand, 1u);
+        if (sl < (uint32_t)kCap) {
+          sh.comp[sl] = composite(order_key(z), v);
+          sh.cw[sl] = m;
+        }
+      }
+    }
+  });
+  __syncthreads();
+  const int n = (int)min(sh.ncand, (uint32_t)kCap);
+  __syncthreads();
+  const u64 c = lds_select<true>(n, need, 0ull, sh);
+  cut = Cut{(uint32_t)(c >> kIdxBits), (int32_t)(kIdxMask - (uint32_t)(c & kIdxMask))};
+  return true;
 }
 
 // Copies into LDS the entries kept by `lim` (positive mass when MASS) whose
@@ -806,6 +962,8 @@ __global__ __launch_bounds__(kThreads) void warp_cut_kernel(const float* __restr
       if (tk) atomicAdd(&sh.cnt[order_key(z) >> 20], 1u);
     });
     zmax = block_max(zm, sh.redf);
+    // Top-p alone over a long row: from a window around the cut when it holds it.
+    if (!tk && tp && V >= 16 * kThreads && top_p_window<VEC>(row, V, R, top_p, inv_t, zmax, sh, cut)) done_p = true;
   }
   if (tk && nk < 0) {
     uint32_t b;
@@ -863,8 +1021,9 @@ __global__ __launch_bounds__(kThreads) void warp_cut_kernel(const float* __restr
       for (int i = threadIdx.x; i < nk; i += kThreads)
         zsum += (double)__builtin_amdgcn_exp2f(fmaf(key_value((uint32_t)(sh.comp[i] >> kIdxBits)), c1, -c2));
     } else {
-      for_row<VEC>(row, V, R, [&](int v, float z) {
-        if (warp_kept(order_key(z), v, cut.key, cut.idx)) zsum += (double)__builtin_amdgcn_exp2f(fmaf(z, c1, -c2));
+      const ValueCut vc = value_cut(cut.key, cut.idx);
+      for_row_lean<VEC, 4>(row, V, R, [&](int v, float z) {
+        if (value_kept(z, v, vc.z, vc.idx)) zsum += (double)__builtin_amdgcn_exp2f(fmaf(z, c1, -c2));
       });
     }
   }

@@ -109,6 +109,7 @@ CASES = [
     (100, 4, 3000, 0.0, 1.0, 900, 0.3, 2, True, 0.02),     # both, ties, one-hot
     (16, 0, 5000, 2.0, 1.0, 10, 0.9, 0, False, 0.02),      # gamma = 0: the bonus row alone
     (8, 7, 128256, 2.5, 0.8, 50, 0.95, 0, False, 0.02),    # a 128K vocabulary
+    (8, 7, 128256, 2.5, 0.8, 0, 0.9, 0, False, 0.05),      # top-p alone over a 128K vocabulary (a window of keys)
     (6, 3, 40003, 2.0, 1.0, 40, 0.9, 0, False, 0.02),      # V % 4 != 0 with a long row
     (24, 3, 32000, 2.0, 1.0, 5000, 1.0, 0, False, 0.02),   # top-k survivors beyond what LDS holds
     (24, 3, 32000, 0.0, 1.0, 100, 1.0, 0, "narrow", 0.02),  # the cut's bucket over capacity: a second level
