@@ -565,6 +565,10 @@ def extensions(args):
     warped = _time_launches(lambda: sd.specdec_verify_step_warped(X, W, draft, tokens, T, k, p, uni, logits, out_tok,
                                                                   out_num, ws, stream=stream), K, Wm, stream)
     emitted_w = int(out_num.sum().item())
+    # top-p alone (its own path: a window of keys around a sampled estimate of the cut)
+    p_only = cfg["top_p_alone"]
+    warped_p = _time_launches(lambda: sd.specdec_verify_step_warped(X, W, draft, tokens, T, 0, p_only, uni, logits,
+                                                                    out_tok, out_num, ws, stream=stream), K, Wm, stream)
     rws = sd.new_workspace(B, g, V)
     tl = logits.view(B, g + 1, V)
     rej = _time_launches(lambda: sd.specdec_reject_sample(tl, draft, tokens, T, uni, out_tok, out_num, rws,
@@ -575,7 +579,9 @@ def extensions(args):
     res["warp"] = {"workload": w.name, "top_k": k, "top_p": p, "plain_step_ms": plain, "warped_step_ms": warped,
                    "warped_positions_per_s": N / (warped * 1e-3), "warped_emitted_per_step": emitted_w,
                    "plain_rule_ms": rej, "warped_rule_ms": rej_w, "warp_overhead_ms": rej_w - rej,
-                   "rows_warped": rows, "row_bytes_read_once": rows * V * 4}
+                   "rows_warped": rows, "row_bytes_read_once": rows * V * 4,
+                   "top_p_alone": p_only, "top_p_alone_step_ms": warped_p,
+                   "top_p_alone_positions_per_s": N / (warped_p * 1e-3)}
     onehot = _time_launches(lambda: sd.specdec_verify_step(X, W, None, tokens, T, uni, logits, out_tok, out_num, ws,
                                                            draft_kind=sd.SPECDEC_DRAFT_ONEHOT, stream=stream),
                             K, Wm, stream)

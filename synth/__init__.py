@@ -163,7 +163,7 @@ WORKLOADS = {
 # Workloads of the extensions beyond the plain step, each timed on its own.
 EXTENSIONS = {
     # Top-k / top-p warping of every target and draft row of the larger LM-head step.
-    "warp": {"workload": "lmhead_b8_g7", "top_k": 50, "top_p": 0.95},
+    "warp": {"workload": "lmhead_b8_g7", "top_k": 50, "top_p": 0.95, "top_p_alone": 0.9},
     # The same step with one-hot drafts (greedy or prompt-lookup drafters): no draft array is read.
     "onehot": {"workload": "lmhead_b8_g7"},
     # Greedy verification of 8 binary trees of 16 nodes (parent of node i is (i - 1) // 2) on a Llama-8B head;
