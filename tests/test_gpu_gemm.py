@@ -166,6 +166,35 @@ def test_split_k_normal_within_fp32_bound(orc, N, d, V):
     assert np.all(np.abs(Y - ref) <= 2e-2 * np.maximum(np.abs(ref), 1e-3 * rms))
 
 
+@pytest.mark.parametrize("N,d,V", [(64, 8192, 1030), (5, 28672, 77), (130, 2048, 500)])
+def test_split_k_workspace_reused(orc, N, d, V):
+    """Back-to-back launches on one workspace (zeroed first, then holding the previous launch's partials): each
+    result is exact, and rounded sums come out in the same bits every time (partials added in group order)."""
+    W_bits = synth.integer_bf16((V, d), 8, 67, V)
+    W = weights(W_bits, True)
+    need = sd.logits_workspace_bytes(N, d, V, sd.SPECDEC_WEIGHTS_PACKED)
+    ws = torch.zeros((need,), dtype=torch.uint8, device="cuda")
+    announce(f"gemm split-k reused workspace N={N} d={d} V={V}")
+    outs = []
+    for i, seed in enumerate((68, 69, 68)):
+        X_bits = synth.integer_bf16((N, d), 8, seed, N)
+        Y = torch.full((N, V), float("nan"), device="cuda")
+        sd.specdec_verify_logits(dev_bf16(X_bits), W, Y, sd.SPECDEC_OUT_F32, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(host(Y))
+        assert np.array_equal(outs[-1].astype(np.float64), orc.linear(X_bits, W_bits)), i
+    # normal inputs (rounded sums): the same bits from two launches
+    X = dev_bf16(synth.normal_bf16((N, d), 1.0, 70, N))
+    Wn = weights(synth.normal_bf16((V, d), 0.02, 71, V), True)
+    Ys = []
+    for _ in range(2):
+        Y = torch.empty((N, V), device="cuda")
+        sd.specdec_verify_logits(X, Wn, Y, sd.SPECDEC_OUT_F32, workspace=ws)
+        torch.cuda.synchronize()
+        Ys.append(host(Y))
+    assert np.array_equal(Ys[0].view(np.uint32), Ys[1].view(np.uint32))
+
+
 @pytest.mark.parametrize("N,d,V", [(8, 9984, 5000), (40, 2048, 300)])
 def test_split_k_bf16_output(orc, N, d, V):
     X = synth.normal_bf16((N, d), 1.0, 65, N)
