@@ -80,12 +80,11 @@ struct Shared {
 // floor(e * 2^40) for e = 2^((z - zmax) * (fl32(1/T) * log2(e))) in [0, 1]
 // (the difference first, then one rounding more than z/T - max/T itself, then
 // the hardware base-2 exponential): 256 e is exact in fp32, its integer part
-// h counts units of 2^32, and (256 e - h) * 2^32, exact too, truncates to the
-// rest.  0 for -inf logits and wherever e underflows.
+// h counts units of 2^32, and its fraction 256 e - h times 2^32, exact too,
+// truncates to the rest.  0 for -inf logits and wherever e underflows.
 __device__ __forceinline__ u64 mass_fixed(float z, float inv_t, float zmax) {
   const float s = __builtin_amdgcn_exp2f((z - zmax) * (inv_t * 1.4426950408889634f)) * 256.0f;
-  const float h = truncf(s);
-  return ((u64)(uint32_t)h << 32) | (u64)(uint32_t)((s - h) * 4294967296.0f);
+  return ((u64)(uint32_t)s << 32) | (u64)(uint32_t)(__builtin_amdgcn_fractf(s) * 4294967296.0f);
 }
 __device__ __forceinline__ u64 composite(uint32_t key, int v) {
   return ((u64)key << kIdxBits) | (u64)(kIdxMask - (uint32_t)v);
@@ -364,14 +363,18 @@ __device__ __forceinline__ float key_floor_value(uint32_t t) {
 // masses, puts the cut in a 12-bit key bucket bc.  One pass over the row then
 // takes every entry's mass (the row's total), the masses above the window of
 // buckets bc - 4 .. bc + 3 (per thread, no atomics), and the window's
-// histogram at 11-bit resolution (4096 bins of 2^11 keys).  The bin where the
-// running mass from the top reaches the target is compacted into LDS and the
-// cut found among its entries, as select_cut's last step does.  Returns false
-// (LDS changed, nothing else) when the cut lies outside the window or its bin
-// holds more than kCap entries; the full passes then run.
+// histogram of masses at 11-bit resolution (4096 bins of 2^11 keys).  The
+// bin where the running mass from the top reaches the target is compacted
+// into LDS and the cut found among its entries, as select_cut's last step
+// does.  The same pass also sums the warped statistics' terms of the entries
+// above that bin (all of them kept), and those of the kept candidates are
+// added after the cut: zpart is this thread's share of Z (the terms as the
+// statistics pass forms them, in another order).  Returns false (LDS changed,
+// nothing else) when the cut lies outside the window or its bin holds more
+// than kCap entries; the full passes then run.
 template <bool VEC>
 __device__ __noinline__ bool top_p_window(const float* __restrict__ row, int V, int R, float top_p, float inv_t, float zmax,
-                             Shared& sh, Cut& cut) {
+                             Shared& sh, Cut& cut, double& zpart) {
   const int q = V / (16 * kThreads);
   u64 stot = 0;
   clear_bins(sh, true);
@@ -417,9 +420,7 @@ __device__ __noinline__ bool top_p_window(const float* __restrict__ row, int V, 
     if (z >= zwhi) {
       hi += m;
     } else if (z >= zwlo && m > 0) {
-      const uint32_t f = (order_key(z) - wlo) >> 11;
-      atomicAdd(&sh.cnt[f], 1u);
-      atomicAdd(&sh.mass[f], m);
+      atomicAdd(&sh.mass[(order_key(z) - wlo) >> 11], m);
     }
   });
   tot = block_sum(tot, sh.red);
@@ -432,18 +433,24 @@ __device__ __noinline__ bool top_p_window(const float* __restrict__ row, int V, 
   u64 above;
   scan_bins<true>(kBins, need, sh, f, above);
   const bool found = above + sh.mass[f] >= need;  // else the window holds less than need
-  const int nf = (int)sh.cnt[f];
   __syncthreads();
-  if (!found || nf > kCap) return false;
+  if (!found) return false;
   need -= above;
   const uint32_t flo = wlo + (f << 11);
   const u64 fhi = (u64)flo + 2048;
   const float zflo = key_floor_value(flo);
   const float zfhi = fhi > 0xffffffffull ? __uint_as_float(0x7fc00000u) : key_floor_value((uint32_t)fhi);
+  // The statistics' terms 2^(z * c1 - c2), as the statistics pass forms them.
+  const float c1 = inv_t * 1.4426950408889634f, c2 = (zmax * inv_t) * 1.4426950408889634f;
   if (threadIdx.x == 0) sh.ncand = 0;
   __syncthreads();
+  double zs = 0.0;
   for_row_lean<VEC, 4>(row, V, R, [&](int v, float z) {
-    if (z >= zflo && !(z >= zfhi)) {
+    if (z >= zfhi) {  // above the cut's bin: kept
+      zs += (double)__builtin_amdgcn_exp2f(fmaf(z, c1, -c2));
+    } else if (z >= zflo) {
+      // In the bin.  Only entries of positive mass can be kept: the cut's own
+      // mass is positive, and masses do not decrease with z.
       const u64 m = mass_fixed(z, inv_t, zmax);
       if (m > 0) {
         const uint32_t sl = atomicAdd(&sh.ncand, 1u);
@@ -455,10 +462,17 @@ __device__ __noinline__ bool top_p_window(const float* __restrict__ row, int V, 
     }
   });
   __syncthreads();
-  const int n = (int)min(sh.ncand, (uint32_t)kCap);
+  const uint32_t napp = sh.ncand;
   __syncthreads();
+  if (napp > (uint32_t)kCap) return false;
+  const int n = (int)napp;
   const u64 c = lds_select<true>(n, need, 0ull, sh);
   cut = Cut{(uint32_t)(c >> kIdxBits), (int32_t)(kIdxMask - (uint32_t)(c & kIdxMask))};
+  for (int i = threadIdx.x; i < n; i += kThreads) {  // the kept candidates: composites at or above the cut's
+    const u64 ci = sh.comp[i];
+    if (ci >= c) zs += (double)__builtin_amdgcn_exp2f(fmaf(key_value((uint32_t)(ci >> kIdxBits)), c1, -c2));
+  }
+  zpart = zs;
   return true;
 }
 
@@ -873,6 +887,8 @@ __global__ __launch_bounds__(kThreads) void warp_cut_kernel(const float* __restr
   Cut cut{0u, 0x7fffffff};  // keeps every entry
   bool done_p = false;
   int nk = -1;  // when the kept entries are ranks [0, nk) of the sorted candidates in LDS
+  bool have_zpart = false;  // the top-p window's share of the warped Z
+  double zpart = 0.0;
   float zmax;
   // A small top-k of a long row, in one pass: a sample of 16 entries per
   // thread spread over the row, histogrammed by key (12 bits, then the next 12 within the
@@ -963,7 +979,10 @@ __global__ __launch_bounds__(kThreads) void warp_cut_kernel(const float* __restr
     });
     zmax = block_max(zm, sh.redf);
     // Top-p alone over a long row: from a window around the cut when it holds it.
-    if (!tk && tp && V >= 16 * kThreads && top_p_window<VEC>(row, V, R, top_p, inv_t, zmax, sh, cut)) done_p = true;
+    if (!tk && tp && V >= 16 * kThreads && top_p_window<VEC>(row, V, R, top_p, inv_t, zmax, sh, cut, zpart)) {
+      done_p = true;
+      have_zpart = true;
+    }
   }
   if (tk && nk < 0) {
     uint32_t b;
@@ -1012,12 +1031,15 @@ __global__ __launch_bounds__(kThreads) void warp_cut_kernel(const float* __restr
   // 2^(z * c1 - c2) with c1 = fl32(1/T) * log2(e), c2 = max * log2(e), fp32
   // terms summed in fp64; and the drafted token's logit (-inf when the cut
   // drops it).  The kept entries are the candidates' ranks [0, nk) when the
-  // cut came from them; otherwise one more pass over the row.
+  // cut came from them; the top-p window has summed them itself; otherwise
+  // one more pass over the row.
   const float mx = zmax * inv_t;
   double zsum = 0.0;
   if (mx > -INFINITY) {
     const float c1 = inv_t * 1.4426950408889634f, c2 = mx * 1.4426950408889634f;
-    if (nk >= 0) {
+    if (have_zpart) {
+      zsum = zpart;
+    } else if (nk >= 0) {
       for (int i = threadIdx.x; i < nk; i += kThreads)
         zsum += (double)__builtin_amdgcn_exp2f(fmaf(key_value((uint32_t)(sh.comp[i] >> kIdxBits)), c1, -c2));
     } else {
