@@ -93,6 +93,19 @@ __device__ __forceinline__ float key_value(uint32_t key) {  // inverse of order_
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
+// Loads from the row through global-memory instructions.  The row is always
+// device memory; in the functions kept out of line its pointer arrives
+// without that knowledge, and generic loads would share their wait counter
+// with the LDS operations of the same loop.
+__device__ __forceinline__ float4 load_row4(const float* p) {
+  typedef float v4 __attribute__((ext_vector_type(4)));
+  const v4 t = *(const __attribute__((address_space(1))) v4*)p;
+  return make_float4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ float load_row1(const float* p) {
+  return *(const __attribute__((address_space(1))) float*)p;
+}
+
 __device__ __forceinline__ float block_max(float v, float* lds) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
@@ -188,14 +201,14 @@ __device__ __forceinline__ void for_row(const float* __restrict__ row, int V, in
     for (int u = 0; u < U; ++u) {
       const int v = base + 256 * u + 4 * lane;
       if (VEC && v + 3 < b1) {
-        const float4 t = *(const float4*)(row + v);
+        const float4 t = load_row4(row + v);
         z[u][0] = t.x;
         z[u][1] = t.y;
         z[u][2] = t.z;
         z[u][3] = t.w;
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) z[u][e] = v + e < b1 ? row[v + e] : 0.0f;
+        for (int e = 0; e < 4; ++e) z[u][e] = v + e < b1 ? load_row1(row + v + e) : 0.0f;
       }
     }
 #pragma unroll
@@ -223,7 +236,7 @@ __device__ __forceinline__ void collect_row(const float* __restrict__ row, int V
     if (whole) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float4 t = *(const float4*)(row + base + 256 * u + 4 * lane);
+        const float4 t = load_row4(row + base + 256 * u + 4 * lane);
         z[u][0] = t.x;
         z[u][1] = t.y;
         z[u][2] = t.z;
@@ -245,7 +258,7 @@ __device__ __forceinline__ void collect_row(const float* __restrict__ row, int V
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int v = base + 256 * u + 4 * lane + e;
-          z[u][e] = v < b1 ? row[v] : -INFINITY;
+          z[u][e] = v < b1 ? load_row1(row + v) : -INFINITY;
         }
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -322,7 +335,7 @@ __device__ __forceinline__ void for_row_lean(const float* __restrict__ row, int 
     if (VEC && base + U * 256 <= b1) {  // wave-uniform
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float4 t = *(const float4*)(row + base + 256 * u + 4 * lane);
+        const float4 t = load_row4(row + base + 256 * u + 4 * lane);
         z[u][0] = t.x;
         z[u][1] = t.y;
         z[u][2] = t.z;
@@ -338,7 +351,7 @@ __device__ __forceinline__ void for_row_lean(const float* __restrict__ row, int 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int v = base + 256 * u + 4 * lane + e;
-          z[u][e] = v < b1 ? row[v] : 0.0f;
+          z[u][e] = v < b1 ? load_row1(row + v) : 0.0f;
         }
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -383,14 +396,14 @@ __device__ __noinline__ bool top_p_window(const float* __restrict__ row, int V, 
     const int v0 = 16 * q * (int)threadIdx.x + 4 * u;  // v0 + 3 < 16 q kThreads <= V
     float z[4];
     if (VEC) {
-      const float4 t = *(const float4*)(row + v0);
+      const float4 t = load_row4(row + v0);
       z[0] = t.x;
       z[1] = t.y;
       z[2] = t.z;
       z[3] = t.w;
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) z[e] = row[v0 + e];
+      for (int e = 0; e < 4; ++e) z[e] = load_row1(row + v0 + e);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -531,7 +544,7 @@ __device__ int ordered_tie(const float* __restrict__ row, int V, int R, uint32_t
       for (int e = 0; e < 4; ++e) {
         hit[e] = false;
         if (v + e < b1) {
-          const uint32_t k = order_key(row[v + e]);
+          const uint32_t k = order_key(load_row1(row + v + e));
           hit[e] = k == ck && warp_kept(k, v + e, lim.key, lim.idx);
         }
         cnt += hit[e];
@@ -912,14 +925,14 @@ __global__ __launch_bounds__(kThreads) void warp_cut_kernel(const float* __restr
     for (int u = 0; u < 4; ++u) {
       const int v0 = 16 * q * (int)threadIdx.x + 4 * u;  // v0 + 3 < 16 q kThreads <= V
       if (VEC) {
-        const float4 t = *(const float4*)(row + v0);
+        const float4 t = load_row4(row + v0);
         ks[4 * u + 0] = order_key(t.x);
         ks[4 * u + 1] = order_key(t.y);
         ks[4 * u + 2] = order_key(t.z);
         ks[4 * u + 3] = order_key(t.w);
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ks[4 * u + e] = order_key(row[v0 + e]);
+        for (int e = 0; e < 4; ++e) ks[4 * u + e] = order_key(load_row1(row + v0 + e));
       }
     }
     // The s0-th largest sample stands for about 3*top_k row entries (mean);
