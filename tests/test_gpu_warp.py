@@ -111,6 +111,7 @@ CASES = [
     (8, 7, 128256, 2.5, 0.8, 50, 0.95, 0, False, 0.02),    # a 128K vocabulary
     (8, 7, 128256, 2.5, 0.8, 0, 0.9, 0, False, 0.05),      # top-p alone over a 128K vocabulary (a window of keys)
     (6, 3, 40003, 2.0, 1.0, 40, 0.9, 0, False, 0.02),      # V % 4 != 0 with a long row
+    (6, 3, 40003, 2.0, 1.0, 0, 0.9, 0, False, 0.05),       # top-p alone, V % 4 != 0: the window with element loads
     (24, 3, 32000, 2.0, 1.0, 5000, 1.0, 0, False, 0.02),   # top-k survivors beyond what LDS holds
     (24, 3, 32000, 0.0, 1.0, 100, 1.0, 0, "narrow", 0.02),  # the cut's bucket over capacity: a second level
     (24, 3, 32000, 0.0, 0.05, 0, 0.5, 0, "narrow", 0.1),   # the same for the top-p cut (broad: T over the range)
@@ -118,6 +119,7 @@ CASES = [
     (24, 3, 32000, 0.0, 1.0, 0, 0.5, 2, "ties", 0.05),     # the same for top-p
     (24, 3, 32000, 0.0, 1.0, 3000, 0.9, 0, "ties", 0.05),  # both, over capacity
     (24, 3, 32000, 2.0, 1.0, 50, 0.9, 0, "spikes", 0.02),  # a few far larger logits: the sample's full histograms
+    (24, 3, 32000, 2.0, 1.0, 0, 0.9, 0, "spikes", 0.05),   # top-p alone with the mass held by a few spikes
 ]
 
 
