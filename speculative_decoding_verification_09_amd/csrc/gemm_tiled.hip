@@ -515,12 +515,16 @@ __global__ __launch_bounds__(NW * 64) void panel_kernel(const uint16_t* __restri
   }
   const int vb = gi % nvb, group = gi / nvb;
   const int c0 = group * cpk, c1 = min(c0 + cpk, nch_all);
-  // Chunk c of the loop reads chunk pc(c): the group's range rotated by a
-  // per-block offset, so that the blocks streaming at the same moment read
-  // different offsets within their W rows rather than all the same one
-  // (measured at N = 64, d = 8192, V = 128256: 313.0 -> 310.4 us).  It also
-  // sets the order in which the block's k-steps are summed.
-  const int krot = c1 > c0 ? (vb * 37) % (c1 - c0) : 0;
+  // Chunk c of the loop reads chunk pc(c): with one k-group, the k range
+  // rotated by a per-block offset, so that the blocks streaming at the same
+  // moment read different offsets within their W rows rather than all the
+  // same one (measured at N = 64, d = 8192, V = 128256: 313.0 -> 310.4 us).
+  // It also sets the order in which the block's k-steps are summed.  With
+  // several k-groups the blocks of a group keep reading the same X chunk at
+  // the same time, which the XCD's L2 then serves once (rotated there, the
+  // scattered X reads missed in L2: 86.9 against 79.7 us at N = 64 on
+  // 28672 -> 8192, 108.8 against 98.2 us at N = 128).
+  const int krot = c1 > c0 && ngroups == 1 ? (vb * 37) % (c1 - c0) : 0;
   auto pc = [&](int c) {
     const int q = c - c0 + krot;
     return c0 + (q >= c1 - c0 ? q - (c1 - c0) : q);
