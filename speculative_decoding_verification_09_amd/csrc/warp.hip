@@ -379,9 +379,9 @@ __device__ __forceinline__ float key_floor_value(uint32_t t) {
 // histogram of masses at 11-bit resolution (4096 bins of 2^11 keys).  The
 // bin where the running mass from the top reaches the target is compacted
 // into LDS and the cut found among its entries, as select_cut's last step
-// does.  The same pass also sums the warped statistics' terms of the entries
-// above that bin (all of them kept), and those of the kept candidates are
-// added after the cut: zpart is this thread's share of Z (the terms as the
+// does.  That compacting pass also sums the warped statistics' terms of the
+// entries above the bin (all of them kept), and those of the kept candidates
+// are added after the cut: zpart is this thread's share of Z (the terms as the
 // statistics pass forms them, in another order).  Returns false (LDS changed,
 // nothing else) when the cut lies outside the window or its bin holds more
 // than kCap entries; the full passes then run.
